@@ -1,0 +1,193 @@
+"""ctypes binding over libkda.so (the C ABI declared in include/kda.h).
+
+Argument marshalling only: this module allocates output tensors with torch,
+checks that tensors are contiguous CUDA tensors of the right dtype, and passes
+raw device pointers and the current stream to the library.  Every step of the
+computation runs in the library's HIP kernels.  If the library is missing,
+every entry point raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_F32 = 0
+KDA_BF16 = 1
+_IO = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    """A non-OK kda_status returned by the library."""
+
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libkda.so once (in-tree build).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} is missing: build it with `python -m gated_delta_rule_112_amd.build` "
+            "(hipcc, gfx950). The KDA ops have no fallback.")
+    lib = ctypes.CDLL(p)
+    vp, f32, i64, ci = ctypes.c_void_p, ctypes.c_float, ctypes.c_int64, ctypes.c_int
+    lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32,
+                                  i64, i64, i64, ci, ci, f32, ci, vp]
+    lib.kda_chunk_fwd.restype = ci
+    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32,
+                                    i64, i64, ci, ci, f32, ci, vp]
+    lib.kda_decode_step.restype = ci
+    lib.kda_gate_rmsnorm.argtypes = [vp, vp, vp, vp, i64, ci, f32, ci, vp]
+    lib.kda_gate_rmsnorm.restype = ci
+    lib.kda_status_string.argtypes = [ci]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_version.argtypes = []
+    lib.kda_version.restype = ci
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(lib, fn: str, status: int):
+    if status != 0:
+        raise KDAError(fn, status, lib.kda_status_string(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def chunk_fwd(q, k, v, g, beta, s0=None, *, scale: float = 1.0, gate=None, norm_w=None,
+              eps: float = 1e-6, output: bool = True, final_state: bool = True,
+              out=None, s_out=None, stream=None) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """Prefill over [B, T, H, *] tensors; returns (o or y, final state).
+
+    ``output=False`` computes the final state only; ``s_out`` may be ``s0``
+    for an in-place state update.
+    """
+    lib = load_library()
+    if q.device.type != "cuda":
+        raise ValueError("kda ops need CUDA (HIP) tensors")
+    dev = q.device
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    io = q.dtype
+    if io not in _IO:
+        raise TypeError(f"unsupported io dtype {io}")
+    _need(q, "q", io, (B, T, H, dk), dev)
+    _need(k, "k", io, (B, T, H, dk), dev)
+    _need(v, "v", io, (B, T, H, dv), dev)
+    _need(g, "g", torch.float32, (B, T, H, dk), dev)
+    _need(beta, "beta", torch.float32, (B, T, H), dev)
+    if s0 is not None:
+        _need(s0, "s0", torch.float32, (B, H, dk, dv), dev)
+    if gate is not None:
+        _need(gate, "gate", io, (B, T, H, dv), dev)
+    if norm_w is not None:
+        _need(norm_w, "norm_w", torch.float32, (dv,), dev)
+    if output and out is None:
+        out = torch.empty((B, T, H, dv), dtype=io, device=dev)
+    if not output:
+        out = None
+    elif out is not None:
+        _need(out, "out", io, (B, T, H, dv), dev)
+    if final_state and s_out is None:
+        s_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if not final_state:
+        s_out = None
+    elif s_out is not None:
+        _need(s_out, "s_out", torch.float32, (B, H, dk, dv), dev)
+    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(out),
+                           _ptr(s_out), _ptr(gate), _ptr(norm_w), float(eps), B, T, H, dk, dv,
+                           float(scale), _IO[io], _stream(dev, stream))
+    _check(lib, "kda_chunk_fwd", st)
+    return out, s_out
+
+
+def decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, gate=None, norm_w=None,
+                eps: float = 1e-6, out=None, stream=None) -> torch.Tensor:
+    """One token per (b, h) against ``state`` [B, H, dk, dv] (updated in place); returns o."""
+    lib = load_library()
+    if q.device.type != "cuda":
+        raise ValueError("kda ops need CUDA (HIP) tensors")
+    dev = q.device
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    io = q.dtype
+    if io not in _IO:
+        raise TypeError(f"unsupported io dtype {io}")
+    _need(q, "q", io, (B, H, dk), dev)
+    _need(k, "k", io, (B, H, dk), dev)
+    _need(v, "v", io, (B, H, dv), dev)
+    _need(g, "g", torch.float32, (B, H, dk), dev)
+    _need(beta, "beta", torch.float32, (B, H), dev)
+    _need(state, "state", torch.float32, (B, H, dk, dv), dev)
+    if gate is not None:
+        _need(gate, "gate", io, (B, H, dv), dev)
+    if norm_w is not None:
+        _need(norm_w, "norm_w", torch.float32, (dv,), dev)
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=io, device=dev)
+    else:
+        _need(out, "out", io, (B, H, dv), dev)
+    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                             _ptr(out), _ptr(gate), _ptr(norm_w), float(eps), B, H, dk, dv,
+                             float(scale), _IO[io], _stream(dev, stream))
+    _check(lib, "kda_decode_step", st)
+    return out
+
+
+def gate_rmsnorm(x, gate, norm_w=None, *, eps: float = 1e-6, out=None, stream=None) -> torch.Tensor:
+    """Head-wise RMSNorm x sigmoid(gate) over the last axis of ``x``."""
+    lib = load_library()
+    if x.device.type != "cuda":
+        raise ValueError("kda ops need CUDA (HIP) tensors")
+    dev, io = x.device, x.dtype
+    if io not in _IO:
+        raise TypeError(f"unsupported io dtype {io}")
+    dv = x.shape[-1]
+    rows = x.numel() // dv
+    _need(x, "x", io, x.shape, dev)
+    _need(gate, "gate", io, x.shape, dev)
+    if norm_w is not None:
+        _need(norm_w, "norm_w", torch.float32, (dv,), dev)
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _need(out, "out", io, x.shape, dev)
+    st = lib.kda_gate_rmsnorm(_ptr(x), _ptr(gate), _ptr(norm_w), _ptr(out), rows, dv, float(eps),
+                              _IO[io], _stream(dev, stream))
+    _check(lib, "kda_gate_rmsnorm", st)
+    return out

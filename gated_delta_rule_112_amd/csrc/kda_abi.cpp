@@ -1,0 +1,156 @@
+// C ABI of the KDA layer core: host-side argument validation and dispatch.
+//
+// Every check runs before any HIP call, so a rejected call launches nothing
+// and touches no output.  The entry points and their contracts are declared
+// and documented in include/kda.h.
+#include "kda.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "kda_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 60;
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+  const void* p;
+  int64_t bytes;
+};
+
+bool overlap(Span a, Span b) {
+  if (a.p == nullptr || b.p == nullptr || a.bytes <= 0 || b.bytes <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + (uintptr_t)b.bytes && b0 < a0 + (uintptr_t)a.bytes;
+}
+
+// a * b * c * d without overflow past kMaxElems; returns -1 on overflow.
+int64_t prod(int64_t a, int64_t b, int64_t c = 1, int64_t d = 1) {
+  int64_t r = 1;
+  for (int64_t x : {a, b, c, d}) {
+    if (x <= 0) return -1;
+    if (r > kMaxElems / x) return -1;
+    r *= x;
+  }
+  return r;
+}
+
+bool force_valu() {
+  const char* e = getenv("KDA_FORCE_VALU");
+  return e != nullptr && e[0] == '1';
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_NULL_POINTER: return "KDA_ERR_NULL_POINTER: a required pointer is NULL";
+    case KDA_ERR_BAD_SHAPE: return "KDA_ERR_BAD_SHAPE: a size is < 1 or the tensor is too large";
+    case KDA_ERR_UNSUPPORTED_DIM: return "KDA_ERR_UNSUPPORTED_DIM: dk and dv must be 16, 32, 64 or 128";
+    case KDA_ERR_BAD_DTYPE: return "KDA_ERR_BAD_DTYPE: io dtype must be KDA_F32 or KDA_BF16";
+    case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED: pointers must be 16-byte aligned";
+    case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
+    case KDA_ERR_BAD_ARGUMENT: return "KDA_ERR_BAD_ARGUMENT: eps or scale is not finite, or eps < 0";
+    case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+int kda_version(void) { return 100; }
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* s0, void* o, float* s_out,
+                         const void* gate, const float* norm_w, float eps, int64_t B, int64_t T,
+                         int64_t H, int dk, int dv, float scale, kda_dtype io, void* stream) {
+  if (!q || !k || !v || !g || !beta) return KDA_ERR_NULL_POINTER;
+  if (!o && !s_out) return KDA_ERR_NULL_POINTER;
+  if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_BAD_DTYPE;
+  if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED_DIM;
+  const int64_t nqk = prod(B, T, H, dk), nv = prod(B, T, H, dv), nb = prod(B, T, H);
+  const int64_t ns = prod(B, H, dk, dv);
+  if (nqk < 0 || nv < 0 || nb < 0 || ns < 0) return KDA_ERR_BAD_SHAPE;
+  if (B * H > 0x7fffffffLL) return KDA_ERR_BAD_SHAPE;  // one workgroup per (b, h)
+  if (!isfinite(scale) || !isfinite(eps) || eps < 0.f) return KDA_ERR_BAD_ARGUMENT;
+  for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)g,
+                        (const void*)beta, (const void*)s0, (const void*)o, (const void*)s_out,
+                        (const void*)gate, (const void*)norm_w})
+    if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+
+  const int64_t es = (io == KDA_BF16) ? 2 : 4;
+  const Span sq{q, nqk * es}, sk{k, nqk * es}, sv{v, nv * es}, sg{g, nqk * 4}, sb{beta, nb * 4};
+  const Span ss0{s0, ns * 4}, so{o, nv * es}, sso{s_out, ns * 4}, sgt{gate, nv * es};
+  const Span sw{norm_w, (int64_t)dv * 4};
+  for (Span in : {sq, sk, sv, sg, sb, ss0, sgt, sw, sso})
+    if (overlap(so, in)) return KDA_ERR_ALIAS;
+  for (Span in : {sq, sk, sv, sg, sb, sgt, sw})
+    if (overlap(sso, in)) return KDA_ERR_ALIAS;
+  if (overlap(sso, ss0) && (const void*)s_out != (const void*)s0) return KDA_ERR_ALIAS;
+
+  kda::ChunkArgs a{q, k, v, g, beta, s0, o, s_out, gate, norm_w, eps,
+                   B, T, H, dk, dv, scale, io == KDA_BF16, stream};
+  hipError_t err;
+  if (!force_valu() && kda::chunk_mfma_supports(a))
+    err = kda::launch_chunk_mfma(a);
+  else
+    err = kda::launch_chunk_valu(a);
+  return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, float* state, void* o, const void* gate,
+                           const float* norm_w, float eps, int64_t B, int64_t H, int dk, int dv,
+                           float scale, kda_dtype io, void* stream) {
+  if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL_POINTER;
+  if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_BAD_DTYPE;
+  if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED_DIM;
+  const int64_t nqk = prod(B, H, dk), nv = prod(B, H, dv), nb = prod(B, H);
+  const int64_t ns = prod(B, H, dk, dv);
+  if (nqk < 0 || nv < 0 || nb < 0 || ns < 0) return KDA_ERR_BAD_SHAPE;
+  if (nb > 0x7fffffffLL) return KDA_ERR_BAD_SHAPE;
+  if (!isfinite(scale) || !isfinite(eps) || eps < 0.f) return KDA_ERR_BAD_ARGUMENT;
+  for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)g,
+                        (const void*)beta, (const void*)state, (const void*)o, (const void*)gate,
+                        (const void*)norm_w})
+    if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+
+  const int64_t es = (io == KDA_BF16) ? 2 : 4;
+  const Span sq{q, nqk * es}, sk{k, nqk * es}, sv{v, nv * es}, sg{g, nqk * 4}, sb{beta, nb * 4};
+  const Span sst{state, ns * 4}, so{o, nv * es}, sgt{gate, nv * es}, sw{norm_w, (int64_t)dv * 4};
+  for (Span in : {sq, sk, sv, sg, sb, sst, sgt, sw})
+    if (overlap(so, in)) return KDA_ERR_ALIAS;
+  for (Span in : {sq, sk, sv, sg, sb, sgt, sw})
+    if (overlap(sst, in)) return KDA_ERR_ALIAS;
+
+  kda::DecodeArgs a{q, k, v, g, beta, state, o, gate, norm_w, eps,
+                    B, H, dk, dv, scale, io == KDA_BF16, stream};
+  return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status kda_gate_rmsnorm(const void* x, const void* gate, const float* norm_w, void* y,
+                            int64_t rows, int dv, float eps, kda_dtype io, void* stream) {
+  if (!x || !gate || !y) return KDA_ERR_NULL_POINTER;
+  if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_BAD_DTYPE;
+  if (!dim_ok(dv)) return KDA_ERR_UNSUPPORTED_DIM;
+  const int64_t n = prod(rows, dv);
+  if (n < 0) return KDA_ERR_BAD_SHAPE;
+  if (!isfinite(eps) || eps < 0.f) return KDA_ERR_BAD_ARGUMENT;
+  for (const void* p : {x, gate, (const void*)norm_w, (const void*)y})
+    if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+  const int64_t es = (io == KDA_BF16) ? 2 : 4;
+  const Span sx{x, n * es}, sgt{gate, n * es}, sy{y, n * es}, sw{norm_w, (int64_t)dv * 4};
+  if (overlap(sy, sgt) || overlap(sy, sw)) return KDA_ERR_ALIAS;
+  if (overlap(sy, sx) && x != y) return KDA_ERR_ALIAS;
+  kda::NormArgs a{x, gate, norm_w, y, rows, dv, eps, io == KDA_BF16, stream};
+  return kda::launch_gate_rmsnorm(a) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // extern "C"

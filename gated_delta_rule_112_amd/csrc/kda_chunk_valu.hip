@@ -1,0 +1,241 @@
+// KDA chunked prefill in plain float32 vector arithmetic.
+//
+// This kernel serves the float32 io dtype (whose results must agree with the
+// float64 recurrence to 1e-4 of the output RMS, beyond what bfloat16 matrix
+// operands allow) and every head size the matrix-core kernel does not cover.
+// It uses the same chunkwise algebra as the matrix-core kernel, one 16-token
+// tile at a time ("Kimi K3: Engineering ...", section "Dimension 1": 16-token
+// tiles whose cumulative log-decay stays in (-80, 0)).  For a tile of n tokens
+// with start state S0, Gamma = in-tile inclusive cumsum of g:
+//   Khat = k e^{Gamma}, Kchk = k e^{-Gamma}, Qhat = q e^{Gamma}
+//   A    = strict_lower(Diag(beta) Khat Kchk^T),  T = (I + A)^{-1} Diag(beta)
+//   W    = T Khat,  U = T V,  Delta = U - W S0
+//   O    = Qhat S0 + lower(Qhat Kchk^T) Delta
+//   S_n  = Diag(e^{Gamma_n}) (S0 + Kchk^T Delta)
+// A partial last tile is padded with g = 0, beta = 0, k = q = v = 0 tokens,
+// which leave the state unchanged.
+//
+// One workgroup of 128 threads owns one (b, h); thread j < DV keeps column j of
+// the state (DK floats) in registers for the whole sequence.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+constexpr int kTile = 16;
+constexpr int kValuThreads = 128;
+
+template <int DK, int DV, typename IO>
+__global__ void __launch_bounds__(kValuThreads)
+kda_chunk_valu_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
+                      const float* __restrict__ g, const float* __restrict__ beta,
+                      const float* __restrict__ s0, IO* __restrict__ o, float* __restrict__ s_out,
+                      const IO* __restrict__ gate, const float* __restrict__ norm_w, float eps,
+                      int64_t T, int64_t H, float scale) {
+  constexpr int C = kTile;
+  __shared__ float sQh[C][DK];
+  __shared__ float sKh[C][DK];
+  __shared__ float sKc[C][DK];
+  __shared__ float sV[C][DV];  // V until W/U are formed, then the tile output O
+  __shared__ float sW[C][DK];
+  __shared__ float sU[C][DV];
+  float (*sO)[DV] = sV;
+  __shared__ float sAkk[C][C];
+  __shared__ float sAqk[C][C];
+  __shared__ float sT[C][C];
+  __shared__ float sB[C];
+  __shared__ float sEn[DK];
+  __shared__ float sRms[C];
+
+  const int tid = threadIdx.x;
+  const int64_t b = blockIdx.x / H;
+  const int64_t h = blockIdx.x % H;
+  const int64_t bh = blockIdx.x;
+  // Token t of this head: element offsets into [B, T, H, *] tensors.
+  auto tok = [&](int64_t t) { return (b * T + t) * H + h; };
+
+  float S[DK];
+  if (tid < DV) {
+#pragma unroll
+    for (int i = 0; i < DK; ++i)
+      S[i] = s0 ? s0[(bh * DK + i) * DV + tid] : 0.f;
+  }
+
+  for (int64_t c0 = 0; c0 < T; c0 += C) {
+    const int n = (int)((T - c0) < C ? (T - c0) : C);
+
+    // 1. Load the tile, padding past the end of the sequence.
+    for (int e = tid; e < C * DK; e += kValuThreads) {
+      const int t = e / DK, c = e % DK;
+      float qq = 0.f, kk = 0.f, gg = 0.f;
+      if (t < n) {
+        const int64_t off = tok(c0 + t) * DK + c;
+        qq = ld_f32(q + off);
+        kk = ld_f32(k + off);
+        gg = g[off];
+      }
+      sQh[t][c] = qq;
+      sKh[t][c] = kk;
+      sKc[t][c] = gg;  // holds g until step 2
+    }
+    for (int e = tid; e < C * DV; e += kValuThreads) {
+      const int t = e / DV, j = e % DV;
+      sV[t][j] = (t < n) ? ld_f32(v + tok(c0 + t) * DV + j) : 0.f;
+    }
+    if (tid < C) sB[tid] = (tid < n) ? beta[tok(c0 + tid)] : 0.f;
+    __syncthreads();
+
+    // 2. In-tile cumulative log-decay and the rescaled operands, per channel.
+    for (int c = tid; c < DK; c += kValuThreads) {
+      float gam = 0.f;
+      float gams[C];
+#pragma unroll
+      for (int t = 0; t < C; ++t) {
+        gam += sKc[t][c];
+        gams[t] = gam;
+      }
+      const float gn = gam;
+      sEn[c] = expf(gn);
+#pragma unroll
+      for (int t = 0; t < C; ++t) {
+        const float kk = sKh[t][c];
+        const float e = expf(gams[t]);
+        sQh[t][c] = sQh[t][c] * e;
+        sKh[t][c] = kk * e;
+        sKc[t][c] = kk * expf(-gams[t]);
+      }
+    }
+    __syncthreads();
+
+    // 3. Intra-tile products: A = strict_lower(Diag(beta) Khat Kchk^T), Aqk = lower(Qhat Kchk^T).
+    for (int e = tid; e < C * C; e += kValuThreads) {
+      const int i = e / C, j = e % C;
+      float akk = 0.f, aqk = 0.f;
+      if (j <= i) {
+        for (int c = 0; c < DK; ++c) {
+          akk += sKh[i][c] * sKc[j][c];
+          aqk += sQh[i][c] * sKc[j][c];
+        }
+      }
+      sAkk[i][j] = (j < i) ? sB[i] * akk : 0.f;
+      sAqk[i][j] = (j <= i) ? aqk : 0.f;
+    }
+    __syncthreads();
+
+    // 4. T = (I + A)^{-1} Diag(beta): forward substitution, one column per thread.
+    if (tid < C) {
+      const int j = tid;
+      float x[C];
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        float acc = (i == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < i; ++m) acc -= sAkk[i][m] * x[m];
+        x[i] = acc;
+      }
+#pragma unroll
+      for (int i = 0; i < C; ++i) sT[i][j] = x[i] * sB[j];
+    }
+    __syncthreads();
+
+    // 5. W = T Khat, U = T V.
+    for (int e = tid; e < C * DK; e += kValuThreads) {
+      const int t = e / DK, c = e % DK;
+      float acc = 0.f;
+#pragma unroll
+      for (int s = 0; s < C; ++s) acc += sT[t][s] * sKh[s][c];
+      sW[t][c] = acc;
+    }
+    for (int e = tid; e < C * DV; e += kValuThreads) {
+      const int t = e / DV, j = e % DV;
+      float acc = 0.f;
+#pragma unroll
+      for (int s = 0; s < C; ++s) acc += sT[t][s] * sV[s][j];
+      sU[t][j] = acc;
+    }
+    __syncthreads();
+
+    // 6. State-dependent part, column j of the state per thread.
+    if (tid < DV) {
+      const int j = tid;
+      float delta[C];
+#pragma unroll
+      for (int t = 0; t < C; ++t) {
+        float ws = 0.f, qs = 0.f;
+#pragma unroll
+        for (int i = 0; i < DK; ++i) {
+          ws += sW[t][i] * S[i];
+          qs += sQh[t][i] * S[i];
+        }
+        delta[t] = sU[t][j] - ws;
+        float ot = qs;
+#pragma unroll
+        for (int s = 0; s <= t; ++s) ot += sAqk[t][s] * delta[s];
+        sO[t][j] = scale * ot;
+      }
+#pragma unroll
+      for (int i = 0; i < DK; ++i) {
+        // Kbar[t][i] = Kchk[t][i] * e^{Gamma_n,i}: both factors finite (|Gamma| < 80).
+        float acc = 0.f;
+#pragma unroll
+        for (int t = 0; t < C; ++t) acc += sKc[t][i] * delta[t];
+        S[i] = sEn[i] * (S[i] + acc);
+      }
+    }
+    __syncthreads();
+
+    // 7. Output, optionally through RMSNorm x sigmoid(gate) over the head's dv vector.
+    if (o != nullptr) {
+      if (gate != nullptr) {
+        if (tid < C) {
+          float ss = 0.f;
+          for (int j = 0; j < DV; ++j) ss += sO[tid][j] * sO[tid][j];
+          sRms[tid] = rsqrtf(ss / (float)DV + eps);
+        }
+        __syncthreads();
+      }
+      for (int e = tid; e < n * DV; e += kValuThreads) {
+        const int t = e / DV, j = e % DV;
+        const int64_t off = tok(c0 + t) * DV + j;
+        float y = sO[t][j];
+        if (gate != nullptr) {
+          const float w = norm_w ? norm_w[j] : 1.f;
+          y = y * sRms[t] * w * sigmoidf_(ld_f32(gate + off));
+        }
+        st_f32(o + off, y);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (s_out != nullptr && tid < DV) {
+#pragma unroll
+    for (int i = 0; i < DK; ++i) s_out[(bh * DK + i) * DV + tid] = S[i];
+  }
+}
+
+template <int DK, int DV, typename IO>
+static hipError_t launch_valu_t(const ChunkArgs& a) {
+  hipLaunchKernelGGL((kda_chunk_valu_kernel<DK, DV, IO>), dim3((unsigned)(a.B * a.H)),
+                     dim3(kValuThreads), 0, (hipStream_t)a.stream, (const IO*)a.q, (const IO*)a.k,
+                     (const IO*)a.v, a.g, a.beta, a.s0, (IO*)a.o, a.s_out, (const IO*)a.gate,
+                     a.norm_w, a.eps, a.T, a.H, a.scale);
+  return hipGetLastError();
+}
+
+template <typename IO>
+static hipError_t dispatch_valu(const ChunkArgs& a) {
+#define KDA_CASE(DKV, DVV) \
+  if (a.dk == DKV && a.dv == DVV) return launch_valu_t<DKV, DVV, IO>(a);
+#define KDA_ROW(DKV) KDA_CASE(DKV, 16) KDA_CASE(DKV, 32) KDA_CASE(DKV, 64) KDA_CASE(DKV, 128)
+  KDA_ROW(16) KDA_ROW(32) KDA_ROW(64) KDA_ROW(128)
+#undef KDA_ROW
+#undef KDA_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_valu(const ChunkArgs& a) {
+  return a.io_bf16 ? dispatch_valu<bf16_t>(a) : dispatch_valu<float>(a);
+}
+
+}  // namespace kda

@@ -1,0 +1,66 @@
+// Internal launch interface between the C ABI (kda_abi.cpp) and the kernels.
+// Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct ChunkArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const float* s0;
+  void* o;
+  float* s_out;
+  const void* gate;
+  const float* norm_w;
+  float eps;
+  int64_t B, T, H;
+  int dk, dv;
+  float scale;
+  bool io_bf16;
+  void* stream;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  float* state;
+  void* o;
+  const void* gate;
+  const float* norm_w;
+  float eps;
+  int64_t B, H;
+  int dk, dv;
+  float scale;
+  bool io_bf16;
+  void* stream;
+};
+
+struct NormArgs {
+  const void* x;
+  const void* gate;
+  const float* norm_w;
+  void* y;
+  int64_t rows;
+  int dv;
+  float eps;
+  bool io_bf16;
+  void* stream;
+};
+
+hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_chunk_valu(const ChunkArgs& a);
+// Returns hipErrorNotSupported when the matrix-core kernel does not cover the shape.
+hipError_t launch_chunk_mfma(const ChunkArgs& a);
+bool chunk_mfma_supports(const ChunkArgs& a);
+hipError_t launch_gate_rmsnorm(const NormArgs& a);
+
+}  // namespace kda

@@ -1,0 +1,150 @@
+/*
+ * kda.h -- C ABI of the Kimi Delta Attention (KDA) layer core for AMD MI355X (gfx950).
+ *
+ * What the library computes (one head of one sequence; every (b, h) pair is
+ * independent):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ *
+ * with S in R^{dk x dv} (rows are key channels), g_t in R^dk the per-channel
+ * log-decay and beta_t a scalar write strength.  Sources:
+ *   - "Kimi K3 from Moonshot AI: 2.8 Trillion Parameters Unveiled", section
+ *     "Kimi Delta Attention (KDA)": delta rule on the generalized Householder
+ *     transformation; chunkwise ("piecewise parallel") reformulation.
+ *   - "Kimi K3 Architecture Explained: KDA, Attention Residuals and LatentMoE",
+ *     section "Token mixing: what KDA is and why 3:1": fixed-size recurrent
+ *     state, error-correcting write, per-channel forget gate, output gate after
+ *     a head-wise RMSNorm, constant per-token decode cost.
+ *   - "Kimi K3: Engineering a 2.8 Trillion Parameter Frontier", section
+ *     "Dimension 1: Sequence Length via Hybrid KDA-Gated MLA": log-decay
+ *     bounded below by -5 through a scaled sigmoid, 16-token tiles whose
+ *     cumulative log-decay stays in (-80, 0), dense matrix products on every
+ *     causal tile.
+ *
+ * Conventions for every entry point:
+ *   - All tensor arguments are DEVICE pointers owned by the caller, contiguous,
+ *     row-major, in the layouts given per argument.  The library never
+ *     allocates, frees or keeps a pointer after the call returns.
+ *   - q, k, v, o, gate (and x, y) are in the io dtype (kda_dtype); g, beta,
+ *     states and norm weights are always float32.
+ *   - Every call is asynchronous on `stream` (NULL = the default stream).
+ *     Arguments are validated on the host first; a non-OK status is returned
+ *     BEFORE anything is launched, and no output is touched.  KDA_ERR_LAUNCH
+ *     means the runtime refused the launch.  Faults inside a kernel surface at
+ *     the caller's next synchronisation.
+ *   - The library keeps no state between calls, never prints, and is safe to
+ *     call from several host threads.
+ *   - Supported head sizes: dk, dv in {16, 32, 64, 128}; any other value gives
+ *     KDA_ERR_UNSUPPORTED_DIM.  Sizes B, T, H must be >= 1 (T >= 1); element
+ *     offsets are 64-bit, so tensors above 2^31 elements are fine.
+ *   - Precondition (documented, not checked): -5 <= g <= 0, as produced by
+ *     g = -5 * sigmoid(.).  The chunked prefill relies on a 16-token sum of g
+ *     staying above -80 so that exp(-sum) stays finite in float32/bfloat16.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL_POINTER = 1,      /* a required pointer is NULL                         */
+  KDA_ERR_BAD_SHAPE = 2,         /* B, T, H or rows < 1, or a size product overflows   */
+  KDA_ERR_UNSUPPORTED_DIM = 3,   /* dk or dv not in {16, 32, 64, 128}                  */
+  KDA_ERR_BAD_DTYPE = 4,         /* io dtype not a kda_dtype value                     */
+  KDA_ERR_MISALIGNED = 5,        /* a pointer is not 16-byte aligned                   */
+  KDA_ERR_ALIAS = 6,             /* an output overlaps an input it may not overlap     */
+  KDA_ERR_BAD_ARGUMENT = 7,      /* a scalar argument is not finite or out of range    */
+  KDA_ERR_LAUNCH = 8             /* the HIP runtime rejected a kernel launch           */
+} kda_status;
+
+typedef enum {
+  KDA_F32 = 0,   /* float32 q, k, v, o, gate: float32 arithmetic throughout            */
+  KDA_BF16 = 1   /* bfloat16 q, k, v, o, gate: float32 accumulation, fp32 state        */
+} kda_dtype;
+
+/*
+ * kda_chunk_fwd -- prefill: run the recurrence over T tokens for B x H heads.
+ *
+ * Computed chunkwise in 16-token tiles ("Kimi K3: Engineering ...", section
+ * "Dimension 1"); the result equals the token-by-token recurrence up to
+ * floating-point rounding.  The running state lives on chip for the whole
+ * sequence; only the final state is written.
+ *
+ *   q     [B, T, H, dk]  io dtype   queries
+ *   k     [B, T, H, dk]  io dtype   keys (the method expects unit L2 norm; not checked)
+ *   v     [B, T, H, dv]  io dtype   values
+ *   g     [B, T, H, dk]  float32    log-decay, alpha = exp(g)
+ *   beta  [B, T, H]      float32    write strength
+ *   s0    [B, H, dk, dv] float32    initial state, or NULL for a zero state
+ *   o     [B, T, H, dv]  io dtype   output, or NULL to compute the final state only.
+ *                                   With gate != NULL, o receives the epilogue
+ *                                   result y (see kda_gate_rmsnorm) instead of raw o.
+ *   s_out [B, H, dk, dv] float32    final state, or NULL.  May equal s0 (in place);
+ *                                   any other overlap with an input is KDA_ERR_ALIAS.
+ *   gate  [B, T, H, dv]  io dtype   output-gate logits, or NULL for no epilogue
+ *   norm_w [dv]          float32    RMSNorm weight, or NULL for a unit weight
+ *   eps                             RMSNorm epsilon (> = 0, finite)
+ *   scale                           output scale (finite)
+ *   o and s_out may not both be NULL.  o may not overlap any input.
+ *   All pointers must be 16-byte aligned.
+ */
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const float* s0,
+                         void* o, float* s_out,
+                         const void* gate, const float* norm_w, float eps,
+                         int64_t B, int64_t T, int64_t H, int dk, int dv,
+                         float scale, kda_dtype io, void* stream);
+
+/*
+ * kda_decode_step -- one token per sequence against a resident state.
+ *
+ * The constant-cost recurrent step ("Kimi K3 Architecture Explained ...",
+ * section "Token mixing"): for every (b, h), with a = exp(g),
+ *   p = (Diag(a) S)^T k,  u = beta (v - p),  S <- Diag(a) S + k u^T,  o = scale S^T q.
+ * The state is read and written exactly once, in place.
+ *
+ *   q, k  [B, H, dk]     io dtype
+ *   v     [B, H, dv]     io dtype
+ *   g     [B, H, dk]     float32
+ *   beta  [B, H]         float32
+ *   state [B, H, dk, dv] float32    read and updated in place
+ *   o     [B, H, dv]     io dtype   output (y when gate != NULL); must not be NULL
+ *   gate  [B, H, dv]     io dtype   or NULL;  norm_w [dv] float32 or NULL;  eps, scale as above
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, float* state,
+                           void* o, const void* gate, const float* norm_w, float eps,
+                           int64_t B, int64_t H, int dk, int dv,
+                           float scale, kda_dtype io, void* stream);
+
+/*
+ * kda_gate_rmsnorm -- the output epilogue on its own.
+ *
+ * "Kimi K3 Architecture Explained ...", section "Token mixing": the output
+ * gate is applied after a head-wise RMSNorm.  For every row r (one head's dv
+ * vector):  y[r] = x[r] / sqrt(mean(x[r]^2) + eps) * w * sigmoid(gate[r]).
+ *
+ *   x, gate, y [rows, dv]  io dtype  (y may equal x; any other overlap is KDA_ERR_ALIAS)
+ *   norm_w     [dv]        float32, or NULL for a unit weight
+ */
+kda_status kda_gate_rmsnorm(const void* x, const void* gate, const float* norm_w, void* y,
+                            int64_t rows, int dv, float eps, kda_dtype io, void* stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* kda_status_string(kda_status s);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,140 @@
+"""Host-side checks of the C ABI that need no GPU.
+
+The library must load, export every function declared in include/kda.h, and
+reject bad arguments on the host before any HIP call.  Pointers used here are
+fake addresses: every call below fails validation, so nothing is launched and
+no pointer is dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, NULLP, SHAPE, DIM, DTYPE, ALIGN, ALIAS, ARG = 0, 1, 2, 3, 4, 5, 6, 7
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from gated_delta_rule_112_amd import load_library
+    return load_library()
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ["kda_chunk_fwd", "kda_decode_step", "kda_gate_rmsnorm", "kda_status_string",
+              "kda_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"libkda.so lacks {missing}"
+
+
+def test_status_strings(lib):
+    for s in range(0, 9):
+        assert lib.kda_status_string(s)
+    assert lib.kda_status_string(0) == b"KDA_OK"
+    assert b"UNKNOWN" in lib.kda_status_string(99)
+    assert lib.kda_version() >= 100
+
+
+# Fake, distinct, 16-byte aligned device addresses far apart from each other.
+BASE = 1 << 40
+
+
+def P(i, off=0):
+    return ctypes.c_void_p(BASE + (i << 34) + off)
+
+
+def chunk(lib, *, q=1, k=2, v=3, g=4, beta=5, s0=None, o=6, s_out=7, gate=None, w=None,
+          eps=1e-6, B=1, T=16, H=1, dk=16, dv=16, scale=1.0, io=1, override=None):
+    ptrs = dict(q=q, k=k, v=v, g=g, beta=beta, s0=s0, o=o, s_out=s_out, gate=gate, w=w)
+    args = {n: (None if x is None else P(x)) for n, x in ptrs.items()}
+    if override:
+        args.update(override)
+    return lib.kda_chunk_fwd(args["q"], args["k"], args["v"], args["g"], args["beta"], args["s0"],
+                             args["o"], args["s_out"], args["gate"], args["w"], eps, B, T, H, dk,
+                             dv, scale, io, None)
+
+
+def test_chunk_null_pointers(lib):
+    for name in ["q", "k", "v", "g", "beta"]:
+        assert chunk(lib, dk=48, **{name: None}) == NULLP
+    assert chunk(lib, o=None, s_out=None) == NULLP
+
+
+def test_chunk_shapes_dims_dtypes(lib):
+    assert chunk(lib, dk=48) == DIM
+    assert chunk(lib, dv=256) == DIM
+    assert chunk(lib, dk=48, io=2) == DTYPE  # dtype checked before dims
+    assert chunk(lib, io=7, dk=16) == DTYPE
+    assert chunk(lib, B=0) == SHAPE
+    assert chunk(lib, T=0) == SHAPE
+    assert chunk(lib, H=-1) == SHAPE
+    assert chunk(lib, B=1 << 30, T=1 << 30, H=1 << 10) == SHAPE
+
+
+def test_chunk_scalars(lib):
+    assert chunk(lib, eps=-1.0) == ARG
+    assert chunk(lib, eps=float("nan")) == ARG
+    assert chunk(lib, scale=float("inf")) == ARG
+
+
+def test_chunk_alignment(lib):
+    assert chunk(lib, override={"q": P(1, 2)}) == ALIGN
+    assert chunk(lib, override={"o": P(6, 8)}) == ALIGN
+    assert chunk(lib, override={"s0": P(9, 4)}) == ALIGN
+
+
+def test_chunk_aliasing(lib):
+    assert chunk(lib, o=1) == ALIAS                 # o == q
+    assert chunk(lib, s_out=2) == ALIAS             # s_out == k
+    assert chunk(lib, o=7, s_out=7) == ALIAS        # o == s_out
+    assert chunk(lib, gate=8, o=8) == ALIAS
+    # s_out == s0 (in place) is allowed (exercised on the GPU); partial overlap is not.
+    assert chunk(lib, s0=9, override={"s_out": P(9, 16)}) == ALIAS
+
+
+def decode(lib, *, q=1, k=2, v=3, g=4, beta=5, state=6, o=7, gate=None, w=None, eps=1e-6,
+           B=1, H=1, dk=16, dv=16, scale=1.0, io=1, override=None):
+    ptrs = dict(q=q, k=k, v=v, g=g, beta=beta, state=state, o=o, gate=gate, w=w)
+    args = {n: (None if x is None else P(x)) for n, x in ptrs.items()}
+    if override:
+        args.update(override)
+    return lib.kda_decode_step(args["q"], args["k"], args["v"], args["g"], args["beta"],
+                               args["state"], args["o"], args["gate"], args["w"], eps, B, H, dk,
+                               dv, scale, io, None)
+
+
+def test_decode_validation(lib):
+    for name in ["q", "k", "v", "g", "beta", "state", "o"]:
+        assert decode(lib, **{name: None}) == NULLP
+    assert decode(lib, dk=100) == DIM
+    assert decode(lib, io=3) == DTYPE
+    assert decode(lib, B=0) == SHAPE
+    assert decode(lib, eps=-0.5) == ARG
+    assert decode(lib, override={"state": P(6, 4)}) == ALIGN
+    assert decode(lib, o=6) == ALIAS       # o == state
+    assert decode(lib, state=1) == ALIAS   # state == q
+
+
+def test_gate_rmsnorm_validation(lib):
+    f = lib.kda_gate_rmsnorm
+    assert f(None, P(2), None, P(3), 4, 16, 1e-6, 1, None) == NULLP
+    assert f(P(1), P(2), None, P(3), 0, 16, 1e-6, 1, None) == SHAPE
+    assert f(P(1), P(2), None, P(3), 4, 24, 1e-6, 1, None) == DIM
+    assert f(P(1), P(2), None, P(3), 4, 16, -1.0, 1, None) == ARG
+    assert f(P(1), P(2), None, P(2), 4, 16, 1e-6, 1, None) == ALIAS       # y == gate
+    assert f(P(1), P(2), None, P(1, 16), 4, 16, 1e-6, 1, None) == ALIAS  # partial y/x overlap
+    assert f(P(1, 4), P(2), None, P(3), 4, 16, 1e-6, 1, None) == ALIGN

@@ -1,0 +1,47 @@
+"""Seeded input generators: determinism, shapes and the stated distributions."""
+import torch
+
+from gated_delta_rule_112_amd.inputs import (WORKLOADS, Workload, make_decode_state,
+                                             make_decode_step_inputs, make_prefill_inputs)
+
+
+def test_prefill_inputs_deterministic_and_shaped():
+    w = Workload("t", B=2, H=3, T=37, dk=16, dv=32, io="bf16", g_std=2.0, s0_std=0.02, gate=True,
+                 seed=5)
+    a = make_prefill_inputs(w)
+    b = make_prefill_inputs(w)
+    for key in ["q", "k", "v", "g", "beta", "s0", "gate"]:
+        assert torch.equal(a[key], b[key]), key
+    assert a["q"].shape == (2, 37, 3, 16) and a["q"].dtype == torch.bfloat16
+    assert a["v"].shape == (2, 37, 3, 32)
+    assert a["g"].dtype == torch.float32 and a["beta"].shape == (2, 37, 3)
+    assert a["s0"].shape == (2, 3, 16, 32)
+    assert float(a["g"].max()) < 0 and float(a["g"].min()) > -5.0
+    assert float(a["beta"].min()) > 0 and float(a["beta"].max()) < 1
+    norms = a["k"].float().norm(dim=-1)
+    assert torch.allclose(norms, torch.ones_like(norms), atol=1e-2)
+    c = make_prefill_inputs(w, seed=6)
+    assert not torch.equal(a["q"], c["q"])
+
+
+def test_forced_decay_channels():
+    w = WORKLOADS["million_token_prefill"]
+    small = Workload("m", B=1, H=w.H, T=4, dk=w.dk, dv=w.dv, io="bf16",
+                     force_every=w.force_every, forced_g=w.forced_g, seed=w.seed)
+    x = make_prefill_inputs(small)
+    g = x["g"].view(-1, w.H * w.dk)
+    forced = (g == torch.tensor(w.forced_g)).all(dim=0)
+    idx = torch.nonzero(forced).flatten().tolist()
+    assert idx == [j for j in range(w.H * w.dk) if j % 1000 == 0]
+    assert len(idx) == 13
+
+
+def test_decode_inputs():
+    w = Workload("d", B=4, H=2, T=1, dk=32, dv=16, io="bf16", s0_std=0.02, steps=3, seed=9)
+    s = make_decode_state(w)
+    assert s.shape == (4, 2, 32, 16) and abs(float(s.std()) - 0.02) < 0.01
+    x0 = make_decode_step_inputs(w, 0)
+    x1 = make_decode_step_inputs(w, 1)
+    assert x0["q"].shape == (4, 2, 32) and x0["beta"].shape == (4, 2)
+    assert not torch.equal(x0["k"], x1["k"])
+    assert torch.equal(x0["k"], make_decode_step_inputs(w, 0)["k"])
