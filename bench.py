@@ -1,0 +1,339 @@
+"""Throughput of the KDA layer core on one MI355X, with roofline and CPU-oracle context.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one ``kda_chunk_fwd`` call (the whole chunkwise prefill: tile load,
+cumulative log-decay, rescaled operands, intra-tile products, UT solve, WY
+factors, delta correction, outputs, state pass, final state and the fused
+RMSNorm x sigmoid(gate) epilogue) over one batch of seeded synthetic inputs
+already resident in HBM.  The default workload is the full-width layer prefill
+(B=1, H=96, T=32768, dk=dv=128, bf16 q/k/v/gate, fp32 g/beta/state, epilogue
+on).  A second leg times the batched decode workload (B=256, H=96, 64
+successive single-token steps against a 1.6 GB fp32 state) and reports its
+HBM rate in the ``decode`` object of the same JSON line.
+
+Output: ONE JSON line on stdout (progress goes to stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s (H=96,dk=dv=128) + decode GB/s, % MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+F32_PEAK_TFLOPS = 157.3        # MI355X fp32, published
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    # kernel name reported by the library -> source file that defines it
+    "kda_chunk_mfma": "gated_delta_rule_112_amd/csrc/kda_chunk_mfma.hip",
+    "kda_chunk_valu": "gated_delta_rule_112_amd/csrc/kda_chunk_valu.hip",
+    "kda_decode": "gated_delta_rule_112_amd/csrc/kda_decode.hip",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- algorithmic units
+def prefill_bytes(B, T, H, dk, dv, es, with_o=True, with_gate=False, with_s0=False, with_sout=True):
+    """Bytes a prefill must move at least: every input read once, every output
+    written once.  Per token-head: q, k (dk each) and v (dv) in the io dtype,
+    g (dk fp32), beta (fp32), o (dv io) and gate (dv io) when present; per
+    (b, h): the fp32 state in and/or out."""
+    per_tok = (2 * dk + dv) * es + 4 * dk + 4
+    if with_o:
+        per_tok += dv * es
+    if with_gate:
+        per_tok += dv * es
+    per_bh = 4 * dk * dv * (int(with_s0) + int(with_sout))
+    return B * T * H * per_tok + B * H * per_bh, per_tok
+
+
+def prefill_flops(B, T, H, dk, dv, C=16):
+    """Flops of the chunked method per token-head: 6*C*dk + 4*C*dv + 6*dk*dv
+    (intra-tile products, WY factors, delta correction, outputs, state pass)."""
+    return B * T * H * (6 * C * dk + 4 * C * dv + 6 * dk * dv)
+
+
+def decode_bytes(B, H, dk, dv, es, with_gate=False):
+    """Per (b, h) per step: the fp32 state read and written once, q, k, v, o in
+    the io dtype, g fp32, beta fp32 (gate when present)."""
+    per = 8 * dk * dv + (2 * dk + dv) * es + 4 * dk + 4 + dv * es
+    if with_gate:
+        per += dv * es
+    return B * H * per, per
+
+
+# ----------------------------------------------------------------------------- HBM traffic record
+def source_digest(kernel):
+    path = KERNEL_SOURCES.get(kernel)
+    if path is None:
+        return None
+    h = hashlib.sha256()
+    for p in (path, "gated_delta_rule_112_amd/csrc/kda_device.h"):
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter record, or None
+    when there is none or the kernel's source changed since it was taken."""
+    path = os.path.join(PROFILES, "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    e = rec.get(kernel, {}).get(workload)
+    if not e or e.get("source_sha256") != source_digest(kernel):
+        return None
+    return e.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- CPU oracle leg
+def _oracle_worker(args):
+    """Run the float64 oracle on a few heads of a workload-shaped sample."""
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    name, heads, T, seed = args
+    import torch  # CPU only in this process
+    torch.set_num_threads(1)
+    from gated_delta_rule_112_amd.inputs import WORKLOADS, make_prefill_inputs
+    from oracle.kda_oracle import gate_rmsnorm, kda_recurrent
+    import dataclasses
+    w = dataclasses.replace(WORKLOADS[name], B=1, H=heads, T=T)
+    x = make_prefill_inputs(w, device="cpu", seed=seed)
+    f = lambda t: None if t is None else t.double().numpy()  # noqa: E731
+    t0 = time.perf_counter()
+    done = 0
+    for h in range(heads):
+        sl = lambda t: None if t is None else t[:, :, h:h + 1]  # noqa: E731
+        o, _ = kda_recurrent(f(sl(x["q"])), f(sl(x["k"])), f(sl(x["v"])), f(sl(x["g"])),
+                             f(sl(x["beta"])), None if x["s0"] is None else f(x["s0"][:, h:h + 1]))
+        if x["gate"] is not None:
+            gate_rmsnorm(o, f(sl(x["gate"])), None, 1e-6)
+        done += T
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(workload, H, workers, heads_per_worker, T):
+    """Oracle token-heads/s on the host cores, converted to tokens/s of the
+    workload (each token carries H heads)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    ctx = mp.get_context("spawn")
+    jobs = [(workload, heads_per_worker, T, 50_000 + i) for i in range(workers)]
+    t0 = time.perf_counter()
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
+        res = list(ex.map(_oracle_worker, jobs))
+    wall = time.perf_counter() - t0
+    token_heads = sum(r[0] for r in res)
+    busy = max(r[1] for r in res)
+    return {
+        "value": token_heads / busy / H,
+        "unit": "tokens/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": (f"{workers} processes x {heads_per_worker} heads x {T} tokens of the "
+                   f"{workload} distributions (float64 token-by-token recurrence"
+                   f"{' + epilogue' if workload == 'full_width_prefill' else ''}); "
+                   f"rate = token-heads/s / H={H}; slowest worker {busy:.1f} s, wall {wall:.1f} s"),
+    }
+
+
+# ----------------------------------------------------------------------------- GPU legs
+def bench_prefill(kda, torch, w, steps, warmup):
+    from gated_delta_rule_112_amd.inputs import make_prefill_inputs
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {w.name} inputs on the device")
+    x = make_prefill_inputs(w, device=dev)
+    io = x["q"].dtype
+    out = torch.empty((w.B, w.T, w.H, w.dv), dtype=io, device=dev)
+    s_out = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], gate=x["gate"],
+                      out=out, s_out=s_out, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({warmup}); timing {steps} prefill steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del x, out, s_out
+    return ms, io
+
+
+def bench_decode(kda, torch, w, repeats=1):
+    from gated_delta_rule_112_amd.inputs import make_decode_state, make_decode_step_inputs
+    dev = torch.device("cuda:0")
+    log(f"[bench] decode: state {w.B}x{w.H}x{w.dk}x{w.dv} fp32, {w.steps} steps")
+    state = make_decode_state(w, device=dev)
+    xs = [make_decode_step_inputs(w, s, device=dev) for s in range(w.steps)]
+    io = xs[0]["q"].dtype
+    outs = [torch.empty((w.B, w.H, w.dv), dtype=io, device=dev) for _ in range(w.steps)]
+    stream = torch.cuda.current_stream(dev)
+
+    def run(n):
+        for s in range(n):
+            x = xs[s]
+            kda.decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], state, gate=x["gate"],
+                            out=outs[s], stream=stream)
+
+    run(1)  # warm-up step
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run(w.steps)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / w.steps
+        best = ms if best is None else min(best, ms)
+    return best, io
+
+
+def copy_probe(torch, nbytes=1 << 30):
+    """A plain device copy of known size, run once so that a counter pass over
+    this process can scale FETCH_SIZE / WRITE_SIZE against it."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy probe: {nbytes} bytes read, {nbytes} bytes written")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="full_width_prefill",
+                    choices=["small_prefill", "full_width_prefill", "million_token_prefill"])
+    ap.add_argument("--decode-repeats", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads-per-worker", type=int, default=4)
+    ap.add_argument("--cpu-tokens", type=int, default=32768)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a 1 GiB device copy (for counter calibration)")
+    a = ap.parse_args()
+
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the KDA layer core here is a single-GPU "
+              "library (heads and batch shard across GPUs without communication), so "
+              "--gpus must be 1.", file=sys.stderr)
+        sys.exit(2)
+
+    from gated_delta_rule_112_amd.inputs import WORKLOADS
+    w = WORKLOADS[a.workload]
+
+    # The oracle leg runs first, in spawned CPU-only processes, before this
+    # process touches the GPU.
+    cpu = None
+    if not a.no_cpu_baseline:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        log(f"[bench] cpu oracle leg: {workers} workers")
+        cpu = cpu_baseline(a.workload, w.H, workers, a.cpu_heads_per_worker,
+                           min(a.cpu_tokens, w.T))
+        log(f"[bench] cpu oracle: {cpu['value']:.1f} tokens/s")
+
+    import torch
+    import gated_delta_rule_112_amd as kda
+    kda.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (HIP device); none is visible", file=sys.stderr)
+        sys.exit(3)
+
+    if a.copy_probe:
+        copy_probe(torch)
+
+    ms, io = bench_prefill(kda, torch, w, a.steps, a.warmup)
+    es = 2 if io == torch.bfloat16 else 4
+    nbytes, per_tok = prefill_bytes(w.B, w.T, w.H, w.dk, w.dv, es, with_o=True,
+                                    with_gate=w.gate, with_s0=w.s0_std is not None)
+    flops = prefill_flops(w.B, w.T, w.H, w.dk, w.dv)
+    kernel = kda.chunk_kernel_name(w.dk, w.dv, io)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    tokens_per_s = w.B * w.T / (ms * 1e-3)
+    mfma = kernel == "kda_chunk_mfma"
+    roofline = {
+        "bound": "hbm",
+        "kernel": kernel,
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": measured_traffic(kernel, w.name),
+        "algorithmic_bytes_per_launch": nbytes,
+        "bytes_per_token_head": per_tok,
+        "matrix_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "matrix_frac": round(flops / (ms * 1e-3) / 1e12 /
+                             (BF16_PEAK_TFLOPS if mfma else F32_PEAK_TFLOPS), 4),
+    }
+    log(f"[bench] prefill {ms:.3f} ms/step, {tokens_per_s / 1e6:.2f} M tok/s, "
+        f"{achieved:.0f} GB/s ({kernel})")
+
+    decode = None
+    if not a.no_decode:
+        wd = WORKLOADS["batched_decode"]
+        dms, dio = bench_decode(kda, torch, wd, a.decode_repeats)
+        des = 2 if dio == torch.bfloat16 else 4
+        dbytes, dper = decode_bytes(wd.B, wd.H, wd.dk, wd.dv, des, wd.gate)
+        dgbs = dbytes / (dms * 1e-3) / 1e9
+        decode = {
+            "workload": wd.name, "B": wd.B, "H": wd.H, "dk": wd.dk, "dv": wd.dv,
+            "steps": wd.steps, "ms_per_step": round(dms, 4),
+            "tokens_per_s": round(wd.B / (dms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "kernel": "kda_decode", "achieved": round(dgbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(dgbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("kda_decode", wd.name),
+                         "algorithmic_bytes_per_launch": dbytes,
+                         "bytes_per_bh": dper},
+        }
+        log(f"[bench] decode {dms:.4f} ms/step, {dgbs:.0f} GB/s")
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if mfma else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
+                   "chunk": 16, "io": w.io, "epilogue": w.gate,
+                   "initial_state": w.s0_std is not None},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "decode": decode,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -54,6 +54,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_gate_rmsnorm.restype = ci
     lib.kda_status_string.argtypes = [ci]
     lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_chunk_fwd_kernel.argtypes = [ci, ci, ci]
+    lib.kda_chunk_fwd_kernel.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
     lib.kda_version.restype = ci
     if path is None:
@@ -167,6 +169,12 @@ def decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, gate=None, norm_
                              float(scale), _IO[io], _stream(dev, stream))
     _check(lib, "kda_decode_step", st)
     return out
+
+
+def chunk_kernel_name(dk: int, dv: int, dtype) -> Optional[str]:
+    """Name of the prefill kernel the library launches for these sizes and io dtype."""
+    name = load_library().kda_chunk_fwd_kernel(int(dk), int(dv), _IO[dtype])
+    return None if name is None else name.decode()
 
 
 def gate_rmsnorm(x, gate, norm_w=None, *, eps: float = 1e-6, out=None, stream=None) -> torch.Tensor:

@@ -67,6 +67,12 @@ const char* kda_status_string(kda_status s) {
 
 int kda_version(void) { return 100; }
 
+const char* kda_chunk_fwd_kernel(int dk, int dv, kda_dtype io) {
+  if ((io != KDA_F32 && io != KDA_BF16) || !dim_ok(dk) || !dim_ok(dv)) return nullptr;
+  if (!force_valu() && kda::chunk_mfma_supports(dk, dv, io == KDA_BF16)) return "kda_chunk_mfma";
+  return "kda_chunk_valu";
+}
+
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const float* s0, void* o, float* s_out,
                          const void* gate, const float* norm_w, float eps, int64_t B, int64_t T,
@@ -98,7 +104,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   kda::ChunkArgs a{q, k, v, g, beta, s0, o, s_out, gate, norm_w, eps,
                    B, T, H, dk, dv, scale, io == KDA_BF16, stream};
   hipError_t err;
-  if (!force_valu() && kda::chunk_mfma_supports(a))
+  if (!force_valu() && kda::chunk_mfma_supports(dk, dv, io == KDA_BF16))
     err = kda::launch_chunk_mfma(a);
   else
     err = kda::launch_chunk_valu(a);

@@ -60,7 +60,7 @@ hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_chunk_valu(const ChunkArgs& a);
 // Returns hipErrorNotSupported when the matrix-core kernel does not cover the shape.
 hipError_t launch_chunk_mfma(const ChunkArgs& a);
-bool chunk_mfma_supports(const ChunkArgs& a);
+bool chunk_mfma_supports(int dk, int dv, bool io_bf16);
 hipError_t launch_gate_rmsnorm(const NormArgs& a);
 
 }  // namespace kda

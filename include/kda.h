@@ -137,6 +137,14 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
 kda_status kda_gate_rmsnorm(const void* x, const void* gate, const float* norm_w, void* y,
                             int64_t rows, int dv, float eps, kda_dtype io, void* stream);
 
+/*
+ * kda_chunk_fwd_kernel -- which prefill kernel kda_chunk_fwd launches for these
+ * head sizes and io dtype: "kda_chunk_mfma" (bfloat16 matrix cores) or
+ * "kda_chunk_valu" (float32 vector arithmetic), or NULL when the combination is
+ * unsupported.  For profiling and reporting only; static storage.
+ */
+const char* kda_chunk_fwd_kernel(int dk, int dv, kda_dtype io);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* kda_status_string(kda_status s);
 

@@ -138,3 +138,10 @@ def test_gate_rmsnorm_validation(lib):
     assert f(P(1), P(2), None, P(2), 4, 16, 1e-6, 1, None) == ALIAS       # y == gate
     assert f(P(1), P(2), None, P(1, 16), 4, 16, 1e-6, 1, None) == ALIAS  # partial y/x overlap
     assert f(P(1, 4), P(2), None, P(3), 4, 16, 1e-6, 1, None) == ALIGN
+
+
+def test_chunk_kernel_query(lib):
+    lib.kda_chunk_fwd_kernel.restype = ctypes.c_char_p
+    assert lib.kda_chunk_fwd_kernel(16, 16, 0) in (b"kda_chunk_valu", b"kda_chunk_mfma")
+    assert lib.kda_chunk_fwd_kernel(48, 16, 0) is None
+    assert lib.kda_chunk_fwd_kernel(16, 16, 5) is None
