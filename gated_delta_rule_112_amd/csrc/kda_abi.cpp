@@ -17,7 +17,9 @@ constexpr int64_t kMaxElems = int64_t(1) << 60;
 
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
-bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const void* p, uintptr_t bytes) {
+  return p == nullptr || (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0;
+}
 
 struct Span {
   const void* p;
@@ -57,7 +59,7 @@ const char* kda_status_string(kda_status s) {
     case KDA_ERR_BAD_SHAPE: return "KDA_ERR_BAD_SHAPE: a size is < 1 or the tensor is too large";
     case KDA_ERR_UNSUPPORTED_DIM: return "KDA_ERR_UNSUPPORTED_DIM: dk and dv must be 16, 32, 64 or 128";
     case KDA_ERR_BAD_DTYPE: return "KDA_ERR_BAD_DTYPE: io dtype must be KDA_F32 or KDA_BF16";
-    case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED: pointers must be 16-byte aligned";
+    case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED: a pointer lacks the alignment its argument requires";
     case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
     case KDA_ERR_BAD_ARGUMENT: return "KDA_ERR_BAD_ARGUMENT: eps or scale is not finite, or eps < 0";
     case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
@@ -86,10 +88,14 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   if (nqk < 0 || nv < 0 || nb < 0 || ns < 0) return KDA_ERR_BAD_SHAPE;
   if (B * H > 0x7fffffffLL) return KDA_ERR_BAD_SHAPE;  // one workgroup per (b, h)
   if (!isfinite(scale) || !isfinite(eps) || eps < 0.f) return KDA_ERR_BAD_ARGUMENT;
+  // Tiles are moved with 16-byte accesses; beta, states and the norm weight
+  // are read element by element.
   for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)g,
-                        (const void*)beta, (const void*)s0, (const void*)o, (const void*)s_out,
-                        (const void*)gate, (const void*)norm_w})
-    if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+                        (const void*)o, (const void*)gate})
+    if (!aligned(p, 16)) return KDA_ERR_MISALIGNED;
+  for (const void* p : {(const void*)beta, (const void*)s0, (const void*)s_out,
+                        (const void*)norm_w})
+    if (!aligned(p, 4)) return KDA_ERR_MISALIGNED;
 
   const int64_t es = (io == KDA_BF16) ? 2 : 4;
   const Span sq{q, nqk * es}, sk{k, nqk * es}, sv{v, nv * es}, sg{g, nqk * 4}, sb{beta, nb * 4};
@@ -123,10 +129,14 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
   if (nqk < 0 || nv < 0 || nb < 0 || ns < 0) return KDA_ERR_BAD_SHAPE;
   if (nb > 0x7fffffffLL) return KDA_ERR_BAD_SHAPE;
   if (!isfinite(scale) || !isfinite(eps) || eps < 0.f) return KDA_ERR_BAD_ARGUMENT;
-  for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)g,
-                        (const void*)beta, (const void*)state, (const void*)o, (const void*)gate,
-                        (const void*)norm_w})
-    if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+  // The state is streamed with 16-byte accesses; the per-token vectors are
+  // read element by element.
+  const uintptr_t ea = (io == KDA_BF16) ? 2 : 4;
+  if (!aligned(state, 16)) return KDA_ERR_MISALIGNED;
+  for (const void* p : {q, k, v, (const void*)o, gate})
+    if (!aligned(p, ea)) return KDA_ERR_MISALIGNED;
+  for (const void* p : {(const void*)g, (const void*)beta, (const void*)norm_w})
+    if (!aligned(p, 4)) return KDA_ERR_MISALIGNED;
 
   const int64_t es = (io == KDA_BF16) ? 2 : 4;
   const Span sq{q, nqk * es}, sk{k, nqk * es}, sv{v, nv * es}, sg{g, nqk * 4}, sb{beta, nb * 4};
@@ -150,7 +160,7 @@ kda_status kda_gate_rmsnorm(const void* x, const void* gate, const float* norm_w
   if (n < 0) return KDA_ERR_BAD_SHAPE;
   if (!isfinite(eps) || eps < 0.f) return KDA_ERR_BAD_ARGUMENT;
   for (const void* p : {x, gate, (const void*)norm_w, (const void*)y})
-    if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+    if (!aligned(p, 16)) return KDA_ERR_MISALIGNED;
   const int64_t es = (io == KDA_BF16) ? 2 : 4;
   const Span sx{x, n * es}, sgt{gate, n * es}, sy{y, n * es}, sw{norm_w, (int64_t)dv * 4};
   if (overlap(sy, sgt) || overlap(sy, sw)) return KDA_ERR_ALIAS;

@@ -58,7 +58,7 @@ typedef enum {
   KDA_ERR_BAD_SHAPE = 2,         /* B, T, H or rows < 1, or a size product overflows   */
   KDA_ERR_UNSUPPORTED_DIM = 3,   /* dk or dv not in {16, 32, 64, 128}                  */
   KDA_ERR_BAD_DTYPE = 4,         /* io dtype not a kda_dtype value                     */
-  KDA_ERR_MISALIGNED = 5,        /* a pointer is not 16-byte aligned                   */
+  KDA_ERR_MISALIGNED = 5,        /* a pointer lacks the alignment its argument requires */
   KDA_ERR_ALIAS = 6,             /* an output overlaps an input it may not overlap     */
   KDA_ERR_BAD_ARGUMENT = 7,      /* a scalar argument is not finite or out of range    */
   KDA_ERR_LAUNCH = 8             /* the HIP runtime rejected a kernel launch           */
@@ -93,7 +93,7 @@ typedef enum {
  *   eps                             RMSNorm epsilon (> = 0, finite)
  *   scale                           output scale (finite)
  *   o and s_out may not both be NULL.  o may not overlap any input.
- *   All pointers must be 16-byte aligned.
+ *   Alignment: q, k, v, g, o and gate 16 bytes; beta, s0, s_out and norm_w 4 bytes.
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
                          const float* g, const float* beta, const float* s0,
@@ -117,6 +117,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
  *   state [B, H, dk, dv] float32    read and updated in place
  *   o     [B, H, dv]     io dtype   output (y when gate != NULL); must not be NULL
  *   gate  [B, H, dv]     io dtype   or NULL;  norm_w [dv] float32 or NULL;  eps, scale as above
+ *   Alignment: state 16 bytes; every other pointer to its element size.
  */
 kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            const float* g, const float* beta, float* state,
@@ -133,6 +134,7 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
  *
  *   x, gate, y [rows, dv]  io dtype  (y may equal x; any other overlap is KDA_ERR_ALIAS)
  *   norm_w     [dv]        float32, or NULL for a unit weight
+ *   Alignment: every pointer 16 bytes.
  */
 kda_status kda_gate_rmsnorm(const void* x, const void* gate, const float* norm_w, void* y,
                             int64_t rows, int dv, float eps, kda_dtype io, void* stream);

@@ -35,6 +35,7 @@ def rel_max_err(x, ref, out_dtype=None):
 
 def assert_close(x, ref, tol, what, out_dtype=None):
     err = rel_max_err(x, ref, out_dtype)
+    print(f"[parity] {what}: max|d|/RMS = {err:.3e} (tol {tol:.0e})")
     assert np.all(np.isfinite(np.asarray(x, dtype=np.float64))), f"{what}: non-finite values"
     assert err <= tol, f"{what}: max|d|/RMS = {err:.3e} > {tol:.1e}"
     return err

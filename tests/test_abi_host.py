@@ -94,7 +94,9 @@ def test_chunk_scalars(lib):
 def test_chunk_alignment(lib):
     assert chunk(lib, override={"q": P(1, 2)}) == ALIGN
     assert chunk(lib, override={"o": P(6, 8)}) == ALIGN
-    assert chunk(lib, override={"s0": P(9, 4)}) == ALIGN
+    assert chunk(lib, override={"s0": P(9, 2)}) == ALIGN      # states need 4 bytes
+    assert chunk(lib, override={"beta": P(5, 2)}) == ALIGN
+    assert chunk(lib, override={"g": P(4, 4)}) == ALIGN       # g tiles move in 16 bytes
 
 
 def test_chunk_aliasing(lib):
@@ -125,6 +127,7 @@ def test_decode_validation(lib):
     assert decode(lib, B=0) == SHAPE
     assert decode(lib, eps=-0.5) == ARG
     assert decode(lib, override={"state": P(6, 4)}) == ALIGN
+    assert decode(lib, override={"q": P(1, 1)}) == ALIGN      # bf16 needs 2 bytes
     assert decode(lib, o=6) == ALIAS       # o == state
     assert decode(lib, state=1) == ALIAS   # state == q
 
