@@ -10,11 +10,14 @@
 // per-token decode cost against a fixed-size state.
 //
 // The kernel is bound by HBM: every state element is read once and written
-// once (8 bytes per element per step).  One workgroup owns one (b, h) state;
-// each thread holds a float4 column strip of RPT rows in registers for the
-// whole step, so the write never re-reads memory.  A wavefront's float4 loads
-// for one row index cover whole 512-byte rows, and all RPT loads of a thread
-// are issued before the first use.
+// once (8 bytes per element per step).  A workgroup holds a float4 column
+// strip of RPT rows per thread in registers between the read and the in-place
+// write, so the write never re-reads memory.  The grid is persistent (one
+// workgroup per compute unit) and walks the (b, h) states with a stride of the
+// grid size; the next state and its per-token vectors are loaded into a
+// second register set while the current one is reduced and written, which
+// keeps reads in flight across the write phase.  Measured on MI355X this runs
+// closer to the read+write streaming ceiling than one workgroup per state.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -28,130 +31,182 @@ struct DecodeShape {
   static constexpr int NT = CG * RG;                                  // threads per block
   static_assert(NT <= 256 && NT % 64 == 0, "decode block must be whole wavefronts");
   static_assert(RPT * RG == DK, "rows must split evenly");
+  static_assert(NT >= DK && NT >= DV, "one thread per key channel and per value column");
+};
+
+// One (b, h): its state strip and per-token vectors, in registers.
+template <int DK, int DV>
+struct DecodeTile {
+  f32x4 s[DecodeShape<DK, DV>::RPT];
+  float q, k, g, v, gate, beta;
 };
 
 template <int DK, int DV, typename IO>
-__global__ void __launch_bounds__((DecodeShape<DK, DV>::NT))
-kda_decode_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
-                  const float* __restrict__ g, const float* __restrict__ beta,
-                  float* __restrict__ state, IO* __restrict__ o,
-                  const IO* __restrict__ gate, const float* __restrict__ norm_w,
-                  float eps, float scale) {
+__device__ __forceinline__ void decode_load(DecodeTile<DK, DV>& t, const IO* __restrict__ q,
+                                            const IO* __restrict__ k, const IO* __restrict__ v,
+                                            const float* __restrict__ g,
+                                            const float* __restrict__ beta,
+                                            const float* __restrict__ state,
+                                            const IO* __restrict__ gate, int64_t bh) {
   using Sh = DecodeShape<DK, DV>;
-  constexpr int CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT;
-
-  __shared__ float s_a[DK];         // a_i = exp(g_i)
-  __shared__ float s_k[DK];         // k_i
-  __shared__ float s_ak[DK];        // a_i * k_i
-  __shared__ float s_aq[DK];        // a_i * q_i
-  __shared__ float s_part[2][RG][DV];
-  __shared__ float s_u[DV];
-  __shared__ float s_qk;
-  __shared__ float s_red[DV];
-
   const int tid = threadIdx.x;
-  const int64_t bh = blockIdx.x;
-  const int cg = tid % CG;
-  const int rg = tid / CG;
-  float* Sp = state + bh * (int64_t)(DK * DV);
-
-  // Issue every state load first: RPT independent float4 loads per thread.
-  f32x4 s[RPT];
+  const int cg = tid % Sh::CG, rg = tid / Sh::CG;
+  const float* Sp = state + bh * (int64_t)(DK * DV);
 #pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int i = rg + m * RG;
-    s[m] = __builtin_nontemporal_load((const f32x4*)(Sp + i * DV + 4 * cg));
-  }
+  for (int m = 0; m < Sh::RPT; ++m)
+    t.s[m] = __builtin_nontemporal_load((const f32x4*)(Sp + (rg + m * Sh::RG) * DV + 4 * cg));
+  const int ci = tid % DK, cj = tid % DV;
+  t.q = ld_f32(q + bh * DK + ci);
+  t.k = ld_f32(k + bh * DK + ci);
+  t.g = g[bh * DK + ci];
+  t.v = ld_f32(v + bh * DV + cj);
+  t.gate = gate ? ld_f32(gate + bh * DV + cj) : 0.f;
+  t.beta = beta[bh];
+}
 
-  // Per-channel factors.
+template <int DK, int DV>
+struct DecodeSmem {
+  using Sh = DecodeShape<DK, DV>;
+  float a[DK];         // a_i = exp(g_i)
+  float kk[DK];        // k_i
+  float ak[DK];        // a_i * k_i
+  float aq[DK];        // a_i * q_i
+  float part[2][Sh::RG][DV];
+  float u[DV];
+  float red[Sh::NT];   // q_i k_i, then o_j^2
+  float qk, ss;
+};
+
+template <int DK, int DV, typename IO>
+__device__ __forceinline__ void decode_one(DecodeSmem<DK, DV>& sm, const DecodeTile<DK, DV>& t,
+                                           float* __restrict__ state, IO* __restrict__ o,
+                                           bool gated, float wn, float eps, float scale,
+                                           int64_t bh) {
+  using Sh = DecodeShape<DK, DV>;
+  constexpr int CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT, NT = Sh::NT;
+  const int tid = threadIdx.x;
+  const int cg = tid % CG, rg = tid / CG;
+
+  // Per-channel factors and q . k (over the undecayed vectors).
   if (tid < DK) {
-    const float a = expf(g[bh * DK + tid]);
-    const float kk = ld_f32(k + bh * DK + tid);
-    const float qq = ld_f32(q + bh * DK + tid);
-    s_a[tid] = a;
-    s_k[tid] = kk;
-    s_ak[tid] = a * kk;
-    s_aq[tid] = a * qq;
+    const float a = __expf(t.g);
+    sm.a[tid] = a;
+    sm.kk[tid] = t.k;
+    sm.ak[tid] = a * t.k;
+    sm.aq[tid] = a * t.q;
   }
-  // q . k over the undecayed vectors (one wavefront reduction).
+  sm.red[tid] = (tid < DK) ? t.q * t.k : 0.f;
+  __syncthreads();
   if (tid < 64) {
     float acc = 0.f;
-    for (int i = tid; i < DK; i += 64) acc += ld_f32(q + bh * DK + i) * ld_f32(k + bh * DK + i);
+    for (int i = tid; i < NT; i += 64) acc += sm.red[i];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (tid == 0) s_qk = acc;
+    if (tid == 0) sm.qk = acc;
   }
-  __syncthreads();
 
   // Partial column sums over this thread's rows.
   f32x4 p = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int i = rg + m * RG;
-    p += s_ak[i] * s[m];
-    r += s_aq[i] * s[m];
+    p += sm.ak[i] * t.s[m];
+    r += sm.aq[i] * t.s[m];
   }
-  *(f32x4*)&s_part[0][rg][4 * cg] = p;
-  *(f32x4*)&s_part[1][rg][4 * cg] = r;
+  *(f32x4*)&sm.part[0][rg][4 * cg] = p;
+  *(f32x4*)&sm.part[1][rg][4 * cg] = r;
   __syncthreads();
 
   // Column j: finish the reductions, form u_j and o_j.
-  const float bt = beta[bh];
   float oj = 0.f;
   if (tid < DV) {
     float pj = 0.f, rj = 0.f;
 #pragma unroll 8
     for (int x = 0; x < RG; ++x) {
-      pj += s_part[0][x][tid];
-      rj += s_part[1][x][tid];
+      pj += sm.part[0][x][tid];
+      rj += sm.part[1][x][tid];
     }
-    const float uj = bt * (ld_f32(v + bh * DV + tid) - pj);
-    s_u[tid] = uj;
-    oj = scale * (rj + s_qk * uj);
+    const float uj = t.beta * (t.v - pj);
+    sm.u[tid] = uj;
+    oj = scale * (rj + sm.qk * uj);
   }
+  if (gated) sm.red[tid] = (tid < DV) ? oj * oj : 0.f;
   __syncthreads();
 
   // State update in place: S_ij <- a_i S_ij + k_i u_j.
   {
-    const f32x4 u4 = *(const f32x4*)&s_u[4 * cg];
+    float* Sp = state + bh * (int64_t)(DK * DV);
+    const f32x4 u4 = *(const f32x4*)&sm.u[4 * cg];
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
       const int i = rg + m * RG;
-      const f32x4 nv = s_a[i] * s[m] + s_k[i] * u4;
+      const f32x4 nv = sm.a[i] * t.s[m] + sm.kk[i] * u4;
       __builtin_nontemporal_store(nv, (f32x4*)(Sp + i * DV + 4 * cg));
     }
   }
 
   // Output, optionally through the head-wise RMSNorm x sigmoid(gate) epilogue.
-  if (gate == nullptr) {
+  if (!gated) {
     if (tid < DV) st_f32(o + bh * DV + tid, oj);
+    __syncthreads();  // the shared buffers are reused by the next state
     return;
   }
-  if (tid < DV) s_red[tid] = oj * oj;
-  __syncthreads();
   if (tid < 64) {
     float acc = 0.f;
-    for (int j = tid; j < DV; j += 64) acc += s_red[j];
+    for (int j = tid; j < NT; j += 64) acc += sm.red[j];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (tid == 0) s_qk = acc;  // reuse: sum of squares
+    if (tid == 0) sm.ss = acc;
   }
   __syncthreads();
   if (tid < DV) {
-    const float inv = rsqrtf(s_qk / (float)DV + eps);
-    const float w = norm_w ? norm_w[tid] : 1.f;
-    const float gt = ld_f32(gate + bh * DV + tid);
-    st_f32(o + bh * DV + tid, oj * inv * w * sigmoidf_(gt));
+    const float inv = rsqrtf(sm.ss / (float)DV + eps);
+    st_f32(o + bh * DV + tid, oj * inv * wn * sigmoidf_(t.gate));
+  }
+  __syncthreads();
+}
+
+template <int DK, int DV, typename IO>
+__global__ void __launch_bounds__((DecodeShape<DK, DV>::NT), 1)
+kda_decode_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
+                  const float* __restrict__ g, const float* __restrict__ beta,
+                  float* __restrict__ state, IO* __restrict__ o,
+                  const IO* __restrict__ gate, const float* __restrict__ norm_w,
+                  float eps, float scale, int64_t BH) {
+  __shared__ DecodeSmem<DK, DV> sm;
+  const int tid = threadIdx.x;
+  const bool gated = gate != nullptr;
+  const float wn = (gated && norm_w != nullptr && tid < DV) ? norm_w[tid] : 1.f;
+  const int64_t stride = gridDim.x;
+
+  // Two register sets: while one state is reduced and written, the next is loading.
+  DecodeTile<DK, DV> t0, t1;
+  int64_t bh = blockIdx.x;
+  if (bh < BH) decode_load<DK, DV, IO>(t0, q, k, v, g, beta, state, gate, bh);
+  while (bh < BH) {
+    const int64_t b1 = bh + stride;
+    if (b1 < BH) decode_load<DK, DV, IO>(t1, q, k, v, g, beta, state, gate, b1);
+    decode_one<DK, DV, IO>(sm, t0, state, o, gated, wn, eps, scale, bh);
+    if (b1 >= BH) break;
+    const int64_t b2 = b1 + stride;
+    if (b2 < BH) decode_load<DK, DV, IO>(t0, q, k, v, g, beta, state, gate, b2);
+    decode_one<DK, DV, IO>(sm, t1, state, o, gated, wn, eps, scale, b1);
+    bh = b2;
   }
 }
 
 template <int DK, int DV, typename IO>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
   using Sh = DecodeShape<DK, DV>;
-  const int64_t nblk = a.B * a.H;
+  const int64_t bhn = a.B * a.H;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (cus < 1) cus = 256;
+  const int64_t nblk = bhn < cus ? bhn : cus;  // one persistent workgroup per compute unit
   hipLaunchKernelGGL((kda_decode_kernel<DK, DV, IO>), dim3((unsigned)nblk), dim3(Sh::NT), 0,
                      (hipStream_t)a.stream, (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g,
-                     a.beta, a.state, (IO*)a.o, (const IO*)a.gate, a.norm_w, a.eps, a.scale);
+                     a.beta, a.state, (IO*)a.o, (const IO*)a.gate, a.norm_w, a.eps, a.scale, bhn);
   return hipGetLastError();
 }
 
