@@ -33,10 +33,12 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 F32_PEAK_TFLOPS = 157.3        # MI355X fp32, published
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
-    # kernel name reported by the library -> source file that defines it
-    "kda_chunk_mfma": "gated_delta_rule_112_amd/csrc/kda_chunk_mfma.hip",
-    "kda_chunk_valu": "gated_delta_rule_112_amd/csrc/kda_chunk_valu.hip",
-    "kda_decode": "gated_delta_rule_112_amd/csrc/kda_decode.hip",
+    # path name reported by the library -> source files of its kernels
+    "kda_chunk_mfma": ["gated_delta_rule_112_amd/csrc/kda_chunk_tile.hip",
+                       "gated_delta_rule_112_amd/csrc/kda_chunk_state.hip",
+                       "gated_delta_rule_112_amd/csrc/kda_chunk_rec.h"],
+    "kda_chunk_valu": ["gated_delta_rule_112_amd/csrc/kda_chunk_valu.hip"],
+    "kda_decode": ["gated_delta_rule_112_amd/csrc/kda_decode.hip"],
 }
 
 
@@ -80,7 +82,7 @@ def source_digest(kernel):
     if path is None:
         return None
     h = hashlib.sha256()
-    for p in (path, "gated_delta_rule_112_amd/csrc/kda_device.h"):
+    for p in [*path, "gated_delta_rule_112_amd/csrc/kda_device.h"]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -159,11 +161,14 @@ def bench_prefill(kda, torch, w, steps, warmup):
     io = x["q"].dtype
     out = torch.empty((w.B, w.T, w.H, w.dv), dtype=io, device=dev)
     s_out = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    nws = kda.chunk_workspace_size(w.B, w.T, w.H, w.dk, w.dv, io)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    log(f"[bench] workspace {nws / 2**20:.1f} MiB")
     stream = torch.cuda.current_stream(dev)
 
     def step():
         kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], gate=x["gate"],
-                      out=out, s_out=s_out, stream=stream)
+                      out=out, s_out=s_out, workspace=ws, stream=stream)
 
     for _ in range(warmup):
         step()
@@ -176,7 +181,7 @@ def bench_prefill(kda, torch, w, steps, warmup):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    del x, out, s_out
+    del x, out, s_out, ws
     return ms, io
 
 

@@ -45,8 +45,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib = ctypes.CDLL(p)
     vp, f32, i64, ci = ctypes.c_void_p, ctypes.c_float, ctypes.c_int64, ctypes.c_int
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32,
-                                  i64, i64, i64, ci, ci, f32, ci, vp]
+                                  i64, i64, i64, ci, ci, f32, ci, vp, ctypes.c_size_t, vp]
     lib.kda_chunk_fwd.restype = ci
+    lib.kda_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, ci, ci, ci]
+    lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32,
                                     i64, i64, ci, ci, f32, ci, vp]
     lib.kda_decode_step.restype = ci
@@ -93,11 +95,13 @@ def _stream(device, stream):
 
 def chunk_fwd(q, k, v, g, beta, s0=None, *, scale: float = 1.0, gate=None, norm_w=None,
               eps: float = 1e-6, output: bool = True, final_state: bool = True,
-              out=None, s_out=None, stream=None) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+              out=None, s_out=None, workspace=None,
+              stream=None) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
     """Prefill over [B, T, H, *] tensors; returns (o or y, final state).
 
     ``output=False`` computes the final state only; ``s_out`` may be ``s0``
-    for an in-place state update.
+    for an in-place state update.  ``workspace`` (a uint8 CUDA tensor of at
+    least ``chunk_workspace_size(...)`` bytes) is allocated per call if absent.
     """
     lib = load_library()
     if q.device.type != "cuda":
@@ -131,9 +135,16 @@ def chunk_fwd(q, k, v, g, beta, s0=None, *, scale: float = 1.0, gate=None, norm_
         s_out = None
     elif s_out is not None:
         _need(s_out, "s_out", torch.float32, (B, H, dk, dv), dev)
+    ws_bytes = lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, _IO[io])
+    if workspace is None and ws_bytes > 0:
+        # torch's caching allocator hands out 512-byte aligned blocks
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, (workspace.numel(),), dev)
     st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(out),
                            _ptr(s_out), _ptr(gate), _ptr(norm_w), float(eps), B, T, H, dk, dv,
-                           float(scale), _IO[io], _stream(dev, stream))
+                           float(scale), _IO[io], _ptr(workspace),
+                           0 if workspace is None else workspace.numel(), _stream(dev, stream))
     _check(lib, "kda_chunk_fwd", st)
     return out, s_out
 
@@ -169,6 +180,12 @@ def decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, gate=None, norm_
                              float(scale), _IO[io], _stream(dev, stream))
     _check(lib, "kda_decode_step", st)
     return out
+
+
+def chunk_workspace_size(B: int, T: int, H: int, dk: int, dv: int, dtype) -> int:
+    """Workspace bytes kda_chunk_fwd needs for these sizes (0: none)."""
+    return int(load_library().kda_chunk_fwd_workspace_size(int(B), int(T), int(H), int(dk),
+                                                           int(dv), _IO[dtype]))
 
 
 def chunk_kernel_name(dk: int, dv: int, dtype) -> Optional[str]:

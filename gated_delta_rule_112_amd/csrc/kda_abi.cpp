@@ -63,11 +63,14 @@ const char* kda_status_string(kda_status s) {
     case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
     case KDA_ERR_BAD_ARGUMENT: return "KDA_ERR_BAD_ARGUMENT: eps or scale is not finite, or eps < 0";
     case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+    case KDA_ERR_WORKSPACE:
+      return "KDA_ERR_WORKSPACE: the workspace is NULL, smaller than "
+             "kda_chunk_fwd_workspace_size() or not 256-byte aligned";
   }
   return "KDA_ERR_UNKNOWN";
 }
 
-int kda_version(void) { return 100; }
+int kda_version(void) { return 200; }
 
 const char* kda_chunk_fwd_kernel(int dk, int dv, kda_dtype io) {
   if ((io != KDA_F32 && io != KDA_BF16) || !dim_ok(dk) || !dim_ok(dv)) return nullptr;
@@ -75,10 +78,19 @@ const char* kda_chunk_fwd_kernel(int dk, int dv, kda_dtype io) {
   return "kda_chunk_valu";
 }
 
+size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk, int dv,
+                                    kda_dtype io) {
+  if ((io != KDA_F32 && io != KDA_BF16) || !dim_ok(dk) || !dim_ok(dv)) return 0;
+  if (prod(B, T, H, dk) < 0 || prod(B, H, dk, dv) < 0) return 0;
+  if (force_valu() || !kda::chunk_mfma_supports(dk, dv, io == KDA_BF16)) return 0;
+  return kda::chunk_mfma_workspace(B, T, H);
+}
+
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const float* s0, void* o, float* s_out,
                          const void* gate, const float* norm_w, float eps, int64_t B, int64_t T,
-                         int64_t H, int dk, int dv, float scale, kda_dtype io, void* stream) {
+                         int64_t H, int dk, int dv, float scale, kda_dtype io, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !g || !beta) return KDA_ERR_NULL_POINTER;
   if (!o && !s_out) return KDA_ERR_NULL_POINTER;
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_BAD_DTYPE;
@@ -107,13 +119,19 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     if (overlap(sso, in)) return KDA_ERR_ALIAS;
   if (overlap(sso, ss0) && (const void*)s_out != (const void*)s0) return KDA_ERR_ALIAS;
 
+  const bool mfma = !force_valu() && kda::chunk_mfma_supports(dk, dv, io == KDA_BF16);
+  if (mfma) {
+    const size_t need = kda::chunk_mfma_workspace(B, T, H);
+    if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
+      return KDA_ERR_WORKSPACE;
+    const Span sws{workspace, (int64_t)need};
+    for (Span in : {sq, sk, sv, sg, sb, ss0, so, sso, sgt, sw})
+      if (overlap(sws, in)) return KDA_ERR_ALIAS;
+  }
+
   kda::ChunkArgs a{q, k, v, g, beta, s0, o, s_out, gate, norm_w, eps,
-                   B, T, H, dk, dv, scale, io == KDA_BF16, stream};
-  hipError_t err;
-  if (!force_valu() && kda::chunk_mfma_supports(dk, dv, io == KDA_BF16))
-    err = kda::launch_chunk_mfma(a);
-  else
-    err = kda::launch_chunk_valu(a);
+                   B, T, H, dk, dv, scale, io == KDA_BF16, workspace, stream};
+  const hipError_t err = mfma ? kda::launch_chunk_mfma(a) : kda::launch_chunk_valu(a);
   return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

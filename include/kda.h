@@ -25,7 +25,8 @@
  * Conventions for every entry point:
  *   - All tensor arguments are DEVICE pointers owned by the caller, contiguous,
  *     row-major, in the layouts given per argument.  The library never
- *     allocates, frees or keeps a pointer after the call returns.
+ *     allocates, frees or keeps a pointer after the call returns; scratch
+ *     memory, where a call needs it, is a caller-provided workspace.
  *   - q, k, v, o, gate (and x, y) are in the io dtype (kda_dtype); g, beta,
  *     states and norm weights are always float32.
  *   - Every call is asynchronous on `stream` (NULL = the default stream).
@@ -61,7 +62,8 @@ typedef enum {
   KDA_ERR_MISALIGNED = 5,        /* a pointer lacks the alignment its argument requires */
   KDA_ERR_ALIAS = 6,             /* an output overlaps an input it may not overlap     */
   KDA_ERR_BAD_ARGUMENT = 7,      /* a scalar argument is not finite or out of range    */
-  KDA_ERR_LAUNCH = 8             /* the HIP runtime rejected a kernel launch           */
+  KDA_ERR_LAUNCH = 8,            /* the HIP runtime rejected a kernel launch           */
+  KDA_ERR_WORKSPACE = 9          /* workspace NULL, too small or not 256-byte aligned  */
 } kda_status;
 
 typedef enum {
@@ -74,8 +76,13 @@ typedef enum {
  *
  * Computed chunkwise in 16-token tiles ("Kimi K3: Engineering ...", section
  * "Dimension 1"); the result equals the token-by-token recurrence up to
- * floating-point rounding.  The running state lives on chip for the whole
- * sequence; only the final state is written.
+ * floating-point rounding.  With bfloat16 io and dk = dv = 128 it runs on the
+ * matrix cores as two kernels per segment of tiles: a tile kernel computes
+ * the state-independent part of every tile of the segment in parallel into
+ * the workspace, then a state kernel walks the tiles of each head in order
+ * with the running state on chip.  The state is written to memory only at
+ * segment boundaries (to s_out, or to the workspace when s_out is NULL) and
+ * at the end.
  *
  *   q     [B, T, H, dk]  io dtype   queries
  *   k     [B, T, H, dk]  io dtype   keys (the method expects unit L2 norm; not checked)
@@ -93,14 +100,31 @@ typedef enum {
  *   eps                             RMSNorm epsilon (> = 0, finite)
  *   scale                           output scale (finite)
  *   o and s_out may not both be NULL.  o may not overlap any input.
+ *   workspace                       device scratch of at least workspace_bytes >=
+ *                                   kda_chunk_fwd_workspace_size(B, T, H, dk, dv, io)
+ *                                   bytes, 256-byte aligned, overlapping no other
+ *                                   argument; its contents are undefined after the
+ *                                   call.  May be NULL when that size is 0.
  *   Alignment: q, k, v, g, o and gate 16 bytes; beta, s0, s_out and norm_w 4 bytes.
+ *   Calls that share a workspace must not run concurrently.
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
                          const float* g, const float* beta, const float* s0,
                          void* o, float* s_out,
                          const void* gate, const float* norm_w, float eps,
                          int64_t B, int64_t T, int64_t H, int dk, int dv,
-                         float scale, kda_dtype io, void* stream);
+                         float scale, kda_dtype io, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_fwd_workspace_size -- bytes of workspace kda_chunk_fwd needs for
+ * these sizes: 0 for the vector-ALU path, otherwise the records of one segment
+ * of tiles (bounded near 128 MiB, or 13,824 bytes per head when one tile of
+ * every head exceeds that) plus one float32 state per head.  Returns 0 for
+ * arguments kda_chunk_fwd would reject.
+ */
+size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk, int dv,
+                                    kda_dtype io);
 
 /*
  * kda_decode_step -- one token per sequence against a resident state.
@@ -150,7 +174,7 @@ const char* kda_chunk_fwd_kernel(int dk, int dv, kda_dtype io);
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* kda_status_string(kda_status s);
 
-/* Library version, major * 10000 + minor * 100 + patch. */
+/* Library version, major * 10000 + minor * 100 + patch (0.2.0). */
 int kda_version(void);
 
 #ifdef __cplusplus

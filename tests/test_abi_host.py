@@ -14,7 +14,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, NULLP, SHAPE, DIM, DTYPE, ALIGN, ALIAS, ARG = 0, 1, 2, 3, 4, 5, 6, 7
+OK, NULLP, SHAPE, DIM, DTYPE, ALIGN, ALIAS, ARG, LAUNCH, WORKSPACE = range(10)
 
 
 def declared_functions():
@@ -31,8 +31,8 @@ def lib():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    for n in ["kda_chunk_fwd", "kda_decode_step", "kda_gate_rmsnorm", "kda_status_string",
-              "kda_version"]:
+    for n in ["kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_decode_step",
+              "kda_gate_rmsnorm", "kda_status_string", "kda_version"]:
         assert n in names
 
 
@@ -42,8 +42,9 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(0, 9):
+    for s in range(0, 10):
         assert lib.kda_status_string(s)
+        assert b"UNKNOWN" not in lib.kda_status_string(s)
     assert lib.kda_status_string(0) == b"KDA_OK"
     assert b"UNKNOWN" in lib.kda_status_string(99)
     assert lib.kda_version() >= 100
@@ -58,14 +59,15 @@ def P(i, off=0):
 
 
 def chunk(lib, *, q=1, k=2, v=3, g=4, beta=5, s0=None, o=6, s_out=7, gate=None, w=None,
-          eps=1e-6, B=1, T=16, H=1, dk=16, dv=16, scale=1.0, io=1, override=None):
-    ptrs = dict(q=q, k=k, v=v, g=g, beta=beta, s0=s0, o=o, s_out=s_out, gate=gate, w=w)
+          eps=1e-6, B=1, T=16, H=1, dk=16, dv=16, scale=1.0, io=1, ws=None, ws_bytes=0,
+          override=None):
+    ptrs = dict(q=q, k=k, v=v, g=g, beta=beta, s0=s0, o=o, s_out=s_out, gate=gate, w=w, ws=ws)
     args = {n: (None if x is None else P(x)) for n, x in ptrs.items()}
     if override:
         args.update(override)
     return lib.kda_chunk_fwd(args["q"], args["k"], args["v"], args["g"], args["beta"], args["s0"],
                              args["o"], args["s_out"], args["gate"], args["w"], eps, B, T, H, dk,
-                             dv, scale, io, None)
+                             dv, scale, io, args["ws"], ws_bytes, None)
 
 
 def test_chunk_null_pointers(lib):
@@ -106,6 +108,27 @@ def test_chunk_aliasing(lib):
     assert chunk(lib, gate=8, o=8) == ALIAS
     # s_out == s0 (in place) is allowed (exercised on the GPU); partial overlap is not.
     assert chunk(lib, s0=9, override={"s_out": P(9, 16)}) == ALIAS
+
+
+def test_chunk_workspace(lib):
+    """The matrix-core path (bf16, dk = dv = 128) needs a workspace: missing, too
+    small, misaligned or overlapping workspaces are rejected before any launch."""
+    size = lib.kda_chunk_fwd_workspace_size
+    need = size(1, 4096, 32, 128, 128, 1)
+    assert need >= 13824 * 32 + 32 * 128 * 128 * 4
+    assert size(1, 4096, 32, 16, 16, 1) == 0          # vector-ALU path: none
+    assert size(1, 4096, 32, 128, 128, 0) == 0        # float32 io: vector-ALU path
+    assert size(0, 4096, 32, 128, 128, 1) == 0        # invalid sizes
+    assert size(1, 4096, 32, 48, 128, 1) == 0
+    # one segment of records stays near 128 MiB however long the sequence is
+    assert size(1, 1 << 20, 96, 128, 128, 1) < (160 << 20)
+    assert size(1, 1 << 20, 96, 128, 128, 1) == size(1, 1 << 22, 96, 128, 128, 1)
+    kw = dict(B=1, T=4096, H=32, dk=128, dv=128, io=1)
+    assert chunk(lib, **kw) == WORKSPACE                             # NULL
+    assert chunk(lib, ws=10, ws_bytes=need - 1, **kw) == WORKSPACE   # too small
+    assert chunk(lib, ws_bytes=need, override={"ws": P(10, 128)}, **kw) == WORKSPACE
+    assert chunk(lib, ws=1, ws_bytes=need, **kw) == ALIAS            # overlaps q
+    assert chunk(lib, ws=10, ws_bytes=need, dk=48, B=1, T=16, H=1) == DIM
 
 
 def decode(lib, *, q=1, k=2, v=3, g=4, beta=5, state=6, o=7, gate=None, w=None, eps=1e-6,
