@@ -34,7 +34,7 @@ F32_PEAK_TFLOPS = 157.3        # MI355X fp32, published
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     # path name reported by the library -> source files of its kernels
-    "kda_chunk_mfma": ["gated_delta_rule_112_amd/csrc/kda_chunk_tile.hip",
+    "kda_chunk_mfma": ["gated_delta_rule_112_amd/csrc/kda_chunk_tile.h",
                        "gated_delta_rule_112_amd/csrc/kda_chunk_state.hip",
                        "gated_delta_rule_112_amd/csrc/kda_chunk_rec.h"],
     "kda_chunk_valu": ["gated_delta_rule_112_amd/csrc/kda_chunk_valu.hip"],

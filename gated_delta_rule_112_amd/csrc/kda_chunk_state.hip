@@ -39,13 +39,16 @@
 // state, the values and D to stay below 65504 in magnitude.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "kda_chunk_rec.h"
+#include "kda_chunk_tile.h"
 #include "kda_launch.h"
 
 namespace kda {
 namespace {
 
-constexpr int kLoaders = 2;       // loader wavefronts
+constexpr int kLoaders = 4;       // loader wavefronts, one per SIMD
 constexpr int kLead = 4;          // tiles in flight ahead of the one being consumed
 constexpr int kRing = kLead + 2;  // + the tile being consumed + the one being finished
 
@@ -53,18 +56,25 @@ constexpr int kRing = kLead + 2;  // + the tile being consumed + the one being f
 constexpr unsigned vmcnt_imm(int n) {
   return (unsigned)((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+// s_waitcnt with vmcnt = N and lgkmcnt = 0.
+constexpr unsigned vmcnt_lgkm0_imm(int n) { return vmcnt_imm(n) & ~(0xFu << 8); }
 
+// A slot is a whole number of 1 KB blocks (one direct-to-LDS load of a wave
+// each); every block holds only record bytes or only v / gate bytes.
 template <int DVW, bool GATE>
 struct SlotCfg {
   static constexpr int kRowB = DVW * 2;                  // bytes per v / gate row
   static constexpr int kCpr = DVW / 8;                   // 16-byte chunks per row
   static constexpr int kTileB = rec::kC * kRowB;         // bytes per v / gate tile
-  static constexpr int kV = rec::kBytes;                 // v tile offset in a slot
+  static constexpr int kRecBlocks = (rec::kBytes + 1023) / 1024;
+  static constexpr int kTileBlocks = kTileB / 1024;
+  static constexpr int kV = kRecBlocks * 1024;           // v tile offset in a slot
   static constexpr int kG = kV + kTileB;                 // gate tile offset
   static constexpr int kData = kG + (GATE ? kTileB : 0);
   static constexpr int kInstr = kLoaders * 1024;         // bytes per loader round
   static constexpr int kSlot = (kData + kInstr - 1) / kInstr * kInstr;
   static constexpr int kPer = kSlot / kInstr;            // loads per loader wave per tile
+  static_assert(kTileB % 1024 == 0, "v tiles must be whole blocks");
   static constexpr int kRowsPerBankLine = 256 / kRowB;   // rows sharing the 64 banks
   // Chunk position of chunk u of row t (an involution in u for fixed t).
   static __device__ __forceinline__ int swz(int t, int u) {
@@ -72,79 +82,154 @@ struct SlotCfg {
   }
 };
 
-template <int DVW, int CPW, bool GATE>
+template <int DVW, int CPW, bool GATE, bool WO>
 __global__ void __launch_bounds__(64 * (DVW / CPW + kLoaders), 1)
 kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restrict__ v,
                  const float* __restrict__ s_in, float* __restrict__ s_next,
                  bf16_t* __restrict__ o, const bf16_t* __restrict__ gate,
                  const float* __restrict__ norm_w, float eps, int64_t T, int64_t H, int64_t BH,
-                 int64_t x0, int64_t nseg) {
+                 int64_t x0, int64_t nseg, int64_t n_state_wg, tile::Args next) {
   using SC = SlotCfg<DVW, GATE>;
   constexpr int NSW = DVW / CPW;   // state wavefronts
   constexpr int NCB = CPW / 16;    // 16-column blocks per state wavefront
   constexpr int NSPLIT = rec::kDV / DVW;
   static_assert(CPW % 16 == 0 && DVW % CPW == 0 && rec::kDV % DVW == 0, "bad column split");
   static_assert(!GATE || NSPLIT == 1, "the gated RMSNorm needs a head's full dv row");
+  static_assert(!GATE || WO, "the gated epilogue only shapes the output");
   static_assert(kLead * SC::kPer <= 63, "outstanding loads per loader wave exceed vmcnt");
 
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[kRing][SC::kSlot];
-  __shared__ __attribute__((aligned(16))) float rs[2][rec::kC][NSW];  // row sums of O^2
+  constexpr int NW = NSW + kLoaders;  // wavefronts per workgroup
+  constexpr int kRingB = kRing * SC::kSlot;
+  constexpr int kRsB = 2 * rec::kC * NSW * 4;
+  constexpr int kStateB = kRingB + kRsB;
+  constexpr int kTileB = NW * (int)sizeof(tile::Scratch);
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kStateB > kTileB ? kStateB : kTileB];
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform
+  const int lane = tid % 64;
   const int lc = lane % 16, lg = lane / 16;
+
+  if ((int64_t)blockIdx.x >= n_state_wg) {
+    // ======================== tile workgroups: records of the next segment
+    tile::Scratch* scratch = (tile::Scratch*)lds;
+    const int64_t first = ((int64_t)blockIdx.x - n_state_wg) * NW + wave;
+    const int64_t stride = ((int64_t)gridDim.x - n_state_wg) * NW;
+    tile::build_range(next, first, stride, scratch[wave], lane);
+    return;
+  }
+
+  // ======================= state workgroups: the tiles of this segment
+  unsigned char (*ring)[SC::kSlot] = (unsigned char (*)[SC::kSlot])lds;
+  float (*rs)[rec::kC][NSW] = (float (*)[rec::kC][NSW])(lds + kRingB);  // row sums of O^2
 
   // Keep the NSPLIT workgroups of one head on one XCD (workgroups are dealt
   // round-robin over the 8 XCDs) so that they share its records in L2.
   int64_t wg = blockIdx.x;
-  const int64_t total = BH * NSPLIT;
+  const int64_t total = n_state_wg;  // BH * NSPLIT
   if (NSPLIT > 1 && total % 8 == 0) wg = (wg % 8) * (total / 8) + wg / 8;
   const int64_t bh = wg / NSPLIT;
   const int col0 = (int)(wg % NSPLIT) * DVW;  // first value column of the workgroup
   const int64_t b = bh / H, h = bh % H;
 
-  auto rowoff = [&](int64_t xl, int r) {  // element offset of a [B, T, H, dv] row, clamped
-    int64_t tok = (x0 + xl) * rec::kC + r;
-    tok = tok < T ? tok : T - 1;
-    return ((b * T + tok) * H + h) * rec::kDV;
-  };
+  const int64_t rstride = H * rec::kDV;  // elements between consecutive tokens of a head
 
   if (wave >= NSW) {
     // ========================================================== loader waves
     const int lw = wave - NSW;
     const unsigned char* R0 = recs + bh * nseg * (int64_t)rec::kBytes;
-    // Copy tile xt (clamped into the segment) into ring slot `slot`: round i
-    // of this wave moves the 64 chunks [(i kLoaders + lw) 64, + 64) of the slot.
+    // Block i kLoaders + lw of a slot is this wave's i-th load.  Its kind and
+    // this lane's source offset are fixed; a tile only moves the base.
+    //   record block j:  R0 + x * kBytes + 16 (64 j + lane)   (the padding of the
+    //                    last record block re-reads record chunks)
+    //   v / gate block:  row t, column chunk u of the tile:
+    //                    base_x + t * row stride + 2 (col0 + 8 u)
+    int kind[SC::kPer];        // 0 record, 1 v, 2 gate (wave-uniform)
+    unsigned loff[SC::kPer];   // byte offset from the tile base (full tiles)
+    int lrow[SC::kPer], lcol[SC::kPer];
+#pragma unroll
+    for (int i = 0; i < SC::kPer; ++i) {
+      const int blk = i * kLoaders + lw;
+      const int c = blk * 64 + lane;
+      if (blk < SC::kRecBlocks) {
+        kind[i] = 0;
+        loff[i] = 16u * (unsigned)(c < rec::kBytes / 16 ? c : c - 64);
+        lrow[i] = lcol[i] = 0;
+      } else {
+        int q = (blk - SC::kRecBlocks) * 64 + lane;
+        const int which = q / (SC::kTileB / 16);
+        kind[i] = (GATE && which == 1) ? 2 : 1;  // past the gate tile: padding, re-reads v
+        q %= SC::kTileB / 16;
+        const int t = q / SC::kCpr, u = SC::swz(t, q % SC::kCpr);
+        lrow[i] = t;
+        lcol[i] = col0 + 8 * u;
+        loff[i] = (unsigned)(2 * (t * rstride + lcol[i]));
+      }
+    }
+    // Copy tile xt (clamped into the segment) into ring slot `slot`.
     auto issue = [&](int64_t xt, int slot) {
       xt = xt < nseg ? xt : nseg - 1;
+      const int64_t row0 = (x0 + xt) * rec::kC;               // first token of the tile
+      const bool full = row0 + rec::kC <= T;
+      const unsigned char* base_r = R0 + xt * rec::kBytes;
+      const int64_t tile0 = ((b * T + row0) * H + h) * rec::kDV;  // element offset of row 0
+      const unsigned char* base_v = (const unsigned char*)(v + tile0);
+      const unsigned char* base_g = (const unsigned char*)((GATE ? gate : v) + tile0);
 #pragma unroll
       for (int i = 0; i < SC::kPer; ++i) {
-        const int base = (i * kLoaders + lw) * 64;  // first chunk of the round
-        const int c = base + lane;                  // chunk of this lane (a round may
-        const bool is_rec = c < SC::kV / 16;        // straddle the record's end)
-        // v or gate chunk; chunks of the padding re-read a v chunk
-        int q = is_rec ? 0 : c - SC::kV / 16;
-        const bool is_gate = GATE && q >= SC::kTileB / 16 && q < 2 * SC::kTileB / 16;
-        q = q % (SC::kTileB / 16);
-        const int t = q / SC::kCpr, u = SC::swz(t, q % SC::kCpr);
-        const unsigned char* src_rec = R0 + xt * rec::kBytes + (is_rec ? c * 16 : 0);
-        const unsigned char* src_tile =
-            (const unsigned char*)((is_gate ? gate : v) + rowoff(xt, t) + col0 + 8 * u);
-        const unsigned char* src = is_rec ? src_rec : src_tile;
+        const unsigned char* bt = kind[i] == 0 ? base_r : (kind[i] == 2 ? base_g : base_v);
+        unsigned off = loff[i];
+        if (kind[i] != 0 && !full) {  // the sequence's last, partial tile: clamp rows into it
+          const int64_t t = row0 + lrow[i] < T ? lrow[i] : T - 1 - row0;
+          off = (unsigned)(2 * (t * rstride + lcol[i]));
+        }
+        const unsigned char* src = bt + off;
         __builtin_amdgcn_global_load_lds(
             (const __attribute__((address_space(1))) void*)src,
-            (__attribute__((address_space(3))) void*)(ring[slot] + base * 16), 16, 0, 0);
+            (__attribute__((address_space(3))) void*)(ring[slot] + (i * kLoaders + lw) * 1024), 16,
+            0, 0);
       }
+    };
+    // Gate chunk of this lane (GATE: kLoaders x 64 lanes cover the tile): it is
+    // replaced in place by w * sigmoid(gate) in float16 one iteration before
+    // the state waves read it.
+    static_assert(!GATE || kLoaders * 64 == SC::kTileB / 16, "one gate chunk per loader lane");
+    const int gp = lw * 64 + lane;                       // chunk position in the tile
+    const int gu = SC::swz(gp / SC::kCpr, gp % SC::kCpr);  // its column chunk
+    float gw[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      gw[e] = (GATE && norm_w != nullptr) ? norm_w[col0 + 8 * gu + e] : 1.f;
+    // The chunk was completed before the last barrier; the direct-to-LDS loads
+    // still in flight target other slots.  Plain loads and stores here would
+    // make the compiler wait for all of those loads first, so the two LDS
+    // accesses are issued directly.
+    auto convert_gate = [&](int slot) {
+      const unsigned addr = (unsigned)(uintptr_t)(
+          (__attribute__((address_space(3))) unsigned char*)(ring[slot] + SC::kG + 16 * gp));
+      i16x8 raw;
+      asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(raw) : "v"(addr));
+      const bf16x8 x = __builtin_bit_cast(bf16x8, raw);
+      f16x8 y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        y[e] = (f16)(gw[e] * __builtin_amdgcn_rcpf(
+                                 1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * (float)x[e])));
+      asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(__builtin_bit_cast(i16x8, y))
+                   : "memory");
     };
 #pragma unroll
     for (int y = 0; y < kLead; ++y) issue(y, y);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((kLead - 1) * SC::kPer));  // tile 0 is in LDS
     __builtin_amdgcn_s_barrier();
-    int slot_issue = kLead;
+    int slot_issue = kLead, slot_cur = 0;
     for (int64_t xl = 0; xl <= nseg; ++xl) {
       issue(xl + kLead, slot_issue);
       slot_issue = slot_issue == kRing - 1 ? 0 : slot_issue + 1;
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((kLead - 1) * SC::kPer));  // tile xl + 1 is in LDS
+      if (GATE && xl < nseg) convert_gate(slot_cur);
+      slot_cur = slot_cur == kRing - 1 ? 0 : slot_cur + 1;
+      // tile xl + 1 is in LDS and the converted gate is written
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((kLead - 1) * SC::kPer));
       __builtin_amdgcn_s_barrier();
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -153,7 +238,6 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
 
   // ============================================================ state waves
   const int wl = wave * CPW;  // first column of this wave, in the workgroup
-  const bool write_o = o != nullptr;
 
   // State: block kb of column block cb, lane (c, g), r = row chan(kb, 4 g + r).
   f32x4 S[NCB][8];
@@ -169,12 +253,6 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
       }
       S[cb][kb] = x;
     }
-  f32x4 wn[NCB];  // norm weight of this lane's 4 output columns (4-byte aligned pointer)
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      wn[cb][r] = (GATE && norm_w != nullptr) ? norm_w[col0 + wl + 16 * cb + 4 * lg + r] : 1.f;
   // Selection matrix for the v transpose: B[k = 4 g + e][c] = (k == c).
   bf16x4 ident;
 #pragma unroll
@@ -187,17 +265,27 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     tile_off[cb] = lc * SC::kRowB + 16 * SC::swz(lc, col / 8) + 2 * (col % 8);
   }
 
-  f32x4 Oprev[NCB];
+  f32x4 Oa[NCB], Ob[NCB];  // outputs of even / odd tiles (finished one tile later)
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) Oprev[cb] = zero4();
+  for (int cb = 0; cb < NCB; ++cb) Oa[cb] = Ob[cb] = zero4();
+  // Output of tile x: this lane writes token lc, columns col0 + wl + 16 cb + 4 lg.
+  const int64_t o_lane = lc * rstride + col0 + wl + 4 * lg;
+  auto o_tile = [&](int64_t x) { return o + ((b * T + (x0 + x) * rec::kC) * H + h) * rec::kDV; };
   __syncthreads();  // tile 0 is in LDS
 
   int slot = 0;  // ring slot of tile xl
-  for (int64_t xl = 0; xl <= nseg; ++xl) {
+  // One tile per call: the epilogue of tile xl - 1 and the state step of tile
+  // xl.  The first and last calls are peeled, so that the steady state is one
+  // basic block and the epilogue's arithmetic can fill the matrix-core chain.
+  // Only the sequence's last tile can be partial (`tail`).
+  auto step = [&](int64_t xl, auto EPI, auto CHAIN, bool tail, f32x4 (&Oprev)[NCB],
+                  f32x4 (&O)[NCB]) {
+    constexpr bool kEpi = decltype(EPI)::value && GATE;
+    constexpr bool kChain = decltype(CHAIN)::value;
     const int slot_prev = slot == 0 ? kRing - 1 : slot - 1;
 
     // ---- epilogue of tile xl - 1: y = O / rms(O) * w * sigmoid(gate)
-    if (GATE && write_o && xl >= 1) {
+    if constexpr (kEpi) {
       float ss = 0.f;
 #pragma unroll
       for (int w = 0; w < NSW; ++w) ss += rs[(xl - 1) & 1][lc][w];
@@ -205,20 +293,17 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
       const int64_t tok = (x0 + xl - 1) * rec::kC + lc;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        const bf16x4 g4 = *(const bf16x4*)(ring[slot_prev] + SC::kG + tile_off[cb]);
+        // w * sigmoid(gate) of this lane's 4 columns, converted by the loader waves
+        const f16x4 sw = *(const f16x4*)(ring[slot_prev] + SC::kG + tile_off[cb]);
         bf16x4 y;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float sg = __builtin_amdgcn_rcpf(
-              1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * (float)g4[r]));
-          y[r] = (bf16_t)(Oprev[cb][r] * inv * wn[cb][r] * sg);
-        }
-        if (tok < T) *(bf16x4*)(o + rowoff(xl - 1, lc) + col0 + wl + 16 * cb + 4 * lg) = y;
+        for (int r = 0; r < 4; ++r) y[r] = (bf16_t)(Oprev[cb][r] * inv * (float)sw[r]);
+        if (!tail || tok < T) *(bf16x4*)(o_tile(xl - 1) + o_lane + 16 * cb) = y;
       }
     }
 
     // ---- state step of tile xl
-    if (xl < nseg) {
+    if constexpr (kChain) {
       const unsigned char* Rs = ring[slot];
       const f16x4 t_op = *(const f16x4*)(Rs + rec::kT + lane * 8);
       const f16x4 aqk_op = *(const f16x4*)(Rs + rec::kAqk + lane * 8);
@@ -229,7 +314,6 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
         q_op[s] = *(const f16x8*)(Rs + rec::kQh + s * 1024 + lane * 16);
       }
       f16x4 d16[NCB];
-      f32x4 O[NCB];
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         f16x8 sop[4];
@@ -237,20 +321,19 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
         for (int s = 0; s < 4; ++s) sop[s] = cat8(to_h4(S[cb][2 * s]), to_h4(S[cb][2 * s + 1]));
         const bf16x4 vn = *(const bf16x4*)(Rs + SC::kV + tile_off[cb]);
         const f16x4 vop = to_h4(mma16b(vn, ident, zero4()));  // lane (c, g): V[4 g + e][c]
-        // T V as a 16x16x32 product with k-values 4..7 of each lane zero: every
-        // accumulation chain uses one instruction shape (a 16x16x16 result fed
-        // straight into a 16x16x32 accumulator read stale values on gfx950).
-        f32x4 d0 = mma32h(cat8(t_op, f16x4{}), cat8(vop, f16x4{}), zero4()), d1 = zero4();
-        f32x4 o0 = zero4(), o1 = zero4();
+        // T V and D^T Aqk^T are 16x16x32 products with k-values 4..7 of each
+        // lane zero: every accumulation chain uses one instruction shape (a
+        // 16x16x16 result fed straight into a 16x16x32 accumulator read stale
+        // values on gfx950).
+        f32x4 d = mma32h(cat8(t_op, f16x4{}), cat8(vop, f16x4{}), zero4());
+        f32x4 oc = zero4();
 #pragma unroll
-        for (int s = 0; s < 4; s += 2) {
-          d0 = mma32h(w_op[s], sop[s], d0);
-          d1 = mma32h(w_op[s + 1], sop[s + 1], d1);
-          o0 = mma32h(sop[s], q_op[s], o0);
-          o1 = mma32h(sop[s + 1], q_op[s + 1], o1);
+        for (int s = 0; s < 4; ++s) {
+          d = mma32h(w_op[s], sop[s], d);
+          oc = mma32h(sop[s], q_op[s], oc);
         }
-        d16[cb] = to_h4(d0 + d1);
-        O[cb] = mma16h(d16[cb], aqk_op, o0 + o1);
+        d16[cb] = to_h4(d);
+        O[cb] = mma32h(cat8(d16[cb], f16x4{}), cat8(aqk_op, f16x4{}), oc);
       }
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
@@ -260,7 +343,7 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) S[cb][kb] = mma16h(ka, d16[cb], S[cb][kb] * e4);
       }
-      if (GATE) {
+      if constexpr (GATE) {
         float p = 0.f;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
@@ -269,23 +352,40 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
         p += __shfl_xor(p, 16);
         p += __shfl_xor(p, 32);
         if (lg == 0) rs[xl & 1][lc][wave] = p;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) Oprev[cb] = O[cb];
-      } else if (write_o) {
+      } else if constexpr (WO) {
         const int64_t tok = (x0 + xl) * rec::kC + lc;
-        if (tok < T) {
+        if (!tail || tok < T) {
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
             const bf16x4 y = {(bf16_t)O[cb][0], (bf16_t)O[cb][1], (bf16_t)O[cb][2],
                               (bf16_t)O[cb][3]};
-            *(bf16x4*)(o + rowoff(xl, lc) + col0 + wl + 16 * cb + 4 * lg) = y;
+            *(bf16x4*)(o_tile(xl) + o_lane + 16 * cb) = y;
           }
         }
       }
     }
     __syncthreads();  // tile xl + 1 is in LDS; the slot of tile xl - 1 may be refilled
     slot = slot == kRing - 1 ? 0 : slot + 1;
+  };
+  using yes = std::true_type;
+  using no = std::false_type;
+  // Tile xl keeps its output in Oa (xl even) or Ob (xl odd).
+  step(0, no{}, yes{}, nseg == 1, Ob, Oa);
+  int64_t xl = 1;
+  for (; xl + 2 < nseg; xl += 2) {
+    step(xl, yes{}, yes{}, false, Oa, Ob);
+    step(xl + 1, yes{}, yes{}, false, Ob, Oa);
   }
+  for (; xl < nseg; ++xl) {  // the last one or two tiles (the last may be partial)
+    if (xl & 1)
+      step(xl, yes{}, yes{}, xl == nseg - 1, Oa, Ob);
+    else
+      step(xl, yes{}, yes{}, xl == nseg - 1, Ob, Oa);
+  }
+  if (nseg & 1)
+    step(nseg, yes{}, no{}, true, Oa, Ob);
+  else
+    step(nseg, yes{}, no{}, true, Ob, Oa);
 
   if (s_next != nullptr) {
 #pragma unroll
@@ -299,37 +399,65 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
   }
 }
 
-template <int DVW, int CPW, bool GATE>
-hipError_t launch_state_t(const ChunkArgs& a, const unsigned char* recs, const float* s_in,
-                          float* s_next, int64_t x0, int64_t nseg) {
-  const int64_t nblk = a.B * a.H * (rec::kDV / DVW);
+// One launch: the state workgroups (first) walk segment `cur` of every head
+// while the remaining workgroups build the records of segment `nxt`.
+struct Seg {
+  int64_t x0 = 0, n = 0;  // first tile, tile count (n = 0: none)
+  unsigned char* recs = nullptr;
+};
+
+int device_cus() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  return cus > 0 ? cus : 256;
+}
+
+template <int DVW, int CPW, bool GATE, bool WO>
+hipError_t launch_state_t(const ChunkArgs& a, Seg cur, const float* s_in, float* s_next, Seg nxt,
+                          int cus) {
+  constexpr int NW = DVW / CPW + kLoaders;
+  const int64_t BH = a.B * a.H;
+  const int64_t n_state = cur.n > 0 ? BH * (rec::kDV / DVW) : 0;
+  int64_t n_tile = 0;
+  if (nxt.n > 0) {
+    const int64_t want = (BH * nxt.n + NW - 1) / NW;  // one tile per wavefront at most
+    int64_t avail = cus - n_state;
+    if (avail < cus / 4) avail = cus / 4;              // always make progress
+    n_tile = want < avail ? want : avail;
+  }
+  const int64_t nblk = n_state + n_tile;
+  if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((kda_state_kernel<DVW, CPW, GATE>), dim3((unsigned)nblk),
-                     dim3(64 * (DVW / CPW + kLoaders)), 0, (hipStream_t)a.stream, recs,
-                     (const bf16_t*)a.v, s_in, s_next, (bf16_t*)a.o, (const bf16_t*)a.gate,
-                     a.norm_w, a.eps, a.T, a.H, a.B * a.H, x0, nseg);
+  tile::Args tb{(const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, nxt.recs,
+                a.T, a.H, BH, nxt.x0, nxt.n > 0 ? nxt.n : 1, a.scale};
+  hipLaunchKernelGGL((kda_state_kernel<DVW, CPW, GATE, WO>), dim3((unsigned)nblk), dim3(64 * NW),
+                     0, (hipStream_t)a.stream, cur.recs, (const bf16_t*)a.v, s_in, s_next,
+                     (bf16_t*)a.o, (const bf16_t*)a.gate, a.norm_w, a.eps, a.T, a.H, BH, cur.x0,
+                     cur.n > 0 ? cur.n : 1, n_state, tb);
   return hipGetLastError();
 }
 
 // Columns per workgroup: a head's whole dv row when the gated norm is fused
-// (it needs the row), otherwise half of it when that is what fills the GPU.
-int split_for(const ChunkArgs& a) {
-  if (a.gate != nullptr) return 1;
+// (it needs the row); otherwise half of it when the state workgroups of the
+// split still leave half of the compute units to the tile workgroups.
+int split_for(const ChunkArgs& a, int cus) {
+  if (a.gate != nullptr && a.o != nullptr) return 1;
   if (const char* e = getenv("KDA_CHUNK_SPLIT")) {
     const int s = atoi(e);
     if (s == 1 || s == 2) return s;
   }
-  return (a.B * a.H < 256) ? 2 : 1;
+  return (2 * a.B * a.H <= cus / 2) ? 2 : 1;
 }
 
-// Tiles per segment: the records of one segment of all heads are written by
-// the tile kernel and read back by the state kernel right after, so a segment
-// is sized to stay resident in the 256 MB memory-side cache.
+// Tiles per segment: one launch per segment, so longer segments amortise the
+// launch and the pipeline fill of the state workgroups; each of the two record
+// buffers holds one segment of all heads (about 256 MiB).
 int64_t seg_tiles(int64_t BH, int64_t nchunks) {
   int64_t seg = 0;
   if (const char* e = getenv("KDA_SEG_TILES")) seg = atoll(e);
   if (seg <= 0) {
-    constexpr int64_t kTarget = int64_t(128) << 20;
+    constexpr int64_t kTarget = int64_t(256) << 20;
     seg = kTarget / (BH * (int64_t)rec::kBytes);
   }
   if (seg < 1) seg = 1;
@@ -345,29 +473,45 @@ bool chunk_mfma_supports(int dk, int dv, bool io_bf16) {
 size_t chunk_mfma_workspace(int64_t B, int64_t T, int64_t H) {
   const int64_t BH = B * H, nch = (T + rec::kC - 1) / rec::kC;
   const int64_t seg = seg_tiles(BH, nch);
-  // records of one segment, then a carried state for when s_out is absent
-  return (size_t)(BH * seg * rec::kBytes) + (size_t)(BH * rec::kDK * rec::kDV * 4);
+  // two record buffers (the segment being consumed and the one being built),
+  // then a carried state for when s_out is absent
+  return (size_t)(2 * BH * seg * rec::kBytes) + (size_t)(BH * rec::kDK * rec::kDV * 4);
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a) {
   if (!chunk_mfma_supports(a.dk, a.dv, a.io_bf16)) return hipErrorNotSupported;
   const int64_t BH = a.B * a.H, nch = (a.T + rec::kC - 1) / rec::kC;
   const int64_t seg = seg_tiles(BH, nch);
-  unsigned char* recs = (unsigned char*)a.workspace;
-  float* carry = a.s_out != nullptr ? a.s_out : (float*)(recs + BH * seg * rec::kBytes);
-  const int split = split_for(a);
-  for (int64_t x0 = 0; x0 < nch; x0 += seg) {
-    const int64_t n = (nch - x0) < seg ? (nch - x0) : seg;
-    hipError_t e = launch_chunk_tiles(a, recs, x0, n);
-    if (e != hipSuccess) return e;
-    const float* s_in = (x0 == 0) ? a.s0 : carry;
-    float* s_next = (x0 + n >= nch) ? a.s_out : carry;
-    if (a.gate != nullptr)
-      e = launch_state_t<128, 32, true>(a, recs, s_in, s_next, x0, n);
+  const int64_t nsegs = (nch + seg - 1) / seg;
+  unsigned char* buf[2] = {(unsigned char*)a.workspace,
+                           (unsigned char*)a.workspace + BH * seg * rec::kBytes};
+  float* carry = a.s_out != nullptr ? a.s_out : (float*)(buf[1] + BH * seg * rec::kBytes);
+  const int cus = device_cus();
+  const int split = split_for(a, cus);
+  auto segment = [&](int64_t j) {
+    Seg sg;
+    if (j >= 0 && j < nsegs) {
+      sg.x0 = j * seg;
+      sg.n = (nch - sg.x0) < seg ? (nch - sg.x0) : seg;
+      sg.recs = buf[j & 1];
+    }
+    return sg;
+  };
+  // Launch j: state pass over segment j, records of segment j + 1.
+  for (int64_t j = -1; j < nsegs; ++j) {
+    const Seg cur = segment(j), nxt = segment(j + 1);
+    const float* s_in = (j <= 0) ? a.s0 : carry;
+    float* s_next = (j == nsegs - 1) ? a.s_out : carry;
+    hipError_t e;
+    if (a.o == nullptr)
+      e = split == 2 ? launch_state_t<64, 32, false, false>(a, cur, s_in, s_next, nxt, cus)
+                     : launch_state_t<128, 32, false, false>(a, cur, s_in, s_next, nxt, cus);
+    else if (a.gate != nullptr)
+      e = launch_state_t<128, 32, true, true>(a, cur, s_in, s_next, nxt, cus);
     else if (split == 2)
-      e = launch_state_t<64, 32, false>(a, recs, s_in, s_next, x0, n);
+      e = launch_state_t<64, 32, false, true>(a, cur, s_in, s_next, nxt, cus);
     else
-      e = launch_state_t<128, 32, false>(a, recs, s_in, s_next, x0, n);
+      e = launch_state_t<128, 32, false, true>(a, cur, s_in, s_next, nxt, cus);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -59,13 +59,11 @@ struct NormArgs {
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_chunk_valu(const ChunkArgs& a);
-// Matrix-core prefill (tile kernel + state kernel, segment by segment).
+// Matrix-core prefill (tile records and state pass, segment by segment).
 // Returns hipErrorNotSupported when it does not cover the shape.
 hipError_t launch_chunk_mfma(const ChunkArgs& a);
 bool chunk_mfma_supports(int dk, int dv, bool io_bf16);
 size_t chunk_mfma_workspace(int64_t B, int64_t T, int64_t H);
-// Tile kernel alone: records of tiles x0 .. x0 + nseg - 1 of every head.
-hipError_t launch_chunk_tiles(const ChunkArgs& a, unsigned char* recs, int64_t x0, int64_t nseg);
 hipError_t launch_gate_rmsnorm(const NormArgs& a);
 
 }  // namespace kda

@@ -77,12 +77,12 @@ typedef enum {
  * Computed chunkwise in 16-token tiles ("Kimi K3: Engineering ...", section
  * "Dimension 1"); the result equals the token-by-token recurrence up to
  * floating-point rounding.  With bfloat16 io and dk = dv = 128 it runs on the
- * matrix cores as two kernels per segment of tiles: a tile kernel computes
- * the state-independent part of every tile of the segment in parallel into
- * the workspace, then a state kernel walks the tiles of each head in order
- * with the running state on chip.  The state is written to memory only at
- * segment boundaries (to s_out, or to the workspace when s_out is NULL) and
- * at the end.
+ * matrix cores, one launch per segment of tiles: its first workgroups walk
+ * the tiles of the segment of each head in order with the running state on
+ * chip, while the other workgroups compute the state-independent part of
+ * every tile of the next segment (the per-tile records) into the workspace.
+ * The state is written to memory only at segment boundaries (to s_out, or to
+ * the workspace when s_out is NULL) and at the end.
  *
  *   q     [B, T, H, dk]  io dtype   queries
  *   k     [B, T, H, dk]  io dtype   keys (the method expects unit L2 norm; not checked)
@@ -118,10 +118,10 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
 
 /*
  * kda_chunk_fwd_workspace_size -- bytes of workspace kda_chunk_fwd needs for
- * these sizes: 0 for the vector-ALU path, otherwise the records of one segment
- * of tiles (bounded near 128 MiB, or 13,824 bytes per head when one tile of
- * every head exceeds that) plus one float32 state per head.  Returns 0 for
- * arguments kda_chunk_fwd would reject.
+ * these sizes: 0 for the vector-ALU path, otherwise two buffers of per-tile
+ * records, each holding one segment of tiles of every head (about 256 MiB, or
+ * 13,824 bytes per head when one tile of every head exceeds that), plus one
+ * float32 state per head.  Returns 0 for arguments kda_chunk_fwd would reject.
  */
 size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk, int dv,
                                     kda_dtype io);
