@@ -211,3 +211,48 @@ def test_full_width_workload_sampled(kda):
     Sg = np.stack([f64(S[b, h]) for b, h in heads])
     assert_close(yg, y_ref, TOL, "y", BF)
     assert_close(Sg, S_ref, TOL, "state")
+
+
+@pytest.fixture(params=["1", "3"])
+def short_segments(request, monkeypatch):
+    """Segments of 1 or 3 tiles: every tile boundary is also a launch boundary
+    (state carried through s_out or the workspace, records double-buffered)."""
+    monkeypatch.setenv("KDA_SEG_TILES", request.param)
+    return int(request.param)
+
+
+@pytest.mark.parametrize("T", [17, 100, 161])
+def test_mfma_segments_ragged(kda, split, short_segments, T):
+    q, k, v, g, beta, s0, _ = gen(1, T, 3, 1200 + T, g_std=2.0, s0_std=0.05)
+    o, S = kda.chunk_fwd(q, k, v, g, beta, s0)
+    o_ref, S_ref = oracle(q, k, v, g, beta, s0)
+    torch.cuda.synchronize()
+    assert_close(f64(o), o_ref, TOL, f"o T={T}", BF)
+    assert_close(f64(S), S_ref, TOL, f"state T={T}")
+
+
+def test_mfma_segments_gate(kda, short_segments):
+    q, k, v, g, beta, s0, gate = gen(2, 90, 2, 1301, s0_std=0.02, gate=True)
+    w = 1.0 + 0.2 * torch.randn(128, device=dev())
+    y, S = kda.chunk_fwd(q, k, v, g, beta, s0, gate=gate, norm_w=w, eps=1e-6)
+    y_ref, S_ref = oracle(q, k, v, g, beta, s0, gate, norm_w=w)
+    torch.cuda.synchronize()
+    assert_close(f64(y), y_ref, TOL, "y", BF)
+    assert_close(f64(S), S_ref, TOL, "state")
+
+
+def test_mfma_segments_state_paths(kda, short_segments):
+    """Output without a final state (the state is carried in the workspace),
+    the final state alone, and the state updated in place (s_out == s0)."""
+    q, k, v, g, beta, s0, _ = gen(2, 70, 2, 1401, s0_std=0.05)
+    o_ref, S_ref = oracle(q, k, v, g, beta, s0)
+    o, none = kda.chunk_fwd(q, k, v, g, beta, s0, final_state=False)
+    assert none is None
+    _, S = kda.chunk_fwd(q, k, v, g, beta, s0, output=False)
+    st = s0.clone()
+    o2, _ = kda.chunk_fwd(q, k, v, g, beta, st, s_out=st)
+    torch.cuda.synchronize()
+    assert_close(f64(o), o_ref, TOL, "o, no final state", BF)
+    assert_close(f64(S), S_ref, TOL, "state only")
+    assert_close(f64(st), S_ref, TOL, "state in place")
+    assert_close(f64(o2), o_ref, TOL, "o, state in place", BF)
