@@ -89,8 +89,9 @@ def source_digest(kernel):
 
 
 def measured_traffic(kernel, workload):
-    """HBM bytes per launch from the committed rocprofv3 counter record, or None
-    when there is none or the kernel's source changed since it was taken."""
+    """HBM bytes per step (one kda_chunk_fwd or kda_decode_step call, summed
+    over its launches) from the committed rocprofv3 counter record, or None
+    when there is none or the kernel's sources changed since it was taken."""
     path = os.path.join(PROFILES, "hbm_traffic.json")
     if not os.path.exists(path):
         return None
@@ -99,7 +100,7 @@ def measured_traffic(kernel, workload):
     e = rec.get(kernel, {}).get(workload)
     if not e or e.get("source_sha256") != source_digest(kernel):
         return None
-    return e.get("bytes_per_launch")
+    return e.get("bytes_per_step")
 
 
 # ----------------------------------------------------------------------------- CPU oracle leg
@@ -288,7 +289,8 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": measured_traffic(kernel, w.name),
-        "algorithmic_bytes_per_launch": nbytes,
+        "algorithmic_bytes_per_step": nbytes,
+        "launches_per_step": kda.chunk_launches(w.B, w.T, w.H, w.dk, w.dv, io),
         "bytes_per_token_head": per_tok,
         "matrix_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
         "matrix_frac": round(flops / (ms * 1e-3) / 1e12 /
@@ -312,7 +314,7 @@ def main():
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(dgbs / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("kda_decode", wd.name),
-                         "algorithmic_bytes_per_launch": dbytes,
+                         "algorithmic_bytes_per_step": dbytes,
                          "bytes_per_bh": dper},
         }
         log(f"[bench] decode {dms:.4f} ms/step, {dgbs:.0f} GB/s")

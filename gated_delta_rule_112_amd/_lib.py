@@ -49,6 +49,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_chunk_fwd.restype = ci
     lib.kda_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, ci, ci, ci]
     lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.kda_chunk_fwd_launches.argtypes = [i64, i64, i64, ci, ci, ci]
+    lib.kda_chunk_fwd_launches.restype = i64
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32,
                                     i64, i64, ci, ci, f32, ci, vp]
     lib.kda_decode_step.restype = ci
@@ -186,6 +188,12 @@ def chunk_workspace_size(B: int, T: int, H: int, dk: int, dv: int, dtype) -> int
     """Workspace bytes kda_chunk_fwd needs for these sizes (0: none)."""
     return int(load_library().kda_chunk_fwd_workspace_size(int(B), int(T), int(H), int(dk),
                                                            int(dv), _IO[dtype]))
+
+
+def chunk_launches(B: int, T: int, H: int, dk: int, dv: int, dtype) -> int:
+    """Kernel launches one chunk_fwd call makes for these sizes."""
+    return int(load_library().kda_chunk_fwd_launches(int(B), int(T), int(H), int(dk), int(dv),
+                                                     _IO[dtype]))
 
 
 def chunk_kernel_name(dk: int, dv: int, dtype) -> Optional[str]:

@@ -86,6 +86,13 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk, int
   return kda::chunk_mfma_workspace(B, T, H);
 }
 
+int64_t kda_chunk_fwd_launches(int64_t B, int64_t T, int64_t H, int dk, int dv, kda_dtype io) {
+  if ((io != KDA_F32 && io != KDA_BF16) || !dim_ok(dk) || !dim_ok(dv)) return 0;
+  if (prod(B, T, H, dk) < 0 || prod(B, H, dk, dv) < 0) return 0;
+  if (force_valu() || !kda::chunk_mfma_supports(dk, dv, io == KDA_BF16)) return 1;
+  return kda::chunk_mfma_launches(B, T, H);
+}
+
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const float* s0, void* o, float* s_out,
                          const void* gate, const float* norm_w, float eps, int64_t B, int64_t T,

@@ -478,6 +478,12 @@ size_t chunk_mfma_workspace(int64_t B, int64_t T, int64_t H) {
   return (size_t)(2 * BH * seg * rec::kBytes) + (size_t)(BH * rec::kDK * rec::kDV * 4);
 }
 
+int64_t chunk_mfma_launches(int64_t B, int64_t T, int64_t H) {
+  const int64_t nch = (T + rec::kC - 1) / rec::kC;
+  const int64_t seg = seg_tiles(B * H, nch);
+  return (nch + seg - 1) / seg + 1;  // one per segment, plus the first segment's records
+}
+
 hipError_t launch_chunk_mfma(const ChunkArgs& a) {
   if (!chunk_mfma_supports(a.dk, a.dv, a.io_bf16)) return hipErrorNotSupported;
   const int64_t BH = a.B * a.H, nch = (a.T + rec::kC - 1) / rec::kC;

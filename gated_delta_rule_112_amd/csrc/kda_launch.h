@@ -64,6 +64,7 @@ hipError_t launch_chunk_valu(const ChunkArgs& a);
 hipError_t launch_chunk_mfma(const ChunkArgs& a);
 bool chunk_mfma_supports(int dk, int dv, bool io_bf16);
 size_t chunk_mfma_workspace(int64_t B, int64_t T, int64_t H);
+int64_t chunk_mfma_launches(int64_t B, int64_t T, int64_t H);
 hipError_t launch_gate_rmsnorm(const NormArgs& a);
 
 }  // namespace kda

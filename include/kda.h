@@ -164,6 +164,13 @@ kda_status kda_gate_rmsnorm(const void* x, const void* gate, const float* norm_w
                             int64_t rows, int dv, float eps, kda_dtype io, void* stream);
 
 /*
+ * kda_chunk_fwd_launches -- number of kernel launches one kda_chunk_fwd call
+ * makes for these sizes (matrix-core path: one per segment of tiles plus one),
+ * or 0 for arguments kda_chunk_fwd would reject.  For profiling and reporting.
+ */
+int64_t kda_chunk_fwd_launches(int64_t B, int64_t T, int64_t H, int dk, int dv, kda_dtype io);
+
+/*
  * kda_chunk_fwd_kernel -- which prefill kernel kda_chunk_fwd launches for these
  * head sizes and io dtype: "kda_chunk_mfma" (bfloat16 matrix cores) or
  * "kda_chunk_valu" (float32 vector arithmetic), or NULL when the combination is

@@ -31,7 +31,8 @@ def lib():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    for n in ["kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_decode_step",
+    for n in ["kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd_launches",
+              "kda_decode_step",
               "kda_gate_rmsnorm", "kda_status_string", "kda_version"]:
         assert n in names
 
@@ -129,6 +130,12 @@ def test_chunk_workspace(lib):
     assert chunk(lib, ws_bytes=need, override={"ws": P(10, 128)}, **kw) == WORKSPACE
     assert chunk(lib, ws=1, ws_bytes=need, **kw) == ALIAS            # overlaps q
     assert chunk(lib, ws=10, ws_bytes=need, dk=48, B=1, T=16, H=1) == DIM
+    launches = lib.kda_chunk_fwd_launches
+    launches.restype = ctypes.c_int64
+    assert launches(1, 4096, 32, 16, 16, 1) == 1          # vector-ALU path: one kernel
+    assert launches(1, 16, 1, 128, 128, 1) == 2           # one segment + its records
+    assert launches(1, 1 << 20, 96, 128, 128, 1) > 2
+    assert launches(1, 16, 1, 48, 128, 1) == 0
 
 
 def decode(lib, *, q=1, k=2, v=3, g=4, beta=5, state=6, o=7, gate=None, w=None, eps=1e-6,
