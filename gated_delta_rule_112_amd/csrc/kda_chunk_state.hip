@@ -115,7 +115,7 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     tile::Scratch* scratch = (tile::Scratch*)lds;
     const int64_t first = ((int64_t)blockIdx.x - n_state_wg) * NW + wave;
     const int64_t stride = ((int64_t)gridDim.x - n_state_wg) * NW;
-    tile::build_range(next, first, stride, scratch[wave], lane);
+    tile::build_range<(NW <= 8)>(next, first, stride, &scratch[wave], lane);
     return;
   }
 
@@ -283,44 +283,62 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     constexpr bool kEpi = decltype(EPI)::value && GATE;
     constexpr bool kChain = decltype(CHAIN)::value;
     const int slot_prev = slot == 0 ? kRing - 1 : slot - 1;
+    const unsigned char* Rs = ring[slot];
+
+    // The LDS operands are read in two batches (those of the D and O products
+    // first, those of the state update once the products are issued), so
+    // that the step waits for LDS twice rather than once per product.
+    float rsum[NSW];
+    f16x4 sw[NCB];
+    if constexpr (kEpi) {
+#pragma unroll
+      for (int w = 0; w < NSW; ++w) rsum[w] = rs[(xl - 1) & 1][lc][w];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        sw[cb] = *(const f16x4*)(ring[slot_prev] + SC::kG + tile_off[cb]);
+    }
+    f16x4 t_op, aqk_op, ka[8];
+    f16x8 w_op[4], q_op[4];
+    bf16x4 vn[NCB];
+    f32x4 e4[8];
+    if constexpr (kChain) {
+      t_op = *(const f16x4*)(Rs + rec::kT + lane * 8);
+      aqk_op = *(const f16x4*)(Rs + rec::kAqk + lane * 8);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) vn[cb] = *(const bf16x4*)(Rs + SC::kV + tile_off[cb]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        w_op[s] = *(const f16x8*)(Rs + rec::kW + s * 1024 + lane * 16);
+        q_op[s] = *(const f16x8*)(Rs + rec::kQh + s * 1024 + lane * 16);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- epilogue of tile xl - 1: y = O / rms(O) * w * sigmoid(gate)
     if constexpr (kEpi) {
       float ss = 0.f;
 #pragma unroll
-      for (int w = 0; w < NSW; ++w) ss += rs[(xl - 1) & 1][lc][w];
+      for (int w = 0; w < NSW; ++w) ss += rsum[w];
       const float inv = rsqrtf(ss * (1.f / (float)rec::kDV) + eps);
       const int64_t tok = (x0 + xl - 1) * rec::kC + lc;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        // w * sigmoid(gate) of this lane's 4 columns, converted by the loader waves
-        const f16x4 sw = *(const f16x4*)(ring[slot_prev] + SC::kG + tile_off[cb]);
         bf16x4 y;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = (bf16_t)(Oprev[cb][r] * inv * (float)sw[r]);
+        for (int r = 0; r < 4; ++r) y[r] = (bf16_t)(Oprev[cb][r] * inv * (float)sw[cb][r]);
         if (!tail || tok < T) *(bf16x4*)(o_tile(xl - 1) + o_lane + 16 * cb) = y;
       }
     }
 
     // ---- state step of tile xl
     if constexpr (kChain) {
-      const unsigned char* Rs = ring[slot];
-      const f16x4 t_op = *(const f16x4*)(Rs + rec::kT + lane * 8);
-      const f16x4 aqk_op = *(const f16x4*)(Rs + rec::kAqk + lane * 8);
-      f16x8 w_op[4], q_op[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        w_op[s] = *(const f16x8*)(Rs + rec::kW + s * 1024 + lane * 16);
-        q_op[s] = *(const f16x8*)(Rs + rec::kQh + s * 1024 + lane * 16);
-      }
       f16x4 d16[NCB];
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         f16x8 sop[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) sop[s] = cat8(to_h4(S[cb][2 * s]), to_h4(S[cb][2 * s + 1]));
-        const bf16x4 vn = *(const bf16x4*)(Rs + SC::kV + tile_off[cb]);
-        const f16x4 vop = to_h4(mma16b(vn, ident, zero4()));  // lane (c, g): V[4 g + e][c]
+        const f16x4 vop = to_h4(mma16b(vn[cb], ident, zero4()));  // lane (c, g): V[4 g + e][c]
         // T V and D^T Aqk^T are 16x16x32 products with k-values 4..7 of each
         // lane zero: every accumulation chain uses one instruction shape (a
         // 16x16x16 result fed straight into a 16x16x32 accumulator read stale
@@ -335,14 +353,17 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
         d16[cb] = to_h4(d);
         O[cb] = mma32h(cat8(d16[cb], f16x4{}), cat8(aqk_op, f16x4{}), oc);
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
-        const f16x4 ka = *(const f16x4*)(Rs + rec::kKb + kb * 512 + lane * 8);
-        const f32x4 e4 =
-            *(const f32x4*)(Rs + rec::kEn + 4 * (32 * (kb / 2) + 8 * lg + 4 * (kb % 2)));
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) S[cb][kb] = mma16h(ka, d16[cb], S[cb][kb] * e4);
+        ka[kb] = *(const f16x4*)(Rs + rec::kKb + kb * 512 + lane * 8);
+        e4[kb] = *(const f32x4*)(Rs + rec::kEn + 4 * (32 * (kb / 2) + 8 * lg + 4 * (kb % 2)));
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) S[cb][kb] = mma16h(ka[kb], d16[cb], S[cb][kb] * e4[kb]);
       if constexpr (GATE) {
         float p = 0.f;
 #pragma unroll
@@ -450,15 +471,23 @@ int split_for(const ChunkArgs& a, int cus) {
   return (2 * a.B * a.H <= cus / 2) ? 2 : 1;
 }
 
-// Tiles per segment: one launch per segment, so longer segments amortise the
-// launch and the pipeline fill of the state workgroups; each of the two record
-// buffers holds one segment of all heads (about 256 MiB).
+// Tiles per segment.  One launch per segment, and the records of the
+// segment being consumed are read back while the next segment's are written:
+// a segment of about 64 MiB of records stays within the 256 MB memory-side
+// cache with the rest of a launch's traffic, which makes the read-back
+// cheaper; longer sequences use longer segments (at most about 64 launches,
+// at most 256 MiB per record buffer) so that the per-launch cost (state load
+// and store, pipeline fill) stays small.
 int64_t seg_tiles(int64_t BH, int64_t nchunks) {
   int64_t seg = 0;
   if (const char* e = getenv("KDA_SEG_TILES")) seg = atoll(e);
   if (seg <= 0) {
-    constexpr int64_t kTarget = int64_t(256) << 20;
-    seg = kTarget / (BH * (int64_t)rec::kBytes);
+    const int64_t per_row = BH * (int64_t)rec::kBytes;  // record bytes of one tile of every head
+    seg = (int64_t(64) << 20) / per_row;
+    const int64_t min_seg = (nchunks + 63) / 64;
+    if (seg < min_seg) seg = min_seg;
+    const int64_t cap = (int64_t(256) << 20) / per_row;
+    if (seg > cap) seg = cap;
   }
   if (seg < 1) seg = 1;
   return seg < nchunks ? seg : nchunks;
@@ -494,6 +523,11 @@ hipError_t launch_chunk_mfma(const ChunkArgs& a) {
   float* carry = a.s_out != nullptr ? a.s_out : (float*)(buf[1] + BH * seg * rec::kBytes);
   const int cus = device_cus();
   const int split = split_for(a, cus);
+  // State columns per state wavefront: 16 (two state wavefronts per SIMD, so
+  // that one's matrix-core and LDS latencies are covered by the other's work)
+  // unless KDA_CPW=32 asks for one wavefront of 32 columns per SIMD.
+  int cpw = 16;
+  if (const char* e = getenv("KDA_CPW")) cpw = atoi(e) == 32 ? 32 : 16;
   auto segment = [&](int64_t j) {
     Seg sg;
     if (j >= 0 && j < nsegs) {
@@ -511,13 +545,16 @@ hipError_t launch_chunk_mfma(const ChunkArgs& a) {
     hipError_t e;
     if (a.o == nullptr)
       e = split == 2 ? launch_state_t<64, 32, false, false>(a, cur, s_in, s_next, nxt, cus)
-                     : launch_state_t<128, 32, false, false>(a, cur, s_in, s_next, nxt, cus);
+          : cpw == 16 ? launch_state_t<128, 16, false, false>(a, cur, s_in, s_next, nxt, cus)
+                      : launch_state_t<128, 32, false, false>(a, cur, s_in, s_next, nxt, cus);
     else if (a.gate != nullptr)
-      e = launch_state_t<128, 32, true, true>(a, cur, s_in, s_next, nxt, cus);
+      e = cpw == 16 ? launch_state_t<128, 16, true, true>(a, cur, s_in, s_next, nxt, cus)
+                    : launch_state_t<128, 32, true, true>(a, cur, s_in, s_next, nxt, cus);
     else if (split == 2)
       e = launch_state_t<64, 32, false, true>(a, cur, s_in, s_next, nxt, cus);
     else
-      e = launch_state_t<128, 32, false, true>(a, cur, s_in, s_next, nxt, cus);
+      e = cpw == 16 ? launch_state_t<128, 16, false, true>(a, cur, s_in, s_next, nxt, cus)
+                    : launch_state_t<128, 32, false, true>(a, cur, s_in, s_next, nxt, cus);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
