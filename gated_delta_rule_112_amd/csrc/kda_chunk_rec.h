@@ -1,6 +1,6 @@
-// Matrix-core chunked prefill (bfloat16 io, dk = dv = 128): the per-tile
-// record that the tile kernel writes and the state kernel reads, and the small
-// device helpers both kernels use.
+// Matrix-core chunked prefill (bfloat16 io, dk = dv = 128): the record that
+// the tile builder writes for every pair of 16-token tiles and the state pass
+// reads, and the small device helpers both use.
 //
 // Chunkwise algebra ("Kimi K3: Engineering a 2.8 Trillion Parameter
 // Frontier", section "Dimension 1": 16-token tiles, cumulative log-decay in
@@ -8,27 +8,38 @@
 // tile of 16 tokens (rows past the end of the sequence are zero inputs with
 // g = beta = 0, which leave the state unchanged) with start state S (dk x dv,
 // rows = key channels) and G = in-tile inclusive cumulative sum of g:
-//   Qh = scale q e^G,  Kh = k e^G,  Kc = k e^-G,  Kb = k e^(G_15 - G)
+//   Qh = scale q e^G,  Kh = k e^G,  Kc = k e^-G,  Kb = k e^(G_15 - G),  E = e^G_15
 //   A  = strict_lower(Diag(beta) Kh Kc^T)     Aqk = lower(Qh Kc^T)
 //   T  = (I + A)^-1 Diag(beta)                W = T Kh
 //   D  = T V - W S                            O = Qh S + Aqk D
-//   S <- Diag(e^G_15) S + Kb^T D
-// Everything but the last three lines is independent of the state, so the
-// tile kernel computes it for all tiles in parallel and stores it as a record;
-// the state kernel then walks the tiles of a head in order.
+//   S <- Diag(E) S + Kb^T D
+// The state pass steps over two tiles a, b at once.  Substituting the state
+// after tile a into tile b's lines gives, with every factor bounded by the
+// tile-local quantities above (so float16 holds them):
+//   D_a = T_a V_a - W_a S
+//   D_b = T_b V_b - W_b' S + P D_a           W_b' = W_b Diag(E_a), P = -W_b Kb_a^T
+//   O_a = Qh_a S + Aqk_a D_a
+//   O_b = Qh_b' S + Q_ba D_a + Aqk_b D_b     Qh_b' = Qh_b Diag(E_a), Q_ba = Qh_b Kb_a^T
+//   S  <- Diag(E_a E_b) S + Kb_a'^T D_a + Kb_b^T D_b      Kb_a' = Kb_a Diag(E_b)
+// so the state is decayed, converted and updated once per 32 tokens, the
+// update being one 32-deep product.  Everything but these lines is
+// independent of the state: the tile builder computes it for all pairs in
+// parallel and stores it as a record; the state pass walks the pairs of a
+// head in order.
 //
 // Record layout.  Matrix operands are stored as the register image of one
 // 64-lane wavefront (lane l = 16 g + c, c = l % 16, g = l / 16) so that the
-// state kernel moves them with linear 16-byte copies and reads every operand
+// state pass moves them with linear 16-byte copies and reads every operand
 // with one conflict-free LDS access per lane:
-//   Qh   [slab s < 4][lane][8] f16   lane (t, g): Qh[t][32 s + 8 g + e]
-//   -W   [slab s < 4][lane][8] f16   lane (i, g): -W[i][32 s + 8 g + e]
-//   Kb^T [block b < 8][lane][4] f16  lane (c, g): Kb[4 g + r][chan(b, c)]
-//   en   [128] f32                   e^(G_15) per key channel
-//   T    [lane][4] f16               lane (i, g): T[i][4 g + r]
-//   Aqk  [lane][4] f16               lane (t, g): Aqk[t][4 g + r]
+//   -W_a, -W_b'  [slab s < 4][lane][8] f16   lane (i, g): -W[i][32 s + 8 g + e]
+//   Qh_a, Qh_b'  [slab s < 4][lane][8] f16   lane (t, g): Qh[t][32 s + 8 g + e]
+//   Kb           [block b < 8][lane][8] f16  lane (c, g): Kb_a'[4 g + e][chan(b, c)] (e < 4),
+//                                                         Kb_b[4 g + e - 4][chan(b, c)] (e >= 4)
+//   en           [128] f32                   E_a E_b per key channel
+//   T_a, T_b, Aqk_a, Aqk_b, P, Q_ba
+//                [lane][4] f16               lane (i, g): X[i][4 g + r]
 // where chan(b, p) = 32 (b / 2) + 8 (p / 4) + 4 (b % 2) + p % 4 is the key
-// channel held in row p of state block b.  The state kernel keeps its state
+// channel held in row p of state block b.  The state pass keeps its state
 // rows in that order: the 16x16 accumulator layout gives lane (c, g) rows
 // 4 g + r of a block, so the rows of blocks 2s and 2s+1 in one lane are
 // exactly channels 32 s + 8 g + 0..7, the k-operand values of that lane in a
@@ -41,15 +52,22 @@ namespace kda {
 namespace rec {
 
 constexpr int kC = 16;       // tokens per tile
+constexpr int kP = 32;       // tokens per pair (one state step)
 constexpr int kDK = 128;     // key head size
 constexpr int kDV = 128;     // value head size
-constexpr int kQh = 0;
-constexpr int kW = 4096;
-constexpr int kKb = 8192;
-constexpr int kEn = 12288;
-constexpr int kT = 12800;
-constexpr int kAqk = 13312;
-constexpr int kBytes = 13824;  // a multiple of 256
+constexpr int kWa = 0;
+constexpr int kWb = 4096;
+constexpr int kQa = 8192;
+constexpr int kQb = 12288;
+constexpr int kKb = 16384;
+constexpr int kEn = 24576;
+constexpr int kTa = 25088;
+constexpr int kTb = 25600;
+constexpr int kAa = 26112;
+constexpr int kAb = 26624;
+constexpr int kPm = 27136;
+constexpr int kQba = 27648;
+constexpr int kBytes = 28160;  // a multiple of 256
 
 __host__ __device__ constexpr int chan(int b, int p) {
   return 32 * (b / 2) + 8 * (p / 4) + 4 * (b % 2) + p % 4;

@@ -1,38 +1,47 @@
-// State kernel of the matrix-core chunked prefill: walks the tiles of one
-// head in order with the float32 state resident in matrix-core accumulators,
-// consuming the per-tile records of the tile kernel (kda_chunk_rec.h):
-//   D = T V - W S,   O = Qh S + Aqk D,   S <- Diag(e^G_15) S + Kb^T D
+// State pass of the matrix-core chunked prefill: walks the pairs of 16-token
+// tiles of one head in order with the float32 state resident in matrix-core
+// accumulators, consuming the per-pair records of the tile builder
+// (kda_chunk_rec.h):
+//   D_a = T_a V_a - W_a S                 O_a = Qh_a S + Aqk_a D_a
+//   D_b = T_b V_b - W_b' S + P D_a        O_b = Qh_b' S + Q_ba D_a + Aqk_b D_b
+//   S  <- Diag(E_a E_b) S + [Kb_a' | Kb_b]^T [D_a ; D_b]
 // ("Kimi K3: Engineering a 2.8 Trillion Parameter Frontier", section
 // "Dimension 1"), and, when a gate is given, the head-wise RMSNorm x
 // sigmoid(gate) epilogue ("Kimi K3 Architecture Explained ...", section
 // "Token mixing").
 //
-// One workgroup owns one (b, h) and DVW of its value columns (all 128, or 64
-// when two workgroups share a head).  It has two kinds of wavefronts:
+// One launch per segment of pairs.  The first workgroups of the launch run
+// the state pass over the segment; the remaining ones build the records of
+// the next segment (kda_chunk_tile.h) into the other half of the workspace.
+//
+// A state workgroup owns one (b, h) and DVW of its value columns (all 128, or
+// 64 when two workgroups share a head).  It has two kinds of wavefronts:
 //   state waves (DVW / CPW): each keeps CPW state columns x 128 rows in 16x16
 //     accumulators, rows in the permuted channel order of the record, so that
 //     the state is the k-operand of its own products without moving between
 //     lanes:
-//       D   (lane (c, g): D[4 g + r][c]) = T V + sum_s (-W)_s S_s          (16x16x32)
-//       O^T (lane (t, g): O[t][4 g + r]) = sum_s S_s^T Qh_s^T + D^T Aqk^T (transposed:
-//            each lane holds 4 consecutive output columns of one token)
-//       S_b <- e^G_15 * S_b + Kb^T_b D                                     (16x16x16)
-//     V is moved from its token-major tile into the k-operand layout by a
-//     bf16 product with a 0/1 selection matrix (exact).  The output of tile x
-//     is normalised and written in iteration x + 1, once the row sums of
-//     squares of all state waves are in LDS.
-//   loader waves (kLoaders): copy each tile's record, v tile and gate tile
-//     from memory straight into an LDS ring slot with direct-to-LDS loads,
-//     kLead tiles ahead of the state waves, and wait for the next tile's
-//     copies before every workgroup barrier.  The state waves issue no
-//     global loads inside the loop.
-// One workgroup barrier per tile.  Each accumulation chain uses a single
-// matrix instruction shape.
+//       D   (lane (c, g): D[4 g + r][c])         16x16x32 products over slabs
+//       O^T (lane (t, g): O[t][4 g + r])         transposed: each lane holds 4
+//                                                consecutive output columns of one token
+//       S_b <- E * S_b + Kb^T_b [D_a ; D_b]      one 16x16x32 product per block
+//     V is moved from its token-major rows into the k-operand layout by a bf16
+//     product with a 0/1 selection matrix (exact).
+//   loader waves (kLoaders): copy each pair's record and v rows into an LDS
+//     ring slot, and its gate rows into a slot of a second ring, from memory
+//     with direct-to-LDS loads, kLead pairs ahead of the state waves, and wait
+//     for the next pair's copies before the barrier that ends a step; with
+//     the gate they also turn the gate rows of the pair being consumed into
+//     w * sigmoid(gate) (float16) in place.
+// One barrier per step (pair).  The output of pair x is normalised and
+// written during step x + 1, once the row sums of squares of all state waves
+// are in LDS, so its arithmetic fills the matrix-core chains of the next
+// pair; its gate rows outlive its record slot by a step, hence the second
+// ring.  Each accumulation chain uses a single matrix instruction shape.
 //
-// LDS ring slot: [record][v tile][gate tile][pad].  The v and gate tiles hold
-// 16 rows of DVW bf16 columns with the 16-byte chunk u of row t stored at
-// chunk position swz(t, u), so that the 8-byte reads of the state waves (one
-// token per lane, 4 columns) fall in distinct banks.
+// LDS ring slot: [record][v rows]; gate slot: [gate rows].  The v and gate
+// areas hold 32 rows of DVW bf16 columns with the 16-byte chunk u of row t
+// stored at chunk position swz(t, u), so that the 8-byte reads of the state
+// waves (one token per lane, 4 columns) fall in distinct banks.
 //
 // Precision: the state and every accumulation are float32; the state and D
 // enter the products as float16 (11-bit significand), which requires the
@@ -48,9 +57,7 @@
 namespace kda {
 namespace {
 
-constexpr int kLoaders = 4;       // loader wavefronts, one per SIMD
-constexpr int kLead = 4;          // tiles in flight ahead of the one being consumed
-constexpr int kRing = kLead + 2;  // + the tile being consumed + the one being finished
+constexpr int kLoaders = 4;  // loader wavefronts, one per SIMD
 
 // s_waitcnt with vmcnt = N and the other counters left alone (gfx9 encoding).
 constexpr unsigned vmcnt_imm(int n) {
@@ -65,16 +72,23 @@ template <int DVW, bool GATE>
 struct SlotCfg {
   static constexpr int kRowB = DVW * 2;                  // bytes per v / gate row
   static constexpr int kCpr = DVW / 8;                   // 16-byte chunks per row
-  static constexpr int kTileB = rec::kC * kRowB;         // bytes per v / gate tile
+  static constexpr int kRowsB = rec::kP * kRowB;         // bytes of a pair's v (or gate) rows
   static constexpr int kRecBlocks = (rec::kBytes + 1023) / 1024;
-  static constexpr int kTileBlocks = kTileB / 1024;
-  static constexpr int kV = kRecBlocks * 1024;           // v tile offset in a slot
-  static constexpr int kG = kV + kTileB;                 // gate tile offset
-  static constexpr int kData = kG + (GATE ? kTileB : 0);
+  static constexpr int kV = kRecBlocks * 1024;           // v rows offset in a slot
+  static constexpr int kData = kV + kRowsB;
   static constexpr int kInstr = kLoaders * 1024;         // bytes per loader round
   static constexpr int kSlot = (kData + kInstr - 1) / kInstr * kInstr;
-  static constexpr int kPer = kSlot / kInstr;            // loads per loader wave per tile
-  static_assert(kTileB % 1024 == 0, "v tiles must be whole blocks");
+  static constexpr int kGSlot = GATE ? kRowsB : 0;       // gate slot
+  static constexpr int kPer = (kSlot + kGSlot) / kInstr; // loads per loader wave per pair
+  // Ring: the pair being consumed and kLead pairs in flight, within 150 KB
+  // with the gate ring (kLead + 2 slots: the gate of the pair before is read
+  // by the epilogue of the step, that of the pair consumed is converted).
+  static constexpr int kRing = (150 * 1024 / (kSlot + kGSlot)) < 4
+                                   ? (150 * 1024 / (kSlot + kGSlot)) : 4;
+  static constexpr int kLead = kRing - 1;
+  static constexpr int kGRing = GATE ? kLead + 2 : 0;
+  static_assert(kRowsB % 1024 == 0 && kGSlot % kInstr == 0, "v and gate rows must be whole rounds");
+  static_assert(kLead >= 1, "the ring needs a slot in flight");
   static constexpr int kRowsPerBankLine = 256 / kRowB;   // rows sharing the 64 banks
   // Chunk position of chunk u of row t (an involution in u for fixed t).
   static __device__ __forceinline__ int swz(int t, int u) {
@@ -90,6 +104,7 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
                  const float* __restrict__ norm_w, float eps, int64_t T, int64_t H, int64_t BH,
                  int64_t x0, int64_t nseg, int64_t n_state_wg, tile::Args next) {
   using SC = SlotCfg<DVW, GATE>;
+  constexpr int kRing = SC::kRing, kLead = SC::kLead;
   constexpr int NSW = DVW / CPW;   // state wavefronts
   constexpr int NCB = CPW / 16;    // 16-column blocks per state wavefront
   constexpr int NSPLIT = rec::kDV / DVW;
@@ -100,8 +115,9 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
 
   constexpr int NW = NSW + kLoaders;  // wavefronts per workgroup
   constexpr int kRingB = kRing * SC::kSlot;
-  constexpr int kRsB = 2 * rec::kC * NSW * 4;
-  constexpr int kStateB = kRingB + kRsB;
+  constexpr int kGRingB = SC::kGRing * SC::kGSlot;
+  constexpr int kRsB = 2 * rec::kP * NSW * 4;
+  constexpr int kStateB = kRingB + kGRingB + kRsB;
   constexpr int kTileB = NW * (int)sizeof(tile::Scratch);
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kStateB > kTileB ? kStateB : kTileB];
 
@@ -115,13 +131,15 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     tile::Scratch* scratch = (tile::Scratch*)lds;
     const int64_t first = ((int64_t)blockIdx.x - n_state_wg) * NW + wave;
     const int64_t stride = ((int64_t)gridDim.x - n_state_wg) * NW;
-    tile::build_range<(NW <= 8)>(next, first, stride, &scratch[wave], lane);
+    tile::build_range(next, first, stride, &scratch[wave], lane);
     return;
   }
 
-  // ======================= state workgroups: the tiles of this segment
+  // ======================= state workgroups: the pairs of this segment
   unsigned char (*ring)[SC::kSlot] = (unsigned char (*)[SC::kSlot])lds;
-  float (*rs)[rec::kC][NSW] = (float (*)[rec::kC][NSW])(lds + kRingB);  // row sums of O^2
+  unsigned char* gring = lds + kRingB;  // gate slots of kGSlot bytes
+  // row sums of O^2, [pair & 1][token of pair][wave]
+  float (*rs)[rec::kP][NSW] = (float (*)[rec::kP][NSW])(lds + kRingB + kGRingB);
 
   // Keep the NSPLIT workgroups of one head on one XCD (workgroups are dealt
   // round-robin over the 8 XCDs) so that they share its records in L2.
@@ -138,14 +156,15 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     // ========================================================== loader waves
     const int lw = wave - NSW;
     const unsigned char* R0 = recs + bh * nseg * (int64_t)rec::kBytes;
-    // Block i kLoaders + lw of a slot is this wave's i-th load.  Its kind and
-    // this lane's source offset are fixed; a tile only moves the base.
+    // Block i kLoaders + lw of a pair (its slot's blocks, then its gate
+    // slot's) is this wave's i-th load.  Its kind and this lane's source
+    // offset are fixed; a pair only moves the base.
     //   record block j:  R0 + x * kBytes + 16 (64 j + lane)   (the padding of the
     //                    last record block re-reads record chunks)
-    //   v / gate block:  row t, column chunk u of the tile:
+    //   v / gate block:  row t (of 32), column chunk u of the pair:
     //                    base_x + t * row stride + 2 (col0 + 8 u)
     int kind[SC::kPer];        // 0 record, 1 v, 2 gate (wave-uniform)
-    unsigned loff[SC::kPer];   // byte offset from the tile base (full tiles)
+    unsigned loff[SC::kPer];   // byte offset from the pair base (full pairs)
     int lrow[SC::kPer], lcol[SC::kPer];
 #pragma unroll
     for (int i = 0; i < SC::kPer; ++i) {
@@ -156,79 +175,99 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
         loff[i] = 16u * (unsigned)(c < rec::kBytes / 16 ? c : c - 64);
         lrow[i] = lcol[i] = 0;
       } else {
-        int q = (blk - SC::kRecBlocks) * 64 + lane;
-        const int which = q / (SC::kTileB / 16);
-        kind[i] = (GATE && which == 1) ? 2 : 1;  // past the gate tile: padding, re-reads v
-        q %= SC::kTileB / 16;
+        int q = (blk < SC::kSlot / 1024 ? blk - SC::kRecBlocks : blk - SC::kSlot / 1024) * 64 + lane;
+        kind[i] = blk < SC::kSlot / 1024 ? 1 : 2;  // v rows (and the slot's padding) or gate rows
+        q %= SC::kRowsB / 16;  // the padding re-reads v rows
         const int t = q / SC::kCpr, u = SC::swz(t, q % SC::kCpr);
         lrow[i] = t;
         lcol[i] = col0 + 8 * u;
         loff[i] = (unsigned)(2 * (t * rstride + lcol[i]));
       }
     }
-    // Copy tile xt (clamped into the segment) into ring slot `slot`.
-    auto issue = [&](int64_t xt, int slot) {
+    // Copy pair xt (clamped into the segment) into ring slot `slot` and gate
+    // slot `gslot`.
+    auto issue = [&](int64_t xt, int slot, int gslot) {
       xt = xt < nseg ? xt : nseg - 1;
-      const int64_t row0 = (x0 + xt) * rec::kC;               // first token of the tile
-      const bool full = row0 + rec::kC <= T;
+      const int64_t row0 = (x0 + xt) * rec::kP;               // first token of the pair
+      const bool full = row0 + rec::kP <= T;
       const unsigned char* base_r = R0 + xt * rec::kBytes;
-      const int64_t tile0 = ((b * T + row0) * H + h) * rec::kDV;  // element offset of row 0
-      const unsigned char* base_v = (const unsigned char*)(v + tile0);
-      const unsigned char* base_g = (const unsigned char*)((GATE ? gate : v) + tile0);
+      const int64_t pair0 = ((b * T + row0) * H + h) * rec::kDV;  // element offset of row 0
+      const unsigned char* base_v = (const unsigned char*)(v + pair0);
+      const unsigned char* base_g = (const unsigned char*)((GATE ? gate : v) + pair0);
 #pragma unroll
       for (int i = 0; i < SC::kPer; ++i) {
         const unsigned char* bt = kind[i] == 0 ? base_r : (kind[i] == 2 ? base_g : base_v);
         unsigned off = loff[i];
-        if (kind[i] != 0 && !full) {  // the sequence's last, partial tile: clamp rows into it
+        if (kind[i] != 0 && !full) {  // the sequence's last, partial pair: clamp rows into it
           const int64_t t = row0 + lrow[i] < T ? lrow[i] : T - 1 - row0;
           off = (unsigned)(2 * (t * rstride + lcol[i]));
         }
         const unsigned char* src = bt + off;
+        const int blk = i * kLoaders + lw;
+        unsigned char* dst = blk < SC::kSlot / 1024
+                                 ? ring[slot] + blk * 1024
+                                 : gring + gslot * SC::kGSlot + (blk - SC::kSlot / 1024) * 1024;
         __builtin_amdgcn_global_load_lds(
             (const __attribute__((address_space(1))) void*)src,
-            (__attribute__((address_space(3))) void*)(ring[slot] + (i * kLoaders + lw) * 1024), 16,
-            0, 0);
+            (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
       }
     };
-    // Gate chunk of this lane (GATE: kLoaders x 64 lanes cover the tile): it is
-    // replaced in place by w * sigmoid(gate) in float16 one iteration before
-    // the state waves read it.
-    static_assert(!GATE || kLoaders * 64 == SC::kTileB / 16, "one gate chunk per loader lane");
-    const int gp = lw * 64 + lane;                       // chunk position in the tile
-    const int gu = SC::swz(gp / SC::kCpr, gp % SC::kCpr);  // its column chunk
-    float gw[8];
+    // Gate chunks of this lane (GATE: the pair's 32 gate rows are
+    // kGateChunks 16-byte chunks, kGatePer per loader lane): replaced in place
+    // by w * sigmoid(gate) in float16 before the barrier after which the
+    // state waves read them.
+    constexpr int kGateChunks = SC::kRowsB / 16;
+    constexpr int kGatePer = kGateChunks / (kLoaders * 64);
+    static_assert(!GATE || kGatePer * kLoaders * 64 == kGateChunks, "whole gate chunks per lane");
+    // Gate chunk gp sits in the pair's block kSlot / 1024 + gp / 64, loaded
+    // by loader wave (that block) % kLoaders = lw: each loader wave converts
+    // only blocks that its own vmcnt wait has seen complete.
+    static_assert((SC::kSlot / 1024) % kLoaders == 0,
+                  "gate blocks must be converted by the wave that loaded them");
+    float gw[kGatePer > 0 ? kGatePer : 1][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      gw[e] = (GATE && norm_w != nullptr) ? norm_w[col0 + 8 * gu + e] : 1.f;
-    // The chunk was completed before the last barrier; the direct-to-LDS loads
-    // still in flight target other slots.  Plain loads and stores here would
-    // make the compiler wait for all of those loads first, so the two LDS
-    // accesses are issued directly.
-    auto convert_gate = [&](int slot) {
-      const unsigned addr = (unsigned)(uintptr_t)(
-          (__attribute__((address_space(3))) unsigned char*)(ring[slot] + SC::kG + 16 * gp));
-      i16x8 raw;
-      asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(raw) : "v"(addr));
-      const bf16x8 x = __builtin_bit_cast(bf16x8, raw);
-      f16x8 y;
+    for (int j = 0; j < kGatePer; ++j) {
+      const int gp = (j * kLoaders + lw) * 64 + lane;             // chunk position in the rows
+      const int gu = SC::swz(gp / SC::kCpr, gp % SC::kCpr);       // its column chunk
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        y[e] = (f16)(gw[e] * __builtin_amdgcn_rcpf(
-                                 1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * (float)x[e])));
-      asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(__builtin_bit_cast(i16x8, y))
-                   : "memory");
+        gw[j][e] = (GATE && norm_w != nullptr) ? norm_w[col0 + 8 * gu + e] : 1.f;
+    }
+    // The chunks were completed before the last barrier; the direct-to-LDS
+    // loads still in flight target other slots.  Plain loads and stores here
+    // would make the compiler wait for all of those loads first, so the LDS
+    // accesses are issued directly.
+    auto convert_gate = [&](int gslot) {
+#pragma unroll
+      for (int j = 0; j < kGatePer; ++j) {
+        const int gp = (j * kLoaders + lw) * 64 + lane;
+        const unsigned addr = lds_addr(gring + gslot * SC::kGSlot + 16 * gp);
+        const bf16x8 x = __builtin_bit_cast(bf16x8, ds_read16(addr));
+        f16x8 y;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          y[e] = (f16)(gw[j][e] * __builtin_amdgcn_rcpf(
+                                      1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * (float)x[e])));
+        ds_write16(addr, as_f4(y));
+      }
     };
 #pragma unroll
-    for (int y = 0; y < kLead; ++y) issue(y, y);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kLead - 1) * SC::kPer));  // tile 0 is in LDS
+    for (int y = 0; y < kLead; ++y) issue(y, y, y);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kLead - 1) * SC::kPer));  // pair 0 is in LDS
     __builtin_amdgcn_s_barrier();
-    int slot_issue = kLead, slot_cur = 0;
-    for (int64_t xl = 0; xl <= nseg; ++xl) {
-      issue(xl + kLead, slot_issue);
+    // Ring slot of pair x: x % kRing; gate slot: x % kGRing.
+    int slot_issue = kLead, gslot_issue = kLead, gslot_cur = 0;
+    for (int64_t xl = 0; xl < nseg; ++xl) {
+      // the slot of pair xl - 1 (free since the last barrier) and the gate
+      // slot of pair xl - 2 (read by the epilogue of the last step)
+      issue(xl + kLead, slot_issue, gslot_issue);
       slot_issue = slot_issue == kRing - 1 ? 0 : slot_issue + 1;
-      if (GATE && xl < nseg) convert_gate(slot_cur);
-      slot_cur = slot_cur == kRing - 1 ? 0 : slot_cur + 1;
-      // tile xl + 1 is in LDS and the converted gate is written
+      if constexpr (GATE) {
+        gslot_issue = gslot_issue == SC::kGRing - 1 ? 0 : gslot_issue + 1;
+        convert_gate(gslot_cur);  // read by the epilogue of the next step
+        gslot_cur = gslot_cur == SC::kGRing - 1 ? 0 : gslot_cur + 1;
+      }
+      // pair xl + 1 is in LDS; the converted gate is written
       __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((kLead - 1) * SC::kPer));
       __builtin_amdgcn_s_barrier();
     }
@@ -257,7 +296,11 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
   bf16x4 ident;
 #pragma unroll
   for (int e = 0; e < 4; ++e) ident[e] = (bf16_t)((4 * lg + e == lc) ? 1.f : 0.f);
-  // LDS byte offset, within a v / gate tile, of this lane's 4 columns of token lc.
+  // LDS byte offset, within the v / gate rows, of this lane's 4 columns of
+  // token lc (tile a); tile b's token lc is 16 rows further, with the same
+  // swizzle (rows 16 apart permute their chunks alike).
+  static_assert(16 % SC::kRowsPerBankLine == 0 && (16 / SC::kRowsPerBankLine) % SC::kCpr == 0,
+                "rows 16 apart must swizzle alike");
   int tile_off[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
@@ -265,148 +308,180 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     tile_off[cb] = lc * SC::kRowB + 16 * SC::swz(lc, col / 8) + 2 * (col % 8);
   }
 
-  f32x4 Oa[NCB], Ob[NCB];  // outputs of even / odd tiles (finished one tile later)
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) Oa[cb] = Ob[cb] = zero4();
-  // Output of tile x: this lane writes token lc, columns col0 + wl + 16 cb + 4 lg.
+  // Output of pair x: this lane writes tokens lc and 16 + lc, columns
+  // col0 + wl + 16 cb + 4 lg.
   const int64_t o_lane = lc * rstride + col0 + wl + 4 * lg;
-  auto o_tile = [&](int64_t x) { return o + ((b * T + (x0 + x) * rec::kC) * H + h) * rec::kDV; };
-  __syncthreads();  // tile 0 is in LDS
+  auto o_pair = [&](int64_t x) { return o + ((b * T + (x0 + x) * rec::kP) * H + h) * rec::kDV; };
+  __syncthreads();  // pair 0 is in LDS
 
-  int slot = 0;  // ring slot of tile xl
-  // One tile per call: the epilogue of tile xl - 1 and the state step of tile
-  // xl.  The first and last calls are peeled, so that the steady state is one
-  // basic block and the epilogue's arithmetic can fill the matrix-core chain.
-  // Only the sequence's last tile can be partial (`tail`).
-  auto step = [&](int64_t xl, auto EPI, auto CHAIN, bool tail, f32x4 (&Oprev)[NCB],
-                  f32x4 (&O)[NCB]) {
-    constexpr bool kEpi = decltype(EPI)::value && GATE;
-    constexpr bool kChain = decltype(CHAIN)::value;
-    const int slot_prev = slot == 0 ? kRing - 1 : slot - 1;
+  // Epilogue of pair x: y = O / rms(O) * w * sigmoid(gate), tokens lc and
+  // 16 + lc, from the row sums of every state wave and the gate rows that the
+  // loader waves converted.
+  auto epilogue = [&](int64_t x, const f32x4 (&Pa)[NCB], const f32x4 (&Pb)[NCB]) {
+    float sa = 0.f, sb = 0.f;
+#pragma unroll
+    for (int w = 0; w < NSW; ++w) {
+      sa += rs[x & 1][lc][w];
+      sb += rs[x & 1][16 + lc][w];
+    }
+    const float inva = rsqrtf(sa * (1.f / (float)rec::kDV) + eps);
+    const float invb = rsqrtf(sb * (1.f / (float)rec::kDV) + eps);
+    const int64_t tok = (x0 + x) * rec::kP + lc;
+    const unsigned char* G = gring + (SC::kGRing > 0 ? (int)(x % SC::kGRing) : 0) * SC::kGSlot;
+    bf16_t* op = o_pair(x) + o_lane;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const f16x4 swa = *(const f16x4*)(G + tile_off[cb]);
+      const f16x4 swb = *(const f16x4*)(G + 16 * SC::kRowB + tile_off[cb]);
+      bf16x4 ya, yb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ya[r] = (bf16_t)(Pa[cb][r] * inva * (float)swa[r]);
+        yb[r] = (bf16_t)(Pb[cb][r] * invb * (float)swb[r]);
+      }
+      if (tok < T) *(bf16x4*)(op + 16 * cb) = ya;
+      if (tok + rec::kC < T) *(bf16x4*)(op + rec::kC * rstride + 16 * cb) = yb;
+    }
+  };
+
+  f32x4 Pa[NCB], Pb[NCB];  // outputs of the previous pair, normalised one step later
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) Pa[cb] = Pb[cb] = zero4();
+  int slot = 0;  // ring slot of pair xl
+  for (int64_t xl = 0; xl < nseg; ++xl) {
+    const bool tail = xl == nseg - 1;  // only the sequence's last pair can be partial
     const unsigned char* Rs = ring[slot];
 
-    // The LDS operands are read in two batches (those of the D and O products
-    // first, those of the state update once the products are issued), so
-    // that the step waits for LDS twice rather than once per product.
-    float rsum[NSW];
-    f16x4 sw[NCB];
-    if constexpr (kEpi) {
+    // The LDS operands are read in batches (those of the D products, those of
+    // the O products, those of the state update), each issued before the
+    // products that precede its use, so that the step waits for LDS a few
+    // times rather than once per product.
+    const f16x4 ta = *(const f16x4*)(Rs + rec::kTa + lane * 8);
+    const f16x4 tb = *(const f16x4*)(Rs + rec::kTb + lane * 8);
+    const f16x4 pm = *(const f16x4*)(Rs + rec::kPm + lane * 8);
+    bf16x4 vna[NCB], vnb[NCB];
 #pragma unroll
-      for (int w = 0; w < NSW; ++w) rsum[w] = rs[(xl - 1) & 1][lc][w];
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-        sw[cb] = *(const f16x4*)(ring[slot_prev] + SC::kG + tile_off[cb]);
+    for (int cb = 0; cb < NCB; ++cb) {
+      vna[cb] = *(const bf16x4*)(Rs + SC::kV + tile_off[cb]);
+      vnb[cb] = *(const bf16x4*)(Rs + SC::kV + 16 * SC::kRowB + tile_off[cb]);
     }
-    f16x4 t_op, aqk_op, ka[8];
-    f16x8 w_op[4], q_op[4];
-    bf16x4 vn[NCB];
-    f32x4 e4[8];
-    if constexpr (kChain) {
-      t_op = *(const f16x4*)(Rs + rec::kT + lane * 8);
-      aqk_op = *(const f16x4*)(Rs + rec::kAqk + lane * 8);
+    f16x8 wa[4], wb[4];
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) vn[cb] = *(const bf16x4*)(Rs + SC::kV + tile_off[cb]);
+    for (int s = 0; s < 4; ++s) {
+      wa[s] = *(const f16x8*)(Rs + rec::kWa + s * 1024 + lane * 16);
+      wb[s] = *(const f16x8*)(Rs + rec::kWb + s * 1024 + lane * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (GATE) {
+      if (xl > 0) epilogue(xl - 1, Pa, Pb);
+    }
+
+    // ---- D_a, D_b.  T V, P D_a and D^T Aqk^T are 16x16x32 products with
+    // k-values 4..7 of each lane zero: every accumulation chain uses one
+    // instruction shape (a 16x16x16 result fed straight into a 16x16x32
+    // accumulator read stale values on gfx950).
+    f16x8 sop[NCB][4];
+    f16x4 da16[NCB], db16[NCB];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        w_op[s] = *(const f16x8*)(Rs + rec::kW + s * 1024 + lane * 16);
-        q_op[s] = *(const f16x8*)(Rs + rec::kQh + s * 1024 + lane * 16);
-      }
+    for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sop[cb][s] = cat8(to_h4(S[cb][2 * s]), to_h4(S[cb][2 * s + 1]));
+      const f16x4 va = to_h4(mma16b(vna[cb], ident, zero4()));  // lane (c, g): V_a[4 g + e][c]
+      const f16x4 vb = to_h4(mma16b(vnb[cb], ident, zero4()));
+      f32x4 d = mma32h(cat8(ta, f16x4{}), cat8(va, f16x4{}), zero4());
+#pragma unroll
+      for (int s = 0; s < 4; ++s) d = mma32h(wa[s], sop[cb][s], d);
+      da16[cb] = to_h4(d);
+      f32x4 e = mma32h(cat8(tb, f16x4{}), cat8(vb, f16x4{}), zero4());
+#pragma unroll
+      for (int s = 0; s < 4; ++s) e = mma32h(wb[s], sop[cb][s], e);
+      e = mma32h(cat8(pm, f16x4{}), cat8(da16[cb], f16x4{}), e);
+      db16[cb] = to_h4(e);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const f16x4 aa = *(const f16x4*)(Rs + rec::kAa + lane * 8);
+    const f16x4 ab = *(const f16x4*)(Rs + rec::kAb + lane * 8);
+    const f16x4 qba = *(const f16x4*)(Rs + rec::kQba + lane * 8);
+    f16x8 qa[4], qb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      qa[s] = *(const f16x8*)(Rs + rec::kQa + s * 1024 + lane * 16);
+      qb[s] = *(const f16x8*)(Rs + rec::kQb + s * 1024 + lane * 16);
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- epilogue of tile xl - 1: y = O / rms(O) * w * sigmoid(gate)
-    if constexpr (kEpi) {
-      float ss = 0.f;
+    // ---- O_a^T, O_b^T (lane (t, g): O[t][4 g + r])
+    f32x4 Oa[NCB], Ob[NCB];
 #pragma unroll
-      for (int w = 0; w < NSW; ++w) ss += rsum[w];
-      const float inv = rsqrtf(ss * (1.f / (float)rec::kDV) + eps);
-      const int64_t tok = (x0 + xl - 1) * rec::kC + lc;
+    for (int cb = 0; cb < NCB; ++cb) {
+      f32x4 x = zero4(), y = zero4();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        x = mma32h(sop[cb][s], qa[s], x);
+        y = mma32h(sop[cb][s], qb[s], y);
+      }
+      Oa[cb] = mma32h(cat8(da16[cb], f16x4{}), cat8(aa, f16x4{}), x);
+      y = mma32h(cat8(da16[cb], f16x4{}), cat8(qba, f16x4{}), y);
+      Ob[cb] = mma32h(cat8(db16[cb], f16x4{}), cat8(ab, f16x4{}), y);
+    }
+    if constexpr (GATE) {
+      float pa = 0.f, pb = 0.f;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pa = fmaf(Oa[cb][r], Oa[cb][r], pa);
+          pb = fmaf(Ob[cb][r], Ob[cb][r], pb);
+        }
+      pa += __shfl_xor(pa, 16);
+      pa += __shfl_xor(pa, 32);
+      pb += __shfl_xor(pb, 16);
+      pb += __shfl_xor(pb, 32);
+      if (lg == 0) {
+        rs[xl & 1][lc][wave] = pa;
+        rs[xl & 1][16 + lc][wave] = pb;
+      }
+    } else if constexpr (WO) {
+      const int64_t tok = (x0 + xl) * rec::kP + lc;
+      bf16_t* op = o_pair(xl) + o_lane;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        bf16x4 y;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = (bf16_t)(Oprev[cb][r] * inv * (float)sw[cb][r]);
-        if (!tail || tok < T) *(bf16x4*)(o_tile(xl - 1) + o_lane + 16 * cb) = y;
+        const bf16x4 ya = {(bf16_t)Oa[cb][0], (bf16_t)Oa[cb][1], (bf16_t)Oa[cb][2],
+                           (bf16_t)Oa[cb][3]};
+        const bf16x4 yb = {(bf16_t)Ob[cb][0], (bf16_t)Ob[cb][1], (bf16_t)Ob[cb][2],
+                           (bf16_t)Ob[cb][3]};
+        if (!tail || tok < T) *(bf16x4*)(op + 16 * cb) = ya;
+        if (!tail || tok + rec::kC < T) *(bf16x4*)(op + rec::kC * rstride + 16 * cb) = yb;
       }
     }
 
-    // ---- state step of tile xl
-    if constexpr (kChain) {
-      f16x4 d16[NCB];
+    // ---- S <- Diag(E_a E_b) S + [Kb_a' | Kb_b]^T [D_a ; D_b]
+    __builtin_amdgcn_sched_barrier(0);
+    f16x8 kb8[8];
+    f32x4 e4[8];
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      kb8[kb] = *(const f16x8*)(Rs + rec::kKb + kb * 1024 + lane * 16);
+      e4[kb] = *(const f32x4*)(Rs + rec::kEn + 4 * (32 * (kb / 2) + 8 * lg + 4 * (kb % 2)));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        S[cb][kb] = mma32h(kb8[kb], cat8(da16[cb], db16[cb]), S[cb][kb] * e4[kb]);
+
+    if constexpr (GATE) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        f16x8 sop[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) sop[s] = cat8(to_h4(S[cb][2 * s]), to_h4(S[cb][2 * s + 1]));
-        const f16x4 vop = to_h4(mma16b(vn[cb], ident, zero4()));  // lane (c, g): V[4 g + e][c]
-        // T V and D^T Aqk^T are 16x16x32 products with k-values 4..7 of each
-        // lane zero: every accumulation chain uses one instruction shape (a
-        // 16x16x16 result fed straight into a 16x16x32 accumulator read stale
-        // values on gfx950).
-        f32x4 d = mma32h(cat8(t_op, f16x4{}), cat8(vop, f16x4{}), zero4());
-        f32x4 oc = zero4();
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          d = mma32h(w_op[s], sop[s], d);
-          oc = mma32h(sop[s], q_op[s], oc);
-        }
-        d16[cb] = to_h4(d);
-        O[cb] = mma32h(cat8(d16[cb], f16x4{}), cat8(aqk_op, f16x4{}), oc);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        ka[kb] = *(const f16x4*)(Rs + rec::kKb + kb * 512 + lane * 8);
-        e4[kb] = *(const f32x4*)(Rs + rec::kEn + 4 * (32 * (kb / 2) + 8 * lg + 4 * (kb % 2)));
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) S[cb][kb] = mma16h(ka[kb], d16[cb], S[cb][kb] * e4[kb]);
-      if constexpr (GATE) {
-        float p = 0.f;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) p = fmaf(O[cb][r], O[cb][r], p);
-        p += __shfl_xor(p, 16);
-        p += __shfl_xor(p, 32);
-        if (lg == 0) rs[xl & 1][lc][wave] = p;
-      } else if constexpr (WO) {
-        const int64_t tok = (x0 + xl) * rec::kC + lc;
-        if (!tail || tok < T) {
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            const bf16x4 y = {(bf16_t)O[cb][0], (bf16_t)O[cb][1], (bf16_t)O[cb][2],
-                              (bf16_t)O[cb][3]};
-            *(bf16x4*)(o_tile(xl) + o_lane + 16 * cb) = y;
-          }
-        }
+        Pa[cb] = Oa[cb];
+        Pb[cb] = Ob[cb];
       }
     }
-    __syncthreads();  // tile xl + 1 is in LDS; the slot of tile xl - 1 may be refilled
+    __syncthreads();  // pair xl + 1 is in LDS; the slot of pair xl may be refilled
     slot = slot == kRing - 1 ? 0 : slot + 1;
-  };
-  using yes = std::true_type;
-  using no = std::false_type;
-  // Tile xl keeps its output in Oa (xl even) or Ob (xl odd).
-  step(0, no{}, yes{}, nseg == 1, Ob, Oa);
-  int64_t xl = 1;
-  for (; xl + 2 < nseg; xl += 2) {
-    step(xl, yes{}, yes{}, false, Oa, Ob);
-    step(xl + 1, yes{}, yes{}, false, Ob, Oa);
   }
-  for (; xl < nseg; ++xl) {  // the last one or two tiles (the last may be partial)
-    if (xl & 1)
-      step(xl, yes{}, yes{}, xl == nseg - 1, Oa, Ob);
-    else
-      step(xl, yes{}, yes{}, xl == nseg - 1, Ob, Oa);
-  }
-  if (nseg & 1)
-    step(nseg, yes{}, no{}, true, Oa, Ob);
-  else
-    step(nseg, yes{}, no{}, true, Ob, Oa);
+  if constexpr (GATE) epilogue(nseg - 1, Pa, Pb);  // its row sums are in LDS since the last barrier
 
   if (s_next != nullptr) {
 #pragma unroll
@@ -423,7 +498,7 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
 // One launch: the state workgroups (first) walk segment `cur` of every head
 // while the remaining workgroups build the records of segment `nxt`.
 struct Seg {
-  int64_t x0 = 0, n = 0;  // first tile, tile count (n = 0: none)
+  int64_t x0 = 0, n = 0;  // first pair, pair count (n = 0: none)
   unsigned char* recs = nullptr;
 };
 
@@ -442,7 +517,7 @@ hipError_t launch_state_t(const ChunkArgs& a, Seg cur, const float* s_in, float*
   const int64_t n_state = cur.n > 0 ? BH * (rec::kDV / DVW) : 0;
   int64_t n_tile = 0;
   if (nxt.n > 0) {
-    const int64_t want = (BH * nxt.n + NW - 1) / NW;  // one tile per wavefront at most
+    const int64_t want = (BH * nxt.n + NW - 1) / NW;  // one pair per wavefront at most
     int64_t avail = cus - n_state;
     if (avail < cus / 4) avail = cus / 4;              // always make progress
     n_tile = want < avail ? want : avail;
@@ -471,27 +546,29 @@ int split_for(const ChunkArgs& a, int cus) {
   return (2 * a.B * a.H <= cus / 2) ? 2 : 1;
 }
 
-// Tiles per segment.  One launch per segment, and the records of the
-// segment being consumed are read back while the next segment's are written:
-// a segment of about 64 MiB of records stays within the 256 MB memory-side
+// Pairs per segment.  One launch per segment, and the records of the segment
+// being consumed are read back while the next segment's are written: a
+// segment of about 64 MiB of records stays within the 256 MB memory-side
 // cache with the rest of a launch's traffic, which makes the read-back
 // cheaper; longer sequences use longer segments (at most about 64 launches,
 // at most 256 MiB per record buffer) so that the per-launch cost (state load
 // and store, pipeline fill) stays small.
-int64_t seg_tiles(int64_t BH, int64_t nchunks) {
+int64_t seg_pairs(int64_t BH, int64_t npairs) {
   int64_t seg = 0;
-  if (const char* e = getenv("KDA_SEG_TILES")) seg = atoll(e);
+  if (const char* e = getenv("KDA_SEG_PAIRS")) seg = atoll(e);
   if (seg <= 0) {
-    const int64_t per_row = BH * (int64_t)rec::kBytes;  // record bytes of one tile of every head
+    const int64_t per_row = BH * (int64_t)rec::kBytes;  // record bytes of one pair of every head
     seg = (int64_t(64) << 20) / per_row;
-    const int64_t min_seg = (nchunks + 63) / 64;
+    const int64_t min_seg = (npairs + 63) / 64;
     if (seg < min_seg) seg = min_seg;
     const int64_t cap = (int64_t(256) << 20) / per_row;
     if (seg > cap) seg = cap;
   }
   if (seg < 1) seg = 1;
-  return seg < nchunks ? seg : nchunks;
+  return seg < npairs ? seg : npairs;
 }
+
+int64_t pairs_of(int64_t T) { return (T + rec::kP - 1) / rec::kP; }
 
 }  // namespace
 
@@ -500,39 +577,38 @@ bool chunk_mfma_supports(int dk, int dv, bool io_bf16) {
 }
 
 size_t chunk_mfma_workspace(int64_t B, int64_t T, int64_t H) {
-  const int64_t BH = B * H, nch = (T + rec::kC - 1) / rec::kC;
-  const int64_t seg = seg_tiles(BH, nch);
+  const int64_t BH = B * H, np = pairs_of(T);
+  const int64_t seg = seg_pairs(BH, np);
   // two record buffers (the segment being consumed and the one being built),
   // then a carried state for when s_out is absent
   return (size_t)(2 * BH * seg * rec::kBytes) + (size_t)(BH * rec::kDK * rec::kDV * 4);
 }
 
 int64_t chunk_mfma_launches(int64_t B, int64_t T, int64_t H) {
-  const int64_t nch = (T + rec::kC - 1) / rec::kC;
-  const int64_t seg = seg_tiles(B * H, nch);
-  return (nch + seg - 1) / seg + 1;  // one per segment, plus the first segment's records
+  const int64_t np = pairs_of(T);
+  const int64_t seg = seg_pairs(B * H, np);
+  return (np + seg - 1) / seg + 1;  // one per segment, plus the first segment's records
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a) {
   if (!chunk_mfma_supports(a.dk, a.dv, a.io_bf16)) return hipErrorNotSupported;
-  const int64_t BH = a.B * a.H, nch = (a.T + rec::kC - 1) / rec::kC;
-  const int64_t seg = seg_tiles(BH, nch);
-  const int64_t nsegs = (nch + seg - 1) / seg;
+  const int64_t BH = a.B * a.H, np = pairs_of(a.T);
+  const int64_t seg = seg_pairs(BH, np);
+  const int64_t nsegs = (np + seg - 1) / seg;
   unsigned char* buf[2] = {(unsigned char*)a.workspace,
                            (unsigned char*)a.workspace + BH * seg * rec::kBytes};
   float* carry = a.s_out != nullptr ? a.s_out : (float*)(buf[1] + BH * seg * rec::kBytes);
   const int cus = device_cus();
   const int split = split_for(a, cus);
-  // State columns per state wavefront: 16 (two state wavefronts per SIMD, so
-  // that one's matrix-core and LDS latencies are covered by the other's work)
-  // unless KDA_CPW=32 asks for one wavefront of 32 columns per SIMD.
-  int cpw = 16;
-  if (const char* e = getenv("KDA_CPW")) cpw = atoi(e) == 32 ? 32 : 16;
+  // State columns per state wavefront: 32 (one state wavefront per SIMD)
+  // unless KDA_CPW=16 asks for two wavefronts of 16 columns per SIMD.
+  int cpw = 32;
+  if (const char* e = getenv("KDA_CPW")) cpw = atoi(e) == 16 ? 16 : 32;
   auto segment = [&](int64_t j) {
     Seg sg;
     if (j >= 0 && j < nsegs) {
       sg.x0 = j * seg;
-      sg.n = (nch - sg.x0) < seg ? (nch - sg.x0) : seg;
+      sg.n = (np - sg.x0) < seg ? (np - sg.x0) : seg;
       sg.recs = buf[j & 1];
     }
     return sg;

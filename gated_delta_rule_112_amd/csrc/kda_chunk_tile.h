@@ -1,24 +1,23 @@
-// Tile builder of the matrix-core chunked prefill: everything about a 16-token
-// tile that does not depend on the running state (kda_chunk_rec.h).
+// Tile builder of the matrix-core chunked prefill: everything about a pair of
+// 16-token tiles that does not depend on the running state (kda_chunk_rec.h).
 //
 // Lane (t, g) = (lane % 16, lane / 16) holds token t and, for each 32-channel
-// slab s, the key channels 32 s + 8 g + 0..7.  Per slab it forms the in-tile
-// cumulative log-decay (a prefix sum over the 16 lanes of a DPP row), the
-// exponentials and the rescaled operands, and accumulates the two intra-tile
-// products over the slab on the matrix cores in float32 (16x16x4: each k step
-// is one of the lane's channels, so the operands come straight from
-// registers):
+// slab s, the key channels 32 s + 8 g + 0..7.  Per slab and tile it forms the
+// in-tile cumulative log-decay (a prefix sum over the 16 lanes of a DPP row),
+// the exponentials and the rescaled operands, and accumulates the two
+// intra-tile products over the slab on the matrix cores in float32 (16x16x4:
+// each k step is one of the lane's channels, so the operands come straight
+// from registers):
 //   lane (i, g) accumulates (Kh Kc^T)[i][4 g + r] and (Qh Kc^T)[i][4 g + r].
 // Kh and Kb are transposed to channel-major 16x16 blocks by a product with a
 // 0/1 selection matrix (exact).  With the products summed over all slabs, the
 // 16x16 unit-lower-triangular system (I + A) Y = I is solved by forward
 // substitution, lane (i, g) holding rows i of columns 4 g + 0..3 and the pivot
 // row broadcast over each DPP row; then T = Y Diag(beta) and W = T Kh, one
-// 32-channel slab of W at a time.
-//
-// The pieces are used whole (one wavefront builds a tile and stores its
-// record in memory) and sliced (four wavefronts build one slab each and
-// write the record into LDS).
+// 32-channel slab of W at a time.  The two tiles of a pair are built slab by
+// slab side by side, so that the cross terms (Kb_a scaled by E_b, Qh_b scaled
+// by E_a, Q_ba = Qh_b Kb_a^T, M = Kh_b Kb_a^T) come from registers;
+// P = -W_b Kb_a^T = -T_b M and W_b scaled by E_a follow tile b's solve.
 //
 // Precision: all sums over key channels and the solve are float32; the stored
 // matrix operands are float16 (11-bit significand), e^G_15 is float32.
@@ -64,17 +63,10 @@ struct SlabIn {
   f32x4 g0, g1;
 };
 
-// One lane's results of one slab, in the record's operand images.
-struct SlabOut {
-  f16x8 qh;      // Qh image of the slab
-  f16x4 kbT[2];  // Kb^T blocks 2s, 2s+1
-  f16x4 khT[2];  // Kh^T blocks 2s, 2s+1 (kept for W)
-  f32x4 en[2];   // e^G_15 of the lane's 8 channels (stored from lanes t == 15)
-};
-
-struct Scratch {  // per wavefront, for the solve
+struct Scratch {  // per wavefront
   float a[16][20];  // A = strict_lower(Diag(beta) Kh Kc^T), row-major, padded rows
   float beta[16];
+  float en_a[rec::kDK];  // E_a of the pair being built, per key channel
 };
 
 // Element offset of the row of token `tok` (clamped into the sequence) of head (b, h).
@@ -101,47 +93,61 @@ __device__ __forceinline__ f16x4 selection(int lane) {
   return id;
 }
 
-// Builds one slab.  lv = 1 for a token of the sequence, 0 past its end (then
-// q = k = g = 0); FULL tiles skip that mask.
+// One lane's rescaled values of one slab of one tile (channels 32 s + 8 g + e).
+struct SlabVals {
+  float kh[8], kc[8], qh[8], kb[8], en[8];
+};
+
+// The rescaled values of one slab, and its contribution to the two
+// intra-tile products.  lv = 1 for a token of the sequence, 0 past its end
+// (then q = k = g = 0); FULL tiles skip that mask.
 template <bool FULL>
-__device__ __forceinline__ void build_slab(const SlabIn& in, float lv, float scale, f16x4 ident,
-                                           f32x4& acc_a, f32x4& acc_q, SlabOut& out) {
+__device__ __forceinline__ void slab_vals(const SlabIn& in, float lv, float scale, SlabVals& o,
+                                          f32x4& acc_a, f32x4& acc_q) {
   const float gm[8] = {in.g0[0], in.g0[1], in.g0[2], in.g0[3],
                        in.g1[0], in.g1[1], in.g1[2], in.g1[3]};
   const float gs = FULL ? kLog2e : kLog2e * lv;
   const float qs = FULL ? scale : scale * lv;
-  float kh[8], kc[8], qh[8], kb[8], en8[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float gl = row_scan16(gm[e] * gs);         // G in log2 units
     const float eg = __builtin_amdgcn_exp2f(gl);     // e^G    <= 1
     const float ieg = __builtin_amdgcn_exp2f(-gl);   // e^-G   <  e^80
-    en8[e] = row_bcast<15>(eg);                      // e^G_15 of this channel
+    o.en[e] = row_bcast<15>(eg);                     // e^G_15 of this channel
     const float kf = FULL ? (float)in.k[e] : (float)in.k[e] * lv;
-    kh[e] = kf * eg;
-    kc[e] = kf * ieg;
-    qh[e] = (float)in.q[e] * qs * eg;
-    kb[e] = kc[e] * en8[e];  // k e^(G_15 - G_t) <= |k|
+    o.kh[e] = kf * eg;
+    o.kc[e] = kf * ieg;
+    o.qh[e] = (float)in.q[e] * qs * eg;
+    o.kb[e] = o.kc[e] * o.en[e];  // k e^(G_15 - G_t) <= |k|
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    acc_a = mma4f(kc[e], kh[e], acc_a);
-    acc_q = mma4f(kc[e], qh[e], acc_q);
+    acc_a = mma4f(o.kc[e], o.kh[e], acc_a);
+    acc_q = mma4f(o.kc[e], o.qh[e], acc_q);
   }
-  out.qh = f16x8{(f16)qh[0], (f16)qh[1], (f16)qh[2], (f16)qh[3],
-                 (f16)qh[4], (f16)qh[5], (f16)qh[6], (f16)qh[7]};
-  // Channel-major blocks 2s (channels 32 s + 8 g + 0..3) and 2s+1 (+ 4..7).
+}
+
+__device__ __forceinline__ void slab_vals_any(bool full, const SlabIn& in, float lv, float scale,
+                                              SlabVals& o, f32x4& acc_a, f32x4& acc_q) {
+  if (full)
+    slab_vals<true>(in, 1.f, scale, o, acc_a, acc_q);
+  else
+    slab_vals<false>(in, lv, scale, o, acc_a, acc_q);
+}
+
+__device__ __forceinline__ f16x8 to_h8(const float (&x)[8]) {
+  return f16x8{(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3],
+               (f16)x[4], (f16)x[5], (f16)x[6], (f16)x[7]};
+}
+
+// Channel-major blocks 2s (channels 32 s + 8 g + 0..3) and 2s+1 (+ 4..7) of a
+// token-major slab: out[hb] lane (c, g) = x[token 4 g + r][chan(2 s + hb, c)].
+__device__ __forceinline__ void transpose_slab(const float (&x)[8], f16x4 ident, f16x4 (&out)[2]) {
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
-    const f16x4 kh4 = {(f16)kh[4 * hb], (f16)kh[4 * hb + 1], (f16)kh[4 * hb + 2],
-                       (f16)kh[4 * hb + 3]};
-    const f16x4 kb4 = {(f16)kb[4 * hb], (f16)kb[4 * hb + 1], (f16)kb[4 * hb + 2],
-                       (f16)kb[4 * hb + 3]};
-    out.khT[hb] = to_h4(mma16h(kh4, ident, zero4()));
-    out.kbT[hb] = to_h4(mma16h(kb4, ident, zero4()));
+    const f16x4 x4 = {(f16)x[4 * hb], (f16)x[4 * hb + 1], (f16)x[4 * hb + 2], (f16)x[4 * hb + 3]};
+    out[hb] = to_h4(mma16h(x4, ident, zero4()));
   }
-  out.en[0] = f32x4{en8[0], en8[1], en8[2], en8[3]};
-  out.en[1] = f32x4{en8[4], en8[5], en8[6], en8[7]};
 }
 
 // One step of the forward substitution: column values y[e] of rows i (this
@@ -189,127 +195,190 @@ __device__ __forceinline__ void finish(f32x4 acc_a, f32x4 acc_q, float bt, Scrat
   tb = f16x4{(f16)(y[0] * bj[0]), (f16)(y[1] * bj[1]), (f16)(y[2] * bj[2]), (f16)(y[3] * bj[3])};
 }
 
-// W^T blocks 2s, 2s+1 = Kh^T T^T: the lane's (i, g) image of -W for slab s,
-// -W[i][32 s + 8 g + e].
-__device__ __forceinline__ f16x8 w_slab(const f16x4 (&khT)[2], f16x4 tb) {
-  const f32x4 w0 = mma16h(khT[0], tb, zero4());
-  const f32x4 w1 = mma16h(khT[1], tb, zero4());
-  return cat8(to_h4(-w0), to_h4(-w1));
+// W^T blocks 2s, 2s+1 = Kh^T T^T: lane (i, g) gets -W[i][32 s + 8 g + e],
+// e < 4 in w[0], e >= 4 in w[1].
+__device__ __forceinline__ void w_slab(const f16x4 (&khT)[2], f16x4 tb, f32x4 (&w)[2]) {
+  w[0] = -mma16h(khT[0], tb, zero4());
+  w[1] = -mma16h(khT[1], tb, zero4());
 }
 
-// ---------------------------------------------------------------- whole tiles
+// ---------------------------------------------------------------- pairs
 
 struct Args {
   const bf16_t* q;
   const bf16_t* k;
   const float* g;
   const float* beta;
-  unsigned char* recs;  // records of the segment, [head][tile]
+  unsigned char* recs;  // records of the segment, [head][pair]
   int64_t T, H, BH;
-  int64_t x0, nseg;     // first tile and tile count of the segment
+  int64_t x0, nseg;     // first pair and pair count of the segment
   float scale;
 };
 
-// Position of a tile: head (b, h) and tile xl of the segment.
+// Position of a pair: head (b, h) and pair xl of the segment.
 struct Pos {
   int64_t b, h, xl;
 };
 
-__device__ __forceinline__ int64_t tile_row(const Args& a, const Pos& p, int lane) {
-  return row_of(p.b, p.h, (a.x0 + p.xl) * rec::kC + lane % 16, a.T, a.H);
+// Inputs of one slab of both tiles of a pair, and the rows they come from.
+struct PairIn {
+  SlabIn a, b;
+};
+
+struct PairRows {
+  int64_t a, b;  // element offsets of this lane's token rows (clamped into the sequence)
+};
+
+__device__ __forceinline__ PairRows pair_rows(const Args& a, const Pos& p, int lane) {
+  const int64_t tok0 = (a.x0 + p.xl) * rec::kP + lane % 16;
+  return PairRows{row_of(p.b, p.h, tok0, a.T, a.H), row_of(p.b, p.h, tok0 + rec::kC, a.T, a.H)};
 }
 
-// Tiles first, first + stride, ... < BH * nseg of one wavefront, numbered
-// head-fastest (tile w is tile w / BH of head w % BH), so that the wavefronts
+__device__ __forceinline__ void load_pair_slab(PairIn& x, const Args& a, const PairRows& r, int s,
+                                               int lane) {
+  load_slab(x.a, a.q, a.k, a.g, r.a, s, lane);
+  load_slab(x.b, a.q, a.k, a.g, r.b, s, lane);
+}
+
+// Builds pair p of head (b, h) and stores its record.  On entry `cur` holds
+// slab 0 of pair p; the next slab's inputs are always in flight while a slab
+// is built, and on return `cur` holds slab 0 of pair `pn` (the wavefront's
+// next pair, or any valid pair when there is none).
+__device__ __forceinline__ void build_pair(const Args& a, const Pos& p, const Pos& pn, PairIn& cur,
+                                           f16x4 ident, Scratch* sm, int lane) {
+  const int t = lane % 16, lg = lane / 16;
+  const int64_t tok0 = (a.x0 + p.xl) * rec::kP;
+  const PairRows rows = pair_rows(a, p, lane), nrows = pair_rows(a, pn, lane);
+  const bool fulla = tok0 + rec::kC <= a.T, fullb = tok0 + rec::kP <= a.T;
+  const float lva = tok0 + t < a.T ? 1.f : 0.f;
+  const float lvb = tok0 + rec::kC + t < a.T ? 1.f : 0.f;
+  const float betaa = a.beta[rows.a] * lva, betab = a.beta[rows.b] * lvb;
+  unsigned char* R = a.recs + ((p.b * a.H + p.h) * a.nseg + p.xl) * (int64_t)rec::kBytes;
+
+  f32x4 aa = zero4(), qa = zero4(), ab = zero4(), qb = zero4(), qba = zero4(), mba = zero4();
+  f16x4 khTa[4][2], khTb[4][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    PairIn nxt;
+    if (s < 3)
+      load_pair_slab(nxt, a, rows, s + 1, lane);
+    else
+      load_pair_slab(nxt, a, nrows, 0, lane);
+    // tile a: its values, then everything that needs only them
+    SlabVals va;
+    slab_vals_any(fulla, cur.a, lva, a.scale, va, aa, qa);
+    transpose_slab(va.kh, ident, khTa[s]);
+    const f16x8 kba = to_h8(va.kb);  // Kb_a, token-major
+    *(f16x8*)(R + rec::kQa + s * 1024 + lane * 16) = to_h8(va.qh);
+    if (t == 0) {
+      const unsigned ea = lds_addr(&sm->en_a[32 * s + 8 * lg]);
+      ds_write16(ea, f32x4{va.en[0], va.en[1], va.en[2], va.en[3]});
+      ds_write16(ea + 16, f32x4{va.en[4], va.en[5], va.en[6], va.en[7]});
+    }
+    // tile b, and the cross terms
+    SlabVals vb;
+    slab_vals_any(fullb, cur.b, lvb, a.scale, vb, ab, qb);
+    transpose_slab(vb.kh, ident, khTb[s]);
+    // Q_ba^T: lane (i, g) accumulates (Qh_b Kb_a^T)[i][4 g + r];
+    // M = Kh_b Kb_a^T: lane (j, g) accumulates M[4 g + r][j]
+    qba = mma32h(kba, to_h8(vb.qh), qba);
+    mba = mma32h(to_h8(vb.kh), kba, mba);
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = vb.qh[e] * va.en[e];
+    *(f16x8*)(R + rec::kQb + s * 1024 + lane * 16) = to_h8(x);
+    f16x4 kta[2], ktb[2];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = va.kb[e] * vb.en[e];
+    transpose_slab(x, ident, kta);
+    transpose_slab(vb.kb, ident, ktb);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+      *(f16x8*)(R + rec::kKb + (2 * s + hb) * 1024 + lane * 16) = cat8(kta[hb], ktb[hb]);
+    if (t == 15) {
+      f32x4* ep = (f32x4*)(R + rec::kEn + (32 * s + 8 * lg) * 4);
+      ep[0] = f32x4{va.en[0] * vb.en[0], va.en[1] * vb.en[1], va.en[2] * vb.en[2],
+                    va.en[3] * vb.en[3]};
+      ep[1] = f32x4{va.en[4] * vb.en[4], va.en[5] * vb.en[5], va.en[6] * vb.en[6],
+                    va.en[7] * vb.en[7]};
+    }
+    cur = nxt;
+  }
+  *(f16x4*)(R + rec::kQba + lane * 8) = to_h4(qba);
+
+  f16x4 ta, aqa, tb, aqb;
+  finish(aa, qa, betaa, sm, lane, ta, aqa);
+  *(f16x4*)(R + rec::kTa + lane * 8) = ta;
+  *(f16x4*)(R + rec::kAa + lane * 8) = aqa;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    f32x4 w[2];
+    w_slab(khTa[s], ta, w);
+    *(f16x8*)(R + rec::kWa + s * 1024 + lane * 16) = cat8(to_h4(w[0]), to_h4(w[1]));
+  }
+  finish(ab, qb, betab, sm, lane, tb, aqb);
+  *(f16x4*)(R + rec::kTb + lane * 8) = tb;
+  *(f16x4*)(R + rec::kAb + lane * 8) = aqb;
+  // P = -W_b Kb_a^T = -T_b M, formed as (M^T T_b^T)^T: lane (i, g) gets P[i][4 g + r]
+  const f32x4 pm = -mma16h(to_h4(mba), tb, zero4());
+  *(f16x4*)(R + rec::kPm + lane * 8) = to_h4(pm);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    f32x4 w[2];
+    w_slab(khTb[s], tb, w);
+    const unsigned ea = lds_addr(&sm->en_a[32 * s + 8 * lg]);
+    f32x4 e0, e1;
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %2 offset:16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(e0), "=v"(e1)
+        : "v"(ea)
+        : "memory");
+    *(f16x8*)(R + rec::kWb + s * 1024 + lane * 16) = cat8(to_h4(w[0] * e0), to_h4(w[1] * e1));
+  }
+}
+
+// Pairs first, first + stride, ... < BH * nseg of one wavefront, numbered
+// head-fastest (pair w is pair w / BH of head w % BH), so that the wavefronts
 // working at one time read neighbouring heads of the same tokens, which are
-// adjacent in memory; every record goes to memory.  PIPE: software pipelined
-// over slabs (as soon as slab s of a tile is built, slab s of the wavefront's
-// next tile is loaded into the same registers, so one tile's inputs are in
-// flight while the rest of the current tile is built; past the last tile the
-// loads repeat the last tile).  Without PIPE each tile loads its own inputs
-// first (for workgroups with enough wavefronts per SIMD to cover the latency,
-// and too few registers per wavefront to hold a second tile's inputs).
-template <bool PIPE>
+// adjacent in memory.
 __device__ __forceinline__ void build_range(const Args& a, int64_t first, int64_t stride,
                                             Scratch* sm, int lane) {
   const int64_t total = a.BH * a.nseg;
   if (first >= total) return;
-  const int t = lane % 16, lg = lane / 16;
   const f16x4 ident = selection(lane);
-  const int64_t B = a.BH / a.H;
   // w = xl BH + b H + h; the stride split the same way, advanced without divisions
+  const int64_t B = a.BH / a.H;
   const int64_t sxl = stride / a.BH, sbh = stride - sxl * a.BH;
   const int64_t sb = sbh / a.H, sh = sbh - sb * a.H;
+  auto advance = [&](Pos q) {
+    q.b += sb;
+    q.h += sh;
+    q.xl += sxl;
+    if (q.h >= a.H) {
+      q.h -= a.H;
+      ++q.b;
+    }
+    if (q.b >= B) {
+      q.b -= B;
+      ++q.xl;
+    }
+    return q;
+  };
   Pos p;
+  p.xl = first / a.BH;
   {
-    p.xl = first / a.BH;
     const int64_t bh = first - p.xl * a.BH;
     p.b = bh / a.H;
     p.h = bh - p.b * a.H;
   }
-  const Pos last{B - 1, a.H - 1, a.nseg - 1};
-  SlabIn in[4];
-  float beta;
-  if constexpr (PIPE) {
-    const int64_t row = tile_row(a, p, lane);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) load_slab(in[s], a.q, a.k, a.g, row, s, lane);
-    beta = a.beta[row];
-  }
+  PairIn cur;
+  load_pair_slab(cur, a, pair_rows(a, p, lane), 0, lane);
   for (int64_t w = first; w < total; w += stride) {
-    if constexpr (!PIPE) {
-      const int64_t row = tile_row(a, p, lane);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) load_slab(in[s], a.q, a.k, a.g, row, s, lane);
-      beta = a.beta[row];
-    }
-    // the wavefront's next tile (clamped to the last tile)
-    Pos n{p.b + sb, p.h + sh, p.xl + sxl};
-    if (n.h >= a.H) {
-      n.h -= a.H;
-      ++n.b;
-    }
-    if (n.b >= B) {
-      n.b -= B;
-      ++n.xl;
-    }
-    const int64_t nrow =
-        PIPE ? (w + stride < total ? tile_row(a, n, lane) : tile_row(a, last, lane)) : 0;
-    const int64_t xl = p.xl, bh = p.b * a.H + p.h;
-
-    const int64_t tok0 = (a.x0 + xl) * rec::kC;
-    const bool full = tok0 + rec::kC <= a.T;
-    const float lv = tok0 + t < a.T ? 1.f : 0.f;
-    unsigned char* R = a.recs + (bh * a.nseg + xl) * (int64_t)rec::kBytes;
-    f32x4 acc_a = zero4(), acc_q = zero4();
-    f16x4 khT[4][2];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      SlabOut so;
-      if (full)
-        build_slab<true>(in[s], 1.f, a.scale, ident, acc_a, acc_q, so);
-      else
-        build_slab<false>(in[s], lv, a.scale, ident, acc_a, acc_q, so);
-      if constexpr (PIPE) load_slab(in[s], a.q, a.k, a.g, nrow, s, lane);
-      *(f16x8*)(R + rec::kQh + s * 1024 + lane * 16) = so.qh;
-      *(f16x4*)(R + rec::kKb + (2 * s) * 512 + lane * 8) = so.kbT[0];
-      *(f16x4*)(R + rec::kKb + (2 * s + 1) * 512 + lane * 8) = so.kbT[1];
-      if (t == 15) {
-        f32x4* ep = (f32x4*)(R + rec::kEn + (32 * s + 8 * lg) * 4);
-        ep[0] = so.en[0];
-        ep[1] = so.en[1];
-      }
-      khT[s][0] = so.khT[0];
-      khT[s][1] = so.khT[1];
-    }
-    f16x4 tb, aq;
-    finish(acc_a, acc_q, beta * lv, sm, lane, tb, aq);
-    if constexpr (PIPE) beta = a.beta[nrow];
-    *(f16x4*)(R + rec::kAqk + lane * 8) = aq;
-    *(f16x4*)(R + rec::kT + lane * 8) = tb;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) *(f16x8*)(R + rec::kW + s * 1024 + lane * 16) = w_slab(khT[s], tb);
-    p = n;
+    const Pos pn = w + stride < total ? advance(p) : p;  // past the last pair: reload this one
+    build_pair(a, p, pn, cur, ident, sm, lane);
+    p = pn;
   }
 }
 

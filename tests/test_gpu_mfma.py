@@ -215,13 +215,14 @@ def test_full_width_workload_sampled(kda):
 
 @pytest.fixture(params=["1", "3"])
 def short_segments(request, monkeypatch):
-    """Segments of 1 or 3 tiles: every tile boundary is also a launch boundary
-    (state carried through s_out or the workspace, records double-buffered)."""
-    monkeypatch.setenv("KDA_SEG_TILES", request.param)
+    """Segments of 1 or 3 pairs of tiles: every state step is also a launch
+    boundary (state carried through s_out or the workspace, records
+    double-buffered)."""
+    monkeypatch.setenv("KDA_SEG_PAIRS", request.param)
     return int(request.param)
 
 
-@pytest.mark.parametrize("T", [17, 100, 161])
+@pytest.mark.parametrize("T", [17, 60, 100, 161])
 def test_mfma_segments_ragged(kda, split, short_segments, T):
     q, k, v, g, beta, s0, _ = gen(1, T, 3, 1200 + T, g_std=2.0, s0_std=0.05)
     o, S = kda.chunk_fwd(q, k, v, g, beta, s0)
