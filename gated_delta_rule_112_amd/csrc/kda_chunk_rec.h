@@ -36,8 +36,12 @@
 //   Kb           [block b < 8][lane][8] f16  lane (c, g): Kb_a'[4 g + e][chan(b, c)] (e < 4),
 //                                                         Kb_b[4 g + e - 4][chan(b, c)] (e >= 4)
 //   en           [128] f32                   E_a E_b per key channel
-//   T_a, T_b, Aqk_a, Aqk_b, P, Q_ba
-//                [lane][4] f16               lane (i, g): X[i][4 g + r]
+//   T_a, Aqk_a   [lane][4] f16               lane (i, g): X[i][4 g + r]
+//   [T_b | P], [Q_ba | Aqk_b]
+//                [lane][8] f16               lane (i, g): X[i][4 g + e] (e < 4),
+//                                                         Y[i][4 g + e - 4] (e >= 4)
+// (the last two are the A and B operands of 32-deep products:
+// D_b = [T_b | P] [V_b ; D_a] and O_b^T = ... + [D_a ; D_b]^T [Q_ba | Aqk_b]^T)
 // where chan(b, p) = 32 (b / 2) + 8 (p / 4) + 4 (b % 2) + p % 4 is the key
 // channel held in row p of state block b.  The state pass keeps its state
 // rows in that order: the 16x16 accumulator layout gives lane (c, g) rows
@@ -62,11 +66,9 @@ constexpr int kQb = 12288;
 constexpr int kKb = 16384;
 constexpr int kEn = 24576;
 constexpr int kTa = 25088;
-constexpr int kTb = 25600;
-constexpr int kAa = 26112;
-constexpr int kAb = 26624;
-constexpr int kPm = 27136;
-constexpr int kQba = 27648;
+constexpr int kAa = 25600;
+constexpr int kTbP = 26112;
+constexpr int kQbaAb = 27136;
 constexpr int kBytes = 28160;  // a multiple of 256
 
 __host__ __device__ constexpr int chan(int b, int p) {

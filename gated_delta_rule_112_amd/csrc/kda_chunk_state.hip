@@ -66,6 +66,12 @@ constexpr unsigned vmcnt_imm(int n) {
 // s_waitcnt with vmcnt = N and lgkmcnt = 0.
 constexpr unsigned vmcnt_lgkm0_imm(int n) { return vmcnt_imm(n) & ~(0xFu << 8); }
 
+// x with its k-values 0..3 replaced by lo (4..7 kept).
+__device__ __forceinline__ f16x8 with_low(f16x8 x, f16x4 lo) {
+  const f16x8 l8 = __builtin_shufflevector(lo, lo, 0, 1, 2, 3, -1, -1, -1, -1);
+  return __builtin_shufflevector(l8, x, 0, 1, 2, 3, 12, 13, 14, 15);
+}
+
 // A slot is a whole number of 1 KB blocks (one direct-to-LDS load of a wave
 // each); every block holds only record bytes or only v / gate bytes.
 template <int DVW, bool GATE>
@@ -347,6 +353,11 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
   f32x4 Pa[NCB], Pb[NCB];  // outputs of the previous pair, normalised one step later
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) Pa[cb] = Pb[cb] = zero4();
+  // T_a and Aqk_a as 8-wide operands whose k-values 4..7 stay zero: the
+  // 16-deep products T_a V_a and D_a^T Aqk_a^T run as 16x16x32 products (one
+  // instruction shape per accumulation chain) whatever the other operand
+  // holds in those k-values.
+  f16x8 ta8 = {}, aa8 = {};
   int slot = 0;  // ring slot of pair xl
   for (int64_t xl = 0; xl < nseg; ++xl) {
     const bool tail = xl == nseg - 1;  // only the sequence's last pair can be partial
@@ -356,9 +367,8 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     // the O products, those of the state update), each issued before the
     // products that precede its use, so that the step waits for LDS a few
     // times rather than once per product.
-    const f16x4 ta = *(const f16x4*)(Rs + rec::kTa + lane * 8);
-    const f16x4 tb = *(const f16x4*)(Rs + rec::kTb + lane * 8);
-    const f16x4 pm = *(const f16x4*)(Rs + rec::kPm + lane * 8);
+    ta8 = with_low(ta8, *(const f16x4*)(Rs + rec::kTa + lane * 8));
+    const f16x8 tbp = *(const f16x8*)(Rs + rec::kTbP + lane * 16);
     bf16x4 vna[NCB], vnb[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
@@ -376,32 +386,29 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
       if (xl > 0) epilogue(xl - 1, Pa, Pb);
     }
 
-    // ---- D_a, D_b.  T V, P D_a and D^T Aqk^T are 16x16x32 products with
-    // k-values 4..7 of each lane zero: every accumulation chain uses one
-    // instruction shape (a 16x16x16 result fed straight into a 16x16x32
-    // accumulator read stale values on gfx950).
+    // ---- D_a, D_b.  Every accumulation chain uses one instruction shape,
+    // 16x16x32 (a 16x16x16 result fed straight into a 16x16x32 accumulator
+    // read stale values on gfx950).
     f16x8 sop[NCB][4];
-    f16x4 da16[NCB], db16[NCB];
+    f16x8 dab[NCB];  // [D_a ; D_b] in k-operand order (lane (c, g): D[4 g + e][c])
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) sop[cb][s] = cat8(to_h4(S[cb][2 * s]), to_h4(S[cb][2 * s + 1]));
       const f16x4 va = to_h4(mma16b(vna[cb], ident, zero4()));  // lane (c, g): V_a[4 g + e][c]
       const f16x4 vb = to_h4(mma16b(vnb[cb], ident, zero4()));
-      f32x4 d = mma32h(cat8(ta, f16x4{}), cat8(va, f16x4{}), zero4());
+      f32x4 d = mma32h(ta8, cat8(va, vb), zero4());  // k-values 4..7 of ta8 are zero
 #pragma unroll
       for (int s = 0; s < 4; ++s) d = mma32h(wa[s], sop[cb][s], d);
-      da16[cb] = to_h4(d);
-      f32x4 e = mma32h(cat8(tb, f16x4{}), cat8(vb, f16x4{}), zero4());
+      const f16x4 da16 = to_h4(d);
+      f32x4 e = mma32h(tbp, cat8(vb, da16), zero4());  // T_b V_b + P D_a
 #pragma unroll
       for (int s = 0; s < 4; ++s) e = mma32h(wb[s], sop[cb][s], e);
-      e = mma32h(cat8(pm, f16x4{}), cat8(da16[cb], f16x4{}), e);
-      db16[cb] = to_h4(e);
+      dab[cb] = cat8(da16, to_h4(e));
     }
     __builtin_amdgcn_sched_barrier(0);
-    const f16x4 aa = *(const f16x4*)(Rs + rec::kAa + lane * 8);
-    const f16x4 ab = *(const f16x4*)(Rs + rec::kAb + lane * 8);
-    const f16x4 qba = *(const f16x4*)(Rs + rec::kQba + lane * 8);
+    aa8 = with_low(aa8, *(const f16x4*)(Rs + rec::kAa + lane * 8));
+    const f16x8 qbaab = *(const f16x8*)(Rs + rec::kQbaAb + lane * 16);
     f16x8 qa[4], qb[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -420,9 +427,8 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
         x = mma32h(sop[cb][s], qa[s], x);
         y = mma32h(sop[cb][s], qb[s], y);
       }
-      Oa[cb] = mma32h(cat8(da16[cb], f16x4{}), cat8(aa, f16x4{}), x);
-      y = mma32h(cat8(da16[cb], f16x4{}), cat8(qba, f16x4{}), y);
-      Ob[cb] = mma32h(cat8(db16[cb], f16x4{}), cat8(ab, f16x4{}), y);
+      Oa[cb] = mma32h(dab[cb], aa8, x);     // + D_a^T Aqk_a^T (k-values 4..7 of aa8 are zero)
+      Ob[cb] = mma32h(dab[cb], qbaab, y);   // + D_a^T Q_ba^T + D_b^T Aqk_b^T
     }
     if constexpr (GATE) {
       float pa = 0.f, pb = 0.f;
@@ -469,7 +475,7 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
-        S[cb][kb] = mma32h(kb8[kb], cat8(da16[cb], db16[cb]), S[cb][kb] * e4[kb]);
+        S[cb][kb] = mma32h(kb8[kb], dab[cb], S[cb][kb] * e4[kb]);
 
     if constexpr (GATE) {
 #pragma unroll

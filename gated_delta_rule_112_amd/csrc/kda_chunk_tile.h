@@ -304,7 +304,6 @@ __device__ __forceinline__ void build_pair(const Args& a, const Pos& p, const Po
     }
     cur = nxt;
   }
-  *(f16x4*)(R + rec::kQba + lane * 8) = to_h4(qba);
 
   f16x4 ta, aqa, tb, aqb;
   finish(aa, qa, betaa, sm, lane, ta, aqa);
@@ -317,11 +316,10 @@ __device__ __forceinline__ void build_pair(const Args& a, const Pos& p, const Po
     *(f16x8*)(R + rec::kWa + s * 1024 + lane * 16) = cat8(to_h4(w[0]), to_h4(w[1]));
   }
   finish(ab, qb, betab, sm, lane, tb, aqb);
-  *(f16x4*)(R + rec::kTb + lane * 8) = tb;
-  *(f16x4*)(R + rec::kAb + lane * 8) = aqb;
   // P = -W_b Kb_a^T = -T_b M, formed as (M^T T_b^T)^T: lane (i, g) gets P[i][4 g + r]
   const f32x4 pm = -mma16h(to_h4(mba), tb, zero4());
-  *(f16x4*)(R + rec::kPm + lane * 8) = to_h4(pm);
+  *(f16x8*)(R + rec::kTbP + lane * 16) = cat8(tb, to_h4(pm));
+  *(f16x8*)(R + rec::kQbaAb + lane * 16) = cat8(to_h4(qba), aqb);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     f32x4 w[2];
