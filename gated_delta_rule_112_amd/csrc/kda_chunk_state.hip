@@ -606,10 +606,6 @@ hipError_t launch_chunk_mfma(const ChunkArgs& a) {
   float* carry = a.s_out != nullptr ? a.s_out : (float*)(buf[1] + BH * seg * rec::kBytes);
   const int cus = device_cus();
   const int split = split_for(a, cus);
-  // State columns per state wavefront: 32 (one state wavefront per SIMD)
-  // unless KDA_CPW=16 asks for two wavefronts of 16 columns per SIMD.
-  int cpw = 32;
-  if (const char* e = getenv("KDA_CPW")) cpw = atoi(e) == 16 ? 16 : 32;
   auto segment = [&](int64_t j) {
     Seg sg;
     if (j >= 0 && j < nsegs) {
@@ -625,18 +621,18 @@ hipError_t launch_chunk_mfma(const ChunkArgs& a) {
     const float* s_in = (j <= 0) ? a.s0 : carry;
     float* s_next = (j == nsegs - 1) ? a.s_out : carry;
     hipError_t e;
+    // 32 state columns per state wavefront: one state and one loader
+    // wavefront per SIMD, each with up to 256 registers (the tile builder
+    // running in the same launch needs them).
     if (a.o == nullptr)
       e = split == 2 ? launch_state_t<64, 32, false, false>(a, cur, s_in, s_next, nxt, cus)
-          : cpw == 16 ? launch_state_t<128, 16, false, false>(a, cur, s_in, s_next, nxt, cus)
-                      : launch_state_t<128, 32, false, false>(a, cur, s_in, s_next, nxt, cus);
+                     : launch_state_t<128, 32, false, false>(a, cur, s_in, s_next, nxt, cus);
     else if (a.gate != nullptr)
-      e = cpw == 16 ? launch_state_t<128, 16, true, true>(a, cur, s_in, s_next, nxt, cus)
-                    : launch_state_t<128, 32, true, true>(a, cur, s_in, s_next, nxt, cus);
+      e = launch_state_t<128, 32, true, true>(a, cur, s_in, s_next, nxt, cus);
     else if (split == 2)
       e = launch_state_t<64, 32, false, true>(a, cur, s_in, s_next, nxt, cus);
     else
-      e = cpw == 16 ? launch_state_t<128, 16, false, true>(a, cur, s_in, s_next, nxt, cus)
-                    : launch_state_t<128, 32, false, true>(a, cur, s_in, s_next, nxt, cus);
+      e = launch_state_t<128, 32, false, true>(a, cur, s_in, s_next, nxt, cus);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

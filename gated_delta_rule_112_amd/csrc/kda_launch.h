@@ -59,7 +59,7 @@ struct NormArgs {
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_chunk_valu(const ChunkArgs& a);
-// Matrix-core prefill (tile records and state pass, segment by segment).
+// Matrix-core prefill (per-pair records and state pass, segment by segment).
 // Returns hipErrorNotSupported when it does not cover the shape.
 hipError_t launch_chunk_mfma(const ChunkArgs& a);
 bool chunk_mfma_supports(int dk, int dv, bool io_bf16);

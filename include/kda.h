@@ -77,10 +77,11 @@ typedef enum {
  * Computed chunkwise in 16-token tiles ("Kimi K3: Engineering ...", section
  * "Dimension 1"); the result equals the token-by-token recurrence up to
  * floating-point rounding.  With bfloat16 io and dk = dv = 128 it runs on the
- * matrix cores, one launch per segment of tiles: its first workgroups walk
- * the tiles of the segment of each head in order with the running state on
- * chip, while the other workgroups compute the state-independent part of
- * every tile of the next segment (the per-tile records) into the workspace.
+ * matrix cores, one launch per segment of pairs of tiles: its first
+ * workgroups walk the pairs of the segment of each head in order with the
+ * running state on chip, while the other workgroups compute the
+ * state-independent part of every pair of the next segment (the per-pair
+ * records) into the workspace.
  * The state is written to memory only at segment boundaries (to s_out, or to
  * the workspace when s_out is NULL) and at the end.
  *
@@ -118,10 +119,11 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
 
 /*
  * kda_chunk_fwd_workspace_size -- bytes of workspace kda_chunk_fwd needs for
- * these sizes: 0 for the vector-ALU path, otherwise two buffers of per-tile
- * records, each holding one segment of tiles of every head (about 256 MiB, or
- * 13,824 bytes per head when one tile of every head exceeds that), plus one
- * float32 state per head.  Returns 0 for arguments kda_chunk_fwd would reject.
+ * these sizes: 0 for the vector-ALU path, otherwise two buffers of per-pair
+ * records, each holding one segment of pairs of 16-token tiles of every head
+ * (28,160 bytes per pair and head; about 64 MiB, at most 256 MiB unless one
+ * pair of every head exceeds that), plus one float32 state per head.
+ * Returns 0 for arguments kda_chunk_fwd would reject.
  */
 size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk, int dv,
                                     kda_dtype io);
