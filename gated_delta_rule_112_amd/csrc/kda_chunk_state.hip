@@ -558,17 +558,32 @@ int split_for(const ChunkArgs& a, int cus) {
 // cache with the rest of a launch's traffic, which makes the read-back
 // cheaper; longer sequences use longer segments (at most about 64 launches,
 // at most 256 MiB per record buffer) so that the per-launch cost (state load
-// and store, pipeline fill) stays small.
-int64_t seg_pairs(int64_t BH, int64_t npairs) {
+// and store, pipeline fill) stays small.  Below that cap the length is a
+// whole number of builder rounds (one pair per tile wavefront of the
+// launch): a launch lasts until its slowest tile wavefront is done, so a
+// short segment one pair over a round costs a whole round more.
+int64_t seg_pairs(int64_t BH, int64_t npairs, int cus, int split) {
   int64_t seg = 0;
   if (const char* e = getenv("KDA_SEG_PAIRS")) seg = atoll(e);
   if (seg <= 0) {
     const int64_t per_row = BH * (int64_t)rec::kBytes;  // record bytes of one pair of every head
-    seg = (int64_t(64) << 20) / per_row;
+    int64_t want = (int64_t(64) << 20) / per_row;
     const int64_t min_seg = (npairs + 63) / 64;
-    if (seg < min_seg) seg = min_seg;
+    if (want < min_seg) want = min_seg;
     const int64_t cap = (int64_t(256) << 20) / per_row;
-    if (seg > cap) seg = cap;
+    // pairs per builder round: tile wavefronts of a launch / heads
+    const int64_t nw = rec::kDV / split / 32 + kLoaders;
+    int64_t avail = cus - BH * split;
+    if (avail < cus / 4) avail = cus / 4;
+    int64_t round = nw * avail / BH;
+    if (round < 1) round = 1;
+    if (want >= cap) {
+      seg = cap;
+    } else {
+      int64_t k = (want + round / 2) / round;  // nearest whole number of rounds
+      if (k < 1) k = 1;
+      seg = k * round < cap ? k * round : cap;
+    }
   }
   if (seg < 1) seg = 1;
   return seg < npairs ? seg : npairs;
@@ -584,7 +599,10 @@ bool chunk_mfma_supports(int dk, int dv, bool io_bf16) {
 
 size_t chunk_mfma_workspace(int64_t B, int64_t T, int64_t H) {
   const int64_t BH = B * H, np = pairs_of(T);
-  const int64_t seg = seg_pairs(BH, np);
+  const int cus = device_cus();
+  // either workgroup layout (it depends on the gate, unknown here)
+  const int64_t s1 = seg_pairs(BH, np, cus, 1), s2 = seg_pairs(BH, np, cus, 2);
+  const int64_t seg = s1 > s2 ? s1 : s2;
   // two record buffers (the segment being consumed and the one being built),
   // then a carried state for when s_out is absent
   return (size_t)(2 * BH * seg * rec::kBytes) + (size_t)(BH * rec::kDK * rec::kDV * 4);
@@ -592,20 +610,28 @@ size_t chunk_mfma_workspace(int64_t B, int64_t T, int64_t H) {
 
 int64_t chunk_mfma_launches(int64_t B, int64_t T, int64_t H) {
   const int64_t np = pairs_of(T);
-  const int64_t seg = seg_pairs(B * H, np);
+  const int cus = device_cus();
+  ChunkArgs a{};
+  a.B = B;
+  a.H = H;
+  const int64_t seg = seg_pairs(B * H, np, cus, split_for(a, cus));  // without the gate
   return (np + seg - 1) / seg + 1;  // one per segment, plus the first segment's records
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a) {
   if (!chunk_mfma_supports(a.dk, a.dv, a.io_bf16)) return hipErrorNotSupported;
   const int64_t BH = a.B * a.H, np = pairs_of(a.T);
-  const int64_t seg = seg_pairs(BH, np);
-  const int64_t nsegs = (np + seg - 1) / seg;
-  unsigned char* buf[2] = {(unsigned char*)a.workspace,
-                           (unsigned char*)a.workspace + BH * seg * rec::kBytes};
-  float* carry = a.s_out != nullptr ? a.s_out : (float*)(buf[1] + BH * seg * rec::kBytes);
   const int cus = device_cus();
   const int split = split_for(a, cus);
+  const int64_t seg = seg_pairs(BH, np, cus, split);
+  const int64_t nsegs = (np + seg - 1) / seg;
+  // record buffers laid out for the workspace size's segment (the larger
+  // of the two layouts'), the carried state after them
+  const int64_t segw = (chunk_mfma_workspace(a.B, a.T, a.H) - (size_t)BH * rec::kDK * rec::kDV * 4) /
+                       (2 * BH * (int64_t)rec::kBytes);
+  unsigned char* buf[2] = {(unsigned char*)a.workspace,
+                           (unsigned char*)a.workspace + BH * segw * rec::kBytes};
+  float* carry = a.s_out != nullptr ? a.s_out : (float*)(buf[1] + BH * segw * rec::kBytes);
   auto segment = [&](int64_t j) {
     Seg sg;
     if (j >= 0 && j < nsegs) {
