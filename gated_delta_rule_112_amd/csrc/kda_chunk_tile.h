@@ -64,7 +64,7 @@ struct SlabIn {
 };
 
 struct Scratch {  // per wavefront
-  float a[16][20];  // A = strict_lower(Diag(beta) Kh Kc^T), row-major, padded rows
+  float a[16][20];  // -A = -strict_lower(Diag(beta) Kh Kc^T), row-major, padded rows
   float beta[16];
   float en_a[rec::kDK];  // E_a of the pair being built, per key channel
 };
@@ -150,14 +150,81 @@ __device__ __forceinline__ void transpose_slab(const float (&x)[8], f16x4 ident,
   }
 }
 
-// One step of the forward substitution: column values y[e] of rows i (this
-// lane's row) receive -A[i][M] * y_M, with y_M broadcast from lane M of the row.
-template <int M>
-__device__ __forceinline__ void forward_sub(float (&y)[4], const f32x4 (&arow)[4]) {
-  const float aim = arow[M / 4][M % 4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) y[e] = fmaf(-aim, row_bcast<M>(y[e]), y[e]);
-  if constexpr (M + 1 < 15) forward_sub<M + 1>(y, arow);
+// Forward substitution for (I + A) Y = I, A strictly lower triangular:
+// y[e] (this lane's row i, column 4 g + e) receives -A[i][M] y_M for
+// M = 0..14, y_M taken from lane M of the row.  One fused DPP multiply-add
+// per column and step (the broadcast is the first source operand of
+// v_fmac_f32_dpp); `an` holds -A[i][0..15].  The four columns of a step are
+// independent, so each broadcast read comes at least three instructions
+// after the write of the value it reads (DPP needs two), and the block
+// opens with the two wait states its first reads need.
+__device__ __forceinline__ void forward_sub(float (&y)[4], const f32x4 (&an)[4]) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %4 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %4 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %4 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %4 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %0, %5 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %5 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %5 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %5 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %0, %6 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %6 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %6 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %6 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %0, %7 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %7 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %7 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %7 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %0, %8 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %8 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %8 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %8 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %0, %9 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %9 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %9 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %9 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %0, %10 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %10 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %10 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %10 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %0, %11 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %11 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %11 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %11 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %0, %12 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %12 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %12 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %12 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %0, %13 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %13 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %13 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %13 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %0, %14 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %14 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %14 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %14 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %0, %15 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %15 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %15 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %15 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %0, %16 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %16 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %16 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %16 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %0, %17 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %17 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %17 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %17 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %0, %18 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %18 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %18 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %18 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+      : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3])
+      : "v"(an[0][0]), "v"(an[0][1]), "v"(an[0][2]), "v"(an[0][3]), "v"(an[1][0]),
+        "v"(an[1][1]), "v"(an[1][2]), "v"(an[1][3]), "v"(an[2][0]), "v"(an[2][1]),
+        "v"(an[2][2]), "v"(an[2][3]), "v"(an[3][0]), "v"(an[3][1]), "v"(an[3][2]));
 }
 
 // From the intra-tile products summed over all slabs: the causal masks, the
@@ -166,11 +233,11 @@ __device__ __forceinline__ void forward_sub(float (&y)[4], const f32x4 (&arow)[4
 __device__ __forceinline__ void finish(f32x4 acc_a, f32x4 acc_q, float bt, Scratch* sm, int lane,
                                        f16x4& tb, f16x4& aq) {
   const int t = lane % 16, lg = lane / 16;
-  f32x4 am;  // selects: masked entries may be huge products of e^-G
+  f32x4 am;  // -A; selects: masked entries may be huge products of e^-G
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int j = 4 * lg + r;
-    am[r] = (j < t) ? bt * acc_a[r] : 0.f;
+    am[r] = (j < t) ? -bt * acc_a[r] : 0.f;
     aq[r] = (f16)((j <= t) ? acc_q[r] : 0.f);
   }
   const unsigned arow_addr = lds_addr(&sm->a[t][0]);
@@ -191,7 +258,7 @@ __device__ __forceinline__ void finish(f32x4 acc_a, f32x4 acc_q, float bt, Scrat
   float y[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) y[e] = (t == 4 * lg + e) ? 1.f : 0.f;
-  forward_sub<0>(y, arow);
+  forward_sub(y, arow);
   tb = f16x4{(f16)(y[0] * bj[0]), (f16)(y[1] * bj[1]), (f16)(y[2] * bj[2]), (f16)(y[3] * bj[3])};
 }
 
