@@ -9,8 +9,8 @@
 // each k step is one of the lane's channels, so the operands come straight
 // from registers):
 //   lane (i, g) accumulates (Kh Kc^T)[i][4 g + r] and (Qh Kc^T)[i][4 g + r].
-// Kh and Kb are transposed to channel-major 16x16 blocks by a product with a
-// 0/1 selection matrix (exact).  With the products summed over all slabs, the
+// Kh and Kb are transposed to channel-major 16x16 blocks through LDS with the
+// transpose read of gfx950 (exact).  With the products summed over all slabs, the
 // 16x16 unit-lower-triangular system (I + A) Y = I is solved by forward
 // substitution, lane (i, g) holding rows i of columns 4 g + 0..3 and the pivot
 // row broadcast over each DPP row; then T = Y Diag(beta) and W = T Kh, one
@@ -64,6 +64,7 @@ struct SlabIn {
 };
 
 struct Scratch {  // per wavefront
+  f16x4 tr[2][64];  // staging of the transposes, [half slab][lane]
   float a[16][20];  // -A = -strict_lower(Diag(beta) Kh Kc^T), row-major, padded rows
   float beta[16];
   float en_a[rec::kDK];  // E_a of the pair being built, per key channel
@@ -83,14 +84,6 @@ __device__ __forceinline__ void load_slab(SlabIn& in, const bf16_t* q, const bf1
   in.k = __builtin_nontemporal_load((const bf16x8*)(k + off));
   in.g0 = __builtin_nontemporal_load((const f32x4*)(g + off));
   in.g1 = __builtin_nontemporal_load((const f32x4*)(g + off + 4));
-}
-
-// Selection matrix for the transposes: B[k = 4 g + e][c] = (k == c).
-__device__ __forceinline__ f16x4 selection(int lane) {
-  f16x4 id;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) id[e] = (f16)((4 * (lane / 16) + e == lane % 16) ? 1.f : 0.f);
-  return id;
 }
 
 // One lane's rescaled values of one slab of one tile (channels 32 s + 8 g + e).
@@ -141,13 +134,26 @@ __device__ __forceinline__ f16x8 to_h8(const float (&x)[8]) {
 }
 
 // Channel-major blocks 2s (channels 32 s + 8 g + 0..3) and 2s+1 (+ 4..7) of a
-// token-major slab: out[hb] lane (c, g) = x[token 4 g + r][chan(2 s + hb, c)].
-__device__ __forceinline__ void transpose_slab(const float (&x)[8], f16x4 ident, f16x4 (&out)[2]) {
+// token-major slab: out[hb] lane (c, g) = x[token 4 g + r][chan(2 s + hb, c)],
+// through LDS.  Each lane stores its 4 channels of a half slab (8 bytes, in
+// lane order); lane 16 g + j then reads the 4 channels 32 s + 8 (j % 4) +
+// 4 hb + 0..3 of token 4 g + j / 4 with the transpose read
+// (ds_read_b64_tr_b16), which hands lane i of each 16-lane group element
+// i % 4 of what lane 4 e + i / 4 of its group read, as its element e.
+__device__ __forceinline__ void transpose_slab(const float (&x)[8], Scratch* sm, int lane,
+                                               f16x4 (&out)[2]) {
+  const int j = lane % 16, g = lane / 16;
+  const int src = (j % 4) * 16 + 4 * g + j / 4;  // lane (token 4 g + j / 4, group j % 4)
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const f16x4 x4 = {(f16)x[4 * hb], (f16)x[4 * hb + 1], (f16)x[4 * hb + 2], (f16)x[4 * hb + 3]};
-    out[hb] = to_h4(mma16h(x4, ident, zero4()));
-  }
+  for (int hb = 0; hb < 2; ++hb)
+    sm->tr[hb][lane] = f16x4{(f16)x[4 * hb], (f16)x[4 * hb + 1], (f16)x[4 * hb + 2],
+                             (f16)x[4 * hb + 3]};
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+    out[hb] = __builtin_bit_cast(
+        f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                   (__attribute__((address_space(3))) i16x4*)(
+                       (__attribute__((address_space(3))) f16x4*)&sm->tr[hb][0] + src)));
 }
 
 // Forward substitution for (I + A) Y = I, A strictly lower triangular:
@@ -312,7 +318,7 @@ __device__ __forceinline__ void load_pair_slab(PairIn& x, const Args& a, const P
 // is built, and on return `cur` holds slab 0 of pair `pn` (the wavefront's
 // next pair, or any valid pair when there is none).
 __device__ __forceinline__ void build_pair(const Args& a, const Pos& p, const Pos& pn, PairIn& cur,
-                                           f16x4 ident, Scratch* sm, int lane) {
+                                           Scratch* sm, int lane) {
   const int t = lane % 16, lg = lane / 16;
   const int64_t tok0 = (a.x0 + p.xl) * rec::kP;
   const PairRows rows = pair_rows(a, p, lane), nrows = pair_rows(a, pn, lane);
@@ -334,7 +340,7 @@ __device__ __forceinline__ void build_pair(const Args& a, const Pos& p, const Po
     // tile a: its values, then everything that needs only them
     SlabVals va;
     slab_vals_any(fulla, cur.a, lva, a.scale, va, aa, qa);
-    transpose_slab(va.kh, ident, khTa[s]);
+    transpose_slab(va.kh, sm, lane, khTa[s]);
     const f16x8 kba = to_h8(va.kb);  // Kb_a, token-major
     *(f16x8*)(R + rec::kQa + s * 1024 + lane * 16) = to_h8(va.qh);
     if (t == 0) {
@@ -345,7 +351,7 @@ __device__ __forceinline__ void build_pair(const Args& a, const Pos& p, const Po
     // tile b, and the cross terms
     SlabVals vb;
     slab_vals_any(fullb, cur.b, lvb, a.scale, vb, ab, qb);
-    transpose_slab(vb.kh, ident, khTb[s]);
+    transpose_slab(vb.kh, sm, lane, khTb[s]);
     // Q_ba^T: lane (i, g) accumulates (Qh_b Kb_a^T)[i][4 g + r];
     // M = Kh_b Kb_a^T: lane (j, g) accumulates M[4 g + r][j]
     qba = mma32h(kba, to_h8(vb.qh), qba);
@@ -357,8 +363,8 @@ __device__ __forceinline__ void build_pair(const Args& a, const Pos& p, const Po
     f16x4 kta[2], ktb[2];
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = va.kb[e] * vb.en[e];
-    transpose_slab(x, ident, kta);
-    transpose_slab(vb.kb, ident, ktb);
+    transpose_slab(x, sm, lane, kta);
+    transpose_slab(vb.kb, sm, lane, ktb);
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
       *(f16x8*)(R + rec::kKb + (2 * s + hb) * 1024 + lane * 16) = cat8(kta[hb], ktb[hb]);
@@ -412,7 +418,6 @@ __device__ __forceinline__ void build_range(const Args& a, int64_t first, int64_
                                             Scratch* sm, int lane) {
   const int64_t total = a.BH * a.nseg;
   if (first >= total) return;
-  const f16x4 ident = selection(lane);
   // w = xl BH + b H + h; the stride split the same way, advanced without divisions
   const int64_t B = a.BH / a.H;
   const int64_t sxl = stride / a.BH, sbh = stride - sxl * a.BH;
@@ -442,7 +447,7 @@ __device__ __forceinline__ void build_range(const Args& a, int64_t first, int64_
   load_pair_slab(cur, a, pair_rows(a, p, lane), 0, lane);
   for (int64_t w = first; w < total; w += stride) {
     const Pos pn = w + stride < total ? advance(p) : p;  // past the last pair: reload this one
-    build_pair(a, p, pn, cur, ident, sm, lane);
+    build_pair(a, p, pn, cur, sm, lane);
     p = pn;
   }
 }
