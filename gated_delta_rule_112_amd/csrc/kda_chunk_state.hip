@@ -72,6 +72,11 @@ __device__ __forceinline__ f16x8 with_low(f16x8 x, f16x4 lo) {
   return __builtin_shufflevector(l8, x, 0, 1, 2, 3, 12, 13, 14, 15);
 }
 
+// Elements 4 h .. 4 h + 3 of x (h = 0 or 1).
+__device__ __forceinline__ bf16x4 half4(bf16x8 x, int h) {
+  return h == 0 ? __builtin_shufflevector(x, x, 0, 1, 2, 3) : __builtin_shufflevector(x, x, 4, 5, 6, 7);
+}
+
 // A slot is a whole number of 1 KB blocks (one direct-to-LDS load of a wave
 // each); every block holds only record bytes or only v / gate bytes.
 template <int DVW, bool GATE>
@@ -113,6 +118,7 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
   constexpr int kRing = SC::kRing, kLead = SC::kLead;
   constexpr int NSW = DVW / CPW;   // state wavefronts
   constexpr int NCB = CPW / 16;    // 16-column blocks per state wavefront
+  static_assert(NCB == 2, "a lane's output columns are one 16-byte run of both column blocks");
   constexpr int NSPLIT = rec::kDV / DVW;
   static_assert(CPW % 16 == 0 && DVW % CPW == 0 && rec::kDV % DVW == 0, "bad column split");
   static_assert(!GATE || NSPLIT == 1, "the gated RMSNorm needs a head's full dv row");
@@ -213,9 +219,17 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
         unsigned char* dst = blk < SC::kSlot / 1024
                                  ? ring[slot] + blk * 1024
                                  : gring + gslot * SC::kGSlot + (blk - SC::kSlot / 1024) * 1024;
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)src,
-            (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        // Records keep the default cache policy (they were just written and
+        // are read once from the memory-side cache); v and gate rows are read
+        // once from HBM and are loaded non-temporal (cache-policy bit nt).
+        if (kind[i] == 0)
+          __builtin_amdgcn_global_load_lds(
+              (const __attribute__((address_space(1))) void*)src,
+              (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        else
+          __builtin_amdgcn_global_load_lds(
+              (const __attribute__((address_space(1))) void*)src,
+              (__attribute__((address_space(3))) void*)dst, 16, 0, 2);
       }
     };
     // Gate chunks of this lane (GATE: the pair's 32 gate rows are
@@ -283,8 +297,13 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
 
   // ============================================================ state waves
   const int wl = wave * CPW;  // first column of this wave, in the workgroup
+  // Value column of index c in column block cb (a relabelling within the
+  // wave's 32 columns): each lane's output elements, rows 4 g + r of both
+  // blocks' O^T, are then 8 adjacent columns, wl + 8 g + [0, 8).
+  auto vcol = [&](int cb, int c) { return wl + 8 * (c / 4) + 4 * cb + c % 4; };
 
-  // State: block kb of column block cb, lane (c, g), r = row chan(kb, 4 g + r).
+  // State: block kb of column block cb, lane (c, g), r = row chan(kb, 4 g + r),
+  // column vcol(cb, c).
   f32x4 S[NCB][8];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
@@ -292,7 +311,7 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     for (int kb = 0; kb < 8; ++kb) {
       f32x4 x = zero4();
       if (s_in != nullptr) {
-        const float* p = s_in + bh * rec::kDK * rec::kDV + col0 + wl + 16 * cb + lc;
+        const float* p = s_in + bh * rec::kDK * rec::kDV + col0 + vcol(cb, lc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] = p[rec::chan(kb, 4 * lg + r) * rec::kDV];
       }
@@ -302,21 +321,17 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
   bf16x4 ident;
 #pragma unroll
   for (int e = 0; e < 4; ++e) ident[e] = (bf16_t)((4 * lg + e == lc) ? 1.f : 0.f);
-  // LDS byte offset, within the v / gate rows, of this lane's 4 columns of
-  // token lc (tile a); tile b's token lc is 16 rows further, with the same
-  // swizzle (rows 16 apart permute their chunks alike).
+  // LDS byte offset, within the v / gate rows, of this lane's 8 columns
+  // vcol(cb, 4 lg + e) (one 16-byte chunk) of token lc (tile a); tile b's
+  // token lc is 16 rows further, with the same swizzle (rows 16 apart permute
+  // their chunks alike).
   static_assert(16 % SC::kRowsPerBankLine == 0 && (16 / SC::kRowsPerBankLine) % SC::kCpr == 0,
                 "rows 16 apart must swizzle alike");
-  int tile_off[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const int col = wl + 16 * cb + 4 * lg;
-    tile_off[cb] = lc * SC::kRowB + 16 * SC::swz(lc, col / 8) + 2 * (col % 8);
-  }
+  const int tile_off = lc * SC::kRowB + 16 * SC::swz(lc, (wl + 8 * lg) / 8);
 
   // Output of pair x: this lane writes tokens lc and 16 + lc, columns
-  // col0 + wl + 16 cb + 4 lg.
-  const int64_t o_lane = lc * rstride + col0 + wl + 4 * lg;
+  // col0 + wl + 8 lg + [0, 8).
+  const int64_t o_lane = lc * rstride + col0 + wl + 8 * lg;
   auto o_pair = [&](int64_t x) { return o + ((b * T + (x0 + x) * rec::kP) * H + h) * rec::kDV; };
   __syncthreads();  // pair 0 is in LDS
 
@@ -335,19 +350,18 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     const int64_t tok = (x0 + x) * rec::kP + lc;
     const unsigned char* G = gring + (SC::kGRing > 0 ? (int)(x % SC::kGRing) : 0) * SC::kGSlot;
     bf16_t* op = o_pair(x) + o_lane;
+    const f16x8 swa = *(const f16x8*)(G + tile_off);
+    const f16x8 swb = *(const f16x8*)(G + 16 * SC::kRowB + tile_off);
+    bf16x8 ya, yb;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const f16x4 swa = *(const f16x4*)(G + tile_off[cb]);
-      const f16x4 swb = *(const f16x4*)(G + 16 * SC::kRowB + tile_off[cb]);
-      bf16x4 ya, yb;
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        ya[r] = (bf16_t)(Pa[cb][r] * inva * (float)swa[r]);
-        yb[r] = (bf16_t)(Pb[cb][r] * invb * (float)swb[r]);
+        ya[4 * cb + r] = (bf16_t)(Pa[cb][r] * inva * (float)swa[4 * cb + r]);
+        yb[4 * cb + r] = (bf16_t)(Pb[cb][r] * invb * (float)swb[4 * cb + r]);
       }
-      if (tok < T) *(bf16x4*)(op + 16 * cb) = ya;
-      if (tok + rec::kC < T) *(bf16x4*)(op + rec::kC * rstride + 16 * cb) = yb;
-    }
+    if (tok < T) __builtin_nontemporal_store(ya, (bf16x8*)op);
+    if (tok + rec::kC < T) __builtin_nontemporal_store(yb, (bf16x8*)(op + rec::kC * rstride));
   };
 
   f32x4 Pa[NCB], Pb[NCB];  // outputs of the previous pair, normalised one step later
@@ -369,12 +383,9 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     // times rather than once per product.
     ta8 = with_low(ta8, *(const f16x4*)(Rs + rec::kTa + lane * 8));
     const f16x8 tbp = *(const f16x8*)(Rs + rec::kTbP + lane * 16);
-    bf16x4 vna[NCB], vnb[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      vna[cb] = *(const bf16x4*)(Rs + SC::kV + tile_off[cb]);
-      vnb[cb] = *(const bf16x4*)(Rs + SC::kV + 16 * SC::kRowB + tile_off[cb]);
-    }
+    // lane (t, g), column block cb: V[t][vcol(cb, 4 g + e)], elements 4 cb + e
+    const bf16x8 vna = *(const bf16x8*)(Rs + SC::kV + tile_off);
+    const bf16x8 vnb = *(const bf16x8*)(Rs + SC::kV + 16 * SC::kRowB + tile_off);
     f16x8 wa[4], wb[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -395,8 +406,9 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) sop[cb][s] = cat8(to_h4(S[cb][2 * s]), to_h4(S[cb][2 * s + 1]));
-      const f16x4 va = to_h4(mma16b(vna[cb], ident, zero4()));  // lane (c, g): V_a[4 g + e][c]
-      const f16x4 vb = to_h4(mma16b(vnb[cb], ident, zero4()));
+      // lane (c, g): V_a[4 g + e][vcol(cb, c)]
+      const f16x4 va = to_h4(mma16b(half4(vna, cb), ident, zero4()));
+      const f16x4 vb = to_h4(mma16b(half4(vnb, cb), ident, zero4()));
       f32x4 d = mma32h(ta8, cat8(va, vb), zero4());  // k-values 4..7 of ta8 are zero
 #pragma unroll
       for (int s = 0; s < 4; ++s) d = mma32h(wa[s], sop[cb][s], d);
@@ -450,15 +462,17 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     } else if constexpr (WO) {
       const int64_t tok = (x0 + xl) * rec::kP + lc;
       bf16_t* op = o_pair(xl) + o_lane;
+      bf16x8 ya, yb;
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const bf16x4 ya = {(bf16_t)Oa[cb][0], (bf16_t)Oa[cb][1], (bf16_t)Oa[cb][2],
-                           (bf16_t)Oa[cb][3]};
-        const bf16x4 yb = {(bf16_t)Ob[cb][0], (bf16_t)Ob[cb][1], (bf16_t)Ob[cb][2],
-                           (bf16_t)Ob[cb][3]};
-        if (!tail || tok < T) *(bf16x4*)(op + 16 * cb) = ya;
-        if (!tail || tok + rec::kC < T) *(bf16x4*)(op + rec::kC * rstride + 16 * cb) = yb;
-      }
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          ya[4 * cb + r] = (bf16_t)Oa[cb][r];
+          yb[4 * cb + r] = (bf16_t)Ob[cb][r];
+        }
+      if (!tail || tok < T) __builtin_nontemporal_store(ya, (bf16x8*)op);
+      if (!tail || tok + rec::kC < T)
+        __builtin_nontemporal_store(yb, (bf16x8*)(op + rec::kC * rstride));
     }
 
     // ---- S <- Diag(E_a E_b) S + [Kb_a' | Kb_b]^T [D_a ; D_b]
@@ -494,7 +508,7 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
-        float* p = s_next + bh * rec::kDK * rec::kDV + col0 + wl + 16 * cb + lc;
+        float* p = s_next + bh * rec::kDK * rec::kDV + col0 + vcol(cb, lc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[rec::chan(kb, 4 * lg + r) * rec::kDV] = S[cb][kb][r];
       }
@@ -555,21 +569,19 @@ int split_for(const ChunkArgs& a, int cus) {
 // Pairs per segment.  One launch per segment, and the records of the segment
 // being consumed are read back while the next segment's are written: a
 // segment of about 64 MiB of records stays within the 256 MB memory-side
-// cache with the rest of a launch's traffic, which makes the read-back
-// cheaper; longer sequences use longer segments (at most about 64 launches,
-// at most 256 MiB per record buffer) so that the per-launch cost (state load
-// and store, pipeline fill) stays small.  Below that cap the length is a
-// whole number of builder rounds (one pair per tile wavefront of the
-// launch): a launch lasts until its slowest tile wavefront is done, so a
-// short segment one pair over a round costs a whole round more.
+// cache with the rest of a launch's traffic (v and gate rows bypass it),
+// which makes the read-back cheap.  The length is the whole number of
+// builder rounds (one pair per tile wavefront of the launch) nearest to that
+// size: a launch lasts until its slowest tile wavefront is done, so a
+// segment one pair over a round costs a whole round more.  At most 256 MiB
+// per record buffer.  Long sequences take more launches of the same length
+// (about 60 us each at 96 heads, far above the launch overhead).
 int64_t seg_pairs(int64_t BH, int64_t npairs, int cus, int split) {
   int64_t seg = 0;
   if (const char* e = getenv("KDA_SEG_PAIRS")) seg = atoll(e);
   if (seg <= 0) {
     const int64_t per_row = BH * (int64_t)rec::kBytes;  // record bytes of one pair of every head
-    int64_t want = (int64_t(64) << 20) / per_row;
-    const int64_t min_seg = (npairs + 63) / 64;
-    if (want < min_seg) want = min_seg;
+    const int64_t want = (int64_t(64) << 20) / per_row;
     const int64_t cap = (int64_t(256) << 20) / per_row;
     // pairs per builder round: tile wavefronts of a launch / heads
     const int64_t nw = rec::kDV / split / 32 + kLoaders;
@@ -577,13 +589,9 @@ int64_t seg_pairs(int64_t BH, int64_t npairs, int cus, int split) {
     if (avail < cus / 4) avail = cus / 4;
     int64_t round = nw * avail / BH;
     if (round < 1) round = 1;
-    if (want >= cap) {
-      seg = cap;
-    } else {
-      int64_t k = (want + round / 2) / round;  // nearest whole number of rounds
-      if (k < 1) k = 1;
-      seg = k * round < cap ? k * round : cap;
-    }
+    int64_t k = (want + round / 2) / round;  // nearest whole number of rounds
+    if (k < 1) k = 1;
+    seg = k * round < cap ? k * round : cap;
   }
   if (seg < 1) seg = 1;
   return seg < npairs ? seg : npairs;
