@@ -567,10 +567,10 @@ int split_for(const ChunkArgs& a, int cus) {
 }
 
 // Pairs per segment.  One launch per segment, and the records of the segment
-// being consumed are read back while the next segment's are written: a
-// segment of about 64 MiB of records stays within the 256 MB memory-side
-// cache with the rest of a launch's traffic (v and gate rows bypass it),
-// which makes the read-back cheap.  The length is the whole number of
+// being consumed are read back while the next segment's are written: two
+// segments of about 96 MiB of records each stay within the 256 MB
+// memory-side cache (v and gate rows and outputs bypass it), which makes the
+// read-back cheap.  The length is the whole number of
 // builder rounds (one pair per tile wavefront of the launch) nearest to that
 // size: a launch lasts until its slowest tile wavefront is done, so a
 // segment one pair over a round costs a whole round more.  At most 256 MiB
@@ -581,7 +581,7 @@ int64_t seg_pairs(int64_t BH, int64_t npairs, int cus, int split) {
   if (const char* e = getenv("KDA_SEG_PAIRS")) seg = atoll(e);
   if (seg <= 0) {
     const int64_t per_row = BH * (int64_t)rec::kBytes;  // record bytes of one pair of every head
-    const int64_t want = (int64_t(64) << 20) / per_row;
+    const int64_t want = (int64_t(96) << 20) / per_row;
     const int64_t cap = (int64_t(256) << 20) / per_row;
     // pairs per builder round: tile wavefronts of a launch / heads
     const int64_t nw = rec::kDV / split / 32 + kLoaders;

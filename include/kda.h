@@ -121,7 +121,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
  * kda_chunk_fwd_workspace_size -- bytes of workspace kda_chunk_fwd needs for
  * these sizes: 0 for the vector-ALU path, otherwise two buffers of per-pair
  * records, each holding one segment of pairs of 16-token tiles of every head
- * (28,160 bytes per pair and head; about 64 MiB, at most 256 MiB unless one
+ * (28,160 bytes per pair and head; about 96 MiB, at most 256 MiB unless one
  * pair of every head exceeds that), plus one float32 state per head.
  * Returns 0 for arguments kda_chunk_fwd would reject.
  */
