@@ -196,10 +196,8 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
         loff[i] = (unsigned)(2 * (t * rstride + lcol[i]));
       }
     }
-    // Copy pair xt (clamped into the segment) into ring slot `slot` and gate
-    // slot `gslot`.
+    // Copy pair xt (< nseg) into ring slot `slot` and gate slot `gslot`.
     auto issue = [&](int64_t xt, int slot, int gslot) {
-      xt = xt < nseg ? xt : nseg - 1;
       const int64_t row0 = (x0 + xt) * rec::kP;               // first token of the pair
       const bool full = row0 + rec::kP <= T;
       const unsigned char* base_r = R0 + xt * rec::kBytes;
@@ -271,16 +269,23 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
         ds_write16(addr, as_f4(y));
       }
     };
+    // No loads past the segment's last pair: the waits below count the loads
+    // in flight, so near the end (fewer pairs in flight) they wait for all.
 #pragma unroll
-    for (int y = 0; y < kLead; ++y) issue(y, y, y);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kLead - 1) * SC::kPer));  // pair 0 is in LDS
+    for (int y = 0; y < kLead; ++y)
+      if (y < nseg) issue(y, y, y);
+    if (kLead <= nseg)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((kLead - 1) * SC::kPer));  // pair 0 is in LDS
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_s_barrier();
     // Ring slot of pair x: x % kRing; gate slot: x % kGRing.
     int slot_issue = kLead, gslot_issue = kLead, gslot_cur = 0;
     for (int64_t xl = 0; xl < nseg; ++xl) {
       // the slot of pair xl - 1 (free since the last barrier) and the gate
       // slot of pair xl - 2 (read by the epilogue of the last step)
-      issue(xl + kLead, slot_issue, gslot_issue);
+      const bool more = xl + kLead < nseg;  // a pair to issue (uniform)
+      if (more) issue(xl + kLead, slot_issue, gslot_issue);
       slot_issue = slot_issue == kRing - 1 ? 0 : slot_issue + 1;
       if constexpr (GATE) {
         gslot_issue = gslot_issue == SC::kGRing - 1 ? 0 : gslot_issue + 1;
@@ -288,7 +293,10 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
         gslot_cur = gslot_cur == SC::kGRing - 1 ? 0 : gslot_cur + 1;
       }
       // pair xl + 1 is in LDS; the converted gate is written
-      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((kLead - 1) * SC::kPer));
+      if (more)
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((kLead - 1) * SC::kPer));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
       __builtin_amdgcn_s_barrier();
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));

@@ -77,11 +77,21 @@ __device__ __forceinline__ int64_t row_of(int64_t b, int64_t h, int64_t tok, int
   return (b * T + tok) * H + h;
 }
 
-__device__ __forceinline__ void load_slab(SlabIn& in, const bf16_t* q, const bf16_t* k,
-                                          const float* g, int64_t row, int s, int lane) {
+// This lane's q and k of slab s (and of slab s + 1, into q1 / k1) and g of slab
+// s.  A slab of q or k is 64 bytes of a token row, half a 128-byte line: the
+// two slabs of a line are loaded by back-to-back instructions, so that each
+// line leaves memory once (loaded a slab apart, the first half's line was
+// often gone when the second half was read).
+__device__ __forceinline__ void load_slab(SlabIn& in, bf16x8& q1, bf16x8& k1, const bf16_t* q,
+                                          const bf16_t* k, const float* g, int64_t row, int s,
+                                          int lane) {
   const int64_t off = row * rec::kDK + 32 * s + 8 * (lane / 16);
-  in.q = __builtin_nontemporal_load((const bf16x8*)(q + off));
-  in.k = __builtin_nontemporal_load((const bf16x8*)(k + off));
+  if (s % 2 == 0) {
+    in.q = __builtin_nontemporal_load((const bf16x8*)(q + off));
+    q1 = __builtin_nontemporal_load((const bf16x8*)(q + off + 32));
+    in.k = __builtin_nontemporal_load((const bf16x8*)(k + off));
+    k1 = __builtin_nontemporal_load((const bf16x8*)(k + off + 32));
+  }
   in.g0 = __builtin_nontemporal_load((const f32x4*)(g + off));
   in.g1 = __builtin_nontemporal_load((const f32x4*)(g + off + 4));
 }
@@ -296,6 +306,7 @@ struct Pos {
 // Inputs of one slab of both tiles of a pair, and the rows they come from.
 struct PairIn {
   SlabIn a, b;
+  bf16x8 qa1, ka1, qb1, kb1;  // q and k of the odd slab that follows an even one
 };
 
 struct PairRows {
@@ -309,12 +320,12 @@ __device__ __forceinline__ PairRows pair_rows(const Args& a, const Pos& p, int l
 
 __device__ __forceinline__ void load_pair_slab(PairIn& x, const Args& a, const PairRows& r, int s,
                                                int lane) {
-  load_slab(x.a, a.q, a.k, a.g, r.a, s, lane);
-  load_slab(x.b, a.q, a.k, a.g, r.b, s, lane);
+  load_slab(x.a, x.qa1, x.ka1, a.q, a.k, a.g, r.a, s, lane);
+  load_slab(x.b, x.qb1, x.kb1, a.q, a.k, a.g, r.b, s, lane);
 }
 
 // Builds pair p of head (b, h) and stores its record.  On entry `cur` holds
-// slab 0 of pair p; the next slab's inputs are always in flight while a slab
+// slab 0 of pair p (and the q and k of its slab 1); the next slab's inputs are always in flight while a slab
 // is built, and on return `cur` holds slab 0 of pair `pn` (the wavefront's
 // next pair, or any valid pair when there is none).
 __device__ __forceinline__ void build_pair(const Args& a, const Pos& p, const Pos& pn, PairIn& cur,
@@ -337,6 +348,12 @@ __device__ __forceinline__ void build_pair(const Args& a, const Pos& p, const Po
       load_pair_slab(nxt, a, rows, s + 1, lane);
     else
       load_pair_slab(nxt, a, nrows, 0, lane);
+    if (s % 2 == 0) {  // the odd slab's q and k came with this one's
+      nxt.a.q = cur.qa1;
+      nxt.a.k = cur.ka1;
+      nxt.b.q = cur.qb1;
+      nxt.b.k = cur.kb1;
+    }
     // tile a: its values, then everything that needs only them
     SlabVals va;
     slab_vals_any(fulla, cur.a, lva, a.scale, va, aa, qa);
