@@ -10,7 +10,9 @@ already resident in HBM.  The default workload is the full-width layer prefill
 (B=1, H=96, T=32768, dk=dv=128, bf16 q/k/v/gate, fp32 g/beta/state, epilogue
 on).  A second leg times the batched decode workload (B=256, H=96, 64
 successive single-token steps against a 1.6 GB fp32 state) and reports its
-HBM rate in the ``decode`` object of the same JSON line.
+HBM rate in the ``decode`` object of the same JSON line; a third times the
+multi-token decode step of speculative decoding (B=256, H=96, 4 draft tokens:
+one verify call and one commit call) in the ``verify`` object.
 
 Output: ONE JSON line on stdout (progress goes to stderr).
 """
@@ -74,6 +76,19 @@ def decode_bytes(B, H, dk, dv, es, with_gate=False):
     if with_gate:
         per += dv * es
     return B * H * per, per
+
+
+def verify_bytes(B, H, K, dk, dv, es, n_commit, with_gate=True):
+    """Multi-token decode (speculative decoding), per (b, h).  Verify (outputs
+    of all K draft tokens, nothing committed): the fp32 state read once and K
+    tokens of q, k, v (io), g, beta (fp32), gate and o (io).  Commit (accepted
+    n_b tokens of sequence b, no outputs): the state read and written once when
+    n_b > 0, n_b tokens of q, k, v, g, beta, and the int32 count."""
+    tok_in = (2 * dk + dv) * es + 4 * dk + 4
+    tok_verify = tok_in + dv * es * (2 if with_gate else 1)
+    verify = B * H * (4 * dk * dv + K * tok_verify)
+    commit = sum(H * ((8 * dk * dv if n > 0 else 0) + n * tok_in) + 4 for n in n_commit)
+    return verify, commit
 
 
 # ----------------------------------------------------------------------------- HBM traffic record
@@ -216,6 +231,39 @@ def bench_decode(kda, torch, w, repeats=1):
     return best, io
 
 
+def bench_verify(kda, torch, w, repeats=20):
+    """Time the verify call (K draft tokens, outputs, state untouched) and the
+    commit call (accepted counts, no outputs) of the multi-token decode step."""
+    from gated_delta_rule_112_amd.inputs import make_decode_state, make_verify_inputs
+    dev = torch.device("cuda:0")
+    log(f"[bench] verify: state {w.B}x{w.H}x{w.dk}x{w.dv} fp32, {w.T} draft tokens")
+    state = make_decode_state(w, device=dev)
+    x = make_verify_inputs(w, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    zeros = torch.zeros(w.B, dtype=torch.int32, device=dev)
+    y = torch.empty((w.B, w.T, w.H, w.dv), dtype=x["q"].dtype, device=dev)
+    ins = [x[key] for key in ["q", "k", "v", "g", "beta"]]
+
+    def verify():
+        kda.decode_multi(*ins, state, zeros, gate=x["gate"], out=y, stream=stream)
+
+    def commit():
+        kda.decode_multi(*ins, state, x["n_commit"], output=False, stream=stream)
+
+    res = {}
+    for name, fn in [("verify", verify), ("commit", commit)]:
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(repeats):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / repeats
+    return res, x["n_commit"].cpu().tolist(), x["q"].dtype
+
+
 def copy_probe(torch, nbytes=1 << 30):
     """A plain device copy of known size, run once so that a counter pass over
     this process can scale FETCH_SIZE / WRITE_SIZE against it."""
@@ -236,6 +284,7 @@ def main():
                     choices=["small_prefill", "full_width_prefill", "million_token_prefill"])
     ap.add_argument("--decode-repeats", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads-per-worker", type=int, default=4)
     ap.add_argument("--cpu-tokens", type=int, default=32768)
@@ -319,6 +368,21 @@ def main():
         }
         log(f"[bench] decode {dms:.4f} ms/step, {dgbs:.0f} GB/s")
 
+    verify = None
+    if not a.no_verify:
+        wv = WORKLOADS["batched_verify"]
+        vms, n_commit, vio = bench_verify(kda, torch, wv)
+        ves = 2 if vio == torch.bfloat16 else 4
+        vb, cb = verify_bytes(wv.B, wv.H, wv.T, wv.dk, wv.dv, ves, n_commit, wv.gate)
+        verify = {"workload": wv.name, "B": wv.B, "H": wv.H, "draft_tokens": wv.T,
+                  "dk": wv.dk, "dv": wv.dv, "accepted_tokens": int(sum(n_commit))}
+        for name, nb in [("verify", vb), ("commit", cb)]:
+            gbs = nb / (vms[name] * 1e-3) / 1e9
+            verify[name] = {"ms": round(vms[name], 4), "algorithmic_bytes": nb,
+                            "achieved": round(gbs, 1), "unit": "GB/s", "peak": HBM_PEAK_GBS,
+                            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+            log(f"[bench] {name} {vms[name]:.4f} ms, {gbs:.0f} GB/s")
+
     line = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -338,6 +402,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "decode": decode,
+        "verify": verify,
     }
     print(json.dumps(line), flush=True)
 

@@ -43,6 +43,8 @@ struct DecodeArgs {
   float scale;
   bool io_bf16;
   void* stream;
+  int64_t K = 0;                   // > 0: K tokens per sequence ([B, K, H, ..] inputs)
+  const int* n_commit = nullptr;   // with K > 0: tokens to commit per sequence, or NULL = K
 };
 
 struct NormArgs {

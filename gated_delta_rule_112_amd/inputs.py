@@ -18,6 +18,8 @@ Distributions (N(mu, s) means mean mu and standard deviation s):
   gate  ~ N(0, 1) in the io dtype, for the output-gate epilogue.
 Optionally every key channel j = h*dk + i with j % force_every == 0 gets
 g = forced_g at every token (stress of the decay floor).
+The multi-token decode workload draws T draft tokens per sequence with the
+same distributions, and an accepted count per sequence uniform in [0, T].
 """
 from __future__ import annotations
 
@@ -27,7 +29,7 @@ from typing import Optional
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "make_prefill_inputs", "make_decode_state",
-           "make_decode_step_inputs"]
+           "make_decode_step_inputs", "make_verify_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -58,6 +60,9 @@ WORKLOADS = {
                                       dv=128, io="bf16", force_every=1000, seed=1004),
     "batched_decode": Workload("batched_decode", B=256, H=96, T=1, dk=128, dv=128, io="bf16",
                                s0_std=0.02, steps=64, seed=1005),
+    # speculative decoding: T = 4 draft tokens per sequence against the resident state
+    "batched_verify": Workload("batched_verify", B=256, H=96, T=4, dk=128, dv=128, io="bf16",
+                               s0_std=0.02, gate=True, seed=1006),
 }
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -148,3 +153,15 @@ def make_decode_step_inputs(w: Workload, step: int, device="cpu"):
     out["gate"] = (torch.randn((B, H, dv), generator=gen, device=device,
                                dtype=torch.float32).to(dt) if w.gate else None)
     return out
+
+
+def make_verify_inputs(w: Workload, device="cpu", seed: Optional[int] = None):
+    """T draft tokens per sequence ([B, T, H, *] tensors, seed w.seed + 1), the
+    gate when the workload has one, and ``n_commit``: an accepted count per
+    sequence, int32 uniform in [0, T]."""
+    x = make_prefill_inputs(w, device=device, seed=(w.seed if seed is None else seed) + 1)
+    gen = _gen((w.seed if seed is None else seed) + 2, device)
+    x["n_commit"] = torch.randint(0, w.T + 1, (w.B,), generator=gen, device=device,
+                                  dtype=torch.int32)
+    del x["s0"]
+    return x

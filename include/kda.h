@@ -152,6 +152,40 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            float scale, kda_dtype io, void* stream);
 
 /*
+ * kda_decode_multi -- K consecutive tokens per sequence against the resident
+ * state, with the state committed after a chosen number of them.
+ *
+ * The same recurrent step as kda_decode_step ("Kimi K3 Architecture Explained
+ * ...", section "Token mixing"), applied to tokens t = 0 .. K-1 of every
+ * (b, h) in order, the state held on chip between tokens.  Meant for
+ * speculative decoding with draft tokens from the multi-token-prediction layer
+ * ("Kimi K3: Engineering a 2.8 Trillion Parameter Frontier", section
+ * "Infrastructure: The Physics of Running a 3T Model", EAGLE-3 item): a
+ * call with n_commit all 0 verifies K draft tokens (outputs only; the state is
+ * read once and not written), and a call with the accepted counts and o = NULL
+ * advances the state by them.
+ *
+ *   q, k     [B, K, H, dk]  io dtype
+ *   v        [B, K, H, dv]  io dtype
+ *   g        [B, K, H, dk]  float32
+ *   beta     [B, K, H]      float32
+ *   state    [B, H, dk, dv] float32    read; overwritten in place by the state after the
+ *                                      first n_commit[b] tokens of sequence b
+ *   n_commit [B] int32 device array, or NULL for K.  A value is clamped into [0, K];
+ *            0 leaves the state of every head of b untouched.
+ *   o        [B, K, H, dv]  io dtype   outputs of all K tokens (y when gate != NULL), or NULL
+ *                                      (then only the committed tokens are run)
+ *   gate     [B, K, H, dv]  io dtype or NULL;  norm_w [dv] float32 or NULL;  eps, scale as above
+ *   Alignment: state 16 bytes; every other pointer to its element size (n_commit 4).
+ *   With K = 1 and n_commit NULL this computes what kda_decode_step does.
+ */
+kda_status kda_decode_multi(const void* q, const void* k, const void* v,
+                            const float* g, const float* beta, float* state,
+                            const int32_t* n_commit, void* o, const void* gate,
+                            const float* norm_w, float eps, int64_t B, int64_t K, int64_t H,
+                            int dk, int dv, float scale, kda_dtype io, void* stream);
+
+/*
  * kda_gate_rmsnorm -- the output epilogue on its own.
  *
  * "Kimi K3 Architecture Explained ...", section "Token mixing": the output

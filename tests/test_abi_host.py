@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ["kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd_launches",
-              "kda_decode_step",
+              "kda_decode_step", "kda_decode_multi",
               "kda_gate_rmsnorm", "kda_status_string", "kda_version"]:
         assert n in names
 
@@ -160,6 +160,32 @@ def test_decode_validation(lib):
     assert decode(lib, override={"q": P(1, 1)}) == ALIGN      # bf16 needs 2 bytes
     assert decode(lib, o=6) == ALIAS       # o == state
     assert decode(lib, state=1) == ALIAS   # state == q
+
+
+def multi(lib, *, q=1, k=2, v=3, g=4, beta=5, state=6, n=8, o=7, gate=None, w=None, eps=1e-6,
+          B=2, K=4, H=3, dk=16, dv=16, scale=1.0, io=1, override=None):
+    ptrs = dict(q=q, k=k, v=v, g=g, beta=beta, state=state, n=n, o=o, gate=gate, w=w)
+    args = {n_: (None if x is None else P(x)) for n_, x in ptrs.items()}
+    if override:
+        args.update(override)
+    return lib.kda_decode_multi(args["q"], args["k"], args["v"], args["g"], args["beta"],
+                                args["state"], args["n"], args["o"], args["gate"], args["w"],
+                                eps, B, K, H, dk, dv, scale, io, None)
+
+
+def test_decode_multi_validation(lib):
+    for name in ["q", "k", "v", "g", "beta", "state"]:
+        assert multi(lib, **{name: None}) == NULLP
+    assert multi(lib, dk=100) == DIM
+    assert multi(lib, io=3) == DTYPE
+    assert multi(lib, K=0) == SHAPE
+    assert multi(lib, B=0) == SHAPE
+    assert multi(lib, scale=float("inf")) == ARG
+    assert multi(lib, override={"state": P(6, 8)}) == ALIGN
+    assert multi(lib, override={"n": P(8, 2)}) == ALIGN          # int32 counts
+    assert multi(lib, o=6) == ALIAS        # o == state
+    assert multi(lib, state=8) == ALIAS    # state == n_commit
+    assert multi(lib, n=7) == ALIAS        # n_commit inside o
 
 
 def test_gate_rmsnorm_validation(lib):

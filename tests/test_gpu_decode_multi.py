@@ -1,0 +1,169 @@
+"""GPU parity of the multi-token decode step (kda_decode_multi), through the C ABI.
+
+K consecutive tokens per sequence against the resident state: the outputs of
+all K tokens, and the state after the first n_commit[b] tokens, are compared
+with the float64 token recurrence of the oracle run over the same tokens.
+Tolerances as for the single-token step: 1e-4 (float32 io) or 2e-2 (bfloat16
+io, half an ulp of the output's final rounding not counted) times RMS of the
+output, 1e-5 times RMS of the float32 state.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle.kda_oracle import gate_rmsnorm as o_gate_rmsnorm
+from oracle.kda_oracle import kda_recurrent as o_recurrent
+from tests.gpu_helpers import assert_close, dev, f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+STATE_TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import gated_delta_rule_112_amd as m
+    m.load_library()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def gen(B, K, H, dk, dv, dtype, seed, gate=False):
+    gen_ = torch.Generator(device=dev())
+    gen_.manual_seed(seed)
+    r = lambda *s: torch.randn(*s, generator=gen_, device=dev())  # noqa: E731
+    q = r(B, K, H, dk)
+    k = r(B, K, H, dk)
+    q = (q / q.norm(dim=-1, keepdim=True)).to(dtype)
+    k = (k / k.norm(dim=-1, keepdim=True)).to(dtype)
+    v = r(B, K, H, dv).to(dtype)
+    g = -5.0 * torch.sigmoid(r(B, K, H, dk))
+    beta = torch.sigmoid(r(B, K, H))
+    state = 0.3 * r(B, H, dk, dv)
+    gt = r(B, K, H, dv).to(dtype) if gate else None
+    return q, k, v, g, beta, state, gt
+
+
+def oracle(q, k, v, g, beta, S0, n, gate=None, norm_w=None, scale=1.0, eps=1e-6):
+    """Outputs of all K tokens from S0, and per sequence b the state after its
+    first n[b] tokens (n clamped into [0, K]), both from the token recurrence."""
+    x = [f64(t) for t in (q, k, v, g, beta)]
+    S0 = f64(S0)
+    o, _ = o_recurrent(*x, S0, scale)
+    if gate is not None:
+        o = o_gate_rmsnorm(o, f64(gate), f64(norm_w), eps)
+    K = x[0].shape[1]
+    states = []
+    for b, nb in enumerate(n):
+        nb = min(max(int(nb), 0), K)
+        if nb == 0:
+            states.append(S0[b])
+        else:
+            _, S = o_recurrent(*(t[b:b + 1, :nb] for t in x), S0[b:b + 1], scale)
+            states.append(S[0])
+    return o, np.stack(states)
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (64, 32), (128, 128)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("with_gate", [False, True])
+@pytest.mark.parametrize("K", [1, 3, 8])
+def test_decode_multi_matches_oracle(kda, dk, dv, dtype, with_gate, K):
+    B, H = 5, 3
+    q, k, v, g, beta, state, gate = gen(B, K, H, dk, dv, dtype, 500 + 7 * K + dk + dv, with_gate)
+    norm_w = (1.0 + 0.1 * torch.randn(dv, device=dev())) if with_gate else None
+    n = [0, 1, K, K // 2, K + 5]            # the last one is clamped to K
+    n_dev = torch.tensor(n, dtype=torch.int32, device=dev())
+    S0 = state.clone()
+    o = kda.decode_multi(q, k, v, g, beta, state, n_dev, scale=0.5, gate=gate, norm_w=norm_w)
+    o_ref, S_ref = oracle(q, k, v, g, beta, S0, n, gate, norm_w, scale=0.5)
+    torch.cuda.synchronize()
+    assert_close(f64(o), o_ref, TOL[dtype], f"o K={K}", dtype)
+    assert_close(f64(state), S_ref, STATE_TOL, f"state K={K}")
+    assert torch.equal(state[0], S0[0]), "n_commit = 0 must leave the state untouched"
+
+
+def test_decode_multi_negative_count_and_default(kda):
+    """A negative count commits nothing; n_commit = None commits all K tokens."""
+    B, K, H, dk, dv = 3, 4, 2, 64, 64
+    q, k, v, g, beta, state, _ = gen(B, K, H, dk, dv, torch.bfloat16, 611)
+    S0 = state.clone()
+    n_dev = torch.tensor([-3, 2, 4], dtype=torch.int32, device=dev())
+    kda.decode_multi(q, k, v, g, beta, state, n_dev)
+    _, S_ref = oracle(q, k, v, g, beta, S0, [-3, 2, 4])
+    st2 = S0.clone()
+    o2 = kda.decode_multi(q, k, v, g, beta, st2, None)
+    o_ref, S_all = oracle(q, k, v, g, beta, S0, [K] * B)
+    torch.cuda.synchronize()
+    assert torch.equal(state[0], S0[0])
+    assert_close(f64(state), S_ref, STATE_TOL, "state, counts -3/2/4")
+    assert_close(f64(st2), S_all, STATE_TOL, "state, all committed")
+    assert_close(f64(o2), o_ref, TOL[torch.bfloat16], "o, all committed", torch.bfloat16)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_decode_multi_k1_equals_decode_step(kda, dtype):
+    """K = 1 with every token committed computes what kda_decode_step does, with
+    the same arithmetic: bit-identical outputs and states."""
+    B, H, dk, dv = 4, 5, 128, 128
+    q, k, v, g, beta, state, gate = gen(B, 1, H, dk, dv, dtype, 620, gate=True)
+    st1, st2 = state.clone(), state.clone()
+    o1 = kda.decode_multi(q, k, v, g, beta, st1, None, gate=gate)
+    o2 = kda.decode_step(*(x[:, 0].contiguous() for x in (q, k, v, g, beta)), st2,
+                         gate=gate[:, 0].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, 0], o2)
+    assert torch.equal(st1, st2)
+
+
+def test_decode_multi_verify_then_commit(kda):
+    """The speculative-decoding pair of calls: verify K draft tokens (outputs,
+    state untouched), then commit the accepted prefix of each sequence without
+    outputs; the committed state is the one the verify pass went through."""
+    B, K, H, dk, dv = 6, 5, 4, 128, 128
+    q, k, v, g, beta, state, gate = gen(B, K, H, dk, dv, torch.bfloat16, 640, gate=True)
+    S0 = state.clone()
+    zeros = torch.zeros(B, dtype=torch.int32, device=dev())
+    y = kda.decode_multi(q, k, v, g, beta, state, zeros, gate=gate)
+    torch.cuda.synchronize()
+    assert torch.equal(state, S0), "a verify pass must not write the state"
+    acc = [0, 1, 2, 3, 5, 4]
+    out = kda.decode_multi(q, k, v, g, beta, state, torch.tensor(acc, dtype=torch.int32,
+                                                                  device=dev()), output=False)
+    assert out is None
+    st_o = S0.clone()
+    kda.decode_multi(q, k, v, g, beta, st_o, torch.tensor(acc, dtype=torch.int32, device=dev()),
+                     gate=gate)
+    y_ref, S_ref = oracle(q, k, v, g, beta, S0, acc, gate)
+    torch.cuda.synchronize()
+    assert_close(f64(y), y_ref, TOL[torch.bfloat16], "verify y", torch.bfloat16)
+    assert_close(f64(state), S_ref, STATE_TOL, "committed state")
+    assert torch.equal(state, st_o), "commit without outputs == commit with outputs"
+
+
+def test_decode_multi_batched_workload_sampled(kda):
+    """256 sequences x 96 heads, 128/128, K = 4 draft tokens with the gated
+    epilogue (the benchmark's verify and commit calls): outputs of every token
+    and the committed state of 24 sampled (b, h) pairs against the oracle."""
+    from gated_delta_rule_112_amd.inputs import WORKLOADS, make_decode_state, make_verify_inputs
+    w = WORKLOADS["batched_verify"]
+    state = make_decode_state(w, device=dev())
+    x = make_verify_inputs(w, device=dev())
+    rng = np.random.default_rng(11)
+    bs = rng.integers(0, w.B, 24)
+    hs = rng.integers(0, w.H, 24)
+    S0 = state[bs, hs].clone()
+    zeros = torch.zeros(w.B, dtype=torch.int32, device=dev())
+    y = kda.decode_multi(x["q"], x["k"], x["v"], x["g"], x["beta"], state, zeros, gate=x["gate"])
+    kda.decode_multi(x["q"], x["k"], x["v"], x["g"], x["beta"], state, x["n_commit"],
+                     output=False)
+    torch.cuda.synchronize()
+    n = x["n_commit"].cpu().numpy()
+    for i, (b, h) in enumerate(zip(bs, hs)):
+        sl = lambda t: t[b:b + 1, :, h:h + 1]  # noqa: E731
+        y_ref, S_ref = oracle(*(sl(x[key]) for key in ["q", "k", "v", "g", "beta"]),
+                              S0[i][None, None], [n[b]], sl(x["gate"]))
+        assert_close(f64(y[b, :, h]), y_ref[0, :, 0], TOL[torch.bfloat16], f"y ({b},{h})",
+                     torch.bfloat16)
+        assert_close(f64(state[b, h]), S_ref[0, 0], STATE_TOL, f"state ({b},{h})")
