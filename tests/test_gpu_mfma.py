@@ -89,6 +89,24 @@ def test_mfma_ragged_lengths(kda, split, T):
     assert_close(f64(S), S_ref, TOL, f"state T={T}")
 
 
+@pytest.mark.parametrize("gated", [False, True])
+def test_mfma_many_heads(kda, gated):
+    """More (b, h) chains than compute units (64 x 24 = 1536 state workgroups):
+    the state workgroups of a launch run in several waves, with the tile
+    workgroups after them.  Every output of 40 sampled chains and every final
+    state."""
+    B, T, H = 64, 70, 24
+    q, k, v, g, beta, s0, gate = gen(B, T, H, 1500 + int(gated), s0_std=0.05, gate=gated)
+    y, S = kda.chunk_fwd(q, k, v, g, beta, s0, gate=gate)
+    rng = np.random.default_rng(3)
+    heads = [(int(b), int(h)) for b, h in zip(rng.integers(0, B, 40), rng.integers(0, H, 40))]
+    y_ref, S_ref = oracle(q, k, v, g, beta, s0, gate=gate, heads=heads)
+    torch.cuda.synchronize()
+    assert_close(np.stack([f64(y[b, :, h]) for b, h in heads]), y_ref, TOL, "y", BF)
+    assert_close(np.stack([f64(S[b, h]) for b, h in heads]), S_ref, TOL, "sampled states")
+    assert np.isfinite(f64(S)).all()
+
+
 def test_mfma_scale_and_zero_state(kda, split):
     q, k, v, g, beta, _, _ = gen(1, 100, 4, 601)
     scale = 128 ** -0.5
