@@ -47,6 +47,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32,
                                   i64, i64, i64, ci, ci, f32, ci, vp, ctypes.c_size_t, vp]
     lib.kda_chunk_fwd.restype = ci
+    lib.kda_chunk_fwd_checkpoints.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32,
+                                              i64, i64, i64, ci, ci, f32, ci, vp,
+                                              ctypes.c_size_t, vp, i64, vp]
+    lib.kda_chunk_fwd_checkpoints.restype = ci
     lib.kda_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, ci, ci, ci]
     lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_chunk_fwd_launches.argtypes = [i64, i64, i64, ci, ci, ci]
@@ -108,6 +112,25 @@ def chunk_fwd(q, k, v, g, beta, s0=None, *, scale: float = 1.0, gate=None, norm_
     for an in-place state update.  ``workspace`` (a uint8 CUDA tensor of at
     least ``chunk_workspace_size(...)`` bytes) is allocated per call if absent.
     """
+    o, s, _ = _chunk_fwd(q, k, v, g, beta, s0, scale, gate, norm_w, eps, output, final_state,
+                         out, s_out, workspace, 0, None, stream)
+    return o, s
+
+
+def chunk_fwd_checkpoints(q, k, v, g, beta, s0=None, *, every: int, scale: float = 1.0,
+                          gate=None, norm_w=None, eps: float = 1e-6, output: bool = True,
+                          final_state: bool = True, out=None, s_out=None, ckpt=None,
+                          workspace=None, stream=None):
+    """``chunk_fwd`` that also returns the state after every ``every`` tokens
+    (a multiple of 32): (o or y, final state, checkpoints [B, T // every, H, dk, dv])."""
+    if every <= 0 or every % 32:
+        raise ValueError(f"checkpoint interval {every} is not a positive multiple of 32")
+    return _chunk_fwd(q, k, v, g, beta, s0, scale, gate, norm_w, eps, output, final_state,
+                      out, s_out, workspace, every, ckpt, stream)
+
+
+def _chunk_fwd(q, k, v, g, beta, s0, scale, gate, norm_w, eps, output, final_state, out, s_out,
+               workspace, every, ckpt, stream):
     lib = load_library()
     if q.device.type != "cuda":
         raise ValueError("kda ops need CUDA (HIP) tensors")
@@ -146,12 +169,21 @@ def chunk_fwd(q, k, v, g, beta, s0=None, *, scale: float = 1.0, gate=None, norm_
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, (workspace.numel(),), dev)
-    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(out),
-                           _ptr(s_out), _ptr(gate), _ptr(norm_w), float(eps), B, T, H, dk, dv,
-                           float(scale), _IO[io], _ptr(workspace),
-                           0 if workspace is None else workspace.numel(), _stream(dev, stream))
-    _check(lib, "kda_chunk_fwd", st)
-    return out, s_out
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(out), _ptr(s_out),
+            _ptr(gate), _ptr(norm_w), float(eps), B, T, H, dk, dv, float(scale), _IO[io],
+            _ptr(workspace), 0 if workspace is None else workspace.numel())
+    nck = T // every if every else 0
+    if every:
+        if ckpt is None:
+            ckpt = torch.empty((B, nck, H, dk, dv), dtype=torch.float32, device=dev)
+        else:
+            _need(ckpt, "ckpt", torch.float32, (B, nck, H, dk, dv), dev)
+    if nck == 0:  # no checkpoint falls inside the sequence
+        _check(lib, "kda_chunk_fwd", lib.kda_chunk_fwd(*args, _stream(dev, stream)))
+        return out, s_out, ckpt
+    st = lib.kda_chunk_fwd_checkpoints(*args, _ptr(ckpt), int(every), _stream(dev, stream))
+    _check(lib, "kda_chunk_fwd_checkpoints", st)
+    return out, s_out, ckpt
 
 
 def decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, gate=None, norm_w=None,

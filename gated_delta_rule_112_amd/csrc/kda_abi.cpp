@@ -93,11 +93,16 @@ int64_t kda_chunk_fwd_launches(int64_t B, int64_t T, int64_t H, int dk, int dv, 
   return kda::chunk_mfma_launches(B, T, H);
 }
 
-kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, const float* s0, void* o, float* s_out,
-                         const void* gate, const float* norm_w, float eps, int64_t B, int64_t T,
-                         int64_t H, int dk, int dv, float scale, kda_dtype io, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// kda_chunk_fwd with optional state checkpoints (ckpt NULL: none).
+kda_status chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                     const float* beta, const float* s0, void* o, float* s_out, const void* gate,
+                     const float* norm_w, float eps, int64_t B, int64_t T, int64_t H, int dk,
+                     int dv, float scale, kda_dtype io, void* workspace, size_t workspace_bytes,
+                     float* ckpt, int64_t ckpt_every, void* stream) {
   if (!q || !k || !v || !g || !beta) return KDA_ERR_NULL_POINTER;
   if (!o && !s_out) return KDA_ERR_NULL_POINTER;
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_BAD_DTYPE;
@@ -125,6 +130,13 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   for (Span in : {sq, sk, sv, sg, sb, sgt, sw})
     if (overlap(sso, in)) return KDA_ERR_ALIAS;
   if (overlap(sso, ss0) && (const void*)s_out != (const void*)s0) return KDA_ERR_ALIAS;
+  if (ckpt != nullptr) {
+    const int64_t nck = T / ckpt_every;
+    const Span sck{ckpt, nck > 0 ? prod(B, nck, H, dk) * dv * 4 : 0};
+    if (nck > 0 && prod(B, nck, H, dk) < 0) return KDA_ERR_BAD_SHAPE;
+    for (Span in : {sq, sk, sv, sg, sb, ss0, so, sso, sgt, sw})
+      if (overlap(sck, in)) return KDA_ERR_ALIAS;
+  }
 
   const bool mfma = !force_valu() && kda::chunk_mfma_supports(dk, dv, io == KDA_BF16);
   if (mfma) {
@@ -134,12 +146,45 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     const Span sws{workspace, (int64_t)need};
     for (Span in : {sq, sk, sv, sg, sb, ss0, so, sso, sgt, sw})
       if (overlap(sws, in)) return KDA_ERR_ALIAS;
+    if (ckpt != nullptr && overlap(sws, Span{ckpt, prod(B, T / ckpt_every, H, dk) * dv * 4}))
+      return KDA_ERR_ALIAS;
   }
 
   kda::ChunkArgs a{q, k, v, g, beta, s0, o, s_out, gate, norm_w, eps,
                    B, T, H, dk, dv, scale, io == KDA_BF16, workspace, stream};
+  if (ckpt != nullptr && T >= ckpt_every) {
+    a.ckpt = ckpt;
+    a.ckpt_every = ckpt_every;
+  }
   const hipError_t err = mfma ? kda::launch_chunk_mfma(a) : kda::launch_chunk_valu(a);
   return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* s0, void* o, float* s_out,
+                         const void* gate, const float* norm_w, float eps, int64_t B, int64_t T,
+                         int64_t H, int dk, int dv, float scale, kda_dtype io, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return chunk_fwd(q, k, v, g, beta, s0, o, s_out, gate, norm_w, eps, B, T, H, dk, dv, scale, io,
+                   workspace, workspace_bytes, nullptr, 0, stream);
+}
+
+kda_status kda_chunk_fwd_checkpoints(const void* q, const void* k, const void* v,
+                                     const float* g, const float* beta, const float* s0,
+                                     void* o, float* s_out, const void* gate,
+                                     const float* norm_w, float eps, int64_t B, int64_t T,
+                                     int64_t H, int dk, int dv, float scale, kda_dtype io,
+                                     void* workspace, size_t workspace_bytes, float* ckpt,
+                                     int64_t ckpt_every, void* stream) {
+  if (ckpt == nullptr) return KDA_ERR_NULL_POINTER;
+  if (ckpt_every <= 0 || ckpt_every % 32 != 0) return KDA_ERR_BAD_SHAPE;
+  if (!aligned(ckpt, 4)) return KDA_ERR_MISALIGNED;
+  return chunk_fwd(q, k, v, g, beta, s0, o, s_out, gate, norm_w, eps, B, T, H, dk, dv, scale, io,
+                   workspace, workspace_bytes, ckpt, ckpt_every, stream);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,

@@ -113,7 +113,8 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
                  const float* __restrict__ s_in, float* __restrict__ s_next,
                  bf16_t* __restrict__ o, const bf16_t* __restrict__ gate,
                  const float* __restrict__ norm_w, float eps, int64_t T, int64_t H, int64_t BH,
-                 int64_t x0, int64_t nseg, int64_t n_state_wg, tile::Args next) {
+                 int64_t x0, int64_t nseg, int64_t n_state_wg, float* __restrict__ ckpt,
+                 int64_t ckpt_every, tile::Args next) {
   using SC = SlotCfg<DVW, GATE>;
   constexpr int kRing = SC::kRing, kLead = SC::kLead;
   constexpr int NSW = DVW / CPW;   // state wavefronts
@@ -313,6 +314,17 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
   // State: block kb of column block cb, lane (c, g), r = row chan(kb, 4 g + r),
   // column vcol(cb, c).
   f32x4 S[NCB][8];
+  // This wave's columns of the state, to a [dk, dv] row-major float32 state at p.
+  auto store_state = [&](float* p) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        float* pc = p + col0 + vcol(cb, lc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pc[rec::chan(kb, 4 * lg + r) * rec::kDV] = S[cb][kb][r];
+      }
+  };
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -499,6 +511,14 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
       for (int cb = 0; cb < NCB; ++cb)
         S[cb][kb] = mma32h(kb8[kb], dab[cb], S[cb][kb] * e4[kb]);
 
+    // State checkpoint after every ckpt_every tokens (a multiple of a pair's 32).
+    if (ckpt != nullptr) {
+      const int64_t done = (x0 + xl + 1) * rec::kP;  // tokens consumed (uniform)
+      if (done % ckpt_every == 0 && done <= T) {
+        const int64_t nck = T / ckpt_every, ic = done / ckpt_every - 1;
+        store_state(ckpt + ((b * nck + ic) * H + h) * (int64_t)(rec::kDK * rec::kDV));
+      }
+    }
     if constexpr (GATE) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
@@ -511,16 +531,7 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
   }
   if constexpr (GATE) epilogue(nseg - 1, Pa, Pb);  // its row sums are in LDS since the last barrier
 
-  if (s_next != nullptr) {
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        float* p = s_next + bh * rec::kDK * rec::kDV + col0 + vcol(cb, lc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[rec::chan(kb, 4 * lg + r) * rec::kDV] = S[cb][kb][r];
-      }
-  }
+  if (s_next != nullptr) store_state(s_next + bh * rec::kDK * rec::kDV);
 }
 
 // One launch: the state workgroups (first) walk segment `cur` of every head
@@ -558,7 +569,7 @@ hipError_t launch_state_t(const ChunkArgs& a, Seg cur, const float* s_in, float*
   hipLaunchKernelGGL((kda_state_kernel<DVW, CPW, GATE, WO>), dim3((unsigned)nblk), dim3(64 * NW),
                      0, (hipStream_t)a.stream, cur.recs, (const bf16_t*)a.v, s_in, s_next,
                      (bf16_t*)a.o, (const bf16_t*)a.gate, a.norm_w, a.eps, a.T, a.H, BH, cur.x0,
-                     cur.n > 0 ? cur.n : 1, n_state, tb);
+                     cur.n > 0 ? cur.n : 1, n_state, a.ckpt, a.ckpt_every, tb);
   return hipGetLastError();
 }
 

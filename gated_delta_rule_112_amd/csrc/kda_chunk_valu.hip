@@ -16,7 +16,8 @@
 // which leave the state unchanged.
 //
 // One workgroup of 128 threads owns one (b, h); thread j < DV keeps column j of
-// the state (DK floats) in registers for the whole sequence.
+// the state (DK floats) in registers for the whole sequence, and stores it at
+// the requested checkpoints.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -31,7 +32,8 @@ kda_chunk_valu_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const 
                       const float* __restrict__ g, const float* __restrict__ beta,
                       const float* __restrict__ s0, IO* __restrict__ o, float* __restrict__ s_out,
                       const IO* __restrict__ gate, const float* __restrict__ norm_w, float eps,
-                      int64_t T, int64_t H, float scale) {
+                      int64_t T, int64_t H, float scale, float* __restrict__ ckpt,
+                      int64_t ckpt_every) {
   constexpr int C = kTile;
   __shared__ float sQh[C][DK];
   __shared__ float sKh[C][DK];
@@ -181,6 +183,13 @@ kda_chunk_valu_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const 
         for (int t = 0; t < C; ++t) acc += sKc[t][i] * delta[t];
         S[i] = sEn[i] * (S[i] + acc);
       }
+      // State checkpoint after every ckpt_every tokens (a multiple of the tile).
+      if (ckpt != nullptr && (c0 + C) % ckpt_every == 0 && c0 + C <= T) {
+        const int64_t nck = T / ckpt_every, ic = (c0 + C) / ckpt_every - 1;
+        float* cp = ckpt + ((b * nck + ic) * H + h) * (int64_t)(DK * DV);
+#pragma unroll
+        for (int i = 0; i < DK; ++i) cp[i * DV + j] = S[i];
+      }
     }
     __syncthreads();
 
@@ -219,7 +228,7 @@ static hipError_t launch_valu_t(const ChunkArgs& a) {
   hipLaunchKernelGGL((kda_chunk_valu_kernel<DK, DV, IO>), dim3((unsigned)(a.B * a.H)),
                      dim3(kValuThreads), 0, (hipStream_t)a.stream, (const IO*)a.q, (const IO*)a.k,
                      (const IO*)a.v, a.g, a.beta, a.s0, (IO*)a.o, a.s_out, (const IO*)a.gate,
-                     a.norm_w, a.eps, a.T, a.H, a.scale);
+                     a.norm_w, a.eps, a.T, a.H, a.scale, a.ckpt, a.ckpt_every);
   return hipGetLastError();
 }
 

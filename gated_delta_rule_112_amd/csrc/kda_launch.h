@@ -25,6 +25,10 @@ struct ChunkArgs {
   bool io_bf16;
   void* workspace;  // device scratch of chunk_mfma_workspace() bytes (matrix-core path)
   void* stream;
+  // Optional state checkpoints: ckpt [B, T / ckpt_every, H, dk, dv] receives the
+  // state after every ckpt_every tokens (a multiple of 32).
+  float* ckpt = nullptr;
+  int64_t ckpt_every = 0;
 };
 
 struct DecodeArgs {

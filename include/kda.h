@@ -129,6 +129,31 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk, int
                                     kda_dtype io);
 
 /*
+ * kda_chunk_fwd_checkpoints -- kda_chunk_fwd that also keeps the state at
+ * regular points of the sequence, for prefix caching (a fixed-size state per
+ * cached prefix instead of a cache that grows with it; "Kimi K3 Architecture
+ * Explained ...", section "Token mixing", and the prefix-caching remark of
+ * "Kimi K3: Engineering a 2.8 Trillion Parameter Frontier").
+ *
+ * Every argument of kda_chunk_fwd, with the same meaning, plus
+ *   ckpt       [B, T / ckpt_every, H, dk, dv] float32: entry [b, i, h] receives the
+ *              state of (b, h) after its first (i + 1) * ckpt_every tokens (the
+ *              state that kda_chunk_fwd over those tokens would leave in s_out).
+ *              Must not overlap any other argument; 4-byte aligned.  With
+ *              T < ckpt_every nothing is written.
+ *   ckpt_every tokens between checkpoints, a positive multiple of 32 (two 16-token
+ *              tiles), else KDA_ERR_BAD_SHAPE.
+ * A checkpoint costs one store of the state per head (64 KiB at dk = dv = 128).
+ */
+kda_status kda_chunk_fwd_checkpoints(const void* q, const void* k, const void* v,
+                                     const float* g, const float* beta, const float* s0,
+                                     void* o, float* s_out, const void* gate,
+                                     const float* norm_w, float eps, int64_t B, int64_t T,
+                                     int64_t H, int dk, int dv, float scale, kda_dtype io,
+                                     void* workspace, size_t workspace_bytes, float* ckpt,
+                                     int64_t ckpt_every, void* stream);
+
+/*
  * kda_decode_step -- one token per sequence against a resident state.
  *
  * The constant-cost recurrent step ("Kimi K3 Architecture Explained ...",

@@ -31,7 +31,8 @@ def lib():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    for n in ["kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd_launches",
+    for n in ["kda_chunk_fwd", "kda_chunk_fwd_checkpoints", "kda_chunk_fwd_workspace_size",
+              "kda_chunk_fwd_launches",
               "kda_decode_step", "kda_decode_multi",
               "kda_gate_rmsnorm", "kda_status_string", "kda_version"]:
         assert n in names
@@ -136,6 +137,23 @@ def test_chunk_workspace(lib):
     assert launches(1, 16, 1, 128, 128, 1) == 2           # one segment + its records
     assert launches(1, 1 << 20, 96, 128, 128, 1) > 2
     assert launches(1, 16, 1, 48, 128, 1) == 0
+
+
+def test_chunk_checkpoints_validation(lib):
+    f = lib.kda_chunk_fwd_checkpoints
+
+    def call(ckpt=P(11), every=64, ws=None):
+        # vector-path sizes (dk = dv = 16): no workspace needed
+        return f(P(1), P(2), P(3), P(4), P(5), None, P(6), P(7), None, None, 1e-6,
+                 2, 200, 3, 16, 16, 1.0, 0, ws, 0, ckpt, every, None)
+
+    assert call(ckpt=None) == NULLP
+    assert call(every=0) == SHAPE
+    assert call(every=48) == SHAPE
+    assert call(every=-32) == SHAPE
+    assert call(ckpt=P(11, 2)) == ALIGN
+    assert call(ckpt=P(1)) == ALIAS          # overlaps q
+    assert call(ckpt=P(7)) == ALIAS          # overlaps s_out
 
 
 def decode(lib, *, q=1, k=2, v=3, g=4, beta=5, state=6, o=7, gate=None, w=None, eps=1e-6,
