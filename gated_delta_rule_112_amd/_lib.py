@@ -51,6 +51,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                               i64, i64, i64, ci, ci, f32, ci, vp,
                                               ctypes.c_size_t, vp, i64, vp]
     lib.kda_chunk_fwd_checkpoints.restype = ci
+    lib.kda_chunk_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp,
+                                         vp, f32, i64, ci, ci, f32, ci, vp, ctypes.c_size_t,
+                                         vp, i64, vp]
+    lib.kda_chunk_fwd_varlen.restype = ci
     lib.kda_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, ci, ci, ci]
     lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_chunk_fwd_launches.argtypes = [i64, i64, i64, ci, ci, ci]
@@ -127,6 +131,74 @@ def chunk_fwd_checkpoints(q, k, v, g, beta, s0=None, *, every: int, scale: float
         raise ValueError(f"checkpoint interval {every} is not a positive multiple of 32")
     return _chunk_fwd(q, k, v, g, beta, s0, scale, gate, norm_w, eps, output, final_state,
                       out, s_out, workspace, every, ckpt, stream)
+
+
+def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, max_len: int, s0=None, *,
+                     scale: float = 1.0, gate=None, norm_w=None, eps: float = 1e-6,
+                     output: bool = True, final_state: bool = True, out=None, s_out=None,
+                     every: int = 0, ckpt=None, workspace=None, stream=None):
+    """Prefill over N sequences packed along the token axis: q, k, g [total, H, dk],
+    v [total, H, dv], beta [total, H]; ``cu_seqlens`` int32 [N + 1] on the device
+    (sequence b is rows cu[b] .. cu[b+1]-1), ``max_len`` >= the longest.  Returns
+    (o or y [total, H, dv], final states [N, H, dk, dv], checkpoints
+    [N, max_len // every, H, dk, dv] or None when ``every`` is 0)."""
+    lib = load_library()
+    if q.device.type != "cuda":
+        raise ValueError("kda ops need CUDA (HIP) tensors")
+    dev = q.device
+    total, H, dk = q.shape
+    dv = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    io = q.dtype
+    if io not in _IO:
+        raise TypeError(f"unsupported io dtype {io}")
+    if N < 1 or max_len < 1:
+        raise ValueError("need at least one sequence and max_len >= 1")
+    if every and (every < 0 or every % 32):
+        raise ValueError(f"checkpoint interval {every} is not a positive multiple of 32")
+    _need(q, "q", io, (total, H, dk), dev)
+    _need(k, "k", io, (total, H, dk), dev)
+    _need(v, "v", io, (total, H, dv), dev)
+    _need(g, "g", torch.float32, (total, H, dk), dev)
+    _need(beta, "beta", torch.float32, (total, H), dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    if s0 is not None:
+        _need(s0, "s0", torch.float32, (N, H, dk, dv), dev)
+    if gate is not None:
+        _need(gate, "gate", io, (total, H, dv), dev)
+    if norm_w is not None:
+        _need(norm_w, "norm_w", torch.float32, (dv,), dev)
+    if not output:
+        out = None
+    elif out is None:
+        out = torch.empty((total, H, dv), dtype=io, device=dev)
+    else:
+        _need(out, "out", io, (total, H, dv), dev)
+    if not final_state:
+        s_out = None
+    elif s_out is None:
+        s_out = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        _need(s_out, "s_out", torch.float32, (N, H, dk, dv), dev)
+    nck = max_len // every if every else 0
+    if every:
+        if ckpt is None:
+            ckpt = torch.empty((N, nck, H, dk, dv), dtype=torch.float32, device=dev)
+        else:
+            _need(ckpt, "ckpt", torch.float32, (N, nck, H, dk, dv), dev)
+    ws_bytes = lib.kda_chunk_fwd_workspace_size(N, max_len, H, dk, dv, _IO[io])
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, (workspace.numel(),), dev)
+    st = lib.kda_chunk_fwd_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, total,
+        int(max_len), _ptr(s0), _ptr(out), _ptr(s_out), _ptr(gate), _ptr(norm_w), float(eps), H,
+        dk, dv, float(scale), _IO[io], _ptr(workspace),
+        0 if workspace is None else workspace.numel(), _ptr(ckpt) if nck else None,
+        int(every), _stream(dev, stream))
+    _check(lib, "kda_chunk_fwd_varlen", st)
+    return out, s_out, ckpt
 
 
 def _chunk_fwd(q, k, v, g, beta, s0, scale, gate, norm_w, eps, output, final_state, out, s_out,

@@ -97,17 +97,21 @@ int64_t kda_chunk_fwd_launches(int64_t B, int64_t T, int64_t H, int dk, int dv, 
 
 namespace {
 
-// kda_chunk_fwd with optional state checkpoints (ckpt NULL: none).
+// kda_chunk_fwd with optional state checkpoints (ckpt NULL: none) and packed
+// sequences (cu non-NULL: B sequences in `total` token rows, T the longest).
 kda_status chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                      const float* beta, const float* s0, void* o, float* s_out, const void* gate,
                      const float* norm_w, float eps, int64_t B, int64_t T, int64_t H, int dk,
                      int dv, float scale, kda_dtype io, void* workspace, size_t workspace_bytes,
-                     float* ckpt, int64_t ckpt_every, void* stream) {
+                     float* ckpt, int64_t ckpt_every, const int32_t* cu, int64_t total,
+                     void* stream) {
   if (!q || !k || !v || !g || !beta) return KDA_ERR_NULL_POINTER;
   if (!o && !s_out) return KDA_ERR_NULL_POINTER;
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_BAD_DTYPE;
   if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED_DIM;
-  const int64_t nqk = prod(B, T, H, dk), nv = prod(B, T, H, dv), nb = prod(B, T, H);
+  const int64_t rows = cu != nullptr ? total : prod(B, T);  // token rows of q, k, v, g, beta, o
+  if (rows < 1 || prod(B, T) < 0) return KDA_ERR_BAD_SHAPE;
+  const int64_t nqk = prod(rows, H, dk), nv = prod(rows, H, dv), nb = prod(rows, H);
   const int64_t ns = prod(B, H, dk, dv);
   if (nqk < 0 || nv < 0 || nb < 0 || ns < 0) return KDA_ERR_BAD_SHAPE;
   if (B * H > 0x7fffffffLL) return KDA_ERR_BAD_SHAPE;  // one workgroup per (b, h)
@@ -124,17 +128,17 @@ kda_status chunk_fwd(const void* q, const void* k, const void* v, const float* g
   const int64_t es = (io == KDA_BF16) ? 2 : 4;
   const Span sq{q, nqk * es}, sk{k, nqk * es}, sv{v, nv * es}, sg{g, nqk * 4}, sb{beta, nb * 4};
   const Span ss0{s0, ns * 4}, so{o, nv * es}, sso{s_out, ns * 4}, sgt{gate, nv * es};
-  const Span sw{norm_w, (int64_t)dv * 4};
-  for (Span in : {sq, sk, sv, sg, sb, ss0, sgt, sw, sso})
+  const Span sw{norm_w, (int64_t)dv * 4}, scu{cu, (B + 1) * 4};
+  for (Span in : {sq, sk, sv, sg, sb, ss0, sgt, sw, sso, scu})
     if (overlap(so, in)) return KDA_ERR_ALIAS;
-  for (Span in : {sq, sk, sv, sg, sb, sgt, sw})
+  for (Span in : {sq, sk, sv, sg, sb, sgt, sw, scu})
     if (overlap(sso, in)) return KDA_ERR_ALIAS;
   if (overlap(sso, ss0) && (const void*)s_out != (const void*)s0) return KDA_ERR_ALIAS;
   if (ckpt != nullptr) {
     const int64_t nck = T / ckpt_every;
     const Span sck{ckpt, nck > 0 ? prod(B, nck, H, dk) * dv * 4 : 0};
     if (nck > 0 && prod(B, nck, H, dk) < 0) return KDA_ERR_BAD_SHAPE;
-    for (Span in : {sq, sk, sv, sg, sb, ss0, so, sso, sgt, sw})
+    for (Span in : {sq, sk, sv, sg, sb, ss0, so, sso, sgt, sw, scu})
       if (overlap(sck, in)) return KDA_ERR_ALIAS;
   }
 
@@ -144,7 +148,7 @@ kda_status chunk_fwd(const void* q, const void* k, const void* v, const float* g
     if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
       return KDA_ERR_WORKSPACE;
     const Span sws{workspace, (int64_t)need};
-    for (Span in : {sq, sk, sv, sg, sb, ss0, so, sso, sgt, sw})
+    for (Span in : {sq, sk, sv, sg, sb, ss0, so, sso, sgt, sw, scu})
       if (overlap(sws, in)) return KDA_ERR_ALIAS;
     if (ckpt != nullptr && overlap(sws, Span{ckpt, prod(B, T / ckpt_every, H, dk) * dv * 4}))
       return KDA_ERR_ALIAS;
@@ -156,6 +160,8 @@ kda_status chunk_fwd(const void* q, const void* k, const void* v, const float* g
     a.ckpt = ckpt;
     a.ckpt_every = ckpt_every;
   }
+  a.cu = cu;
+  a.total = rows;
   const hipError_t err = mfma ? kda::launch_chunk_mfma(a) : kda::launch_chunk_valu(a);
   return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
@@ -170,7 +176,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          int64_t H, int dk, int dv, float scale, kda_dtype io, void* workspace,
                          size_t workspace_bytes, void* stream) {
   return chunk_fwd(q, k, v, g, beta, s0, o, s_out, gate, norm_w, eps, B, T, H, dk, dv, scale, io,
-                   workspace, workspace_bytes, nullptr, 0, stream);
+                   workspace, workspace_bytes, nullptr, 0, nullptr, 0, stream);
 }
 
 kda_status kda_chunk_fwd_checkpoints(const void* q, const void* k, const void* v,
@@ -184,7 +190,26 @@ kda_status kda_chunk_fwd_checkpoints(const void* q, const void* k, const void* v
   if (ckpt_every <= 0 || ckpt_every % 32 != 0) return KDA_ERR_BAD_SHAPE;
   if (!aligned(ckpt, 4)) return KDA_ERR_MISALIGNED;
   return chunk_fwd(q, k, v, g, beta, s0, o, s_out, gate, norm_w, eps, B, T, H, dk, dv, scale, io,
-                   workspace, workspace_bytes, ckpt, ckpt_every, stream);
+                   workspace, workspace_bytes, ckpt, ckpt_every, nullptr, 0, stream);
+}
+
+kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, const int32_t* cu_seqlens, int64_t N,
+                                int64_t total, int64_t max_len, const float* s0, void* o,
+                                float* s_out, const void* gate, const float* norm_w, float eps,
+                                int64_t H, int dk, int dv, float scale, kda_dtype io,
+                                void* workspace, size_t workspace_bytes, float* ckpt,
+                                int64_t ckpt_every, void* stream) {
+  if (cu_seqlens == nullptr) return KDA_ERR_NULL_POINTER;
+  if (N < 1 || total < 1 || max_len < 1) return KDA_ERR_BAD_SHAPE;
+  if (!aligned(cu_seqlens, 4)) return KDA_ERR_MISALIGNED;
+  if (ckpt != nullptr) {
+    if (ckpt_every <= 0 || ckpt_every % 32 != 0) return KDA_ERR_BAD_SHAPE;
+    if (!aligned(ckpt, 4)) return KDA_ERR_MISALIGNED;
+  }
+  return chunk_fwd(q, k, v, g, beta, s0, o, s_out, gate, norm_w, eps, N, max_len, H, dk, dv,
+                   scale, io, workspace, workspace_bytes, ckpt, ckpt_every, cu_seqlens, total,
+                   stream);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,

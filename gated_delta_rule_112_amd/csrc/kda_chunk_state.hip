@@ -107,14 +107,15 @@ struct SlotCfg {
   }
 };
 
-template <int DVW, int CPW, bool GATE, bool WO>
+template <int DVW, int CPW, bool GATE, bool WO, bool PACKED>
 __global__ void __launch_bounds__(64 * (DVW / CPW + kLoaders), 1)
 kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restrict__ v,
                  const float* __restrict__ s_in, float* __restrict__ s_next,
                  bf16_t* __restrict__ o, const bf16_t* __restrict__ gate,
-                 const float* __restrict__ norm_w, float eps, int64_t T, int64_t H, int64_t BH,
+                 const float* __restrict__ norm_w, float eps, Seqs<PACKED> seqs, int64_t H,
+                 int64_t BH,
                  int64_t x0, int64_t nseg, int64_t n_state_wg, float* __restrict__ ckpt,
-                 int64_t ckpt_every, tile::Args next) {
+                 int64_t ckpt_every, tile::Args<PACKED> next) {
   using SC = SlotCfg<DVW, GATE>;
   constexpr int kRing = SC::kRing, kLead = SC::kLead;
   constexpr int NSW = DVW / CPW;   // state wavefronts
@@ -162,6 +163,8 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
   const int64_t bh = wg / NSPLIT;
   const int col0 = (int)(wg % NSPLIT) * DVW;  // first value column of the workgroup
   const int64_t b = bh / H, h = bh % H;
+  // This head's sequence: T tokens from row t0 (pairs past T hold identity tokens).
+  const int64_t T = seqs.len(b), t0 = seqs.start(b);
 
   const int64_t rstride = H * rec::kDV;  // elements between consecutive tokens of a head
 
@@ -198,22 +201,25 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
       }
     }
     // Copy pair xt (< nseg) into ring slot `slot` and gate slot `gslot`.
+    const bf16_t* vg = GATE ? gate : v;
     auto issue = [&](int64_t xt, int slot, int gslot) {
       const int64_t row0 = (x0 + xt) * rec::kP;               // first token of the pair
       const bool full = row0 + rec::kP <= T;
       const unsigned char* base_r = R0 + xt * rec::kBytes;
-      const int64_t pair0 = ((b * T + row0) * H + h) * rec::kDV;  // element offset of row 0
+      const int64_t pair0 = ((t0 + row0) * H + h) * rec::kDV;  // element offset of row 0 (full)
       const unsigned char* base_v = (const unsigned char*)(v + pair0);
-      const unsigned char* base_g = (const unsigned char*)((GATE ? gate : v) + pair0);
+      const unsigned char* base_g = (const unsigned char*)(vg + pair0);
 #pragma unroll
       for (int i = 0; i < SC::kPer; ++i) {
-        const unsigned char* bt = kind[i] == 0 ? base_r : (kind[i] == 2 ? base_g : base_v);
-        unsigned off = loff[i];
-        if (kind[i] != 0 && !full) {  // the sequence's last, partial pair: clamp rows into it
-          const int64_t t = row0 + lrow[i] < T ? lrow[i] : T - 1 - row0;
-          off = (unsigned)(2 * (t * rstride + lcol[i]));
+        const unsigned char* src =
+            (kind[i] == 0 ? base_r : (kind[i] == 2 ? base_g : base_v)) + loff[i];
+        if (kind[i] != 0 && !full) {
+          // a pair at or past the sequence's end: rows clamped into the sequence
+          // (their tokens are identity tokens; the values read do not matter)
+          const int64_t r = seqs.row(b, row0 + lrow[i]);
+          src = (const unsigned char*)((kind[i] == 2 ? vg : v) + (r * H + h) * rec::kDV +
+                                       lcol[i]);
         }
-        const unsigned char* src = bt + off;
         const int blk = i * kLoaders + lw;
         unsigned char* dst = blk < SC::kSlot / 1024
                                  ? ring[slot] + blk * 1024
@@ -352,7 +358,7 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
   // Output of pair x: this lane writes tokens lc and 16 + lc, columns
   // col0 + wl + 8 lg + [0, 8).
   const int64_t o_lane = lc * rstride + col0 + wl + 8 * lg;
-  auto o_pair = [&](int64_t x) { return o + ((b * T + (x0 + x) * rec::kP) * H + h) * rec::kDV; };
+  auto o_pair = [&](int64_t x) { return o + ((t0 + (x0 + x) * rec::kP) * H + h) * rec::kDV; };
   __syncthreads();  // pair 0 is in LDS
 
   // Epilogue of pair x: y = O / rms(O) * w * sigmoid(gate), tokens lc and
@@ -394,7 +400,7 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
   f16x8 ta8 = {}, aa8 = {};
   int slot = 0;  // ring slot of pair xl
   for (int64_t xl = 0; xl < nseg; ++xl) {
-    const bool tail = xl == nseg - 1;  // only the sequence's last pair can be partial
+    const bool pfull = (x0 + xl + 1) * rec::kP <= T;  // every token of the pair is in the sequence
     const unsigned char* Rs = ring[slot];
 
     // The LDS operands are read in batches (those of the D products, those of
@@ -490,8 +496,8 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
           ya[4 * cb + r] = (bf16_t)Oa[cb][r];
           yb[4 * cb + r] = (bf16_t)Ob[cb][r];
         }
-      if (!tail || tok < T) __builtin_nontemporal_store(ya, (bf16x8*)op);
-      if (!tail || tok + rec::kC < T)
+      if (pfull || tok < T) __builtin_nontemporal_store(ya, (bf16x8*)op);
+      if (pfull || tok + rec::kC < T)
         __builtin_nontemporal_store(yb, (bf16x8*)(op + rec::kC * rstride));
     }
 
@@ -515,7 +521,7 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     if (ckpt != nullptr) {
       const int64_t done = (x0 + xl + 1) * rec::kP;  // tokens consumed (uniform)
       if (done % ckpt_every == 0 && done <= T) {
-        const int64_t nck = T / ckpt_every, ic = done / ckpt_every - 1;
+        const int64_t nck = seqs.T / ckpt_every, ic = done / ckpt_every - 1;
         store_state(ckpt + ((b * nck + ic) * H + h) * (int64_t)(rec::kDK * rec::kDV));
       }
     }
@@ -548,7 +554,7 @@ int device_cus() {
   return cus > 0 ? cus : 256;
 }
 
-template <int DVW, int CPW, bool GATE, bool WO>
+template <int DVW, int CPW, bool GATE, bool WO, bool PACKED>
 hipError_t launch_state_t(const ChunkArgs& a, Seg cur, const float* s_in, float* s_next, Seg nxt,
                           int cus) {
   constexpr int NW = DVW / CPW + kLoaders;
@@ -564,11 +570,13 @@ hipError_t launch_state_t(const ChunkArgs& a, Seg cur, const float* s_in, float*
   const int64_t nblk = n_state + n_tile;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-  tile::Args tb{(const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, nxt.recs,
-                a.T, a.H, BH, nxt.x0, nxt.n > 0 ? nxt.n : 1, a.scale};
-  hipLaunchKernelGGL((kda_state_kernel<DVW, CPW, GATE, WO>), dim3((unsigned)nblk), dim3(64 * NW),
+  const Seqs<PACKED> seqs{a.cu, a.T, PACKED ? a.total : a.B * a.T};
+  tile::Args<PACKED> tb{(const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, nxt.recs,
+                seqs, a.H, BH, nxt.x0, nxt.n > 0 ? nxt.n : 1, a.scale};
+  hipLaunchKernelGGL((kda_state_kernel<DVW, CPW, GATE, WO, PACKED>), dim3((unsigned)nblk),
+                     dim3(64 * NW),
                      0, (hipStream_t)a.stream, cur.recs, (const bf16_t*)a.v, s_in, s_next,
-                     (bf16_t*)a.o, (const bf16_t*)a.gate, a.norm_w, a.eps, a.T, a.H, BH, cur.x0,
+                     (bf16_t*)a.o, (const bf16_t*)a.gate, a.norm_w, a.eps, seqs, a.H, BH, cur.x0,
                      cur.n > 0 ? cur.n : 1, n_state, a.ckpt, a.ckpt_every, tb);
   return hipGetLastError();
 }
@@ -617,6 +625,21 @@ int64_t seg_pairs(int64_t BH, int64_t npairs, int cus, int split) {
 }
 
 int64_t pairs_of(int64_t T) { return (T + rec::kP - 1) / rec::kP; }
+
+// The kernel instance for the call's workgroup layout.
+template <bool PACKED>
+hipError_t launch_layout(const ChunkArgs& a, int split, Seg cur, const float* s_in,
+                         float* s_next, Seg nxt, int cus) {
+  if (a.o == nullptr)
+    return split == 2
+               ? launch_state_t<64, 32, false, false, PACKED>(a, cur, s_in, s_next, nxt, cus)
+               : launch_state_t<128, 32, false, false, PACKED>(a, cur, s_in, s_next, nxt, cus);
+  if (a.gate != nullptr)
+    return launch_state_t<128, 32, true, true, PACKED>(a, cur, s_in, s_next, nxt, cus);
+  if (split == 2)
+    return launch_state_t<64, 32, false, true, PACKED>(a, cur, s_in, s_next, nxt, cus);
+  return launch_state_t<128, 32, false, true, PACKED>(a, cur, s_in, s_next, nxt, cus);
+}
 
 }  // namespace
 
@@ -673,19 +696,11 @@ hipError_t launch_chunk_mfma(const ChunkArgs& a) {
     const Seg cur = segment(j), nxt = segment(j + 1);
     const float* s_in = (j <= 0) ? a.s0 : carry;
     float* s_next = (j == nsegs - 1) ? a.s_out : carry;
-    hipError_t e;
     // 32 state columns per state wavefront: one state and one loader
     // wavefront per SIMD, each with up to 256 registers (the tile builder
     // running in the same launch needs them).
-    if (a.o == nullptr)
-      e = split == 2 ? launch_state_t<64, 32, false, false>(a, cur, s_in, s_next, nxt, cus)
-                     : launch_state_t<128, 32, false, false>(a, cur, s_in, s_next, nxt, cus);
-    else if (a.gate != nullptr)
-      e = launch_state_t<128, 32, true, true>(a, cur, s_in, s_next, nxt, cus);
-    else if (split == 2)
-      e = launch_state_t<64, 32, false, true>(a, cur, s_in, s_next, nxt, cus);
-    else
-      e = launch_state_t<128, 32, false, true>(a, cur, s_in, s_next, nxt, cus);
+    const hipError_t e = a.cu != nullptr ? launch_layout<true>(a, split, cur, s_in, s_next, nxt, cus)
+                        : launch_layout<false>(a, split, cur, s_in, s_next, nxt, cus);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -70,11 +70,12 @@ struct Scratch {  // per wavefront
   float en_a[rec::kDK];  // E_a of the pair being built, per key channel
 };
 
-// Element offset of the row of token `tok` (clamped into the sequence) of head (b, h).
-__device__ __forceinline__ int64_t row_of(int64_t b, int64_t h, int64_t tok, int64_t T,
-                                          int64_t H) {
-  tok = tok < T ? tok : T - 1;
-  return (b * T + tok) * H + h;
+// Row index (into [rows, H, *] tensors) of token `tok` of head (b, h), the
+// token clamped into its sequence.
+template <bool PACKED>
+__device__ __forceinline__ int64_t row_of(const Seqs<PACKED>& sq, int64_t b, int64_t h,
+                                          int64_t tok, int64_t H) {
+  return sq.row(b, tok) * H + h;
 }
 
 // This lane's q and k of slab s (and of slab s + 1, into q1 / k1) and g of slab
@@ -287,13 +288,15 @@ __device__ __forceinline__ void w_slab(const f16x4 (&khT)[2], f16x4 tb, f32x4 (&
 
 // ---------------------------------------------------------------- pairs
 
+template <bool PACKED>
 struct Args {
   const bf16_t* q;
   const bf16_t* k;
   const float* g;
   const float* beta;
   unsigned char* recs;  // records of the segment, [head][pair]
-  int64_t T, H, BH;
+  Seqs<PACKED> seqs;    // where each sequence's tokens are; seqs.T = longest length
+  int64_t H, BH;
   int64_t x0, nseg;     // first pair and pair count of the segment
   float scale;
 };
@@ -313,13 +316,16 @@ struct PairRows {
   int64_t a, b;  // element offsets of this lane's token rows (clamped into the sequence)
 };
 
-__device__ __forceinline__ PairRows pair_rows(const Args& a, const Pos& p, int lane) {
+template <bool PACKED>
+__device__ __forceinline__ PairRows pair_rows(const Args<PACKED>& a, const Pos& p, int lane) {
   const int64_t tok0 = (a.x0 + p.xl) * rec::kP + lane % 16;
-  return PairRows{row_of(p.b, p.h, tok0, a.T, a.H), row_of(p.b, p.h, tok0 + rec::kC, a.T, a.H)};
+  return PairRows{row_of(a.seqs, p.b, p.h, tok0, a.H),
+                  row_of(a.seqs, p.b, p.h, tok0 + rec::kC, a.H)};
 }
 
-__device__ __forceinline__ void load_pair_slab(PairIn& x, const Args& a, const PairRows& r, int s,
-                                               int lane) {
+template <bool PACKED>
+__device__ __forceinline__ void load_pair_slab(PairIn& x, const Args<PACKED>& a,
+                                               const PairRows& r, int s, int lane) {
   load_slab(x.a, x.qa1, x.ka1, a.q, a.k, a.g, r.a, s, lane);
   load_slab(x.b, x.qb1, x.kb1, a.q, a.k, a.g, r.b, s, lane);
 }
@@ -328,14 +334,16 @@ __device__ __forceinline__ void load_pair_slab(PairIn& x, const Args& a, const P
 // slab 0 of pair p (and the q and k of its slab 1); the next slab's inputs are always in flight while a slab
 // is built, and on return `cur` holds slab 0 of pair `pn` (the wavefront's
 // next pair, or any valid pair when there is none).
-__device__ __forceinline__ void build_pair(const Args& a, const Pos& p, const Pos& pn, PairIn& cur,
-                                           Scratch* sm, int lane) {
+template <bool PACKED>
+__device__ __forceinline__ void build_pair(const Args<PACKED>& a, const Pos& p, const Pos& pn,
+                                           PairIn& cur, Scratch* sm, int lane) {
   const int t = lane % 16, lg = lane / 16;
   const int64_t tok0 = (a.x0 + p.xl) * rec::kP;
   const PairRows rows = pair_rows(a, p, lane), nrows = pair_rows(a, pn, lane);
-  const bool fulla = tok0 + rec::kC <= a.T, fullb = tok0 + rec::kP <= a.T;
-  const float lva = tok0 + t < a.T ? 1.f : 0.f;
-  const float lvb = tok0 + rec::kC + t < a.T ? 1.f : 0.f;
+  const int64_t T = a.seqs.len(p.b);  // tokens past it are identity (g = beta = k = q = 0)
+  const bool fulla = tok0 + rec::kC <= T, fullb = tok0 + rec::kP <= T;
+  const float lva = tok0 + t < T ? 1.f : 0.f;
+  const float lvb = tok0 + rec::kC + t < T ? 1.f : 0.f;
   const float betaa = a.beta[rows.a] * lva, betab = a.beta[rows.b] * lvb;
   unsigned char* R = a.recs + ((p.b * a.H + p.h) * a.nseg + p.xl) * (int64_t)rec::kBytes;
 
@@ -431,7 +439,8 @@ __device__ __forceinline__ void build_pair(const Args& a, const Pos& p, const Po
 // head-fastest (pair w is pair w / BH of head w % BH), so that the wavefronts
 // working at one time read neighbouring heads of the same tokens, which are
 // adjacent in memory.
-__device__ __forceinline__ void build_range(const Args& a, int64_t first, int64_t stride,
+template <bool PACKED>
+__device__ __forceinline__ void build_range(const Args<PACKED>& a, int64_t first, int64_t stride,
                                             Scratch* sm, int lane) {
   const int64_t total = a.BH * a.nseg;
   if (first >= total) return;

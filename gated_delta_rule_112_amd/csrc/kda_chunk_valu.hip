@@ -26,13 +26,13 @@ namespace kda {
 constexpr int kTile = 16;
 constexpr int kValuThreads = 128;
 
-template <int DK, int DV, typename IO>
+template <int DK, int DV, typename IO, bool PACKED>
 __global__ void __launch_bounds__(kValuThreads)
 kda_chunk_valu_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
                       const float* __restrict__ g, const float* __restrict__ beta,
                       const float* __restrict__ s0, IO* __restrict__ o, float* __restrict__ s_out,
                       const IO* __restrict__ gate, const float* __restrict__ norm_w, float eps,
-                      int64_t T, int64_t H, float scale, float* __restrict__ ckpt,
+                      Seqs<PACKED> seqs, int64_t H, float scale, float* __restrict__ ckpt,
                       int64_t ckpt_every) {
   constexpr int C = kTile;
   __shared__ float sQh[C][DK];
@@ -53,8 +53,9 @@ kda_chunk_valu_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const 
   const int64_t b = blockIdx.x / H;
   const int64_t h = blockIdx.x % H;
   const int64_t bh = blockIdx.x;
-  // Token t of this head: element offsets into [B, T, H, *] tensors.
-  auto tok = [&](int64_t t) { return (b * T + t) * H + h; };
+  // Token t (< T) of this head: element offsets into [rows, H, *] tensors.
+  const int64_t T = seqs.len(b), t0 = seqs.start(b);
+  auto tok = [&](int64_t t) { return (t0 + t) * H + h; };
 
   float S[DK];
   if (tid < DV) {
@@ -185,7 +186,7 @@ kda_chunk_valu_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const 
       }
       // State checkpoint after every ckpt_every tokens (a multiple of the tile).
       if (ckpt != nullptr && (c0 + C) % ckpt_every == 0 && c0 + C <= T) {
-        const int64_t nck = T / ckpt_every, ic = (c0 + C) / ckpt_every - 1;
+        const int64_t nck = seqs.T / ckpt_every, ic = (c0 + C) / ckpt_every - 1;
         float* cp = ckpt + ((b * nck + ic) * H + h) * (int64_t)(DK * DV);
 #pragma unroll
         for (int i = 0; i < DK; ++i) cp[i * DV + j] = S[i];
@@ -223,13 +224,19 @@ kda_chunk_valu_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const 
   }
 }
 
-template <int DK, int DV, typename IO>
-static hipError_t launch_valu_t(const ChunkArgs& a) {
-  hipLaunchKernelGGL((kda_chunk_valu_kernel<DK, DV, IO>), dim3((unsigned)(a.B * a.H)),
+template <int DK, int DV, typename IO, bool PACKED>
+static hipError_t launch_valu_p(const ChunkArgs& a) {
+  hipLaunchKernelGGL((kda_chunk_valu_kernel<DK, DV, IO, PACKED>), dim3((unsigned)(a.B * a.H)),
                      dim3(kValuThreads), 0, (hipStream_t)a.stream, (const IO*)a.q, (const IO*)a.k,
                      (const IO*)a.v, a.g, a.beta, a.s0, (IO*)a.o, a.s_out, (const IO*)a.gate,
-                     a.norm_w, a.eps, a.T, a.H, a.scale, a.ckpt, a.ckpt_every);
+                     a.norm_w, a.eps, Seqs<PACKED>{a.cu, a.T, PACKED ? a.total : a.B * a.T}, a.H,
+                     a.scale, a.ckpt, a.ckpt_every);
   return hipGetLastError();
+}
+
+template <int DK, int DV, typename IO>
+static hipError_t launch_valu_t(const ChunkArgs& a) {
+  return a.cu != nullptr ? launch_valu_p<DK, DV, IO, true>(a) : launch_valu_p<DK, DV, IO, false>(a);
 }
 
 template <typename IO>

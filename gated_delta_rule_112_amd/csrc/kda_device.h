@@ -47,4 +47,46 @@ __device__ __forceinline__ void st4(bf16_t* p, f32x4 x) {
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
+// Where the tokens of sequence b sit among the `total` token rows of a
+// [rows, H, d] tensor: B sequences of T rows each (PACKED false, total = B T),
+// or packed sequences occupying rows cu[b] .. cu[b + 1] - 1 (T is then the
+// longest length).  Packed bounds are clamped into [0, total] and lengths to T,
+// so every row index a kernel forms stays below `total` whatever cu holds.  A
+// compile-time choice: the uniform layout keeps its plain arithmetic.
+template <bool PACKED>
+struct Seqs {
+  const int* cu;
+  int64_t T, total;
+
+  __device__ __forceinline__ int64_t start(int64_t b) const {
+    if constexpr (!PACKED) {
+      return b * T;
+    } else {
+      const int64_t s = cu[b];
+      return s < 0 ? 0 : (s > total ? total : s);
+    }
+  }
+  __device__ __forceinline__ int64_t len(int64_t b) const {
+    if constexpr (!PACKED) {
+      return T;
+    } else {
+      const int64_t s = start(b);
+      int64_t e = cu[b + 1];
+      e = e < s ? s : (e > total ? total : e);
+      return e - s < T ? e - s : T;
+    }
+  }
+  // Row of token `tok` (>= 0) of sequence b, clamped into the sequence (into
+  // the tensor when the sequence is empty).
+  __device__ __forceinline__ int64_t row(int64_t b, int64_t tok) const {
+    if constexpr (!PACKED) {
+      return b * T + (tok < T ? tok : T - 1);
+    } else {
+      const int64_t n = len(b);
+      const int64_t r = start(b) + (tok < n ? tok : n - 1);
+      return r < 0 ? 0 : (r >= total ? total - 1 : r);
+    }
+  }
+};
+
 }  // namespace kda

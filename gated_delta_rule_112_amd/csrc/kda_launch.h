@@ -29,6 +29,10 @@ struct ChunkArgs {
   // state after every ckpt_every tokens (a multiple of 32).
   float* ckpt = nullptr;
   int64_t ckpt_every = 0;
+  // Packed sequences: B sequences at rows cu[b] .. cu[b + 1] - 1 of total rows
+  // (device array of B + 1 entries), T the longest; NULL for B x T.
+  const int* cu = nullptr;
+  int64_t total = 0;
 };
 
 struct DecodeArgs {

@@ -154,6 +154,43 @@ kda_status kda_chunk_fwd_checkpoints(const void* q, const void* k, const void* v
                                      int64_t ckpt_every, void* stream);
 
 /*
+ * kda_chunk_fwd_varlen -- kda_chunk_fwd over N sequences of different lengths
+ * packed along the token axis (a serving batch), with optional checkpoints.
+ *
+ * Sequence b occupies token rows cu_seqlens[b] .. cu_seqlens[b + 1] - 1 of the
+ * packed tensors and runs its own recurrence from s0[b] (or zero) to s_out[b].
+ * The work is laid out as for N sequences of max_len tokens: tokens past a
+ * sequence's end are identity tokens (g = 0, beta = 0, k = 0), which leave the
+ * state unchanged, and produce no output.
+ *
+ *   q, k, g    [total, H, dk]  (io dtype; g float32)      packed
+ *   v, o, gate [total, H, dv]  io dtype                    packed (o, gate may be NULL as in
+ *                                                          kda_chunk_fwd)
+ *   beta       [total, H]      float32
+ *   cu_seqlens [N + 1] int32 device array: 0 = cu[0] <= cu[1] <= ... <= cu[N] = total,
+ *              every cu[b + 1] - cu[b] <= max_len.  Not checked; a violation gives
+ *              undefined results (but no access outside the tensors: bounds are clamped
+ *              into [0, total] and lengths to max_len).
+ *   N, total, max_len  >= 1 (host values)
+ *   s0, s_out  [N, H, dk, dv] float32, as in kda_chunk_fwd
+ *   ckpt       [N, max_len / ckpt_every, H, dk, dv] float32 or NULL: entry [b, i, h] receives
+ *              the state after the first (i + 1) * ckpt_every tokens of sequence b when it
+ *              has that many (others are not written); ckpt_every as in
+ *              kda_chunk_fwd_checkpoints (ignored when ckpt is NULL).
+ *   workspace  at least kda_chunk_fwd_workspace_size(N, max_len, H, dk, dv, io) bytes.
+ *   Every other argument, alignment and aliasing rule as in kda_chunk_fwd (cu_seqlens
+ *   4 bytes, overlapping no output).
+ */
+kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v,
+                                const float* g, const float* beta,
+                                const int32_t* cu_seqlens, int64_t N, int64_t total,
+                                int64_t max_len, const float* s0, void* o, float* s_out,
+                                const void* gate, const float* norm_w, float eps, int64_t H,
+                                int dk, int dv, float scale, kda_dtype io, void* workspace,
+                                size_t workspace_bytes, float* ckpt, int64_t ckpt_every,
+                                void* stream);
+
+/*
  * kda_decode_step -- one token per sequence against a resident state.
  *
  * The constant-cost recurrent step ("Kimi K3 Architecture Explained ...",

@@ -31,7 +31,8 @@ def lib():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    for n in ["kda_chunk_fwd", "kda_chunk_fwd_checkpoints", "kda_chunk_fwd_workspace_size",
+    for n in ["kda_chunk_fwd", "kda_chunk_fwd_checkpoints", "kda_chunk_fwd_varlen",
+              "kda_chunk_fwd_workspace_size",
               "kda_chunk_fwd_launches",
               "kda_decode_step", "kda_decode_multi",
               "kda_gate_rmsnorm", "kda_status_string", "kda_version"]:
@@ -154,6 +155,24 @@ def test_chunk_checkpoints_validation(lib):
     assert call(ckpt=P(11, 2)) == ALIGN
     assert call(ckpt=P(1)) == ALIAS          # overlaps q
     assert call(ckpt=P(7)) == ALIAS          # overlaps s_out
+
+
+def test_chunk_varlen_validation(lib):
+    f = lib.kda_chunk_fwd_varlen
+
+    def call(cu=P(12), N=3, total=200, max_len=100, o=6, ckpt=None, every=0):
+        # vector-path sizes (dk = dv = 16): no workspace needed
+        return f(P(1), P(2), P(3), P(4), P(5), cu, N, total, max_len, None, P(o), P(7), None,
+                 None, 1e-6, 3, 16, 16, 1.0, 0, None, 0, ckpt, every, None)
+
+    assert call(cu=None) == NULLP
+    assert call(N=0) == SHAPE
+    assert call(total=0) == SHAPE
+    assert call(max_len=0) == SHAPE
+    assert call(cu=P(12, 2)) == ALIGN
+    assert call(cu=P(6)) == ALIAS             # cu_seqlens inside o
+    assert call(ckpt=P(11), every=40) == SHAPE
+    assert call(ckpt=P(1), every=32) == ALIAS   # checkpoints overlap q
 
 
 def decode(lib, *, q=1, k=2, v=3, g=4, beta=5, state=6, o=7, gate=None, w=None, eps=1e-6,

@@ -1,0 +1,107 @@
+"""GPU parity of packed variable-length prefill (kda_chunk_fwd_varlen), through the C ABI.
+
+Every sequence of the packed batch must equal the float64 token recurrence of
+the oracle run on that sequence alone, from its own initial state: outputs,
+final state and checkpoints.  Tolerances as for the uniform prefill: 1e-4 x RMS
+for float32 io (vector path), 2e-2 x RMS for bfloat16 io (matrix-core path; half
+an ulp of the bfloat16 output's rounding not counted).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle.kda_oracle import gate_rmsnorm as o_gate_rmsnorm
+from oracle.kda_oracle import kda_recurrent as o_recurrent
+from tests.gpu_helpers import assert_close, dev, f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import gated_delta_rule_112_amd as m
+    m.load_library()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def gen(lens, H, dk, dv, dtype, seed, gate=False):
+    total = int(sum(lens))
+    gen_ = torch.Generator(device=dev())
+    gen_.manual_seed(seed)
+    r = lambda *s: torch.randn(*s, generator=gen_, device=dev())  # noqa: E731
+    q = r(total, H, dk)
+    k = r(total, H, dk)
+    q = (q / q.norm(dim=-1, keepdim=True)).to(dtype)
+    k = (k / k.norm(dim=-1, keepdim=True)).to(dtype)
+    v = r(total, H, dv).to(dtype)
+    g = -5.0 * torch.sigmoid(r(total, H, dk))
+    beta = torch.sigmoid(r(total, H))
+    s0 = 0.05 * r(len(lens), H, dk, dv)
+    gt = r(total, H, dv).to(dtype) if gate else None
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev())
+    return q, k, v, g, beta, s0, gt, cu
+
+
+def check(kda, lens, H, dk, dv, dtype, seed, gate=False, every=0, heads=None):
+    q, k, v, g, beta, s0, gt, cu = gen(lens, H, dk, dv, dtype, seed, gate)
+    max_len = max(max(lens), 1)
+    y, S, ck = kda.chunk_fwd_varlen(q, k, v, g, beta, cu, max_len, s0, gate=gt, every=every)
+    torch.cuda.synchronize()
+    cuh = cu.cpu().numpy()
+    for b, n in enumerate(lens):
+        a = int(cuh[b])
+        if n == 0:
+            assert torch.equal(S[b], s0[b]), "an empty sequence keeps its initial state"
+            continue
+        x = [f64(t[a:a + n])[None] for t in (q, k, v, g, beta)]
+        o_ref, S_ref = o_recurrent(*x, f64(s0[b:b + 1]))
+        if gt is not None:
+            o_ref = o_gate_rmsnorm(o_ref, f64(gt[a:a + n])[None], None, 1e-6)
+        assert_close(f64(y[a:a + n]), o_ref[0], TOL[dtype], f"y seq {b} (len {n})", dtype)
+        assert_close(f64(S[b]), S_ref[0], TOL[dtype], f"state seq {b}")
+        for i in range(n // every if every else 0):
+            _, Si = o_recurrent(*(t[:, :(i + 1) * every] for t in x), f64(s0[b:b + 1]))
+            assert_close(f64(ck[b, i]), Si[0], TOL[dtype], f"checkpoint {i} seq {b}")
+    return y, S
+
+
+LENS = [1, 37, 0, 100, 64, 33]
+
+
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, torch.bfloat16), (64, 32, torch.float32),
+                                         (128, 128, torch.float32)])
+@pytest.mark.parametrize("gated", [False, True])
+def test_varlen_matches_oracle(kda, dk, dv, dtype, gated):
+    check(kda, LENS, 3, dk, dv, dtype, 1700 + dk + dv, gate=gated, every=32)
+
+
+@pytest.mark.parametrize("split", ["1", "2"])
+@pytest.mark.parametrize("seg", ["1", "3"])
+def test_varlen_segments(kda, monkeypatch, split, seg):
+    """Matrix-core path with segments of one and three pairs, one or two state
+    workgroups per head: sequences end inside, at, and before segments."""
+    monkeypatch.setenv("KDA_CHUNK_SPLIT", split)
+    monkeypatch.setenv("KDA_SEG_PAIRS", seg)
+    check(kda, [130, 5, 64, 96, 31], 2, 128, 128, torch.bfloat16, 1750 + int(seg), every=64)
+
+
+def test_varlen_equal_lengths_equal_uniform(kda):
+    """Equal lengths: the packed call computes what the [B, T] call does, bit for bit."""
+    B, T, H = 3, 80, 4
+    q, k, v, g, beta, s0, gt, cu = gen([T] * B, H, 128, 128, torch.bfloat16, 1780, gate=True)
+    y, S, _ = kda.chunk_fwd_varlen(q, k, v, g, beta, cu, T, s0, gate=gt)
+    rs = lambda t: t.view(B, T, *t.shape[1:])  # noqa: E731
+    y2, S2 = kda.chunk_fwd(rs(q), rs(k), rs(v), rs(g), rs(beta), s0, gate=rs(gt))
+    torch.cuda.synchronize()
+    assert torch.equal(rs(y), y2) and torch.equal(S, S2)
+
+
+def test_varlen_serving_batch(kda):
+    """64 sequences of 1 to 700 tokens, 8 heads, the gated epilogue: a serving
+    batch on the matrix-core path, every sequence against the oracle."""
+    rng = np.random.default_rng(5)
+    lens = [int(x) for x in rng.integers(1, 701, 64)]
+    check(kda, lens, 8, 128, 128, torch.bfloat16, 1790, gate=True)
