@@ -163,8 +163,12 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
   const int64_t bh = wg / NSPLIT;
   const int col0 = (int)(wg % NSPLIT) * DVW;  // first value column of the workgroup
   const int64_t b = bh / H, h = bh % H;
-  // This head's sequence: T tokens from row t0 (pairs past T hold identity tokens).
+  // This head's sequence: T tokens from row t0.  Only its live pairs (those
+  // with a token of the sequence) are walked; past them the state is carried
+  // unchanged (the tile workgroups build no records for them either).
   const int64_t T = seqs.len(b), t0 = seqs.start(b);
+  int64_t live = (T + rec::kP - 1) / rec::kP - x0;
+  live = live < 0 ? 0 : (live > nseg ? nseg : live);
 
   const int64_t rstride = H * rec::kDV;  // elements between consecutive tokens of a head
 
@@ -200,7 +204,7 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
         loff[i] = (unsigned)(2 * (t * rstride + lcol[i]));
       }
     }
-    // Copy pair xt (< nseg) into ring slot `slot` and gate slot `gslot`.
+    // Copy pair xt (< live) into ring slot `slot` and gate slot `gslot`.
     const bf16_t* vg = GATE ? gate : v;
     auto issue = [&](int64_t xt, int slot, int gslot) {
       const int64_t row0 = (x0 + xt) * rec::kP;               // first token of the pair
@@ -280,18 +284,18 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     // in flight, so near the end (fewer pairs in flight) they wait for all.
 #pragma unroll
     for (int y = 0; y < kLead; ++y)
-      if (y < nseg) issue(y, y, y);
-    if (kLead <= nseg)
+      if (y < live) issue(y, y, y);
+    if (kLead <= live)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm((kLead - 1) * SC::kPer));  // pair 0 is in LDS
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_s_barrier();
     // Ring slot of pair x: x % kRing; gate slot: x % kGRing.
     int slot_issue = kLead, gslot_issue = kLead, gslot_cur = 0;
-    for (int64_t xl = 0; xl < nseg; ++xl) {
+    for (int64_t xl = 0; xl < live; ++xl) {
       // the slot of pair xl - 1 (free since the last barrier) and the gate
       // slot of pair xl - 2 (read by the epilogue of the last step)
-      const bool more = xl + kLead < nseg;  // a pair to issue (uniform)
+      const bool more = xl + kLead < live;  // a pair to issue (uniform)
       if (more) issue(xl + kLead, slot_issue, gslot_issue);
       slot_issue = slot_issue == kRing - 1 ? 0 : slot_issue + 1;
       if constexpr (GATE) {
@@ -399,7 +403,7 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
   // holds in those k-values.
   f16x8 ta8 = {}, aa8 = {};
   int slot = 0;  // ring slot of pair xl
-  for (int64_t xl = 0; xl < nseg; ++xl) {
+  for (int64_t xl = 0; xl < live; ++xl) {
     const bool pfull = (x0 + xl + 1) * rec::kP <= T;  // every token of the pair is in the sequence
     const unsigned char* Rs = ring[slot];
 
@@ -535,7 +539,9 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     __syncthreads();  // pair xl + 1 is in LDS; the slot of pair xl may be refilled
     slot = slot == kRing - 1 ? 0 : slot + 1;
   }
-  if constexpr (GATE) epilogue(nseg - 1, Pa, Pb);  // its row sums are in LDS since the last barrier
+  if constexpr (GATE) {
+    if (live > 0) epilogue(live - 1, Pa, Pb);  // its row sums are in LDS since the last barrier
+  }
 
   if (s_next != nullptr) store_state(s_next + bh * rec::kDK * rec::kDV);
 }
@@ -647,9 +653,20 @@ bool chunk_mfma_supports(int dk, int dv, bool io_bf16) {
   return io_bf16 && dk == rec::kDK && dv == rec::kDV;
 }
 
+// Sequences per launch group.  The state workgroups of a group take about
+// 3/8 of the compute units (96 of 256: the layout the segment length and the
+// builder rounds are tuned for, with the other 5/8 building records); a larger
+// batch runs group after group, each through the whole segment pipeline,
+// rather than state and tile workgroups taking turns on the compute units.
+int64_t group_seqs(int64_t B, int64_t H, int cus) {
+  int64_t g = (3 * (int64_t)cus / 8) / H;
+  if (g < 1) g = 1;
+  return g < B ? g : B;
+}
+
 size_t chunk_mfma_workspace(int64_t B, int64_t T, int64_t H) {
-  const int64_t BH = B * H, np = pairs_of(T);
   const int cus = device_cus();
+  const int64_t BH = group_seqs(B, H, cus) * H, np = pairs_of(T);
   // either workgroup layout (it depends on the gate, unknown here)
   const int64_t s1 = seg_pairs(BH, np, cus, 1), s2 = seg_pairs(BH, np, cus, 2);
   const int64_t seg = s1 > s2 ? s1 : s2;
@@ -661,24 +678,32 @@ size_t chunk_mfma_workspace(int64_t B, int64_t T, int64_t H) {
 int64_t chunk_mfma_launches(int64_t B, int64_t T, int64_t H) {
   const int64_t np = pairs_of(T);
   const int cus = device_cus();
-  ChunkArgs a{};
-  a.B = B;
-  a.H = H;
-  const int64_t seg = seg_pairs(B * H, np, cus, split_for(a, cus));  // without the gate
-  return (np + seg - 1) / seg + 1;  // one per segment, plus the first segment's records
+  const int64_t gB = group_seqs(B, H, cus);
+  int64_t n = 0;
+  for (int64_t b0 = 0; b0 < B; b0 += gB) {
+    ChunkArgs a{};
+    a.B = (B - b0) < gB ? (B - b0) : gB;
+    a.H = H;
+    const int64_t seg = seg_pairs(a.B * H, np, cus, split_for(a, cus));  // without the gate
+    n += (np + seg - 1) / seg + 1;  // one per segment, plus the first segment's records
+  }
+  return n;
 }
 
-hipError_t launch_chunk_mfma(const ChunkArgs& a) {
-  if (!chunk_mfma_supports(a.dk, a.dv, a.io_bf16)) return hipErrorNotSupported;
+namespace {
+
+// The segment pipeline over one group of sequences; ws_bytes is the
+// workspace size for the whole call.
+hipError_t launch_group(const ChunkArgs& a, size_t ws_bytes, int cus) {
   const int64_t BH = a.B * a.H, np = pairs_of(a.T);
-  const int cus = device_cus();
   const int split = split_for(a, cus);
-  const int64_t seg = seg_pairs(BH, np, cus, split);
+  // record buffers: the workspace less the carried state, split in two
+  const int64_t state_bytes = BH * rec::kDK * rec::kDV * 4;
+  const int64_t segw = ((int64_t)ws_bytes - state_bytes) / (2 * BH * (int64_t)rec::kBytes);
+  int64_t seg = seg_pairs(BH, np, cus, split);
+  seg = seg < segw ? seg : segw;
+  if (seg < 1) return hipErrorInvalidValue;
   const int64_t nsegs = (np + seg - 1) / seg;
-  // record buffers laid out for the workspace size's segment (the larger
-  // of the two layouts'), the carried state after them
-  const int64_t segw = (chunk_mfma_workspace(a.B, a.T, a.H) - (size_t)BH * rec::kDK * rec::kDV * 4) /
-                       (2 * BH * (int64_t)rec::kBytes);
   unsigned char* buf[2] = {(unsigned char*)a.workspace,
                            (unsigned char*)a.workspace + BH * segw * rec::kBytes};
   float* carry = a.s_out != nullptr ? a.s_out : (float*)(buf[1] + BH * segw * rec::kBytes);
@@ -699,8 +724,41 @@ hipError_t launch_chunk_mfma(const ChunkArgs& a) {
     // 32 state columns per state wavefront: one state and one loader
     // wavefront per SIMD, each with up to 256 registers (the tile builder
     // running in the same launch needs them).
-    const hipError_t e = a.cu != nullptr ? launch_layout<true>(a, split, cur, s_in, s_next, nxt, cus)
-                        : launch_layout<false>(a, split, cur, s_in, s_next, nxt, cus);
+    const hipError_t e = a.cu != nullptr
+                             ? launch_layout<true>(a, split, cur, s_in, s_next, nxt, cus)
+                             : launch_layout<false>(a, split, cur, s_in, s_next, nxt, cus);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_chunk_mfma(const ChunkArgs& a) {
+  if (!chunk_mfma_supports(a.dk, a.dv, a.io_bf16)) return hipErrorNotSupported;
+  const int cus = device_cus();
+  const size_t ws_bytes = chunk_mfma_workspace(a.B, a.T, a.H);
+  const int64_t gB = group_seqs(a.B, a.H, cus);
+  const int64_t sd = a.H * rec::kDK * rec::kDV;  // state elements per sequence
+  for (int64_t b0 = 0; b0 < a.B; b0 += gB) {
+    ChunkArgs g = a;
+    g.B = (a.B - b0) < gB ? (a.B - b0) : gB;
+    if (a.cu != nullptr) {
+      g.cu = a.cu + b0;  // packed rows stay absolute
+    } else {
+      const int64_t rows = b0 * a.T * a.H;  // token rows of the sequences before the group
+      g.q = (const bf16_t*)a.q + rows * rec::kDK;
+      g.k = (const bf16_t*)a.k + rows * rec::kDK;
+      g.v = (const bf16_t*)a.v + rows * rec::kDV;
+      g.g = a.g + rows * rec::kDK;
+      g.beta = a.beta + rows;
+      if (a.o != nullptr) g.o = (bf16_t*)a.o + rows * rec::kDV;
+      if (a.gate != nullptr) g.gate = (const bf16_t*)a.gate + rows * rec::kDV;
+    }
+    if (a.s0 != nullptr) g.s0 = a.s0 + b0 * sd;
+    if (a.s_out != nullptr) g.s_out = a.s_out + b0 * sd;
+    if (a.ckpt != nullptr) g.ckpt = a.ckpt + b0 * (a.T / a.ckpt_every) * sd;
+    const hipError_t e = launch_group(g, ws_bytes, cus);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

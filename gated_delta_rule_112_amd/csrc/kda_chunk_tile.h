@@ -473,7 +473,11 @@ __device__ __forceinline__ void build_range(const Args<PACKED>& a, int64_t first
   load_pair_slab(cur, a, pair_rows(a, p, lane), 0, lane);
   for (int64_t w = first; w < total; w += stride) {
     const Pos pn = w + stride < total ? advance(p) : p;  // past the last pair: reload this one
-    build_pair(a, p, pn, cur, sm, lane);
+    // a pair past the end of its sequence is never read: no record for it
+    if ((a.x0 + p.xl) * rec::kP < a.seqs.len(p.b))
+      build_pair(a, p, pn, cur, sm, lane);
+    else
+      load_pair_slab(cur, a, pair_rows(a, pn, lane), 0, lane);
     p = pn;
   }
 }

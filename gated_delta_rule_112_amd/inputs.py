@@ -20,6 +20,8 @@ Optionally every key channel j = h*dk + i with j % force_every == 0 gets
 g = forced_g at every token (stress of the decay floor).
 The multi-token decode workload draws T draft tokens per sequence with the
 same distributions, and an accepted count per sequence uniform in [0, T].
+The packed workload draws B sequence lengths uniform in [T/4, 7T/4) (mean T)
+and packs the sequences along the token axis.
 """
 from __future__ import annotations
 
@@ -29,7 +31,7 @@ from typing import Optional
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "make_prefill_inputs", "make_decode_state",
-           "make_decode_step_inputs", "make_verify_inputs"]
+           "make_decode_step_inputs", "make_verify_inputs", "make_packed_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -60,6 +62,9 @@ WORKLOADS = {
                                       dv=128, io="bf16", force_every=1000, seed=1004),
     "batched_decode": Workload("batched_decode", B=256, H=96, T=1, dk=128, dv=128, io="bf16",
                                s0_std=0.02, steps=64, seed=1005),
+    # a serving batch: 16 sequences of 512 .. 3583 tokens packed along the token axis
+    "packed_prefill": Workload("packed_prefill", B=16, H=96, T=2048, dk=128, dv=128,
+                               io="bf16", gate=True, seed=1007),
     # speculative decoding: T = 4 draft tokens per sequence against the resident state
     "batched_verify": Workload("batched_verify", B=256, H=96, T=4, dk=128, dv=128, io="bf16",
                                s0_std=0.02, gate=True, seed=1006),
@@ -165,3 +170,21 @@ def make_verify_inputs(w: Workload, device="cpu", seed: Optional[int] = None):
                                   dtype=torch.int32)
     del x["s0"]
     return x
+
+
+def make_packed_inputs(w: Workload, device="cpu", seed: Optional[int] = None):
+    """B sequences of lengths uniform in [T/4, 7T/4) packed along the token axis:
+    q, k, g [total, H, dk], v, gate [total, H, dv], beta [total, H], the int32
+    offsets ``cu_seqlens`` [B + 1] and the host list ``lens``."""
+    seed = w.seed if seed is None else seed
+    lens = torch.randint(w.T // 4, 7 * w.T // 4, (w.B,), generator=_gen(seed + 3, "cpu"))
+    total = int(lens.sum())
+    flat = dataclasses.replace(w, B=1, T=total)
+    x = make_prefill_inputs(flat, device=device, seed=seed)
+    out = {key: (t[0] if t is not None and key != "s0" else t) for key, t in x.items()}
+    del out["s0"]
+    cu = torch.zeros(w.B + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(lens, 0)
+    out["cu_seqlens"] = cu.to(device)
+    out["lens"] = [int(n) for n in lens]
+    return out
