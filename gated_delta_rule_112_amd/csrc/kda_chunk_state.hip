@@ -48,6 +48,8 @@
 // state, the values and D to stay below 65504 in magnitude.
 #include <stdlib.h>
 
+#include <vector>
+
 #include <type_traits>
 
 #include "kda_chunk_rec.h"
@@ -561,14 +563,14 @@ int device_cus() {
 }
 
 template <int DVW, int CPW, bool GATE, bool WO, bool PACKED>
-hipError_t launch_state_t(const ChunkArgs& a, Seg cur, const float* s_in, float* s_next, Seg nxt,
-                          int cus) {
+hipError_t launch_state_t(const ChunkArgs& a, Seg cur, const float* s_in, float* s_next,
+                          const ChunkArgs& ab, Seg nxt, int cus) {
   constexpr int NW = DVW / CPW + kLoaders;
-  const int64_t BH = a.B * a.H;
+  const int64_t BH = a.B * a.H, BHb = ab.B * ab.H;
   const int64_t n_state = cur.n > 0 ? BH * (rec::kDV / DVW) : 0;
   int64_t n_tile = 0;
   if (nxt.n > 0) {
-    const int64_t want = (BH * nxt.n + NW - 1) / NW;  // one pair per wavefront at most
+    const int64_t want = (BHb * nxt.n + NW - 1) / NW;  // one pair per wavefront at most
     int64_t avail = cus - n_state;
     if (avail < cus / 4) avail = cus / 4;              // always make progress
     n_tile = want < avail ? want : avail;
@@ -577,8 +579,9 @@ hipError_t launch_state_t(const ChunkArgs& a, Seg cur, const float* s_in, float*
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
   const Seqs<PACKED> seqs{a.cu, a.T, PACKED ? a.total : a.B * a.T};
-  tile::Args<PACKED> tb{(const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, nxt.recs,
-                seqs, a.H, BH, nxt.x0, nxt.n > 0 ? nxt.n : 1, a.scale};
+  const Seqs<PACKED> seqb{ab.cu, ab.T, PACKED ? ab.total : ab.B * ab.T};
+  tile::Args<PACKED> tb{(const bf16_t*)ab.q, (const bf16_t*)ab.k, ab.g, ab.beta, nxt.recs,
+                        seqb, ab.H, BHb, nxt.x0, nxt.n > 0 ? nxt.n : 1, ab.scale};
   hipLaunchKernelGGL((kda_state_kernel<DVW, CPW, GATE, WO, PACKED>), dim3((unsigned)nblk),
                      dim3(64 * NW),
                      0, (hipStream_t)a.stream, cur.recs, (const bf16_t*)a.v, s_in, s_next,
@@ -635,16 +638,17 @@ int64_t pairs_of(int64_t T) { return (T + rec::kP - 1) / rec::kP; }
 // The kernel instance for the call's workgroup layout.
 template <bool PACKED>
 hipError_t launch_layout(const ChunkArgs& a, int split, Seg cur, const float* s_in,
-                         float* s_next, Seg nxt, int cus) {
+                         float* s_next, const ChunkArgs& ab, Seg nxt, int cus) {
   if (a.o == nullptr)
-    return split == 2
-               ? launch_state_t<64, 32, false, false, PACKED>(a, cur, s_in, s_next, nxt, cus)
-               : launch_state_t<128, 32, false, false, PACKED>(a, cur, s_in, s_next, nxt, cus);
+    return split == 2 ? launch_state_t<64, 32, false, false, PACKED>(a, cur, s_in, s_next, ab,
+                                                                    nxt, cus)
+                      : launch_state_t<128, 32, false, false, PACKED>(a, cur, s_in, s_next, ab,
+                                                                     nxt, cus);
   if (a.gate != nullptr)
-    return launch_state_t<128, 32, true, true, PACKED>(a, cur, s_in, s_next, nxt, cus);
+    return launch_state_t<128, 32, true, true, PACKED>(a, cur, s_in, s_next, ab, nxt, cus);
   if (split == 2)
-    return launch_state_t<64, 32, false, true, PACKED>(a, cur, s_in, s_next, nxt, cus);
-  return launch_state_t<128, 32, false, true, PACKED>(a, cur, s_in, s_next, nxt, cus);
+    return launch_state_t<64, 32, false, true, PACKED>(a, cur, s_in, s_next, ab, nxt, cus);
+  return launch_state_t<128, 32, false, true, PACKED>(a, cur, s_in, s_next, ab, nxt, cus);
 }
 
 }  // namespace
@@ -675,73 +679,27 @@ size_t chunk_mfma_workspace(int64_t B, int64_t T, int64_t H) {
   return (size_t)(2 * BH * seg * rec::kBytes) + (size_t)(BH * rec::kDK * rec::kDV * 4);
 }
 
-int64_t chunk_mfma_launches(int64_t B, int64_t T, int64_t H) {
-  const int64_t np = pairs_of(T);
-  const int cus = device_cus();
-  const int64_t gB = group_seqs(B, H, cus);
-  int64_t n = 0;
-  for (int64_t b0 = 0; b0 < B; b0 += gB) {
-    ChunkArgs a{};
-    a.B = (B - b0) < gB ? (B - b0) : gB;
-    a.H = H;
-    const int64_t seg = seg_pairs(a.B * H, np, cus, split_for(a, cus));  // without the gate
-    n += (np + seg - 1) / seg + 1;  // one per segment, plus the first segment's records
-  }
-  return n;
-}
-
 namespace {
 
-// The segment pipeline over one group of sequences; ws_bytes is the
-// workspace size for the whole call.
-hipError_t launch_group(const ChunkArgs& a, size_t ws_bytes, int cus) {
-  const int64_t BH = a.B * a.H, np = pairs_of(a.T);
-  const int split = split_for(a, cus);
-  // record buffers: the workspace less the carried state, split in two
-  const int64_t state_bytes = BH * rec::kDK * rec::kDV * 4;
-  const int64_t segw = ((int64_t)ws_bytes - state_bytes) / (2 * BH * (int64_t)rec::kBytes);
-  int64_t seg = seg_pairs(BH, np, cus, split);
-  seg = seg < segw ? seg : segw;
-  if (seg < 1) return hipErrorInvalidValue;
-  const int64_t nsegs = (np + seg - 1) / seg;
-  unsigned char* buf[2] = {(unsigned char*)a.workspace,
-                           (unsigned char*)a.workspace + BH * segw * rec::kBytes};
-  float* carry = a.s_out != nullptr ? a.s_out : (float*)(buf[1] + BH * segw * rec::kBytes);
-  auto segment = [&](int64_t j) {
-    Seg sg;
-    if (j >= 0 && j < nsegs) {
-      sg.x0 = j * seg;
-      sg.n = (np - sg.x0) < seg ? (np - sg.x0) : seg;
-      sg.recs = buf[j & 1];
-    }
-    return sg;
-  };
-  // Launch j: state pass over segment j, records of segment j + 1.
-  for (int64_t j = -1; j < nsegs; ++j) {
-    const Seg cur = segment(j), nxt = segment(j + 1);
-    const float* s_in = (j <= 0) ? a.s0 : carry;
-    float* s_next = (j == nsegs - 1) ? a.s_out : carry;
-    // 32 state columns per state wavefront: one state and one loader
-    // wavefront per SIMD, each with up to 256 registers (the tile builder
-    // running in the same launch needs them).
-    const hipError_t e = a.cu != nullptr
-                             ? launch_layout<true>(a, split, cur, s_in, s_next, nxt, cus)
-                             : launch_layout<false>(a, split, cur, s_in, s_next, nxt, cus);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
-}
+// One group of sequences as the state pass and the tile builder see it: the
+// call's arguments offset to the group, its workgroup layout and segments.
+struct Group {
+  ChunkArgs a;
+  int split = 1;
+  int64_t seg = 1, nsegs = 0;
+};
 
-}  // namespace
-
-hipError_t launch_chunk_mfma(const ChunkArgs& a) {
-  if (!chunk_mfma_supports(a.dk, a.dv, a.io_bf16)) return hipErrorNotSupported;
-  const int cus = device_cus();
-  const size_t ws_bytes = chunk_mfma_workspace(a.B, a.T, a.H);
-  const int64_t gB = group_seqs(a.B, a.H, cus);
+// The groups of a call, in order.  ws_half is the size of one record buffer
+// (the workspace holds two and a carried state): a group's segments are
+// capped so that its records fit.
+template <typename F>
+void for_each_group(const ChunkArgs& a, int cus, int64_t ws_half, F&& f) {
+  const int64_t gB = group_seqs(a.B, a.H, cus), np = pairs_of(a.T);
   const int64_t sd = a.H * rec::kDK * rec::kDV;  // state elements per sequence
   for (int64_t b0 = 0; b0 < a.B; b0 += gB) {
-    ChunkArgs g = a;
+    Group gr;
+    ChunkArgs& g = gr.a;
+    g = a;
     g.B = (a.B - b0) < gB ? (a.B - b0) : gB;
     if (a.cu != nullptr) {
       g.cu = a.cu + b0;  // packed rows stay absolute
@@ -758,7 +716,83 @@ hipError_t launch_chunk_mfma(const ChunkArgs& a) {
     if (a.s0 != nullptr) g.s0 = a.s0 + b0 * sd;
     if (a.s_out != nullptr) g.s_out = a.s_out + b0 * sd;
     if (a.ckpt != nullptr) g.ckpt = a.ckpt + b0 * (a.T / a.ckpt_every) * sd;
-    const hipError_t e = launch_group(g, ws_bytes, cus);
+    const int64_t BH = g.B * g.H;
+    gr.split = split_for(g, cus);
+    gr.seg = seg_pairs(BH, np, cus, gr.split);
+    const int64_t fit = ws_half / (BH * (int64_t)rec::kBytes);
+    if (gr.seg > fit) gr.seg = fit;
+    if (gr.seg < 1) gr.seg = 1;
+    gr.nsegs = (np + gr.seg - 1) / gr.seg;
+    f(gr);
+  }
+}
+
+int64_t record_half(int64_t B, int64_t T, int64_t H, int cus) {
+  const int64_t BH = group_seqs(B, H, cus) * H;
+  return ((int64_t)chunk_mfma_workspace(B, T, H) - BH * rec::kDK * rec::kDV * 4) / 2;
+}
+
+}  // namespace
+
+int64_t chunk_mfma_launches(int64_t B, int64_t T, int64_t H) {
+  const int cus = device_cus();
+  ChunkArgs a{};
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  int64_t n = 1;  // the first segment's records
+  for_each_group(a, cus, record_half(B, T, H, cus), [&](const Group& g) { n += g.nsegs; });
+  return n;
+}
+
+hipError_t launch_chunk_mfma(const ChunkArgs& a) {
+  if (!chunk_mfma_supports(a.dk, a.dv, a.io_bf16)) return hipErrorNotSupported;
+  const int cus = device_cus();
+  const int64_t half = record_half(a.B, a.T, a.H, cus);
+  const int64_t np = pairs_of(a.T);
+  // Every segment of every group, in order, as one pipeline: launch i runs
+  // the state pass over item i and builds the records of item i + 1, also
+  // when that item starts the next group.  Records alternate between the two
+  // halves of the workspace; the carried state follows them.
+  struct Item {
+    int group;
+    int64_t j;
+  };
+  std::vector<Group> groups;
+  std::vector<Item> items;
+  for_each_group(a, cus, half, [&](const Group& g) {
+    for (int64_t j = 0; j < g.nsegs; ++j) items.push_back({(int)groups.size(), j});
+    groups.push_back(g);
+  });
+  unsigned char* buf[2] = {(unsigned char*)a.workspace, (unsigned char*)a.workspace + half};
+  float* carry_ws = (float*)((unsigned char*)a.workspace + 2 * half);
+  auto seg_of = [&](int64_t i) {
+    Seg sg;
+    if (i >= 0 && i < (int64_t)items.size()) {
+      const Group& g = groups[items[i].group];
+      sg.x0 = items[i].j * g.seg;
+      sg.n = (np - sg.x0) < g.seg ? (np - sg.x0) : g.seg;
+      sg.recs = buf[i & 1];
+    }
+    return sg;
+  };
+  const int64_t n_items = (int64_t)items.size();
+  for (int64_t i = -1; i < n_items; ++i) {
+    const Seg cur = seg_of(i), nxt = seg_of(i + 1);
+    const Group& gs = groups[items[i < 0 ? 0 : i].group];                   // state pass
+    const Group& gb = groups[items[i + 1 < n_items ? i + 1 : i].group];     // tile builder
+    const ChunkArgs& as = gs.a;
+    float* carry = as.s_out != nullptr ? as.s_out : carry_ws;
+    const int64_t j = i < 0 ? 0 : items[i].j;
+    const float* s_in = j == 0 ? as.s0 : carry;
+    float* s_next = j == gs.nsegs - 1 ? as.s_out : carry;
+    // 32 state columns per state wavefront: one state and one loader
+    // wavefront per SIMD, each with up to 256 registers (the tile builder
+    // running in the same launch needs them).
+    const hipError_t e =
+        a.cu != nullptr
+            ? launch_layout<true>(as, gs.split, cur, s_in, s_next, gb.a, nxt, cus)
+            : launch_layout<false>(as, gs.split, cur, s_in, s_next, gb.a, nxt, cus);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
