@@ -59,6 +59,7 @@ __all__ = [
     "kda_recurrent",
     "gate_rmsnorm",
     "kda_chunked",
+    "decay_gates",
 ]
 
 
@@ -167,3 +168,18 @@ def kda_chunked(q, k, v, g, beta, s0=None, scale=1.0, chunk=16):
                 S = np.exp(Gam[-1])[:, None] * S + Kbar.T @ Delta
             S_all[b, h] = S
     return o, S_all
+
+
+def decay_gates(a, b):
+    """Log-decay and write strength from their logits.
+
+    "Kimi K3: Engineering a 2.8 Trillion Parameter Frontier", section
+    "Dimension 1", and "Kimi K3 Architecture Explained ...", section "Token
+    mixing": the log-decay is bounded below by -5 through a scaled sigmoid,
+    g = -5 * sigmoid(a), so every retention factor exp(g) lies in (e^-5, 1).
+    The write strength is read as beta = sigmoid(b) (the workloads draw beta
+    that way).  a: [..., dk] logits per key channel; b: [...] one per token and
+    head.  Returns (g, beta) in float64.
+    """
+    a, b = _f64(a), _f64(b)
+    return -5.0 / (1.0 + np.exp(-a)), 1.0 / (1.0 + np.exp(-b))

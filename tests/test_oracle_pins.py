@@ -359,3 +359,22 @@ def test_mutants_are_caught(mutant):
         except AssertionError:
             failures += 1
     assert failures > 0, f"{mutant.__name__} passed every pin"
+
+
+def test_decay_gates_closed_forms():
+    """g = -5 sigmoid(a), beta = sigmoid(b): values at 0 and the limits, the
+    bound g in (-5, 0), monotonicity, and sigmoid(x) + sigmoid(-x) = 1."""
+    from oracle.kda_oracle import decay_gates
+    g, beta = decay_gates(np.array([0.0, 40.0, -40.0]), np.array([0.0, 40.0, -40.0]))
+    assert g[0] == -2.5 and beta[0] == 0.5
+    assert abs(g[1] + 5.0) < 1e-15 and abs(g[2]) < 1e-16
+    assert abs(beta[1] - 1.0) < 1e-15 and beta[2] < 1e-17
+    x = np.linspace(-30, 30, 601)
+    g, beta = decay_gates(x, x)
+    assert np.all(g > -5.0) and np.all(g < 0.0) and np.all(np.diff(g) < 0)
+    gm, bm = decay_gates(-x, -x)
+    assert np.allclose(beta + bm, 1.0, atol=1e-15)
+    assert np.allclose(g + gm, -5.0, atol=1e-14)
+    # ln 3 maps to sigmoid = 3/4 exactly (up to rounding): g = -3.75
+    g, beta = decay_gates(np.log(3.0), np.log(3.0))
+    assert abs(g + 3.75) < 1e-15 and abs(beta - 0.75) < 1e-16
