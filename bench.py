@@ -15,7 +15,8 @@ multi-token decode step of speculative decoding (B=256, H=96, 4 draft tokens:
 one verify call and one commit call) in the ``verify`` object, and the prefill
 with a state checkpoint every 2048 tokens in the ``checkpoints`` object, and a
 packed serving batch (16 sequences of 512-3583 tokens, H=96, gated) in the
-``packed`` object.
+``packed`` object; the same layer with the decay and write strength given as
+logits (formed in the kernels) in the ``gates`` object.
 
 Output: ONE JSON line on stdout (progress goes to stderr).
 """
@@ -233,6 +234,39 @@ def bench_checkpoints(kda, torch, w, every, steps):
     return e0.elapsed_time(e1) / steps
 
 
+def bench_gates(kda, torch, w, steps):
+    """The prefill of ``bench_prefill`` with the decay and write strength as
+    logits (a in the io dtype in place of float32 g, b in place of beta);
+    returns ms per step."""
+    from gated_delta_rule_112_amd.inputs import make_prefill_inputs
+    dev = torch.device("cuda:0")
+    x = make_prefill_inputs(w, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed + 11)
+    a = torch.randn(x["g"].shape, generator=gen, device=dev).to(x["q"].dtype)
+    b = torch.randn(x["beta"].shape, generator=gen, device=dev)
+    del x["g"], x["beta"]
+    out = torch.empty((w.B, w.T, w.H, w.dv), dtype=x["q"].dtype, device=dev)
+    s_out = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    nws = kda.chunk_workspace_size(w.B, w.T, w.H, w.dk, w.dv, x["q"].dtype)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        kda.chunk_fwd(x["q"], x["k"], x["v"], a, b, x["s0"], gate=x["gate"], out=out,
+                      s_out=s_out, workspace=ws, logits=True, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def bench_packed(kda, torch, w, steps):
     """Prefill of a packed serving batch (kda_chunk_fwd_varlen); returns
     (ms per step, total tokens, longest length)."""
@@ -349,6 +383,7 @@ def main():
     ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-checkpoints", action="store_true")
     ap.add_argument("--no-packed", action="store_true")
+    ap.add_argument("--no-gates", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads-per-worker", type=int, default=4)
     ap.add_argument("--cpu-tokens", type=int, default=32768)
@@ -422,6 +457,17 @@ def main():
                        "overhead_vs_prefill": round(cms / ms - 1.0, 4)}
         log(f"[bench] prefill with a checkpoint every {every} tokens: {cms:.3f} ms/step")
 
+    gates = None
+    if not a.no_gates:
+        gms = bench_gates(kda, torch, w, a.steps)
+        gbytes = nbytes - w.B * w.T * w.H * w.dk * (4 - es)  # a in the io dtype, not fp32 g
+        ggbs = gbytes / (gms * 1e-3) / 1e9
+        gates = {"ms_per_step": round(gms, 4), "tokens_per_s": round(w.B * w.T / (gms * 1e-3), 1),
+                 "algorithmic_bytes_per_step": gbytes, "achieved": round(ggbs, 1),
+                 "unit": "GB/s", "peak": HBM_PEAK_GBS, "frac": round(ggbs / HBM_PEAK_GBS, 4)}
+        log(f"[bench] prefill with decay/write logits: {gms:.3f} ms/step, "
+            f"{w.B * w.T / (gms * 1e-3) / 1e6:.2f} M tok/s")
+
     packed = None
     if not a.no_packed:
         wp = WORKLOADS["packed_prefill"]
@@ -493,6 +539,7 @@ def main():
         "cpu_baseline": cpu,
         "checkpoints": checkpoints,
         "packed": packed,
+        "gates": gates,
         "decode": decode,
         "verify": verify,
     }

@@ -104,8 +104,9 @@ kda_status chunk_fwd(const void* q, const void* k, const void* v, const float* g
                      const float* norm_w, float eps, int64_t B, int64_t T, int64_t H, int dk,
                      int dv, float scale, kda_dtype io, void* workspace, size_t workspace_bytes,
                      float* ckpt, int64_t ckpt_every, const int32_t* cu, int64_t total,
-                     void* stream) {
-  if (!q || !k || !v || !g || !beta) return KDA_ERR_NULL_POINTER;
+                     const void* ga, void* stream) {
+  // ga: the log-decay logits a (g = -5 sigmoid(a)) in place of g; beta then holds logits
+  if (!q || !k || !v || (!g && !ga) || !beta) return KDA_ERR_NULL_POINTER;
   if (!o && !s_out) return KDA_ERR_NULL_POINTER;
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_BAD_DTYPE;
   if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED_DIM;
@@ -119,14 +120,16 @@ kda_status chunk_fwd(const void* q, const void* k, const void* v, const float* g
   // Tiles are moved with 16-byte accesses; beta, states and the norm weight
   // are read element by element.
   for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)g,
-                        (const void*)o, (const void*)gate})
+                        (const void*)o, (const void*)gate, ga})
     if (!aligned(p, 16)) return KDA_ERR_MISALIGNED;
   for (const void* p : {(const void*)beta, (const void*)s0, (const void*)s_out,
                         (const void*)norm_w})
     if (!aligned(p, 4)) return KDA_ERR_MISALIGNED;
 
   const int64_t es = (io == KDA_BF16) ? 2 : 4;
-  const Span sq{q, nqk * es}, sk{k, nqk * es}, sv{v, nv * es}, sg{g, nqk * 4}, sb{beta, nb * 4};
+  // the decay input: float32 g, or its logits in the io dtype
+  const Span sg = ga != nullptr ? Span{ga, nqk * es} : Span{g, nqk * 4};
+  const Span sq{q, nqk * es}, sk{k, nqk * es}, sv{v, nv * es}, sb{beta, nb * 4};
   const Span ss0{s0, ns * 4}, so{o, nv * es}, sso{s_out, ns * 4}, sgt{gate, nv * es};
   const Span sw{norm_w, (int64_t)dv * 4}, scu{cu, (B + 1) * 4};
   for (Span in : {sq, sk, sv, sg, sb, ss0, sgt, sw, sso, scu})
@@ -162,6 +165,10 @@ kda_status chunk_fwd(const void* q, const void* k, const void* v, const float* g
   }
   a.cu = cu;
   a.total = rows;
+  if (ga != nullptr) {
+    a.g = nullptr;
+    a.ga = ga;
+  }
   const hipError_t err = mfma ? kda::launch_chunk_mfma(a) : kda::launch_chunk_valu(a);
   return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
@@ -176,7 +183,17 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          int64_t H, int dk, int dv, float scale, kda_dtype io, void* workspace,
                          size_t workspace_bytes, void* stream) {
   return chunk_fwd(q, k, v, g, beta, s0, o, s_out, gate, norm_w, eps, B, T, H, dk, dv, scale, io,
-                   workspace, workspace_bytes, nullptr, 0, nullptr, 0, stream);
+                   workspace, workspace_bytes, nullptr, 0, nullptr, 0, nullptr, stream);
+}
+
+kda_status kda_chunk_fwd_gates(const void* q, const void* k, const void* v, const void* a,
+                               const float* b, const float* s0, void* o, float* s_out,
+                               const void* gate, const float* norm_w, float eps, int64_t B,
+                               int64_t T, int64_t H, int dk, int dv, float scale, kda_dtype io,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (a == nullptr) return KDA_ERR_NULL_POINTER;
+  return chunk_fwd(q, k, v, nullptr, b, s0, o, s_out, gate, norm_w, eps, B, T, H, dk, dv, scale,
+                   io, workspace, workspace_bytes, nullptr, 0, nullptr, 0, a, stream);
 }
 
 kda_status kda_chunk_fwd_checkpoints(const void* q, const void* k, const void* v,
@@ -190,7 +207,7 @@ kda_status kda_chunk_fwd_checkpoints(const void* q, const void* k, const void* v
   if (ckpt_every <= 0 || ckpt_every % 32 != 0) return KDA_ERR_BAD_SHAPE;
   if (!aligned(ckpt, 4)) return KDA_ERR_MISALIGNED;
   return chunk_fwd(q, k, v, g, beta, s0, o, s_out, gate, norm_w, eps, B, T, H, dk, dv, scale, io,
-                   workspace, workspace_bytes, ckpt, ckpt_every, nullptr, 0, stream);
+                   workspace, workspace_bytes, ckpt, ckpt_every, nullptr, 0, nullptr, stream);
 }
 
 kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
@@ -209,14 +226,19 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
   }
   return chunk_fwd(q, k, v, g, beta, s0, o, s_out, gate, norm_w, eps, N, max_len, H, dk, dv,
                    scale, io, workspace, workspace_bytes, ckpt, ckpt_every, cu_seqlens, total,
-                   stream);
+                   nullptr, stream);
 }
 
-kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
-                           const float* beta, float* state, void* o, const void* gate,
-                           const float* norm_w, float eps, int64_t B, int64_t H, int dk, int dv,
-                           float scale, kda_dtype io, void* stream) {
-  if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL_POINTER;
+}  // extern "C"
+
+namespace {
+
+// kda_decode_step, with the gates from their logits when ga is non-NULL.
+kda_status decode_step(const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, float* state, void* o, const void* gate,
+                       const float* norm_w, float eps, int64_t B, int64_t H, int dk, int dv,
+                       float scale, kda_dtype io, const void* ga, void* stream) {
+  if (!q || !k || !v || (!g && !ga) || !beta || !state || !o) return KDA_ERR_NULL_POINTER;
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_BAD_DTYPE;
   if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED_DIM;
   const int64_t nqk = prod(B, H, dk), nv = prod(B, H, dv), nb = prod(B, H);
@@ -228,13 +250,14 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
   // read element by element.
   const uintptr_t ea = (io == KDA_BF16) ? 2 : 4;
   if (!aligned(state, 16)) return KDA_ERR_MISALIGNED;
-  for (const void* p : {q, k, v, (const void*)o, gate})
+  for (const void* p : {q, k, v, (const void*)o, gate, ga})
     if (!aligned(p, ea)) return KDA_ERR_MISALIGNED;
   for (const void* p : {(const void*)g, (const void*)beta, (const void*)norm_w})
     if (!aligned(p, 4)) return KDA_ERR_MISALIGNED;
 
   const int64_t es = (io == KDA_BF16) ? 2 : 4;
-  const Span sq{q, nqk * es}, sk{k, nqk * es}, sv{v, nv * es}, sg{g, nqk * 4}, sb{beta, nb * 4};
+  const Span sg = ga != nullptr ? Span{ga, nqk * es} : Span{g, nqk * 4};
+  const Span sq{q, nqk * es}, sk{k, nqk * es}, sv{v, nv * es}, sb{beta, nb * 4};
   const Span sst{state, ns * 4}, so{o, nv * es}, sgt{gate, nv * es}, sw{norm_w, (int64_t)dv * 4};
   for (Span in : {sq, sk, sv, sg, sb, sst, sgt, sw})
     if (overlap(so, in)) return KDA_ERR_ALIAS;
@@ -243,7 +266,29 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
 
   kda::DecodeArgs a{q, k, v, g, beta, state, o, gate, norm_w, eps,
                     B, H, dk, dv, scale, io == KDA_BF16, stream};
+  a.ga = ga;
   return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, float* state, void* o, const void* gate,
+                           const float* norm_w, float eps, int64_t B, int64_t H, int dk, int dv,
+                           float scale, kda_dtype io, void* stream) {
+  return decode_step(q, k, v, g, beta, state, o, gate, norm_w, eps, B, H, dk, dv, scale, io,
+                     nullptr, stream);
+}
+
+kda_status kda_decode_step_gates(const void* q, const void* k, const void* v, const void* a,
+                                 const float* b, float* state, void* o, const void* gate,
+                                 const float* norm_w, float eps, int64_t B, int64_t H, int dk,
+                                 int dv, float scale, kda_dtype io, void* stream) {
+  if (a == nullptr) return KDA_ERR_NULL_POINTER;
+  return decode_step(q, k, v, nullptr, b, state, o, gate, norm_w, eps, B, H, dk, dv, scale, io,
+                     a, stream);
 }
 
 kda_status kda_decode_multi(const void* q, const void* k, const void* v, const float* g,

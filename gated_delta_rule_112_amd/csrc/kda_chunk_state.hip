@@ -109,7 +109,7 @@ struct SlotCfg {
   }
 };
 
-template <int DVW, int CPW, bool GATE, bool WO, bool PACKED>
+template <int DVW, int CPW, bool GATE, bool WO, bool PACKED, bool LOGITS>
 __global__ void __launch_bounds__(64 * (DVW / CPW + kLoaders), 1)
 kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restrict__ v,
                  const float* __restrict__ s_in, float* __restrict__ s_next,
@@ -117,7 +117,7 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
                  const float* __restrict__ norm_w, float eps, Seqs<PACKED> seqs, int64_t H,
                  int64_t BH,
                  int64_t x0, int64_t nseg, int64_t n_state_wg, float* __restrict__ ckpt,
-                 int64_t ckpt_every, tile::Args<PACKED> next) {
+                 int64_t ckpt_every, tile::Args<PACKED, LOGITS> next) {
   using SC = SlotCfg<DVW, GATE>;
   constexpr int kRing = SC::kRing, kLead = SC::kLead;
   constexpr int NSW = DVW / CPW;   // state wavefronts
@@ -562,7 +562,7 @@ int device_cus() {
   return cus > 0 ? cus : 256;
 }
 
-template <int DVW, int CPW, bool GATE, bool WO, bool PACKED>
+template <int DVW, int CPW, bool GATE, bool WO, bool PACKED, bool LOGITS>
 hipError_t launch_state_t(const ChunkArgs& a, Seg cur, const float* s_in, float* s_next,
                           const ChunkArgs& ab, Seg nxt, int cus) {
   constexpr int NW = DVW / CPW + kLoaders;
@@ -580,10 +580,11 @@ hipError_t launch_state_t(const ChunkArgs& a, Seg cur, const float* s_in, float*
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
   const Seqs<PACKED> seqs{a.cu, a.T, PACKED ? a.total : a.B * a.T};
   const Seqs<PACKED> seqb{ab.cu, ab.T, PACKED ? ab.total : ab.B * ab.T};
-  tile::Args<PACKED> tb{(const bf16_t*)ab.q, (const bf16_t*)ab.k, ab.g, ab.beta, nxt.recs,
-                        seqb, ab.H, BHb, nxt.x0, nxt.n > 0 ? nxt.n : 1, ab.scale};
-  hipLaunchKernelGGL((kda_state_kernel<DVW, CPW, GATE, WO, PACKED>), dim3((unsigned)nblk),
-                     dim3(64 * NW),
+  tile::Args<PACKED, LOGITS> tb{(const bf16_t*)ab.q, (const bf16_t*)ab.k, ab.g, ab.beta,
+                                (const bf16_t*)ab.ga, nxt.recs, seqb, ab.H, BHb, nxt.x0,
+                                nxt.n > 0 ? nxt.n : 1, ab.scale};
+  hipLaunchKernelGGL((kda_state_kernel<DVW, CPW, GATE, WO, PACKED, LOGITS>),
+                     dim3((unsigned)nblk), dim3(64 * NW),
                      0, (hipStream_t)a.stream, cur.recs, (const bf16_t*)a.v, s_in, s_next,
                      (bf16_t*)a.o, (const bf16_t*)a.gate, a.norm_w, a.eps, seqs, a.H, BH, cur.x0,
                      cur.n > 0 ? cur.n : 1, n_state, a.ckpt, a.ckpt_every, tb);
@@ -636,19 +637,16 @@ int64_t seg_pairs(int64_t BH, int64_t npairs, int cus, int split) {
 int64_t pairs_of(int64_t T) { return (T + rec::kP - 1) / rec::kP; }
 
 // The kernel instance for the call's workgroup layout.
-template <bool PACKED>
+template <bool PACKED, bool LOGITS>
 hipError_t launch_layout(const ChunkArgs& a, int split, Seg cur, const float* s_in,
                          float* s_next, const ChunkArgs& ab, Seg nxt, int cus) {
+#define KDA_LAUNCH(DVW, GATE, WO) \
+  launch_state_t<DVW, 32, GATE, WO, PACKED, LOGITS>(a, cur, s_in, s_next, ab, nxt, cus)
   if (a.o == nullptr)
-    return split == 2 ? launch_state_t<64, 32, false, false, PACKED>(a, cur, s_in, s_next, ab,
-                                                                    nxt, cus)
-                      : launch_state_t<128, 32, false, false, PACKED>(a, cur, s_in, s_next, ab,
-                                                                     nxt, cus);
-  if (a.gate != nullptr)
-    return launch_state_t<128, 32, true, true, PACKED>(a, cur, s_in, s_next, ab, nxt, cus);
-  if (split == 2)
-    return launch_state_t<64, 32, false, true, PACKED>(a, cur, s_in, s_next, ab, nxt, cus);
-  return launch_state_t<128, 32, false, true, PACKED>(a, cur, s_in, s_next, ab, nxt, cus);
+    return split == 2 ? KDA_LAUNCH(64, false, false) : KDA_LAUNCH(128, false, false);
+  if (a.gate != nullptr) return KDA_LAUNCH(128, true, true);
+  return split == 2 ? KDA_LAUNCH(64, false, true) : KDA_LAUNCH(128, false, true);
+#undef KDA_LAUNCH
 }
 
 }  // namespace
@@ -708,7 +706,8 @@ void for_each_group(const ChunkArgs& a, int cus, int64_t ws_half, F&& f) {
       g.q = (const bf16_t*)a.q + rows * rec::kDK;
       g.k = (const bf16_t*)a.k + rows * rec::kDK;
       g.v = (const bf16_t*)a.v + rows * rec::kDV;
-      g.g = a.g + rows * rec::kDK;
+      if (a.g != nullptr) g.g = a.g + rows * rec::kDK;
+      if (a.ga != nullptr) g.ga = (const bf16_t*)a.ga + rows * rec::kDK;
       g.beta = a.beta + rows;
       if (a.o != nullptr) g.o = (bf16_t*)a.o + rows * rec::kDV;
       if (a.gate != nullptr) g.gate = (const bf16_t*)a.gate + rows * rec::kDV;
@@ -747,6 +746,7 @@ int64_t chunk_mfma_launches(int64_t B, int64_t T, int64_t H) {
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a) {
   if (!chunk_mfma_supports(a.dk, a.dv, a.io_bf16)) return hipErrorNotSupported;
+  if (a.cu != nullptr && a.ga != nullptr) return hipErrorNotSupported;
   const int cus = device_cus();
   const int64_t half = record_half(a.B, a.T, a.H, cus);
   const int64_t np = pairs_of(a.T);
@@ -789,10 +789,14 @@ hipError_t launch_chunk_mfma(const ChunkArgs& a) {
     // 32 state columns per state wavefront: one state and one loader
     // wavefront per SIMD, each with up to 256 registers (the tile builder
     // running in the same launch needs them).
-    const hipError_t e =
-        a.cu != nullptr
-            ? launch_layout<true>(as, gs.split, cur, s_in, s_next, gb.a, nxt, cus)
-            : launch_layout<false>(as, gs.split, cur, s_in, s_next, gb.a, nxt, cus);
+    // (packed sequences take g and beta as given)
+    hipError_t e;
+    if (a.cu != nullptr)
+      e = launch_layout<true, false>(as, gs.split, cur, s_in, s_next, gb.a, nxt, cus);
+    else if (a.ga != nullptr)
+      e = launch_layout<false, true>(as, gs.split, cur, s_in, s_next, gb.a, nxt, cus);
+    else
+      e = launch_layout<false, false>(as, gs.split, cur, s_in, s_next, gb.a, nxt, cus);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -57,10 +57,11 @@ namespace tile {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// One lane's inputs of one 32-channel slab of a tile.
+// One lane's inputs of one 32-channel slab of a tile: g, or its logits.
 struct SlabIn {
   bf16x8 q, k;
   f32x4 g0, g1;
+  bf16x8 ga;
 };
 
 struct Scratch {  // per wavefront
@@ -83,9 +84,10 @@ __device__ __forceinline__ int64_t row_of(const Seqs<PACKED>& sq, int64_t b, int
 // two slabs of a line are loaded by back-to-back instructions, so that each
 // line leaves memory once (loaded a slab apart, the first half's line was
 // often gone when the second half was read).
+template <bool LOGITS>
 __device__ __forceinline__ void load_slab(SlabIn& in, bf16x8& q1, bf16x8& k1, const bf16_t* q,
-                                          const bf16_t* k, const float* g, int64_t row, int s,
-                                          int lane) {
+                                          const bf16_t* k, const float* g, const bf16_t* ga,
+                                          int64_t row, int s, int lane) {
   const int64_t off = row * rec::kDK + 32 * s + 8 * (lane / 16);
   if (s % 2 == 0) {
     in.q = __builtin_nontemporal_load((const bf16x8*)(q + off));
@@ -93,8 +95,17 @@ __device__ __forceinline__ void load_slab(SlabIn& in, bf16x8& q1, bf16x8& k1, co
     in.k = __builtin_nontemporal_load((const bf16x8*)(k + off));
     k1 = __builtin_nontemporal_load((const bf16x8*)(k + off + 32));
   }
-  in.g0 = __builtin_nontemporal_load((const f32x4*)(g + off));
-  in.g1 = __builtin_nontemporal_load((const f32x4*)(g + off + 4));
+  if constexpr (LOGITS) {
+    in.ga = __builtin_nontemporal_load((const bf16x8*)(ga + off));
+  } else {
+    in.g0 = __builtin_nontemporal_load((const f32x4*)(g + off));
+    in.g1 = __builtin_nontemporal_load((const f32x4*)(g + off + 4));
+  }
+}
+
+// sigmoid(x) with the hardware exponential and reciprocal.
+__device__ __forceinline__ float fast_sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * x));
 }
 
 // One lane's rescaled values of one slab of one tile (channels 32 s + 8 g + e).
@@ -105,11 +116,17 @@ struct SlabVals {
 // The rescaled values of one slab, and its contribution to the two
 // intra-tile products.  lv = 1 for a token of the sequence, 0 past its end
 // (then q = k = g = 0); FULL tiles skip that mask.
-template <bool FULL>
+template <bool FULL, bool LOGITS>
 __device__ __forceinline__ void slab_vals(const SlabIn& in, float lv, float scale, SlabVals& o,
                                           f32x4& acc_a, f32x4& acc_q) {
-  const float gm[8] = {in.g0[0], in.g0[1], in.g0[2], in.g0[3],
-                       in.g1[0], in.g1[1], in.g1[2], in.g1[3]};
+  float gm[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if constexpr (LOGITS)
+      gm[e] = -5.f * fast_sigmoid((float)in.ga[e]);  // the decay floor: g = -5 sigmoid(a)
+    else
+      gm[e] = e < 4 ? in.g0[e] : in.g1[e - 4];
+  }
   const float gs = FULL ? kLog2e : kLog2e * lv;
   const float qs = FULL ? scale : scale * lv;
 #pragma unroll
@@ -131,12 +148,13 @@ __device__ __forceinline__ void slab_vals(const SlabIn& in, float lv, float scal
   }
 }
 
+template <bool LOGITS>
 __device__ __forceinline__ void slab_vals_any(bool full, const SlabIn& in, float lv, float scale,
                                               SlabVals& o, f32x4& acc_a, f32x4& acc_q) {
   if (full)
-    slab_vals<true>(in, 1.f, scale, o, acc_a, acc_q);
+    slab_vals<true, LOGITS>(in, 1.f, scale, o, acc_a, acc_q);
   else
-    slab_vals<false>(in, lv, scale, o, acc_a, acc_q);
+    slab_vals<false, LOGITS>(in, lv, scale, o, acc_a, acc_q);
 }
 
 __device__ __forceinline__ f16x8 to_h8(const float (&x)[8]) {
@@ -288,12 +306,15 @@ __device__ __forceinline__ void w_slab(const f16x4 (&khT)[2], f16x4 tb, f32x4 (&
 
 // ---------------------------------------------------------------- pairs
 
-template <bool PACKED>
+// LOGITS: g and beta come as logits (ga [rows, H, dk] bfloat16, beta the
+// float32 logit of the write strength) and are formed here.
+template <bool PACKED, bool LOGITS = false>
 struct Args {
   const bf16_t* q;
   const bf16_t* k;
   const float* g;
   const float* beta;
+  const bf16_t* ga;
   unsigned char* recs;  // records of the segment, [head][pair]
   Seqs<PACKED> seqs;    // where each sequence's tokens are; seqs.T = longest length
   int64_t H, BH;
@@ -316,27 +337,28 @@ struct PairRows {
   int64_t a, b;  // element offsets of this lane's token rows (clamped into the sequence)
 };
 
-template <bool PACKED>
-__device__ __forceinline__ PairRows pair_rows(const Args<PACKED>& a, const Pos& p, int lane) {
+template <bool PACKED, bool LOGITS>
+__device__ __forceinline__ PairRows pair_rows(const Args<PACKED, LOGITS>& a, const Pos& p,
+                                              int lane) {
   const int64_t tok0 = (a.x0 + p.xl) * rec::kP + lane % 16;
   return PairRows{row_of(a.seqs, p.b, p.h, tok0, a.H),
                   row_of(a.seqs, p.b, p.h, tok0 + rec::kC, a.H)};
 }
 
-template <bool PACKED>
-__device__ __forceinline__ void load_pair_slab(PairIn& x, const Args<PACKED>& a,
+template <bool PACKED, bool LOGITS>
+__device__ __forceinline__ void load_pair_slab(PairIn& x, const Args<PACKED, LOGITS>& a,
                                                const PairRows& r, int s, int lane) {
-  load_slab(x.a, x.qa1, x.ka1, a.q, a.k, a.g, r.a, s, lane);
-  load_slab(x.b, x.qb1, x.kb1, a.q, a.k, a.g, r.b, s, lane);
+  load_slab<LOGITS>(x.a, x.qa1, x.ka1, a.q, a.k, a.g, a.ga, r.a, s, lane);
+  load_slab<LOGITS>(x.b, x.qb1, x.kb1, a.q, a.k, a.g, a.ga, r.b, s, lane);
 }
 
 // Builds pair p of head (b, h) and stores its record.  On entry `cur` holds
 // slab 0 of pair p (and the q and k of its slab 1); the next slab's inputs are always in flight while a slab
 // is built, and on return `cur` holds slab 0 of pair `pn` (the wavefront's
 // next pair, or any valid pair when there is none).
-template <bool PACKED>
-__device__ __forceinline__ void build_pair(const Args<PACKED>& a, const Pos& p, const Pos& pn,
-                                           PairIn& cur, Scratch* sm, int lane) {
+template <bool PACKED, bool LOGITS>
+__device__ __forceinline__ void build_pair(const Args<PACKED, LOGITS>& a, const Pos& p,
+                                           const Pos& pn, PairIn& cur, Scratch* sm, int lane) {
   const int t = lane % 16, lg = lane / 16;
   const int64_t tok0 = (a.x0 + p.xl) * rec::kP;
   const PairRows rows = pair_rows(a, p, lane), nrows = pair_rows(a, pn, lane);
@@ -344,7 +366,13 @@ __device__ __forceinline__ void build_pair(const Args<PACKED>& a, const Pos& p, 
   const bool fulla = tok0 + rec::kC <= T, fullb = tok0 + rec::kP <= T;
   const float lva = tok0 + t < T ? 1.f : 0.f;
   const float lvb = tok0 + rec::kC + t < T ? 1.f : 0.f;
-  const float betaa = a.beta[rows.a] * lva, betab = a.beta[rows.b] * lvb;
+  float betaa = a.beta[rows.a], betab = a.beta[rows.b];
+  if constexpr (LOGITS) {
+    betaa = fast_sigmoid(betaa);
+    betab = fast_sigmoid(betab);
+  }
+  betaa *= lva;
+  betab *= lvb;
   unsigned char* R = a.recs + ((p.b * a.H + p.h) * a.nseg + p.xl) * (int64_t)rec::kBytes;
 
   f32x4 aa = zero4(), qa = zero4(), ab = zero4(), qb = zero4(), qba = zero4(), mba = zero4();
@@ -364,7 +392,7 @@ __device__ __forceinline__ void build_pair(const Args<PACKED>& a, const Pos& p, 
     }
     // tile a: its values, then everything that needs only them
     SlabVals va;
-    slab_vals_any(fulla, cur.a, lva, a.scale, va, aa, qa);
+    slab_vals_any<LOGITS>(fulla, cur.a, lva, a.scale, va, aa, qa);
     transpose_slab(va.kh, sm, lane, khTa[s]);
     const f16x8 kba = to_h8(va.kb);  // Kb_a, token-major
     *(f16x8*)(R + rec::kQa + s * 1024 + lane * 16) = to_h8(va.qh);
@@ -375,7 +403,7 @@ __device__ __forceinline__ void build_pair(const Args<PACKED>& a, const Pos& p, 
     }
     // tile b, and the cross terms
     SlabVals vb;
-    slab_vals_any(fullb, cur.b, lvb, a.scale, vb, ab, qb);
+    slab_vals_any<LOGITS>(fullb, cur.b, lvb, a.scale, vb, ab, qb);
     transpose_slab(vb.kh, sm, lane, khTb[s]);
     // Q_ba^T: lane (i, g) accumulates (Qh_b Kb_a^T)[i][4 g + r];
     // M = Kh_b Kb_a^T: lane (j, g) accumulates M[4 g + r][j]
@@ -439,9 +467,9 @@ __device__ __forceinline__ void build_pair(const Args<PACKED>& a, const Pos& p, 
 // head-fastest (pair w is pair w / BH of head w % BH), so that the wavefronts
 // working at one time read neighbouring heads of the same tokens, which are
 // adjacent in memory.
-template <bool PACKED>
-__device__ __forceinline__ void build_range(const Args<PACKED>& a, int64_t first, int64_t stride,
-                                            Scratch* sm, int lane) {
+template <bool PACKED, bool LOGITS>
+__device__ __forceinline__ void build_range(const Args<PACKED, LOGITS>& a, int64_t first,
+                                            int64_t stride, Scratch* sm, int lane) {
   const int64_t total = a.BH * a.nseg;
   if (first >= total) return;
   // w = xl BH + b H + h; the stride split the same way, advanced without divisions

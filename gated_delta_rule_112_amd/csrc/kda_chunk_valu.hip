@@ -13,7 +13,8 @@
 //   O    = Qhat S0 + lower(Qhat Kchk^T) Delta
 //   S_n  = Diag(e^{Gamma_n}) (S0 + Kchk^T Delta)
 // A partial last tile is padded with g = 0, beta = 0, k = q = v = 0 tokens,
-// which leave the state unchanged.
+// which leave the state unchanged.  With `ga`, g = -5 sigmoid(a) and
+// beta = sigmoid(b) are formed from their logits (a in ga, b in beta).
 //
 // One workgroup of 128 threads owns one (b, h); thread j < DV keeps column j of
 // the state (DK floats) in registers for the whole sequence, and stores it at
@@ -33,7 +34,7 @@ kda_chunk_valu_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const 
                       const float* __restrict__ s0, IO* __restrict__ o, float* __restrict__ s_out,
                       const IO* __restrict__ gate, const float* __restrict__ norm_w, float eps,
                       Seqs<PACKED> seqs, int64_t H, float scale, float* __restrict__ ckpt,
-                      int64_t ckpt_every) {
+                      int64_t ckpt_every, const IO* __restrict__ ga) {
   constexpr int C = kTile;
   __shared__ float sQh[C][DK];
   __shared__ float sKh[C][DK];
@@ -75,7 +76,7 @@ kda_chunk_valu_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const 
         const int64_t off = tok(c0 + t) * DK + c;
         qq = ld_f32(q + off);
         kk = ld_f32(k + off);
-        gg = g[off];
+        gg = ga != nullptr ? -5.f * sigmoidf_(ld_f32(ga + off)) : g[off];  // g = -5 sigmoid(a)
       }
       sQh[t][c] = qq;
       sKh[t][c] = kk;
@@ -85,7 +86,10 @@ kda_chunk_valu_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const 
       const int t = e / DV, j = e % DV;
       sV[t][j] = (t < n) ? ld_f32(v + tok(c0 + t) * DV + j) : 0.f;
     }
-    if (tid < C) sB[tid] = (tid < n) ? beta[tok(c0 + tid)] : 0.f;
+    if (tid < C) {
+      const float bt = (tid < n) ? beta[tok(c0 + tid)] : 0.f;
+      sB[tid] = (tid < n) ? (ga != nullptr ? sigmoidf_(bt) : bt) : 0.f;  // beta = sigmoid(b)
+    }
     __syncthreads();
 
     // 2. In-tile cumulative log-decay and the rescaled operands, per channel.
@@ -230,7 +234,7 @@ static hipError_t launch_valu_p(const ChunkArgs& a) {
                      dim3(kValuThreads), 0, (hipStream_t)a.stream, (const IO*)a.q, (const IO*)a.k,
                      (const IO*)a.v, a.g, a.beta, a.s0, (IO*)a.o, a.s_out, (const IO*)a.gate,
                      a.norm_w, a.eps, Seqs<PACKED>{a.cu, a.T, PACKED ? a.total : a.B * a.T}, a.H,
-                     a.scale, a.ckpt, a.ckpt_every);
+                     a.scale, a.ckpt, a.ckpt_every, (const IO*)a.ga);
   return hipGetLastError();
 }
 

@@ -55,16 +55,22 @@ __device__ __forceinline__ DecodeTok decode_load_tok(const IO* __restrict__ q,
                                                      const IO* __restrict__ v,
                                                      const float* __restrict__ g,
                                                      const float* __restrict__ beta,
-                                                     const IO* __restrict__ gate, int64_t row) {
+                                                     const IO* __restrict__ gate, int64_t row,
+                                                     const IO* __restrict__ ga) {
   const int tid = threadIdx.x;
   const int ci = tid % DK, cj = tid % DV;
   DecodeTok x;
   x.q = ld_f32(q + row * DK + ci);
   x.k = ld_f32(k + row * DK + ci);
-  x.g = g[row * DK + ci];
   x.v = ld_f32(v + row * DV + cj);
   x.gate = gate ? ld_f32(gate + row * DV + cj) : 0.f;
-  x.beta = beta[row];
+  if (ga != nullptr) {  // from logits: g = -5 sigmoid(a), beta = sigmoid(b)
+    x.g = -5.f * sigmoidf_(ld_f32(ga + row * DK + ci));
+    x.beta = sigmoidf_(beta[row]);
+  } else {
+    x.g = g[row * DK + ci];
+    x.beta = beta[row];
+  }
   return x;
 }
 
@@ -76,7 +82,7 @@ __device__ __forceinline__ void decode_load(DecodeTile<DK, DV>& t, const IO* __r
                                             const float* __restrict__ beta,
                                             const float* __restrict__ state,
                                             const IO* __restrict__ gate, int64_t bh,
-                                            int64_t row) {
+                                            int64_t row, const IO* __restrict__ ga) {
   using Sh = DecodeShape<DK, DV>;
   const int tid = threadIdx.x;
   const int cg = tid % Sh::CG, rg = tid / Sh::CG;
@@ -84,7 +90,7 @@ __device__ __forceinline__ void decode_load(DecodeTile<DK, DV>& t, const IO* __r
 #pragma unroll
   for (int m = 0; m < Sh::RPT; ++m)
     t.s[m] = __builtin_nontemporal_load((const f32x4*)(Sp + (rg + m * Sh::RG) * DV + 4 * cg));
-  t.x = decode_load_tok<DK, DV, IO>(q, k, v, g, beta, gate, row);
+  t.x = decode_load_tok<DK, DV, IO>(q, k, v, g, beta, gate, row, ga);
 }
 
 template <int DK, int DV>
@@ -199,7 +205,7 @@ kda_decode_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* 
                   const float* __restrict__ g, const float* __restrict__ beta,
                   float* __restrict__ state, IO* __restrict__ o,
                   const IO* __restrict__ gate, const float* __restrict__ norm_w,
-                  float eps, float scale, int64_t BH) {
+                  float eps, float scale, int64_t BH, const IO* __restrict__ ga) {
   __shared__ DecodeSmem<DK, DV> sm;
   const int tid = threadIdx.x;
   const bool gated = gate != nullptr;
@@ -213,14 +219,14 @@ kda_decode_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* 
     decode_one<DK, DV, IO, false>(sm, t.s, t.x, state + u * (int64_t)(DK * DV), o + u * DV,
                                   gated, wn, eps, scale);
   };
-  if (bh < BH) decode_load<DK, DV, IO>(t0, q, k, v, g, beta, state, gate, bh, bh);
+  if (bh < BH) decode_load<DK, DV, IO>(t0, q, k, v, g, beta, state, gate, bh, bh, ga);
   while (bh < BH) {
     const int64_t b1 = bh + stride;
-    if (b1 < BH) decode_load<DK, DV, IO>(t1, q, k, v, g, beta, state, gate, b1, b1);
+    if (b1 < BH) decode_load<DK, DV, IO>(t1, q, k, v, g, beta, state, gate, b1, b1, ga);
     run(t0, bh);
     if (b1 >= BH) break;
     const int64_t b2 = b1 + stride;
-    if (b2 < BH) decode_load<DK, DV, IO>(t0, q, k, v, g, beta, state, gate, b2, b2);
+    if (b2 < BH) decode_load<DK, DV, IO>(t0, q, k, v, g, beta, state, gate, b2, b2, ga);
     run(t1, b1);
     bh = b2;
   }
@@ -247,7 +253,7 @@ kda_decode_multi_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
                         const float* __restrict__ beta, float* __restrict__ state,
                         const int* __restrict__ n_commit, IO* __restrict__ o,
                         const IO* __restrict__ gate, const float* __restrict__ norm_w, float eps,
-                        float scale, int64_t B, int64_t K, int64_t H) {
+                        float scale, int64_t B, int64_t K, int64_t H, const IO* __restrict__ ga) {
   __shared__ DecodeSmem<DK, DV> sm;
   const int tid = threadIdx.x;
   const bool gated = gate != nullptr;
@@ -264,7 +270,7 @@ kda_decode_multi_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
   auto runs = [&](int64_t u) { return o != nullptr ? K : commit(u); };
   // the state and first token of u, unless u has nothing to run
   auto load = [&](DecodeTile<DK, DV>& t, int64_t u) {
-    if (runs(u) > 0) decode_load<DK, DV, IO>(t, q, k, v, g, beta, state, gate, u, row(u, 0));
+    if (runs(u) > 0) decode_load<DK, DV, IO>(t, q, k, v, g, beta, state, gate, u, row(u, 0), ga);
   };
 
   auto run = [&](DecodeTile<DK, DV>& cur, int64_t u) {
@@ -273,7 +279,7 @@ kda_decode_multi_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
     DecodeTok x = cur.x;
     for (int64_t t = 0; t < last; ++t) {
       DecodeTok xn = x;
-      if (t + 1 < last) xn = decode_load_tok<DK, DV, IO>(q, k, v, g, beta, gate, row(u, t + 1));
+      if (t + 1 < last) xn = decode_load_tok<DK, DV, IO>(q, k, v, g, beta, gate, row(u, t + 1), ga);
       decode_one<DK, DV, IO, true>(sm, cur.s, x, t + 1 == n ? Sp : nullptr,
                                    o != nullptr ? o + row(u, t) * DV : nullptr, gated, wn, eps,
                                    scale);
@@ -306,12 +312,13 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
     hipLaunchKernelGGL((kda_decode_multi_kernel<DK, DV, IO>), dim3((unsigned)mblk), dim3(Sh::NT),
                        0, (hipStream_t)a.stream, (const IO*)a.q, (const IO*)a.k, (const IO*)a.v,
                        a.g, a.beta, a.state, a.n_commit, (IO*)a.o, (const IO*)a.gate, a.norm_w,
-                       a.eps, a.scale, a.B, a.K, a.H);
+                       a.eps, a.scale, a.B, a.K, a.H, (const IO*)a.ga);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((kda_decode_kernel<DK, DV, IO>), dim3((unsigned)nblk), dim3(Sh::NT), 0,
                      (hipStream_t)a.stream, (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g,
-                     a.beta, a.state, (IO*)a.o, (const IO*)a.gate, a.norm_w, a.eps, a.scale, bhn);
+                     a.beta, a.state, (IO*)a.o, (const IO*)a.gate, a.norm_w, a.eps, a.scale, bhn,
+                     (const IO*)a.ga);
   return hipGetLastError();
 }
 

@@ -33,6 +33,9 @@ struct ChunkArgs {
   // (device array of B + 1 entries), T the longest; NULL for B x T.
   const int* cu = nullptr;
   int64_t total = 0;
+  // Gates from logits: ga [rows, H, dk] in the io dtype holds a, and g = -5 sigmoid(a);
+  // beta then holds the logit b of the write strength, beta = sigmoid(b).  NULL: g, beta given.
+  const void* ga = nullptr;
 };
 
 struct DecodeArgs {
@@ -53,6 +56,7 @@ struct DecodeArgs {
   void* stream;
   int64_t K = 0;                   // > 0: K tokens per sequence ([B, K, H, ..] inputs)
   const int* n_commit = nullptr;   // with K > 0: tokens to commit per sequence, or NULL = K
+  const void* ga = nullptr;        // gates from logits, as in ChunkArgs
 };
 
 struct NormArgs {

@@ -129,6 +129,28 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk, int
                                     kda_dtype io);
 
 /*
+ * kda_chunk_fwd_gates -- kda_chunk_fwd with the decay and the write strength
+ * formed in the kernels from their logits.
+ *
+ * "Kimi K3: Engineering a 2.8 Trillion Parameter Frontier", section
+ * "Dimension 1": the log-decay is bounded below by a scaled sigmoid,
+ * g = -5 sigmoid(a), so every retention factor exceeds e^-5; the write strength
+ * is beta = sigmoid(b).  Reading a in the io dtype instead of float32 g halves
+ * the largest input (bfloat16: 2 dk instead of 4 dk bytes per token and head).
+ *
+ *   a  [B, T, H, dk]  io dtype   log-decay logits (in place of g)
+ *   b  [B, T, H]      float32    write-strength logits (in place of beta)
+ * Every other argument, alignment (a: 16 bytes) and aliasing rule as in
+ * kda_chunk_fwd, including its workspace.  q and k are used as given (the
+ * method expects them L2-normalised per head).
+ */
+kda_status kda_chunk_fwd_gates(const void* q, const void* k, const void* v, const void* a,
+                               const float* b, const float* s0, void* o, float* s_out,
+                               const void* gate, const float* norm_w, float eps, int64_t B,
+                               int64_t T, int64_t H, int dk, int dv, float scale, kda_dtype io,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * kda_chunk_fwd_checkpoints -- kda_chunk_fwd that also keeps the state at
  * regular points of the sequence, for prefix caching (a fixed-size state per
  * cached prefix instead of a cache that grows with it; "Kimi K3 Architecture
@@ -212,6 +234,16 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            void* o, const void* gate, const float* norm_w, float eps,
                            int64_t B, int64_t H, int dk, int dv,
                            float scale, kda_dtype io, void* stream);
+
+/*
+ * kda_decode_step_gates -- kda_decode_step with g = -5 sigmoid(a) and
+ * beta = sigmoid(b) formed in the kernel: a [B, H, dk] in the io dtype in place
+ * of g, b [B, H] float32 in place of beta; everything else as kda_decode_step.
+ */
+kda_status kda_decode_step_gates(const void* q, const void* k, const void* v, const void* a,
+                                 const float* b, float* state, void* o, const void* gate,
+                                 const float* norm_w, float eps, int64_t B, int64_t H, int dk,
+                                 int dv, float scale, kda_dtype io, void* stream);
 
 /*
  * kda_decode_multi -- K consecutive tokens per sequence against the resident
