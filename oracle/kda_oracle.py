@@ -60,6 +60,7 @@ __all__ = [
     "gate_rmsnorm",
     "kda_chunked",
     "decay_gates",
+    "l2_normalize",
 ]
 
 
@@ -183,3 +184,16 @@ def decay_gates(a, b):
     """
     a, b = _f64(a), _f64(b)
     return -5.0 / (1.0 + np.exp(-a)), 1.0 / (1.0 + np.exp(-b))
+
+
+def l2_normalize(x, eps=1e-12):
+    """x / max(||x||, eps) over the last axis (one head's dk vector).
+
+    The method's keys (and queries) are unit vectors per head: the erase
+    replaces what the state predicts for a unit key ("Kimi K3 Architecture
+    Explained ...", section "Token mixing"), and the workloads normalise q and
+    k this way.  eps only keeps a zero vector at zero.
+    """
+    x = _f64(x)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(n, eps)

@@ -378,3 +378,17 @@ def test_decay_gates_closed_forms():
     # ln 3 maps to sigmoid = 3/4 exactly (up to rounding): g = -3.75
     g, beta = decay_gates(np.log(3.0), np.log(3.0))
     assert abs(g + 3.75) < 1e-15 and abs(beta - 0.75) < 1e-16
+
+
+def test_l2_normalize_pins():
+    """Unit norm, direction kept, a zero vector stays zero, scale invariance,
+    and the 3-4-5 triangle exactly."""
+    from oracle.kda_oracle import l2_normalize
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((5, 7, 16))
+    y = l2_normalize(x)
+    assert np.allclose(np.linalg.norm(y, axis=-1), 1.0, atol=1e-15)
+    assert np.allclose(np.sum(y * x, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-14)
+    assert np.allclose(l2_normalize(3.7 * x), y, atol=1e-15)
+    assert np.all(l2_normalize(np.zeros((2, 4))) == 0.0)
+    assert np.array_equal(l2_normalize(np.array([3.0, 4.0])), np.array([0.6, 0.8]))
