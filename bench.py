@@ -15,8 +15,9 @@ multi-token decode step of speculative decoding (B=256, H=96, 4 draft tokens:
 one verify call and one commit call) in the ``verify`` object, and the prefill
 with a state checkpoint every 2048 tokens in the ``checkpoints`` object, and a
 packed serving batch (16 sequences of 512-3583 tokens, H=96, gated) in the
-``packed`` object; the same layer with the decay and write strength given as
-logits (formed in the kernels) in the ``gates`` object.
+``packed`` object; the same layer from the raw projections (q, k normalised
+and the decay and write strength formed from logits in the kernels) in the
+``prologue`` object.
 
 Output: ONE JSON line on stdout (progress goes to stderr).
 """
@@ -234,8 +235,9 @@ def bench_checkpoints(kda, torch, w, every, steps):
     return e0.elapsed_time(e1) / steps
 
 
-def bench_gates(kda, torch, w, steps):
-    """The prefill of ``bench_prefill`` with the decay and write strength as
+def bench_prologue(kda, torch, w, steps):
+    """The prefill of ``bench_prefill`` from the raw projections: q and k
+    unnormalised (normalised in the kernels), the decay and write strength as
     logits (a in the io dtype in place of float32 g, b in place of beta);
     returns ms per step."""
     from gated_delta_rule_112_amd.inputs import make_prefill_inputs
@@ -246,6 +248,8 @@ def bench_gates(kda, torch, w, steps):
     a = torch.randn(x["g"].shape, generator=gen, device=dev).to(x["q"].dtype)
     b = torch.randn(x["beta"].shape, generator=gen, device=dev)
     del x["g"], x["beta"]
+    x["q"] = (3.0 * x["q"].float()).to(x["v"].dtype)  # raw projections: not unit vectors
+    x["k"] = (0.5 * x["k"].float()).to(x["v"].dtype)
     out = torch.empty((w.B, w.T, w.H, w.dv), dtype=x["q"].dtype, device=dev)
     s_out = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
     nws = kda.chunk_workspace_size(w.B, w.T, w.H, w.dk, w.dv, x["q"].dtype)
@@ -254,7 +258,7 @@ def bench_gates(kda, torch, w, steps):
 
     def step():
         kda.chunk_fwd(x["q"], x["k"], x["v"], a, b, x["s0"], gate=x["gate"], out=out,
-                      s_out=s_out, workspace=ws, logits=True, stream=stream)
+                      s_out=s_out, workspace=ws, prologue=True, stream=stream)
 
     step()
     torch.cuda.synchronize()
@@ -383,7 +387,7 @@ def main():
     ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-checkpoints", action="store_true")
     ap.add_argument("--no-packed", action="store_true")
-    ap.add_argument("--no-gates", action="store_true")
+    ap.add_argument("--no-prologue", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads-per-worker", type=int, default=4)
     ap.add_argument("--cpu-tokens", type=int, default=32768)
@@ -457,15 +461,15 @@ def main():
                        "overhead_vs_prefill": round(cms / ms - 1.0, 4)}
         log(f"[bench] prefill with a checkpoint every {every} tokens: {cms:.3f} ms/step")
 
-    gates = None
-    if not a.no_gates:
-        gms = bench_gates(kda, torch, w, a.steps)
+    prologue = None
+    if not a.no_prologue:
+        gms = bench_prologue(kda, torch, w, a.steps)
         gbytes = nbytes - w.B * w.T * w.H * w.dk * (4 - es)  # a in the io dtype, not fp32 g
         ggbs = gbytes / (gms * 1e-3) / 1e9
-        gates = {"ms_per_step": round(gms, 4), "tokens_per_s": round(w.B * w.T / (gms * 1e-3), 1),
+        prologue = {"ms_per_step": round(gms, 4), "tokens_per_s": round(w.B * w.T / (gms * 1e-3), 1),
                  "algorithmic_bytes_per_step": gbytes, "achieved": round(ggbs, 1),
                  "unit": "GB/s", "peak": HBM_PEAK_GBS, "frac": round(ggbs / HBM_PEAK_GBS, 4)}
-        log(f"[bench] prefill with decay/write logits: {gms:.3f} ms/step, "
+        log(f"[bench] prefill from raw q, k and gate logits: {gms:.3f} ms/step, "
             f"{w.B * w.T / (gms * 1e-3) / 1e6:.2f} M tok/s")
 
     packed = None
@@ -539,7 +543,7 @@ def main():
         "cpu_baseline": cpu,
         "checkpoints": checkpoints,
         "packed": packed,
-        "gates": gates,
+        "prologue": prologue,
         "decode": decode,
         "verify": verify,
     }

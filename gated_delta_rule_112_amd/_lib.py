@@ -62,10 +62,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32,
                                     i64, i64, ci, ci, f32, ci, vp]
     lib.kda_decode_step.restype = ci
-    lib.kda_chunk_fwd_gates.argtypes = lib.kda_chunk_fwd.argtypes
-    lib.kda_chunk_fwd_gates.restype = ci
-    lib.kda_decode_step_gates.argtypes = lib.kda_decode_step.argtypes
-    lib.kda_decode_step_gates.restype = ci
+    lib.kda_chunk_fwd_prologue.argtypes = lib.kda_chunk_fwd.argtypes
+    lib.kda_chunk_fwd_prologue.restype = ci
+    lib.kda_decode_step_prologue.argtypes = lib.kda_decode_step.argtypes
+    lib.kda_decode_step_prologue.restype = ci
     lib.kda_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32,
                                      i64, i64, i64, ci, ci, f32, ci, vp]
     lib.kda_decode_multi.restype = ci
@@ -112,19 +112,20 @@ def _stream(device, stream):
 
 def chunk_fwd(q, k, v, g, beta, s0=None, *, scale: float = 1.0, gate=None, norm_w=None,
               eps: float = 1e-6, output: bool = True, final_state: bool = True,
-              out=None, s_out=None, workspace=None, logits: bool = False,
+              out=None, s_out=None, workspace=None, prologue: bool = False,
               stream=None) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
     """Prefill over [B, T, H, *] tensors; returns (o or y, final state).
 
     ``output=False`` computes the final state only; ``s_out`` may be ``s0``
     for an in-place state update.  ``workspace`` (a uint8 CUDA tensor of at
     least ``chunk_workspace_size(...)`` bytes) is allocated per call if absent.
-    ``logits=True``: ``g`` holds the log-decay logits a (io dtype) and ``beta``
-    the write-strength logits b; the kernels form g = -5 sigmoid(a) and
+    ``prologue=True``: q and k are the raw projections (normalised in the
+    kernels), ``g`` holds the log-decay logits a (io dtype) and ``beta`` the
+    write-strength logits b; the kernels form g = -5 sigmoid(a) and
     beta = sigmoid(b).
     """
     o, s, _ = _chunk_fwd(q, k, v, g, beta, s0, scale, gate, norm_w, eps, output, final_state,
-                         out, s_out, workspace, 0, None, stream, logits)
+                         out, s_out, workspace, 0, None, stream, prologue)
     return o, s
 
 
@@ -209,7 +210,7 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, max_len: int, s0=None, *,
 
 
 def _chunk_fwd(q, k, v, g, beta, s0, scale, gate, norm_w, eps, output, final_state, out, s_out,
-               workspace, every, ckpt, stream, logits=False):
+               workspace, every, ckpt, stream, prologue=False):
     lib = load_library()
     if q.device.type != "cuda":
         raise ValueError("kda ops need CUDA (HIP) tensors")
@@ -222,7 +223,7 @@ def _chunk_fwd(q, k, v, g, beta, s0, scale, gate, norm_w, eps, output, final_sta
     _need(q, "q", io, (B, T, H, dk), dev)
     _need(k, "k", io, (B, T, H, dk), dev)
     _need(v, "v", io, (B, T, H, dv), dev)
-    _need(g, "a" if logits else "g", io if logits else torch.float32, (B, T, H, dk), dev)
+    _need(g, "a" if prologue else "g", io if prologue else torch.float32, (B, T, H, dk), dev)
     _need(beta, "beta", torch.float32, (B, T, H), dev)
     if s0 is not None:
         _need(s0, "s0", torch.float32, (B, H, dk, dv), dev)
@@ -257,8 +258,9 @@ def _chunk_fwd(q, k, v, g, beta, s0, scale, gate, norm_w, eps, output, final_sta
             ckpt = torch.empty((B, nck, H, dk, dv), dtype=torch.float32, device=dev)
         else:
             _need(ckpt, "ckpt", torch.float32, (B, nck, H, dk, dv), dev)
-    if logits:
-        _check(lib, "kda_chunk_fwd_gates", lib.kda_chunk_fwd_gates(*args, _stream(dev, stream)))
+    if prologue:
+        st = lib.kda_chunk_fwd_prologue(*args, _stream(dev, stream))
+        _check(lib, "kda_chunk_fwd_prologue", st)
         return out, s_out, None
     if nck == 0:  # no checkpoint falls inside the sequence
         _check(lib, "kda_chunk_fwd", lib.kda_chunk_fwd(*args, _stream(dev, stream)))
@@ -269,9 +271,10 @@ def _chunk_fwd(q, k, v, g, beta, s0, scale, gate, norm_w, eps, output, final_sta
 
 
 def decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, gate=None, norm_w=None,
-                eps: float = 1e-6, out=None, logits: bool = False, stream=None) -> torch.Tensor:
+                eps: float = 1e-6, out=None, prologue: bool = False, stream=None) -> torch.Tensor:
     """One token per (b, h) against ``state`` [B, H, dk, dv] (updated in place); returns o.
-    ``logits=True``: ``g`` and ``beta`` hold the logits a (io dtype) and b, as in chunk_fwd."""
+    ``prologue=True``: raw q, k and the logits a (io dtype) and b in g and beta, as in
+    chunk_fwd."""
     lib = load_library()
     if q.device.type != "cuda":
         raise ValueError("kda ops need CUDA (HIP) tensors")
@@ -284,7 +287,7 @@ def decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, gate=None, norm_
     _need(q, "q", io, (B, H, dk), dev)
     _need(k, "k", io, (B, H, dk), dev)
     _need(v, "v", io, (B, H, dv), dev)
-    _need(g, "a" if logits else "g", io if logits else torch.float32, (B, H, dk), dev)
+    _need(g, "a" if prologue else "g", io if prologue else torch.float32, (B, H, dk), dev)
     _need(beta, "beta", torch.float32, (B, H), dev)
     _need(state, "state", torch.float32, (B, H, dk, dv), dev)
     if gate is not None:
@@ -295,10 +298,10 @@ def decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, gate=None, norm_
         out = torch.empty((B, H, dv), dtype=io, device=dev)
     else:
         _need(out, "out", io, (B, H, dv), dev)
-    fn = lib.kda_decode_step_gates if logits else lib.kda_decode_step
+    fn = lib.kda_decode_step_prologue if prologue else lib.kda_decode_step
     st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out), _ptr(gate),
             _ptr(norm_w), float(eps), B, H, dk, dv, float(scale), _IO[io], _stream(dev, stream))
-    _check(lib, "kda_decode_step_gates" if logits else "kda_decode_step", st)
+    _check(lib, "kda_decode_step_prologue" if prologue else "kda_decode_step", st)
     return out
 
 

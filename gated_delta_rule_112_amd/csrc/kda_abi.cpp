@@ -105,7 +105,8 @@ kda_status chunk_fwd(const void* q, const void* k, const void* v, const float* g
                      int dv, float scale, kda_dtype io, void* workspace, size_t workspace_bytes,
                      float* ckpt, int64_t ckpt_every, const int32_t* cu, int64_t total,
                      const void* ga, void* stream) {
-  // ga: the log-decay logits a (g = -5 sigmoid(a)) in place of g; beta then holds logits
+  // ga: the log-decay logits a (g = -5 sigmoid(a)) in place of g; beta then holds logits,
+  // and q, k are L2-normalised in the kernels
   if (!q || !k || !v || (!g && !ga) || !beta) return KDA_ERR_NULL_POINTER;
   if (!o && !s_out) return KDA_ERR_NULL_POINTER;
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_BAD_DTYPE;
@@ -186,11 +187,12 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                    workspace, workspace_bytes, nullptr, 0, nullptr, 0, nullptr, stream);
 }
 
-kda_status kda_chunk_fwd_gates(const void* q, const void* k, const void* v, const void* a,
-                               const float* b, const float* s0, void* o, float* s_out,
-                               const void* gate, const float* norm_w, float eps, int64_t B,
-                               int64_t T, int64_t H, int dk, int dv, float scale, kda_dtype io,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+kda_status kda_chunk_fwd_prologue(const void* q, const void* k, const void* v, const void* a,
+                                  const float* b, const float* s0, void* o, float* s_out,
+                                  const void* gate, const float* norm_w, float eps, int64_t B,
+                                  int64_t T, int64_t H, int dk, int dv, float scale,
+                                  kda_dtype io, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
   if (a == nullptr) return KDA_ERR_NULL_POINTER;
   return chunk_fwd(q, k, v, nullptr, b, s0, o, s_out, gate, norm_w, eps, B, T, H, dk, dv, scale,
                    io, workspace, workspace_bytes, nullptr, 0, nullptr, 0, a, stream);
@@ -233,7 +235,8 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
 
 namespace {
 
-// kda_decode_step, with the gates from their logits when ga is non-NULL.
+// kda_decode_step, with the prologue (q, k normalised, gates from their logits)
+// when ga is non-NULL.
 kda_status decode_step(const void* q, const void* k, const void* v, const float* g,
                        const float* beta, float* state, void* o, const void* gate,
                        const float* norm_w, float eps, int64_t B, int64_t H, int dk, int dv,
@@ -282,10 +285,11 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
                      nullptr, stream);
 }
 
-kda_status kda_decode_step_gates(const void* q, const void* k, const void* v, const void* a,
-                                 const float* b, float* state, void* o, const void* gate,
-                                 const float* norm_w, float eps, int64_t B, int64_t H, int dk,
-                                 int dv, float scale, kda_dtype io, void* stream) {
+kda_status kda_decode_step_prologue(const void* q, const void* k, const void* v,
+                                    const void* a, const float* b, float* state, void* o,
+                                    const void* gate, const float* norm_w, float eps, int64_t B,
+                                    int64_t H, int dk, int dv, float scale, kda_dtype io,
+                                    void* stream) {
   if (a == nullptr) return KDA_ERR_NULL_POINTER;
   return decode_step(q, k, v, nullptr, b, state, o, gate, norm_w, eps, B, H, dk, dv, scale, io,
                      a, stream);

@@ -40,7 +40,12 @@
 //   [T_b | P], [Q_ba | Aqk_b]
 //                [lane][8] f16               lane (i, g): X[i][4 g + e] (e < 4),
 //                                                         Y[i][4 g + e - 4] (e >= 4)
-// (the last two are the A and B operands of 32-deep products:
+//   norms        [2][16] f32                 1/|q_a|, 1/|q_b| per token, when q and k are
+//                                            normalised in the kernels (else unused; the key
+//                                            norms are then folded into T, W and P, whose rows
+//                                            carry 1/|k|, so that D' = Diag(1/|k|) D is what the
+//                                            state pass forms)
+// (the [T_b | P] and [Q_ba | Aqk_b] blocks are the A and B operands of 32-deep products:
 // D_b = [T_b | P] [V_b ; D_a] and O_b^T = ... + [D_a ; D_b]^T [Q_ba | Aqk_b]^T)
 // where chan(b, p) = 32 (b / 2) + 8 (p / 4) + 4 (b % 2) + p % 4 is the key
 // channel held in row p of state block b.  The state pass keeps its state
@@ -69,7 +74,8 @@ constexpr int kTa = 25088;
 constexpr int kAa = 25600;
 constexpr int kTbP = 26112;
 constexpr int kQbaAb = 27136;
-constexpr int kBytes = 28160;  // a multiple of 256
+constexpr int kNorm = 28160;   // with q and k normalised in the kernels: 1/|q| per token
+constexpr int kBytes = 28416;  // record stride, a multiple of 256
 
 __host__ __device__ constexpr int chan(int b, int p) {
   return 32 * (b / 2) + 8 * (p / 4) + 4 * (b % 2) + p % 4;

@@ -194,7 +194,9 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
       const int c = blk * 64 + lane;
       if (blk < SC::kRecBlocks) {
         kind[i] = 0;
-        loff[i] = 16u * (unsigned)(c < rec::kBytes / 16 ? c : c - 64);
+        // record bytes to copy: the norm area only when q and k are normalised here
+        constexpr int kRead = LOGITS ? rec::kBytes : rec::kNorm;
+        loff[i] = 16u * (unsigned)(c < kRead / 16 ? c : c - 64);
         lrow[i] = lcol[i] = 0;
       } else {
         int q = (blk < SC::kSlot / 1024 ? blk - SC::kRecBlocks : blk - SC::kSlot / 1024) * 64 + lane;
@@ -462,6 +464,14 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- O_a^T, O_b^T (lane (t, g): O[t][4 g + r])
+    // With q and k normalised in the kernels, D above is D' = Diag(1/|k|) D
+    // (the record's T, W and P rows carry 1/|k|), which is what the raw-key
+    // factors Kb, Aqk and Q_ba take, and each output row takes 1/|q| of its token.
+    float rqa = 1.f, rqb = 1.f;
+    if constexpr (LOGITS) {
+      rqa = ((const float*)(Rs + rec::kNorm))[lc];
+      rqb = ((const float*)(Rs + rec::kNorm))[16 + lc];
+    }
     f32x4 Oa[NCB], Ob[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
@@ -473,6 +483,10 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
       }
       Oa[cb] = mma32h(dab[cb], aa8, x);     // + D_a^T Aqk_a^T (k-values 4..7 of aa8 are zero)
       Ob[cb] = mma32h(dab[cb], qbaab, y);   // + D_a^T Q_ba^T + D_b^T Aqk_b^T
+      if constexpr (LOGITS) {  // the raw-query rows, normalised
+        Oa[cb] *= rqa;
+        Ob[cb] *= rqb;
+      }
     }
     if constexpr (GATE) {
       float pa = 0.f, pb = 0.f;

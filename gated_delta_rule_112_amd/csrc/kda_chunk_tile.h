@@ -68,6 +68,7 @@ struct Scratch {  // per wavefront
   f16x4 tr[2][64];  // staging of the transposes, [half slab][lane]
   float a[16][20];  // -A = -strict_lower(Diag(beta) Kh Kc^T), row-major, padded rows
   float beta[16];
+  float rk[16];     // 1/|k| per token of the tile being finished (keys normalised here)
   float en_a[rec::kDK];  // E_a of the pair being built, per key channel
 };
 
@@ -116,9 +117,10 @@ struct SlabVals {
 // The rescaled values of one slab, and its contribution to the two
 // intra-tile products.  lv = 1 for a token of the sequence, 0 past its end
 // (then q = k = g = 0); FULL tiles skip that mask.
+// With LOGITS, nq and nk also accumulate this lane's part of |q|^2 and |k|^2.
 template <bool FULL, bool LOGITS>
 __device__ __forceinline__ void slab_vals(const SlabIn& in, float lv, float scale, SlabVals& o,
-                                          f32x4& acc_a, f32x4& acc_q) {
+                                          f32x4& acc_a, f32x4& acc_q, float& nq, float& nk) {
   float gm[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -136,9 +138,14 @@ __device__ __forceinline__ void slab_vals(const SlabIn& in, float lv, float scal
     const float ieg = __builtin_amdgcn_exp2f(-gl);   // e^-G   <  e^80
     o.en[e] = row_bcast<15>(eg);                     // e^G_15 of this channel
     const float kf = FULL ? (float)in.k[e] : (float)in.k[e] * lv;
+    const float qf = (float)in.q[e];
+    if constexpr (LOGITS) {
+      nq = fmaf(qf, qf, nq);
+      nk = fmaf(kf, kf, nk);
+    }
     o.kh[e] = kf * eg;
     o.kc[e] = kf * ieg;
-    o.qh[e] = (float)in.q[e] * qs * eg;
+    o.qh[e] = qf * qs * eg;
     o.kb[e] = o.kc[e] * o.en[e];  // k e^(G_15 - G_t) <= |k|
   }
 #pragma unroll
@@ -150,11 +157,12 @@ __device__ __forceinline__ void slab_vals(const SlabIn& in, float lv, float scal
 
 template <bool LOGITS>
 __device__ __forceinline__ void slab_vals_any(bool full, const SlabIn& in, float lv, float scale,
-                                              SlabVals& o, f32x4& acc_a, f32x4& acc_q) {
+                                              SlabVals& o, f32x4& acc_a, f32x4& acc_q, float& nq,
+                                              float& nk) {
   if (full)
-    slab_vals<true, LOGITS>(in, 1.f, scale, o, acc_a, acc_q);
+    slab_vals<true, LOGITS>(in, 1.f, scale, o, acc_a, acc_q, nq, nk);
   else
-    slab_vals<false, LOGITS>(in, lv, scale, o, acc_a, acc_q);
+    slab_vals<false, LOGITS>(in, lv, scale, o, acc_a, acc_q, nq, nk);
 }
 
 __device__ __forceinline__ f16x8 to_h8(const float (&x)[8]) {
@@ -265,14 +273,23 @@ __device__ __forceinline__ void forward_sub(float (&y)[4], const f32x4 (&an)[4])
 // From the intra-tile products summed over all slabs: the causal masks, the
 // solve and T.  bt = beta of this lane's token (0 past the sequence end).
 // Returns this lane's T image (lane (i, g): T[i][4 g + e]) and Aqk image.
-__device__ __forceinline__ void finish(f32x4 acc_a, f32x4 acc_q, float bt, Scratch* sm, int lane,
-                                       f16x4& tb, f16x4& aq) {
+// NORM: the keys are normalised here, rkt = 1/|k| of this lane's token and
+// sm->rk holds it for every token of the tile.  A takes the norms of its row
+// and column (the products were formed from the raw keys); tb receives
+// Diag(1/|k|) T and tw Diag(1/|k|) T Diag(1/|k|), the factor that turns the raw
+// keys into Diag(1/|k|) W, so that the state pass computes D' = Diag(1/|k|) D,
+// the operand the raw keys Kb and Kc need, with no extra step.
+template <bool NORM>
+__device__ __forceinline__ void finish(f32x4 acc_a, f32x4 acc_q, float bt, float rkt,
+                                       Scratch* sm, int lane, f16x4& tb, f16x4& aq, f16x4& tw) {
   const int t = lane % 16, lg = lane / 16;
+  f32x4 rkj = {1.f, 1.f, 1.f, 1.f};  // 1/|k| of columns 4 g + r
+  if constexpr (NORM) rkj = ds_read16(lds_addr(&sm->rk[4 * lg]));
   f32x4 am;  // -A; selects: masked entries may be huge products of e^-G
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int j = 4 * lg + r;
-    am[r] = (j < t) ? -bt * acc_a[r] : 0.f;
+    am[r] = (j < t) ? -bt * (NORM ? rkt * rkj[r] : 1.f) * acc_a[r] : 0.f;
     aq[r] = (f16)((j <= t) ? acc_q[r] : 0.f);
   }
   const unsigned arow_addr = lds_addr(&sm->a[t][0]);
@@ -294,7 +311,15 @@ __device__ __forceinline__ void finish(f32x4 acc_a, f32x4 acc_q, float bt, Scrat
 #pragma unroll
   for (int e = 0; e < 4; ++e) y[e] = (t == 4 * lg + e) ? 1.f : 0.f;
   forward_sub(y, arow);
-  tb = f16x4{(f16)(y[0] * bj[0]), (f16)(y[1] * bj[1]), (f16)(y[2] * bj[2]), (f16)(y[3] * bj[3])};
+  if constexpr (NORM) {
+    tb = f16x4{(f16)(y[0] * bj[0] * rkt), (f16)(y[1] * bj[1] * rkt), (f16)(y[2] * bj[2] * rkt),
+               (f16)(y[3] * bj[3] * rkt)};
+    tw = f16x4{(f16)(y[0] * bj[0] * rkt * rkj[0]), (f16)(y[1] * bj[1] * rkt * rkj[1]),
+               (f16)(y[2] * bj[2] * rkt * rkj[2]), (f16)(y[3] * bj[3] * rkt * rkj[3])};
+  } else {
+    tb = f16x4{(f16)(y[0] * bj[0]), (f16)(y[1] * bj[1]), (f16)(y[2] * bj[2]), (f16)(y[3] * bj[3])};
+    tw = tb;
+  }
 }
 
 // W^T blocks 2s, 2s+1 = Kh^T T^T: lane (i, g) gets -W[i][32 s + 8 g + e],
@@ -377,6 +402,7 @@ __device__ __forceinline__ void build_pair(const Args<PACKED, LOGITS>& a, const 
 
   f32x4 aa = zero4(), qa = zero4(), ab = zero4(), qb = zero4(), qba = zero4(), mba = zero4();
   f16x4 khTa[4][2], khTb[4][2];
+  float nqa = 0.f, nka = 0.f, nqb = 0.f, nkb = 0.f;  // this lane's part of |q|^2, |k|^2
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     PairIn nxt;
@@ -392,7 +418,7 @@ __device__ __forceinline__ void build_pair(const Args<PACKED, LOGITS>& a, const 
     }
     // tile a: its values, then everything that needs only them
     SlabVals va;
-    slab_vals_any<LOGITS>(fulla, cur.a, lva, a.scale, va, aa, qa);
+    slab_vals_any<LOGITS>(fulla, cur.a, lva, a.scale, va, aa, qa, nqa, nka);
     transpose_slab(va.kh, sm, lane, khTa[s]);
     const f16x8 kba = to_h8(va.kb);  // Kb_a, token-major
     *(f16x8*)(R + rec::kQa + s * 1024 + lane * 16) = to_h8(va.qh);
@@ -403,7 +429,7 @@ __device__ __forceinline__ void build_pair(const Args<PACKED, LOGITS>& a, const 
     }
     // tile b, and the cross terms
     SlabVals vb;
-    slab_vals_any<LOGITS>(fullb, cur.b, lvb, a.scale, vb, ab, qb);
+    slab_vals_any<LOGITS>(fullb, cur.b, lvb, a.scale, vb, ab, qb, nqb, nkb);
     transpose_slab(vb.kh, sm, lane, khTb[s]);
     // Q_ba^T: lane (i, g) accumulates (Qh_b Kb_a^T)[i][4 g + r];
     // M = Kh_b Kb_a^T: lane (j, g) accumulates M[4 g + r][j]
@@ -431,25 +457,52 @@ __device__ __forceinline__ void build_pair(const Args<PACKED, LOGITS>& a, const 
     cur = nxt;
   }
 
-  f16x4 ta, aqa, tb, aqb;
-  finish(aa, qa, betaa, sm, lane, ta, aqa);
+  // 1/|q|, 1/|k| per token: the four lanes of a token hold a quarter each
+  float rqa = 1.f, rka = 1.f, rqb = 1.f, rkb = 1.f;
+  if constexpr (LOGITS) {
+    nqa += __shfl_xor(nqa, 16);
+    nka += __shfl_xor(nka, 16);
+    nqb += __shfl_xor(nqb, 16);
+    nkb += __shfl_xor(nkb, 16);
+    nqa += __shfl_xor(nqa, 32);
+    nka += __shfl_xor(nka, 32);
+    nqb += __shfl_xor(nqb, 32);
+    nkb += __shfl_xor(nkb, 32);
+    rqa = rsqrtf(fmaxf(nqa, 1e-24f));
+    rka = rsqrtf(fmaxf(nka, 1e-24f));
+    rqb = rsqrtf(fmaxf(nqb, 1e-24f));
+    rkb = rsqrtf(fmaxf(nkb, 1e-24f));
+    if (lg == 0) {
+      float* nr = (float*)(R + rec::kNorm);
+      nr[t] = rqa;
+      nr[16 + t] = rqb;
+      ds_write4(lds_addr(&sm->rk[t]), rka);
+    }
+  }
+
+  f16x4 ta, aqa, tb, aqb, twa, twb;
+  finish<LOGITS>(aa, qa, betaa, rka, sm, lane, ta, aqa, twa);
   *(f16x4*)(R + rec::kTa + lane * 8) = ta;
   *(f16x4*)(R + rec::kAa + lane * 8) = aqa;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     f32x4 w[2];
-    w_slab(khTa[s], ta, w);
+    w_slab(khTa[s], twa, w);
     *(f16x8*)(R + rec::kWa + s * 1024 + lane * 16) = cat8(to_h4(w[0]), to_h4(w[1]));
   }
-  finish(ab, qb, betab, sm, lane, tb, aqb);
+  if constexpr (LOGITS) {
+    if (lg == 0) ds_write4(lds_addr(&sm->rk[t]), rkb);
+  }
+  finish<LOGITS>(ab, qb, betab, rkb, sm, lane, tb, aqb, twb);
   // P = -W_b Kb_a^T = -T_b M, formed as (M^T T_b^T)^T: lane (i, g) gets P[i][4 g + r]
-  const f32x4 pm = -mma16h(to_h4(mba), tb, zero4());
+  // (with normalised keys, Diag(1/|k_b|) P Diag(|k_a|): it multiplies D_a' and gives D_b')
+  const f32x4 pm = -mma16h(to_h4(mba), twb, zero4());
   *(f16x8*)(R + rec::kTbP + lane * 16) = cat8(tb, to_h4(pm));
   *(f16x8*)(R + rec::kQbaAb + lane * 16) = cat8(to_h4(qba), aqb);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     f32x4 w[2];
-    w_slab(khTb[s], tb, w);
+    w_slab(khTb[s], twb, w);
     const unsigned ea = lds_addr(&sm->en_a[32 * s + 8 * lg]);
     f32x4 e0, e1;
     asm volatile(

@@ -13,8 +13,9 @@
 //   O    = Qhat S0 + lower(Qhat Kchk^T) Delta
 //   S_n  = Diag(e^{Gamma_n}) (S0 + Kchk^T Delta)
 // A partial last tile is padded with g = 0, beta = 0, k = q = v = 0 tokens,
-// which leave the state unchanged.  With `ga`, g = -5 sigmoid(a) and
-// beta = sigmoid(b) are formed from their logits (a in ga, b in beta).
+// which leave the state unchanged.  With `ga`, q and k are L2-normalised per
+// token and g = -5 sigmoid(a), beta = sigmoid(b) are formed from their logits
+// (a in ga, b in beta).
 //
 // One workgroup of 128 threads owns one (b, h); thread j < DV keeps column j of
 // the state (DK floats) in registers for the whole sequence, and stores it at
@@ -49,6 +50,7 @@ kda_chunk_valu_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const 
   __shared__ float sB[C];
   __shared__ float sEn[DK];
   __shared__ float sRms[C];
+  __shared__ float sNrm[2 * C];  // 1/|q|, 1/|k| per token (q, k normalised here)
 
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.x / H;
@@ -91,6 +93,22 @@ kda_chunk_valu_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const 
       sB[tid] = (tid < n) ? (ga != nullptr ? sigmoidf_(bt) : bt) : 0.f;  // beta = sigmoid(b)
     }
     __syncthreads();
+    if (ga != nullptr) {  // q and k L2-normalised per token
+      if (tid < 2 * C) {
+        const int t = tid % C;
+        const float* src = tid < C ? sQh[t] : sKh[t];
+        float ss = 0.f;
+        for (int c = 0; c < DK; ++c) ss = fmaf(src[c], src[c], ss);
+        sNrm[tid] = rsqrtf(fmaxf(ss, 1e-24f));
+      }
+      __syncthreads();
+      for (int e = tid; e < C * DK; e += kValuThreads) {
+        const int t = e / DK, c = e % DK;
+        sQh[t][c] *= sNrm[t];
+        sKh[t][c] *= sNrm[C + t];
+      }
+      __syncthreads();
+    }
 
     // 2. In-tile cumulative log-decay and the rescaled operands, per channel.
     for (int c = tid; c < DK; c += kValuThreads) {

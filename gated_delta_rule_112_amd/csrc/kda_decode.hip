@@ -103,7 +103,8 @@ struct DecodeSmem {
   float part[2][Sh::RG][DV];
   float u[DV];
   float red[Sh::NT];   // q_i k_i, then o_j^2
-  float qk, ss;
+  float red2[Sh::NT];  // k_i^2 (with q_i^2 in red) when q and k are normalised here
+  float qk, ss, nq, nk;
 };
 
 // One token against the state strip s.  The updated state is stored to Sp
@@ -112,13 +113,40 @@ struct DecodeSmem {
 template <int DK, int DV, typename IO, bool KEEP>
 __device__ __forceinline__ void decode_one(DecodeSmem<DK, DV>& sm,
                                            f32x4 (&s)[DecodeShape<DK, DV>::RPT],
-                                           const DecodeTok& t, float* __restrict__ Sp,
+                                           const DecodeTok& tin, float* __restrict__ Sp,
                                            IO* __restrict__ orow, bool gated, float wn,
-                                           float eps, float scale) {
+                                           float eps, float scale, bool norm) {
   using Sh = DecodeShape<DK, DV>;
   constexpr int CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT, NT = Sh::NT;
   const int tid = threadIdx.x;
   const int cg = tid % CG, rg = tid / CG;
+  DecodeTok t = tin;
+
+  // q and k L2-normalised over the dk channels (with the gates from logits).
+  if (norm) {
+    sm.red[tid] = (tid < DK) ? t.q * t.q : 0.f;
+    sm.red2[tid] = (tid < DK) ? t.k * t.k : 0.f;
+    __syncthreads();
+    if (tid < 64) {
+      float aq = 0.f, ak = 0.f;
+      for (int i = tid; i < NT; i += 64) {
+        aq += sm.red[i];
+        ak += sm.red2[i];
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        aq += __shfl_xor(aq, off);
+        ak += __shfl_xor(ak, off);
+      }
+      if (tid == 0) {
+        sm.nq = rsqrtf(fmaxf(aq, 1e-24f));
+        sm.nk = rsqrtf(fmaxf(ak, 1e-24f));
+      }
+    }
+    __syncthreads();
+    t.q *= sm.nq;
+    t.k *= sm.nk;
+  }
 
   // Per-channel factors and q . k (over the undecayed vectors).
   if (tid < DK) {
@@ -217,7 +245,7 @@ kda_decode_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* 
   int64_t bh = blockIdx.x;
   auto run = [&](DecodeTile<DK, DV>& t, int64_t u) {
     decode_one<DK, DV, IO, false>(sm, t.s, t.x, state + u * (int64_t)(DK * DV), o + u * DV,
-                                  gated, wn, eps, scale);
+                                  gated, wn, eps, scale, ga != nullptr);
   };
   if (bh < BH) decode_load<DK, DV, IO>(t0, q, k, v, g, beta, state, gate, bh, bh, ga);
   while (bh < BH) {
@@ -282,7 +310,7 @@ kda_decode_multi_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
       if (t + 1 < last) xn = decode_load_tok<DK, DV, IO>(q, k, v, g, beta, gate, row(u, t + 1), ga);
       decode_one<DK, DV, IO, true>(sm, cur.s, x, t + 1 == n ? Sp : nullptr,
                                    o != nullptr ? o + row(u, t) * DV : nullptr, gated, wn, eps,
-                                   scale);
+                                   scale, ga != nullptr);
       x = xn;
     }
   };

@@ -129,26 +129,32 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk, int
                                     kda_dtype io);
 
 /*
- * kda_chunk_fwd_gates -- kda_chunk_fwd with the decay and the write strength
- * formed in the kernels from their logits.
+ * kda_chunk_fwd_prologue -- kda_chunk_fwd from the raw projections: q and k
+ * are L2-normalised per head, and the decay and the write strength are formed
+ * from their logits, all inside the kernels.
  *
  * "Kimi K3: Engineering a 2.8 Trillion Parameter Frontier", section
  * "Dimension 1": the log-decay is bounded below by a scaled sigmoid,
  * g = -5 sigmoid(a), so every retention factor exceeds e^-5; the write strength
- * is beta = sigmoid(b).  Reading a in the io dtype instead of float32 g halves
- * the largest input (bfloat16: 2 dk instead of 4 dk bytes per token and head).
+ * is beta = sigmoid(b); "Kimi K3 Architecture Explained ...", section "Token
+ * mixing": the delta-rule write replaces what the state predicts for a unit
+ * key, so q <- q / max(|q|, 1e-12) and k likewise, per token and head.  Reading
+ * a in the io dtype instead of float32 g halves the largest input (bfloat16:
+ * 2 dk instead of 4 dk bytes per token and head), and no separate pass over
+ * q, k, g or beta is needed.
  *
- *   a  [B, T, H, dk]  io dtype   log-decay logits (in place of g)
- *   b  [B, T, H]      float32    write-strength logits (in place of beta)
+ *   q, k [B, T, H, dk]  io dtype   raw (unnormalised) queries and keys
+ *   a    [B, T, H, dk]  io dtype   log-decay logits (in place of g)
+ *   b    [B, T, H]      float32    write-strength logits (in place of beta)
  * Every other argument, alignment (a: 16 bytes) and aliasing rule as in
- * kda_chunk_fwd, including its workspace.  q and k are used as given (the
- * method expects them L2-normalised per head).
+ * kda_chunk_fwd, including its workspace.
  */
-kda_status kda_chunk_fwd_gates(const void* q, const void* k, const void* v, const void* a,
-                               const float* b, const float* s0, void* o, float* s_out,
-                               const void* gate, const float* norm_w, float eps, int64_t B,
-                               int64_t T, int64_t H, int dk, int dv, float scale, kda_dtype io,
-                               void* workspace, size_t workspace_bytes, void* stream);
+kda_status kda_chunk_fwd_prologue(const void* q, const void* k, const void* v, const void* a,
+                                  const float* b, const float* s0, void* o, float* s_out,
+                                  const void* gate, const float* norm_w, float eps, int64_t B,
+                                  int64_t T, int64_t H, int dk, int dv, float scale,
+                                  kda_dtype io, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /*
  * kda_chunk_fwd_checkpoints -- kda_chunk_fwd that also keeps the state at
@@ -236,14 +242,16 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            float scale, kda_dtype io, void* stream);
 
 /*
- * kda_decode_step_gates -- kda_decode_step with g = -5 sigmoid(a) and
- * beta = sigmoid(b) formed in the kernel: a [B, H, dk] in the io dtype in place
- * of g, b [B, H] float32 in place of beta; everything else as kda_decode_step.
+ * kda_decode_step_prologue -- kda_decode_step from the raw projections: q and
+ * k L2-normalised, g = -5 sigmoid(a) and beta = sigmoid(b) formed in the kernel
+ * (as kda_chunk_fwd_prologue): a [B, H, dk] in the io dtype in place of g,
+ * b [B, H] float32 in place of beta; everything else as kda_decode_step.
  */
-kda_status kda_decode_step_gates(const void* q, const void* k, const void* v, const void* a,
-                                 const float* b, float* state, void* o, const void* gate,
-                                 const float* norm_w, float eps, int64_t B, int64_t H, int dk,
-                                 int dv, float scale, kda_dtype io, void* stream);
+kda_status kda_decode_step_prologue(const void* q, const void* k, const void* v,
+                                    const void* a, const float* b, float* state, void* o,
+                                    const void* gate, const float* norm_w, float eps, int64_t B,
+                                    int64_t H, int dk, int dv, float scale, kda_dtype io,
+                                    void* stream);
 
 /*
  * kda_decode_multi -- K consecutive tokens per sequence against the resident

@@ -34,8 +34,8 @@ def test_header_declares_entry_points():
     for n in ["kda_chunk_fwd", "kda_chunk_fwd_checkpoints", "kda_chunk_fwd_varlen",
               "kda_chunk_fwd_workspace_size",
               "kda_chunk_fwd_launches",
-              "kda_decode_step", "kda_decode_multi", "kda_chunk_fwd_gates",
-              "kda_decode_step_gates",
+              "kda_decode_step", "kda_decode_multi", "kda_chunk_fwd_prologue",
+              "kda_decode_step_prologue",
               "kda_gate_rmsnorm", "kda_status_string", "kda_version"]:
         assert n in names
 
@@ -176,17 +176,17 @@ def test_chunk_varlen_validation(lib):
     assert call(ckpt=P(1), every=32) == ALIAS   # checkpoints overlap q
 
 
-def test_gates_validation(lib):
-    """The logits entry points: a NULL logit array is rejected, the rest is
+def test_prologue_validation(lib):
+    """The prologue entry points: a NULL logit array is rejected, the rest is
     kda_chunk_fwd's and kda_decode_step's validation."""
-    f = lib.kda_chunk_fwd_gates
+    f = lib.kda_chunk_fwd_prologue
     args = [P(1), P(2), P(3), P(4), P(5), None, P(6), P(7), None, None, 1e-6, 2, 64, 3, 16, 16,
             1.0, 0, None, 0, None]
     assert f(*args[:3], None, *args[4:]) == NULLP
     assert f(*args[:4], None, *args[5:]) == NULLP
     assert f(*args[:3], P(4, 8), *args[4:]) == ALIGN
     assert f(*args[:3], P(6), *args[4:]) == ALIAS  # o overlaps the logits
-    d = lib.kda_decode_step_gates
+    d = lib.kda_decode_step_prologue
     dargs = [P(1), P(2), P(3), P(4), P(5), P(6), P(7), None, None, 1e-6, 1, 1, 16, 16, 1.0, 1,
              None]
     assert d(*dargs[:3], None, *dargs[4:]) == NULLP

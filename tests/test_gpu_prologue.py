@@ -1,15 +1,16 @@
-"""GPU parity of the gates-from-logits entry points (kda_chunk_fwd_gates,
-kda_decode_step_gates), through the C ABI.
+"""GPU parity of the prologue entry points (kda_chunk_fwd_prologue,
+kda_decode_step_prologue), through the C ABI.
 
-The kernels form g = -5 sigmoid(a) and beta = sigmoid(b) from the logits; the
-oracle forms them in float64 from the same logits (decay_gates) and runs the
-token recurrence.  Tolerances as for the plain entry points.
+The kernels L2-normalise the raw q and k and form g = -5 sigmoid(a) and
+beta = sigmoid(b) from the logits; the oracle does the same in float64 from the
+same inputs (l2_normalize, decay_gates) and runs the token recurrence.
+Tolerances as for the plain entry points.
 """
 import numpy as np
 import pytest
 import torch
 
-from oracle.kda_oracle import decay_gates
+from oracle.kda_oracle import decay_gates, l2_normalize
 from oracle.kda_oracle import gate_rmsnorm as o_gate_rmsnorm
 from oracle.kda_oracle import kda_decode_step as o_decode
 from oracle.kda_oracle import kda_recurrent as o_recurrent
@@ -32,10 +33,8 @@ def gen(B, T, H, dk, dv, dtype, seed, a_std=1.0, gate=False):
     gen_ = torch.Generator(device=dev())
     gen_.manual_seed(seed)
     r = lambda *s: torch.randn(*s, generator=gen_, device=dev())  # noqa: E731
-    q = r(B, T, H, dk)
-    k = r(B, T, H, dk)
-    q = (q / q.norm(dim=-1, keepdim=True)).to(dtype)
-    k = (k / k.norm(dim=-1, keepdim=True)).to(dtype)
+    q = (0.3 * r(B, T, H, dk)).to(dtype)     # raw projections: not unit vectors
+    k = (2.0 * r(B, T, H, dk)).to(dtype)
     v = r(B, T, H, dv).to(dtype)
     a = (a_std * r(B, T, H, dk)).to(dtype)   # log-decay logits, io dtype
     b = r(B, T, H)                           # write-strength logits, float32
@@ -46,7 +45,7 @@ def gen(B, T, H, dk, dv, dtype, seed, a_std=1.0, gate=False):
 
 def oracle(q, k, v, a, b, s0, gate=None):
     g, beta = decay_gates(f64(a), f64(b))
-    o, S = o_recurrent(f64(q), f64(k), f64(v), g, beta, f64(s0))
+    o, S = o_recurrent(l2_normalize(f64(q)), l2_normalize(f64(k)), f64(v), g, beta, f64(s0))
     if gate is not None:
         o = o_gate_rmsnorm(o, f64(gate), None, 1e-6)
     return o, S
@@ -56,9 +55,9 @@ def oracle(q, k, v, a, b, s0, gate=None):
                                          (128, 128, torch.float32)])
 @pytest.mark.parametrize("T", [17, 100])
 @pytest.mark.parametrize("gated", [False, True])
-def test_chunk_gates_match_oracle(kda, dk, dv, dtype, T, gated):
+def test_chunk_prologue_match_oracle(kda, dk, dv, dtype, T, gated):
     q, k, v, a, b, s0, gt = gen(2, T, 3, dk, dv, dtype, 2100 + T + dk, gate=gated)
-    y, S = kda.chunk_fwd(q, k, v, a, b, s0, gate=gt, logits=True)
+    y, S = kda.chunk_fwd(q, k, v, a, b, s0, gate=gt, prologue=True)
     y_ref, S_ref = oracle(q, k, v, a, b, s0, gt)
     torch.cuda.synchronize()
     assert_close(f64(y), y_ref, TOL[dtype], f"y T={T}", dtype)
@@ -67,46 +66,34 @@ def test_chunk_gates_match_oracle(kda, dk, dv, dtype, T, gated):
 
 @pytest.mark.parametrize("split", ["1", "2"])
 @pytest.mark.parametrize("seg", ["1", "3"])
-def test_chunk_gates_segments(kda, monkeypatch, split, seg):
+def test_chunk_prologue_segments(kda, monkeypatch, split, seg):
     """Matrix-core path: segments of one and three pairs, one or two state
     workgroups per head, state only and output only."""
     monkeypatch.setenv("KDA_CHUNK_SPLIT", split)
     monkeypatch.setenv("KDA_SEG_PAIRS", seg)
     q, k, v, a, b, s0, _ = gen(2, 130, 2, 128, 128, torch.bfloat16, 2150 + int(seg), a_std=2.0)
     o_ref, S_ref = oracle(q, k, v, a, b, s0)
-    o, _ = kda.chunk_fwd(q, k, v, a, b, s0, final_state=False, logits=True)
-    _, S = kda.chunk_fwd(q, k, v, a, b, s0, output=False, logits=True)
+    o, _ = kda.chunk_fwd(q, k, v, a, b, s0, final_state=False, prologue=True)
+    _, S = kda.chunk_fwd(q, k, v, a, b, s0, output=False, prologue=True)
     torch.cuda.synchronize()
     assert_close(f64(o), o_ref, TOL[torch.bfloat16], "o", torch.bfloat16)
     assert_close(f64(S), S_ref, TOL[torch.bfloat16], "state")
 
 
-def test_chunk_gates_decay_floor(kda):
+def test_chunk_prologue_decay_floor(kda):
     """Logits far in the positive tail put whole channels at the floor
     (g = -5 in float32 for every token): finite and within the bar."""
     q, k, v, a, b, s0, _ = gen(1, 64, 2, 128, 128, torch.bfloat16, 2170)
     a[..., ::7] = 60.0
-    y, S = kda.chunk_fwd(q, k, v, a, b, s0, logits=True)
+    y, S = kda.chunk_fwd(q, k, v, a, b, s0, prologue=True)
     y_ref, S_ref = oracle(q, k, v, a, b, s0)
     torch.cuda.synchronize()
     assert_close(f64(y), y_ref, TOL[torch.bfloat16], "o", torch.bfloat16)
     assert_close(f64(S), S_ref, TOL[torch.bfloat16], "state")
 
 
-def test_chunk_gates_equal_given_gates(kda):
-    """Logits in, versus g and beta formed on the host from the same logits:
-    the same result within rounding of the sigmoid."""
-    q, k, v, a, b, s0, gt = gen(1, 96, 4, 128, 128, torch.bfloat16, 2180, gate=True)
-    y1, S1 = kda.chunk_fwd(q, k, v, a, b, s0, gate=gt, logits=True)
-    g = -5.0 * torch.sigmoid(a.float())
-    y2, S2 = kda.chunk_fwd(q, k, v, g, torch.sigmoid(b), s0, gate=gt)
-    torch.cuda.synchronize()
-    assert_close(f64(S1), f64(S2), 1e-3, "state")
-    assert_close(f64(y1), f64(y2), 1e-2, "y", torch.bfloat16)
-
-
-def test_full_width_gates_sampled(kda):
-    """B=1, H=96, T=32768 with the gated epilogue, logits in: 3 sampled heads
+def test_full_width_prologue_sampled(kda):
+    """B=1, H=96, T=32768 with the gated epilogue, raw q, k and logits in: 3 sampled heads
     over the whole sequence against the oracle."""
     from gated_delta_rule_112_amd.inputs import WORKLOADS, make_prefill_inputs
     from oracle.kda_oracle import kda_chunked
@@ -116,11 +103,14 @@ def test_full_width_gates_sampled(kda):
     gen_.manual_seed(2190)
     a = torch.randn(x["g"].shape, generator=gen_, device=dev()).to(torch.bfloat16)
     b = torch.randn(x["beta"].shape, generator=gen_, device=dev())
-    y, S = kda.chunk_fwd(x["q"], x["k"], x["v"], a, b, None, gate=x["gate"], logits=True)
+    qr = (3.0 * x["q"].float()).to(torch.bfloat16)  # raw projections: not unit vectors
+    kr = (0.5 * x["k"].float()).to(torch.bfloat16)
+    y, S = kda.chunk_fwd(qr, kr, x["v"], a, b, None, gate=x["gate"], prologue=True)
     torch.cuda.synchronize()
     for h in [0, 50, 95]:
         g, beta = decay_gates(f64(a[:, :, h:h + 1]), f64(b[:, :, h:h + 1]))
-        o_ref, S_ref = kda_chunked(f64(x["q"][:, :, h:h + 1]), f64(x["k"][:, :, h:h + 1]),
+        o_ref, S_ref = kda_chunked(l2_normalize(f64(qr[:, :, h:h + 1])),
+                                   l2_normalize(f64(kr[:, :, h:h + 1])),
                                    f64(x["v"][:, :, h:h + 1]), g, beta)
         y_ref = o_gate_rmsnorm(o_ref, f64(x["gate"][:, :, h:h + 1]), None, 1e-6)
         assert_close(f64(y[:, :, h:h + 1]), y_ref, TOL[torch.bfloat16], f"y head {h}",
@@ -130,7 +120,7 @@ def test_full_width_gates_sampled(kda):
 
 @pytest.mark.parametrize("dk,dv", [(16, 32), (128, 128)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_decode_gates_match_oracle(kda, dk, dv, dtype):
+def test_decode_prologue_match_oracle(kda, dk, dv, dtype):
     B, H = 3, 4
     gen_ = torch.Generator(device=dev())
     gen_.manual_seed(2200 + dk)
@@ -139,9 +129,10 @@ def test_decode_gates_match_oracle(kda, dk, dv, dtype):
     for step in range(3):
         q, k, v, a, b, _, gt = gen(B, 1, H, dk, dv, dtype, 2210 + step, gate=True)
         q, k, v, a, b, gt = (x[:, 0].contiguous() for x in (q, k, v, a, b, gt))
-        o = kda.decode_step(q, k, v, a, b, state, gate=gt, logits=True)
+        o = kda.decode_step(q, k, v, a, b, state, gate=gt, prologue=True)
         g, beta = decay_gates(f64(a), f64(b))
-        o_ref, S_ref = o_decode(f64(q), f64(k), f64(v), g, beta, S_ref)
+        o_ref, S_ref = o_decode(l2_normalize(f64(q)), l2_normalize(f64(k)), f64(v), g, beta,
+                                S_ref)
         o_ref = o_gate_rmsnorm(o_ref, f64(gt), None, 1e-6)
         torch.cuda.synchronize()
         assert_close(f64(o), o_ref, TOL[dtype], f"decode y step {step}", dtype)
