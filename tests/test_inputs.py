@@ -45,3 +45,21 @@ def test_decode_inputs():
     assert x0["q"].shape == (4, 2, 32) and x0["beta"].shape == (4, 2)
     assert not torch.equal(x0["k"], x1["k"])
     assert torch.equal(x0["k"], make_decode_step_inputs(w, 0)["k"])
+
+
+def test_bench_byte_accounting():
+    """The benchmark's algorithmic bytes, against the per-element sizes written
+    out: prefill 1,796 B per token-head with the gate at bf16 and 128/128 (q, k,
+    v, o, gate 2 B each; g 4 B per channel; beta 4 B), decode 132,612 B per
+    (b, h) and step, and the multi-token verify / commit split."""
+    import bench
+    total, per = bench.prefill_bytes(1, 32768, 96, 128, 128, 2, with_o=True, with_gate=True)
+    assert per == 2 * 128 * 2 + 128 * 2 + 128 * 4 + 4 + 128 * 2 + 128 * 2 == 1796
+    assert total == 32768 * 96 * 1796 + 96 * 128 * 128 * 4        # plus the final state
+    _, per_d = bench.decode_bytes(256, 96, 128, 128, 2)
+    assert per_d == 8 * 128 * 128 + 3 * 128 * 2 + 4 * 128 + 4 + 128 * 2 == 132612
+    v, c = bench.verify_bytes(2, 3, 4, 128, 128, 2, [0, 3])
+    tok_in = 3 * 128 * 2 + 4 * 128 + 4
+    assert v == 2 * 3 * (4 * 128 * 128 + 4 * (tok_in + 2 * 128 * 2))
+    assert c == 4 + (3 * (8 * 128 * 128 + 3 * tok_in) + 4)          # nothing read for 0 accepted
+    assert bench.prefill_flops(1, 1, 1, 128, 128) == 6 * 16 * 128 + 4 * 16 * 128 + 6 * 128 * 128
