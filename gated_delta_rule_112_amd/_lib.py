@@ -69,6 +69,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32,
                                      i64, i64, i64, ci, ci, f32, ci, vp]
     lib.kda_decode_multi.restype = ci
+    lib.kda_decode_multi_prologue.argtypes = lib.kda_decode_multi.argtypes
+    lib.kda_decode_multi_prologue.restype = ci
     lib.kda_gate_rmsnorm.argtypes = [vp, vp, vp, vp, i64, ci, f32, ci, vp]
     lib.kda_gate_rmsnorm.restype = ci
     lib.kda_status_string.argtypes = [ci]
@@ -307,13 +309,14 @@ def decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, gate=None, norm_
 
 def decode_multi(q, k, v, g, beta, state, n_commit=None, *, scale: float = 1.0, gate=None,
                  norm_w=None, eps: float = 1e-6, output: bool = True, out=None,
-                 stream=None) -> Optional[torch.Tensor]:
+                 prologue: bool = False, stream=None) -> Optional[torch.Tensor]:
     """K tokens per sequence ([B, K, H, *] inputs) against ``state`` [B, H, dk, dv].
 
     Returns the outputs of all K tokens ([B, K, H, dv], or None with
     ``output=False``).  ``state`` is replaced in place by the state after the
     first ``n_commit[b]`` tokens of sequence b (``n_commit``: int32 [B] on the
     device, values clamped into [0, K]; None commits all K tokens).
+    ``prologue=True``: raw q, k and the logits a (io dtype) and b in g and beta.
     """
     lib = load_library()
     if q.device.type != "cuda":
@@ -327,7 +330,7 @@ def decode_multi(q, k, v, g, beta, state, n_commit=None, *, scale: float = 1.0, 
     _need(q, "q", io, (B, K, H, dk), dev)
     _need(k, "k", io, (B, K, H, dk), dev)
     _need(v, "v", io, (B, K, H, dv), dev)
-    _need(g, "g", torch.float32, (B, K, H, dk), dev)
+    _need(g, "a" if prologue else "g", io if prologue else torch.float32, (B, K, H, dk), dev)
     _need(beta, "beta", torch.float32, (B, K, H), dev)
     _need(state, "state", torch.float32, (B, H, dk, dv), dev)
     if n_commit is not None:
@@ -342,10 +345,11 @@ def decode_multi(q, k, v, g, beta, state, n_commit=None, *, scale: float = 1.0, 
         out = torch.empty((B, K, H, dv), dtype=io, device=dev)
     else:
         _need(out, "out", io, (B, K, H, dv), dev)
-    st = lib.kda_decode_multi(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
-                              _ptr(n_commit), _ptr(out), _ptr(gate), _ptr(norm_w), float(eps),
-                              B, K, H, dk, dv, float(scale), _IO[io], _stream(dev, stream))
-    _check(lib, "kda_decode_multi", st)
+    fn = lib.kda_decode_multi_prologue if prologue else lib.kda_decode_multi
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(n_commit),
+            _ptr(out), _ptr(gate), _ptr(norm_w), float(eps), B, K, H, dk, dv, float(scale),
+            _IO[io], _stream(dev, stream))
+    _check(lib, "kda_decode_multi_prologue" if prologue else "kda_decode_multi", st)
     return out
 
 

@@ -295,12 +295,18 @@ kda_status kda_decode_step_prologue(const void* q, const void* k, const void* v,
                      a, stream);
 }
 
-kda_status kda_decode_multi(const void* q, const void* k, const void* v, const float* g,
-                            const float* beta, float* state, const int32_t* n_commit, void* o,
-                            const void* gate, const float* norm_w, float eps, int64_t B,
-                            int64_t K, int64_t H, int dk, int dv, float scale, kda_dtype io,
-                            void* stream) {
-  if (!q || !k || !v || !g || !beta || !state) return KDA_ERR_NULL_POINTER;
+}  // extern "C"
+
+namespace {
+
+// kda_decode_multi, with the prologue (q, k normalised, gates from their
+// logits) when ga is non-NULL.
+kda_status decode_multi(const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, float* state, const int32_t* n_commit, void* o,
+                        const void* gate, const float* norm_w, float eps, int64_t B, int64_t K,
+                        int64_t H, int dk, int dv, float scale, kda_dtype io, const void* ga,
+                        void* stream) {
+  if (!q || !k || !v || (!g && !ga) || !beta || !state) return KDA_ERR_NULL_POINTER;
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_BAD_DTYPE;
   if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED_DIM;
   const int64_t nqk = prod(B, K, H, dk), nv = prod(B, K, H, dv), nb = prod(B, K, H);
@@ -310,14 +316,15 @@ kda_status kda_decode_multi(const void* q, const void* k, const void* v, const f
   if (!isfinite(scale) || !isfinite(eps) || eps < 0.f) return KDA_ERR_BAD_ARGUMENT;
   const uintptr_t ea = (io == KDA_BF16) ? 2 : 4;
   if (!aligned(state, 16)) return KDA_ERR_MISALIGNED;
-  for (const void* p : {q, k, v, (const void*)o, gate})
+  for (const void* p : {q, k, v, (const void*)o, gate, ga})
     if (!aligned(p, ea)) return KDA_ERR_MISALIGNED;
   for (const void* p : {(const void*)g, (const void*)beta, (const void*)norm_w,
                         (const void*)n_commit})
     if (!aligned(p, 4)) return KDA_ERR_MISALIGNED;
 
   const int64_t es = (io == KDA_BF16) ? 2 : 4;
-  const Span sq{q, nqk * es}, sk{k, nqk * es}, sv{v, nv * es}, sg{g, nqk * 4}, sb{beta, nb * 4};
+  const Span sg = ga != nullptr ? Span{ga, nqk * es} : Span{g, nqk * 4};
+  const Span sq{q, nqk * es}, sk{k, nqk * es}, sv{v, nv * es}, sb{beta, nb * 4};
   const Span sst{state, ns * 4}, so{o, nv * es}, sgt{gate, nv * es}, sw{norm_w, (int64_t)dv * 4};
   const Span sn{n_commit, B * 4};
   for (Span in : {sq, sk, sv, sg, sb, sst, sgt, sw, sn})
@@ -329,8 +336,33 @@ kda_status kda_decode_multi(const void* q, const void* k, const void* v, const f
                     B, H, dk, dv, scale, io == KDA_BF16, stream};
   a.K = K;
   a.n_commit = n_commit;
+  a.ga = ga;
   return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_decode_multi(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, float* state, const int32_t* n_commit, void* o,
+                            const void* gate, const float* norm_w, float eps, int64_t B,
+                            int64_t K, int64_t H, int dk, int dv, float scale, kda_dtype io,
+                            void* stream) {
+  return decode_multi(q, k, v, g, beta, state, n_commit, o, gate, norm_w, eps, B, K, H, dk, dv,
+                      scale, io, nullptr, stream);
+}
+
+kda_status kda_decode_multi_prologue(const void* q, const void* k, const void* v, const void* a,
+                                     const float* b, float* state, const int32_t* n_commit,
+                                     void* o, const void* gate, const float* norm_w, float eps,
+                                     int64_t B, int64_t K, int64_t H, int dk, int dv, float scale,
+                                     kda_dtype io, void* stream) {
+  if (a == nullptr) return KDA_ERR_NULL_POINTER;
+  return decode_multi(q, k, v, nullptr, b, state, n_commit, o, gate, norm_w, eps, B, K, H, dk,
+                      dv, scale, io, a, stream);
+}
+
 
 kda_status kda_gate_rmsnorm(const void* x, const void* gate, const float* norm_w, void* y,
                             int64_t rows, int dv, float eps, kda_dtype io, void* stream) {

@@ -288,6 +288,19 @@ kda_status kda_decode_multi(const void* q, const void* k, const void* v,
                             int dk, int dv, float scale, kda_dtype io, void* stream);
 
 /*
+ * kda_decode_multi_prologue -- kda_decode_multi from the raw projections: q and
+ * k L2-normalised, g = -5 sigmoid(a) and beta = sigmoid(b) formed in the kernel
+ * (as kda_chunk_fwd_prologue): a [B, K, H, dk] in the io dtype in place of g,
+ * b [B, K, H] float32 in place of beta; everything else as kda_decode_multi.
+ */
+kda_status kda_decode_multi_prologue(const void* q, const void* k, const void* v,
+                                     const void* a, const float* b, float* state,
+                                     const int32_t* n_commit, void* o, const void* gate,
+                                     const float* norm_w, float eps, int64_t B, int64_t K,
+                                     int64_t H, int dk, int dv, float scale, kda_dtype io,
+                                     void* stream);
+
+/*
  * kda_gate_rmsnorm -- the output epilogue on its own.
  *
  * "Kimi K3 Architecture Explained ...", section "Token mixing": the output

@@ -35,7 +35,7 @@ def test_header_declares_entry_points():
               "kda_chunk_fwd_workspace_size",
               "kda_chunk_fwd_launches",
               "kda_decode_step", "kda_decode_multi", "kda_chunk_fwd_prologue",
-              "kda_decode_step_prologue",
+              "kda_decode_step_prologue", "kda_decode_multi_prologue",
               "kda_gate_rmsnorm", "kda_status_string", "kda_version"]:
         assert n in names
 

@@ -137,3 +137,32 @@ def test_decode_prologue_match_oracle(kda, dk, dv, dtype):
         torch.cuda.synchronize()
         assert_close(f64(o), o_ref, TOL[dtype], f"decode y step {step}", dtype)
     assert_close(f64(state), S_ref, 1e-5, "decode state")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_decode_multi_prologue_match_oracle(kda, dtype):
+    """K = 5 raw tokens per sequence, verify then commit of the accepted counts."""
+    B, K, H, dk, dv = 4, 5, 3, 128, 128
+    q, k, v, a, b, _, gt = gen(B, K, H, dk, dv, dtype, 2250, gate=True)
+    gen_ = torch.Generator(device=dev())
+    gen_.manual_seed(2251)
+    state = 0.3 * torch.randn(B, H, dk, dv, generator=gen_, device=dev())
+    S0 = state.clone()
+    y = kda.decode_multi(q, k, v, a, b, state, torch.zeros(B, dtype=torch.int32, device=dev()),
+                         gate=gt, prologue=True)
+    acc = [0, 2, 5, 3]
+    kda.decode_multi(q, k, v, a, b, state, torch.tensor(acc, dtype=torch.int32, device=dev()),
+                     output=False, prologue=True)
+    g, beta = decay_gates(f64(a), f64(b))
+    qn, kn = l2_normalize(f64(q)), l2_normalize(f64(k))
+    o_ref, _ = o_recurrent(qn, kn, f64(v), g, beta, f64(S0))
+    y_ref = o_gate_rmsnorm(o_ref, f64(gt), None, 1e-6)
+    torch.cuda.synchronize()
+    assert_close(f64(y), y_ref, TOL[dtype], "verify y", dtype)
+    for bi, n in enumerate(acc):
+        if n == 0:
+            assert torch.equal(state[bi], S0[bi])
+            continue
+        _, S_ref = o_recurrent(qn[bi:bi + 1, :n], kn[bi:bi + 1, :n], f64(v[bi:bi + 1, :n]),
+                               g[bi:bi + 1, :n], beta[bi:bi + 1, :n], f64(S0[bi:bi + 1]))
+        assert_close(f64(state[bi]), S_ref[0], 1e-5, f"committed state {bi}")
