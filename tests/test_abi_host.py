@@ -141,6 +141,26 @@ def test_chunk_workspace(lib):
     assert launches(1, 16, 1, 48, 128, 1) == 0
 
 
+def test_launch_groups(lib):
+    """Large batches run in groups of sequences whose state workgroups take
+    about 3/8 of the compute units, every segment of every group in one launch
+    pipeline: the launch count is one plus the groups' segments, and the
+    workspace is sized for one group (host logic; the compute-unit count falls
+    back to 256 without a device)."""
+    launches = lib.kda_chunk_fwd_launches
+    launches.restype = ctypes.c_int64
+    ws = lib.kda_chunk_fwd_workspace_size
+    ws.restype = ctypes.c_size_t
+    one = launches(1, 4096, 96, 128, 128, 1)     # one sequence: one group
+    assert one >= 2
+    assert launches(16, 4096, 96, 128, 128, 1) == 1 + 16 * (one - 1)
+    assert ws(16, 4096, 96, 128, 128, 1) == ws(1, 4096, 96, 128, 128, 1)
+    # 32 heads: three sequences per group (96 state workgroups)
+    three = launches(3, 4096, 32, 128, 128, 1)
+    assert launches(9, 4096, 32, 128, 128, 1) == 1 + 3 * (three - 1)
+    assert ws(9, 4096, 32, 128, 128, 1) == ws(3, 4096, 32, 128, 128, 1)
+
+
 def test_chunk_checkpoints_validation(lib):
     f = lib.kda_chunk_fwd_checkpoints
 
