@@ -322,6 +322,192 @@ kda_decode_multi_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
   }
 }
 
+// 2 <= K <= 4 tokens of every (b, h), with outputs, in the chunkwise form of
+// the recurrence (the algebra of the chunked prefill, "Kimi K3: Engineering
+// ...", section "Dimension 1", on one small tile): with G the cumulative
+// log-decay over the tokens, Kh = k e^G, Qh = scale q e^G, Kc = k e^-G,
+//   P = Kh S,  R = Qh S                      (one pass over the state)
+//   A = strict_lower(Diag(beta) Kh Kc^T),  Aqk = lower(Qh Kc^T),  T = (I + A)^-1 Diag(beta)
+//   D = T (V - P),  O = R + Aqk D
+//   S_n = Diag(e^G_{n-1}) (S + Kc[:n]^T D[:n])   (the state after the first n tokens)
+// so the K dependent token steps of kda_decode_multi_kernel become a few
+// block-wide phases.  dk = dv = 128, the state in the same float4 strips as
+// the single-token kernel; same contract as kda_decode_multi_kernel.
+template <typename IO>
+__global__ void __launch_bounds__(256, 3)
+kda_multi_chunk_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
+                       const IO* __restrict__ v, const float* __restrict__ g,
+                       const float* __restrict__ beta, float* __restrict__ state,
+                       const int* __restrict__ n_commit, IO* __restrict__ o,
+                       const IO* __restrict__ gate, const float* __restrict__ norm_w, float eps,
+                       float scale, int64_t B, int64_t K, int64_t H) {
+  constexpr int D = 128, KM = 4, CG = D / 4, RG = 256 / CG, RPT = D / RG;
+  __shared__ float kh[KM][D], qh[KM][D], kc[KM][D], ex[KM][D];
+  __shared__ float vv[KM][D];            // values, then D (the deltas)
+  __shared__ f32x4 part[2][KM][RG][CG];  // P, R partial sums per row group
+  __shared__ float pr[2][KM][D];         // P, R
+  __shared__ float am[KM][KM], aq[KM][KM], tt[KM][KM], bt[KM];
+  __shared__ float rs[2][KM];            // row sums of O^2 per wave (gated epilogue)
+  const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
+  const int64_t BH = B * H;
+  const bool gated = gate != nullptr;
+  const float wn = (gated && norm_w != nullptr && tid < D) ? norm_w[tid] : 1.f;
+  auto row = [&](int64_t u, int64_t t) { return ((u / H) * K + t) * H + u % H; };
+
+  for (int64_t u = blockIdx.x; u < BH; u += gridDim.x) {
+    int64_t n = n_commit != nullptr ? (int64_t)n_commit[u / H] : K;
+    n = n < 0 ? 0 : (n > K ? K : n);
+    const int L = (int)K;
+    float* Sp = state + u * (int64_t)(D * D);
+    // 1. the state strip and the tokens' inputs
+    f32x4 s[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+      s[m] = __builtin_nontemporal_load((const f32x4*)(Sp + (rg + m * RG) * D + 4 * cg));
+#pragma unroll 1
+    for (int e = tid; e < L * D; e += 256) {
+      const int t = e / D, c = e % D;
+      const int64_t rw = row(u, t);
+      kh[t][c] = ld_f32(k + rw * D + c);
+      qh[t][c] = ld_f32(q + rw * D + c);
+      kc[t][c] = g[rw * D + c];
+      vv[t][c] = ld_f32(v + rw * D + c);
+    }
+    if (tid < L) bt[tid] = beta[row(u, tid)];
+    __syncthreads();
+    // 2. cumulative log-decay per channel, the rescaled keys and queries
+    if (tid < D) {
+      float gam = 0.f;
+      for (int t = 0; t < L; ++t) {
+        gam += kc[t][tid];
+        const float e = __expf(gam), kk = kh[t][tid];
+        ex[t][tid] = e;
+        kh[t][tid] = kk * e;
+        qh[t][tid] = scale * qh[t][tid] * e;
+        kc[t][tid] = kk * __expf(-gam);
+      }
+    }
+    __syncthreads();
+    // 3. P, R over this thread's rows; the intra-tile products
+#pragma unroll 1
+    for (int t = 0; t < L; ++t) {
+      f32x4 p = {0.f, 0.f, 0.f, 0.f}, r = p;
+#pragma unroll
+      for (int m = 0; m < RPT; ++m) {
+        p += kh[t][rg + m * RG] * s[m];
+        r += qh[t][rg + m * RG] * s[m];
+      }
+      part[0][t][rg][cg] = p;
+      part[1][t][rg][cg] = r;
+    }
+    {  // the 16 (t, c) products, 16 lanes each over 8 channels
+      const int t = tid / (16 * KM), c = (tid / 16) % KM, sub = tid % 16;
+      float a = 0.f, b2 = 0.f;
+#pragma unroll
+      for (int m = 0; m < D / 16; ++m) {
+        const int i = sub + 16 * m;
+        a = fmaf(kh[t][i], kc[c][i], a);
+        b2 = fmaf(qh[t][i], kc[c][i], b2);
+      }
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) {
+        a += __shfl_xor(a, off);
+        b2 += __shfl_xor(b2, off);
+      }
+      if (sub == 0 && t < L && c < L) {
+        am[t][c] = c < t ? bt[t] * a : 0.f;
+        aq[t][c] = c <= t ? b2 : 0.f;
+      }
+    }
+    __syncthreads();
+    // 4. P and R per column; T = (I + A)^-1 Diag(beta) by forward substitution
+#pragma unroll 1
+    for (int e = tid; e < 2 * L * D; e += 256) {
+      const int w = e / (L * D), t = (e / D) % L, j = e % D;
+      float acc = 0.f;
+#pragma unroll
+      for (int x = 0; x < RG; ++x) acc += ((const float*)&part[w][t][x][0])[j];
+      pr[w][t][j] = acc;
+    }
+    if (tid < L) {
+      const int c = tid;
+      float y[KM];
+#pragma unroll
+      for (int t = 0; t < KM; ++t) {
+        float acc = (t == c) ? 1.f : 0.f;
+        for (int m = c; m < t; ++m) acc -= am[t][m] * y[m];
+        y[t] = (t < c || t >= L) ? 0.f : acc;
+      }
+#pragma unroll
+      for (int t = 0; t < KM; ++t)
+        if (t < L) tt[t][c] = y[t] * bt[c];
+    }
+    __syncthreads();
+    // 5. D = T (V - P) and O = R + Aqk D, column j = tid (its values and
+    // deltas are read and written by its thread alone)
+    float ot[KM];
+    if (tid < D) {
+      const int j = tid;
+      float dcol[KM];
+#pragma unroll
+      for (int t = 0; t < KM; ++t) {
+        float acc = 0.f;
+        if (t < L)
+          for (int c = 0; c <= t; ++c) acc = fmaf(tt[t][c], vv[c][j] - pr[0][c][j], acc);
+        dcol[t] = acc;
+      }
+#pragma unroll
+      for (int t = 0; t < KM; ++t) {
+        float acc = 0.f;
+        if (t < L) {
+          acc = pr[1][t][j];
+          for (int c = 0; c <= t; ++c) acc = fmaf(aq[t][c], dcol[c], acc);
+        }
+        ot[t] = acc;
+      }
+#pragma unroll
+      for (int t = 0; t < KM; ++t)
+        if (t < L) vv[t][j] = dcol[t];
+      if (gated) {
+#pragma unroll
+        for (int t = 0; t < KM; ++t) {
+          float x = ot[t] * ot[t];
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+          if (tid % 64 == 0) rs[tid / 64][t] = x;
+        }
+      }
+    }
+    __syncthreads();  // D in vv; the row sums in rs
+    // 6. outputs
+    if (tid < D) {
+      const int j = tid;
+#pragma unroll
+      for (int t = 0; t < KM; ++t) {
+        if (t >= L) break;
+        float y = ot[t];
+        if (gated) {
+          const float inv = rsqrtf((rs[0][t] + rs[1][t]) / (float)D + eps);
+          y = y * inv * wn * sigmoidf_(ld_f32(gate + row(u, t) * D + j));
+        }
+        st_f32(o + row(u, t) * D + j, y);
+      }
+    }
+    // 7. the state after n tokens
+    if (n > 0) {
+      const int nn = (int)n;
+#pragma unroll
+      for (int m = 0; m < RPT; ++m) {
+        const int i = rg + m * RG;
+        f32x4 acc = s[m];
+        for (int t = 0; t < nn; ++t) acc += kc[t][i] * *(const f32x4*)&vv[t][4 * cg];
+        __builtin_nontemporal_store(ex[nn - 1][i] * acc, (f32x4*)(Sp + i * D + 4 * cg));
+      }
+    }
+    __syncthreads();  // the shared arrays are reused by the next (b, h)
+  }
+}
+
 int decode_grid(int64_t units) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess)
@@ -335,6 +521,15 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
   using Sh = DecodeShape<DK, DV>;
   const int64_t bhn = a.B * a.H;
   const int nblk = decode_grid(bhn);
+  if (a.K >= 2 && a.K <= 4 && a.o != nullptr && DK == 128 && DV == 128 && a.ga == nullptr) {
+    // verify calls with few draft tokens: the chunkwise form, three workgroups per CU
+    const int64_t cblk = bhn < 3 * (int64_t)nblk ? bhn : 3 * (int64_t)nblk;
+    hipLaunchKernelGGL((kda_multi_chunk_kernel<IO>), dim3((unsigned)cblk), dim3(256), 0,
+                       (hipStream_t)a.stream, (const IO*)a.q, (const IO*)a.k, (const IO*)a.v,
+                       a.g, a.beta, a.state, a.n_commit, (IO*)a.o, (const IO*)a.gate,
+                       a.norm_w, a.eps, a.scale, a.B, a.K, a.H);
+    return hipGetLastError();
+  }
   if (a.K > 0) {
     const int64_t mblk = bhn < 3 * (int64_t)nblk ? bhn : 3 * (int64_t)nblk;  // three per CU
     hipLaunchKernelGGL((kda_decode_multi_kernel<DK, DV, IO>), dim3((unsigned)mblk), dim3(Sh::NT),

@@ -68,7 +68,7 @@ def oracle(q, k, v, g, beta, S0, n, gate=None, norm_w=None, scale=1.0, eps=1e-6)
 @pytest.mark.parametrize("dk,dv", [(16, 16), (64, 32), (128, 128)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("with_gate", [False, True])
-@pytest.mark.parametrize("K", [1, 3, 8])
+@pytest.mark.parametrize("K", [1, 2, 3, 4, 8])
 def test_decode_multi_matches_oracle(kda, dk, dv, dtype, with_gate, K):
     B, H = 5, 3
     q, k, v, g, beta, state, gate = gen(B, K, H, dk, dv, dtype, 500 + 7 * K + dk + dv, with_gate)
