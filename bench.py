@@ -271,12 +271,21 @@ def bench_prologue(kda, torch, w, steps):
     return e0.elapsed_time(e1) / steps
 
 
-def bench_packed(kda, torch, w, steps):
-    """Prefill of a packed serving batch (kda_chunk_fwd_varlen); returns
-    (ms per step, total tokens, longest length)."""
+def bench_packed(kda, torch, w, steps, prologue=False):
+    """Prefill of a packed serving batch (kda_chunk_fwd_varlen; with
+    ``prologue``, from the raw projections as in ``bench_prologue``:
+    kda_chunk_fwd_varlen_prologue); returns (ms per step, total tokens, longest
+    length)."""
     from gated_delta_rule_112_amd.inputs import make_packed_inputs
     dev = torch.device("cuda:0")
     x = make_packed_inputs(w, device=dev)
+    if prologue:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(w.seed + 11)
+        x["g"] = torch.randn(x["g"].shape, generator=gen, device=dev).to(x["q"].dtype)
+        x["beta"] = torch.randn(x["beta"].shape, generator=gen, device=dev)
+        x["q"] = (3.0 * x["q"].float()).to(x["v"].dtype)
+        x["k"] = (0.5 * x["k"].float()).to(x["v"].dtype)
     max_len = max(x["lens"])
     total = x["q"].shape[0]
     out = torch.empty((total, w.H, w.dv), dtype=x["q"].dtype, device=dev)
@@ -288,7 +297,7 @@ def bench_packed(kda, torch, w, steps):
     def step():
         kda.chunk_fwd_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu_seqlens"],
                              max_len, gate=x["gate"], out=out, s_out=s_out, workspace=ws,
-                             stream=stream)
+                             stream=stream, prologue=prologue)
 
     step()
     torch.cuda.synchronize()
@@ -487,6 +496,12 @@ def main():
                   "frac": round(pgbs / HBM_PEAK_GBS, 4)}
         log(f"[bench] packed batch: {wp.B} sequences, {ptot} tokens (longest {pmax}): "
             f"{pms:.3f} ms, {ptot / (pms * 1e-3) / 1e6:.2f} M tok/s")
+        if not a.no_prologue:  # the same batch from the raw projections
+            rms, _, _ = bench_packed(kda, torch, wp, a.steps, prologue=True)
+            packed["prologue_ms"] = round(rms, 4)
+            packed["prologue_tokens_per_s"] = round(ptot / (rms * 1e-3), 1)
+            log(f"[bench] packed batch from raw projections: {rms:.3f} ms, "
+                f"{ptot / (rms * 1e-3) / 1e6:.2f} M tok/s")
 
     decode = None
     if not a.no_decode:

@@ -55,6 +55,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                          vp, f32, i64, ci, ci, f32, ci, vp, ctypes.c_size_t,
                                          vp, i64, vp]
     lib.kda_chunk_fwd_varlen.restype = ci
+    lib.kda_chunk_fwd_varlen_prologue.argtypes = lib.kda_chunk_fwd_varlen.argtypes
+    lib.kda_chunk_fwd_varlen_prologue.restype = ci
     lib.kda_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, ci, ci, ci]
     lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_chunk_fwd_launches.argtypes = [i64, i64, i64, ci, ci, ci]
@@ -146,12 +148,15 @@ def chunk_fwd_checkpoints(q, k, v, g, beta, s0=None, *, every: int, scale: float
 def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, max_len: int, s0=None, *,
                      scale: float = 1.0, gate=None, norm_w=None, eps: float = 1e-6,
                      output: bool = True, final_state: bool = True, out=None, s_out=None,
-                     every: int = 0, ckpt=None, workspace=None, stream=None):
+                     every: int = 0, ckpt=None, workspace=None, stream=None,
+                     prologue: bool = False):
     """Prefill over N sequences packed along the token axis: q, k, g [total, H, dk],
     v [total, H, dv], beta [total, H]; ``cu_seqlens`` int32 [N + 1] on the device
     (sequence b is rows cu[b] .. cu[b+1]-1), ``max_len`` >= the longest.  Returns
     (o or y [total, H, dv], final states [N, H, dk, dv], checkpoints
-    [N, max_len // every, H, dk, dv] or None when ``every`` is 0)."""
+    [N, max_len // every, H, dk, dv] or None when ``every`` is 0).  With
+    ``prologue``, q and k are raw, g holds the decay logits a (io dtype) and beta
+    the write-strength logits b (kda_chunk_fwd_varlen_prologue)."""
     lib = load_library()
     if q.device.type != "cuda":
         raise ValueError("kda ops need CUDA (HIP) tensors")
@@ -169,7 +174,7 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, max_len: int, s0=None, *,
     _need(q, "q", io, (total, H, dk), dev)
     _need(k, "k", io, (total, H, dk), dev)
     _need(v, "v", io, (total, H, dv), dev)
-    _need(g, "g", torch.float32, (total, H, dk), dev)
+    _need(g, "a" if prologue else "g", io if prologue else torch.float32, (total, H, dk), dev)
     _need(beta, "beta", torch.float32, (total, H), dev)
     _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
     if s0 is not None:
@@ -201,13 +206,14 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, max_len: int, s0=None, *,
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, (workspace.numel(),), dev)
-    st = lib.kda_chunk_fwd_varlen(
+    fn = "kda_chunk_fwd_varlen_prologue" if prologue else "kda_chunk_fwd_varlen"
+    st = getattr(lib, fn)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, total,
         int(max_len), _ptr(s0), _ptr(out), _ptr(s_out), _ptr(gate), _ptr(norm_w), float(eps), H,
         dk, dv, float(scale), _IO[io], _ptr(workspace),
         0 if workspace is None else workspace.numel(), _ptr(ckpt) if nck else None,
         int(every), _stream(dev, stream))
-    _check(lib, "kda_chunk_fwd_varlen", st)
+    _check(lib, fn, st)
     return out, s_out, ckpt
 
 

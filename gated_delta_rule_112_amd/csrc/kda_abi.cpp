@@ -174,6 +174,25 @@ kda_status chunk_fwd(const void* q, const void* k, const void* v, const float* g
   return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+// Packed sequences: the checks of the varlen entry points, then chunk_fwd.
+kda_status varlen_fwd(const void* q, const void* k, const void* v, const float* g,
+                      const float* beta, const int32_t* cu_seqlens, int64_t N, int64_t total,
+                      int64_t max_len, const float* s0, void* o, float* s_out, const void* gate,
+                      const float* norm_w, float eps, int64_t H, int dk, int dv, float scale,
+                      kda_dtype io, void* workspace, size_t workspace_bytes, float* ckpt,
+                      int64_t ckpt_every, const void* ga, void* stream) {
+  if (cu_seqlens == nullptr) return KDA_ERR_NULL_POINTER;
+  if (N < 1 || total < 1 || max_len < 1) return KDA_ERR_BAD_SHAPE;
+  if (!aligned(cu_seqlens, 4)) return KDA_ERR_MISALIGNED;
+  if (ckpt != nullptr) {
+    if (ckpt_every <= 0 || ckpt_every % 32 != 0) return KDA_ERR_BAD_SHAPE;
+    if (!aligned(ckpt, 4)) return KDA_ERR_MISALIGNED;
+  }
+  return chunk_fwd(q, k, v, g, beta, s0, o, s_out, gate, norm_w, eps, N, max_len, H, dk, dv,
+                   scale, io, workspace, workspace_bytes, ckpt, ckpt_every, cu_seqlens, total,
+                   ga, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -219,16 +238,23 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
                                 int64_t H, int dk, int dv, float scale, kda_dtype io,
                                 void* workspace, size_t workspace_bytes, float* ckpt,
                                 int64_t ckpt_every, void* stream) {
-  if (cu_seqlens == nullptr) return KDA_ERR_NULL_POINTER;
-  if (N < 1 || total < 1 || max_len < 1) return KDA_ERR_BAD_SHAPE;
-  if (!aligned(cu_seqlens, 4)) return KDA_ERR_MISALIGNED;
-  if (ckpt != nullptr) {
-    if (ckpt_every <= 0 || ckpt_every % 32 != 0) return KDA_ERR_BAD_SHAPE;
-    if (!aligned(ckpt, 4)) return KDA_ERR_MISALIGNED;
-  }
-  return chunk_fwd(q, k, v, g, beta, s0, o, s_out, gate, norm_w, eps, N, max_len, H, dk, dv,
-                   scale, io, workspace, workspace_bytes, ckpt, ckpt_every, cu_seqlens, total,
-                   nullptr, stream);
+  return varlen_fwd(q, k, v, g, beta, cu_seqlens, N, total, max_len, s0, o, s_out, gate, norm_w,
+                    eps, H, dk, dv, scale, io, workspace, workspace_bytes, ckpt, ckpt_every,
+                    nullptr, stream);
+}
+
+kda_status kda_chunk_fwd_varlen_prologue(const void* q, const void* k, const void* v,
+                                         const void* a, const float* b,
+                                         const int32_t* cu_seqlens, int64_t N, int64_t total,
+                                         int64_t max_len, const float* s0, void* o,
+                                         float* s_out, const void* gate, const float* norm_w,
+                                         float eps, int64_t H, int dk, int dv, float scale,
+                                         kda_dtype io, void* workspace, size_t workspace_bytes,
+                                         float* ckpt, int64_t ckpt_every, void* stream) {
+  if (a == nullptr) return KDA_ERR_NULL_POINTER;
+  return varlen_fwd(q, k, v, nullptr, b, cu_seqlens, N, total, max_len, s0, o, s_out, gate,
+                    norm_w, eps, H, dk, dv, scale, io, workspace, workspace_bytes, ckpt,
+                    ckpt_every, a, stream);
 }
 
 }  // extern "C"

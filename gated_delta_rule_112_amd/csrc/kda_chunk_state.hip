@@ -760,7 +760,6 @@ int64_t chunk_mfma_launches(int64_t B, int64_t T, int64_t H) {
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a) {
   if (!chunk_mfma_supports(a.dk, a.dv, a.io_bf16)) return hipErrorNotSupported;
-  if (a.cu != nullptr && a.ga != nullptr) return hipErrorNotSupported;
   const int cus = device_cus();
   const int64_t half = record_half(a.B, a.T, a.H, cus);
   const int64_t np = pairs_of(a.T);
@@ -803,9 +802,10 @@ hipError_t launch_chunk_mfma(const ChunkArgs& a) {
     // 32 state columns per state wavefront: one state and one loader
     // wavefront per SIMD, each with up to 256 registers (the tile builder
     // running in the same launch needs them).
-    // (packed sequences take g and beta as given)
     hipError_t e;
-    if (a.cu != nullptr)
+    if (a.cu != nullptr && a.ga != nullptr)
+      e = launch_layout<true, true>(as, gs.split, cur, s_in, s_next, gb.a, nxt, cus);
+    else if (a.cu != nullptr)
       e = launch_layout<true, false>(as, gs.split, cur, s_in, s_next, gb.a, nxt, cus);
     else if (a.ga != nullptr)
       e = launch_layout<false, true>(as, gs.split, cur, s_in, s_next, gb.a, nxt, cus);

@@ -219,6 +219,22 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v,
                                 void* stream);
 
 /*
+ * kda_chunk_fwd_varlen_prologue -- kda_chunk_fwd_varlen from the raw
+ * projections: q and k L2-normalised, g = -5 sigmoid(a) and beta = sigmoid(b)
+ * formed in the kernels (as kda_chunk_fwd_prologue): a [total, H, dk] in the io
+ * dtype in place of g, b [total, H] float32 in place of beta; everything else,
+ * checkpoints included, as kda_chunk_fwd_varlen.
+ */
+kda_status kda_chunk_fwd_varlen_prologue(const void* q, const void* k, const void* v,
+                                         const void* a, const float* b,
+                                         const int32_t* cu_seqlens, int64_t N, int64_t total,
+                                         int64_t max_len, const float* s0, void* o,
+                                         float* s_out, const void* gate, const float* norm_w,
+                                         float eps, int64_t H, int dk, int dv, float scale,
+                                         kda_dtype io, void* workspace, size_t workspace_bytes,
+                                         float* ckpt, int64_t ckpt_every, void* stream);
+
+/*
  * kda_decode_step -- one token per sequence against a resident state.
  *
  * The constant-cost recurrent step ("Kimi K3 Architecture Explained ...",

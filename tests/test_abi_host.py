@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ["kda_chunk_fwd", "kda_chunk_fwd_checkpoints", "kda_chunk_fwd_varlen",
-              "kda_chunk_fwd_workspace_size",
+              "kda_chunk_fwd_varlen_prologue", "kda_chunk_fwd_workspace_size",
               "kda_chunk_fwd_launches",
               "kda_decode_step", "kda_decode_multi", "kda_chunk_fwd_prologue",
               "kda_decode_step_prologue", "kda_decode_multi_prologue",
@@ -194,6 +194,23 @@ def test_chunk_varlen_validation(lib):
     assert call(cu=P(6)) == ALIAS             # cu_seqlens inside o
     assert call(ckpt=P(11), every=40) == SHAPE
     assert call(ckpt=P(1), every=32) == ALIAS   # checkpoints overlap q
+
+
+def test_chunk_varlen_prologue_validation(lib):
+    """The packed entry point from raw projections: a NULL logit array is
+    rejected, then kda_chunk_fwd_varlen's checks apply."""
+    f = lib.kda_chunk_fwd_varlen_prologue
+
+    def call(a=P(4), cu=P(12), N=3, o=6, ckpt=None, every=0):
+        return f(P(1), P(2), P(3), a, P(5), cu, N, 200, 100, None, P(o), P(7), None, None,
+                 1e-6, 3, 16, 16, 1.0, 0, None, 0, ckpt, every, None)
+
+    assert call(a=None) == NULLP
+    assert call(cu=None) == NULLP
+    assert call(N=0) == SHAPE
+    assert call(a=P(4, 8)) == ALIGN
+    assert call(o=4) == ALIAS                 # o overlaps the logits
+    assert call(ckpt=P(11), every=40) == SHAPE
 
 
 def test_prologue_validation(lib):

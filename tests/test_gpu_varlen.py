@@ -105,3 +105,45 @@ def test_varlen_serving_batch(kda):
     rng = np.random.default_rng(5)
     lens = [int(x) for x in rng.integers(1, 701, 64)]
     check(kda, lens, 8, 128, 128, torch.bfloat16, 1790, gate=True)
+
+
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, torch.bfloat16), (64, 32, torch.float32)])
+@pytest.mark.parametrize("gated", [False, True])
+def test_varlen_prologue_matches_oracle(kda, dk, dv, dtype, gated):
+    """kda_chunk_fwd_varlen_prologue: raw q and k (norms far from 1), decay and
+    write-strength logits; per sequence the oracle normalises q and k
+    (l2_normalize), forms g and beta (decay_gates) and runs the token
+    recurrence from the sequence's own initial state; checkpoints too."""
+    from oracle.kda_oracle import decay_gates, l2_normalize
+    lens, H, every = [1, 37, 0, 100, 64, 33], 3, 32
+    total = sum(lens)
+    gen_ = torch.Generator(device=dev())
+    gen_.manual_seed(1800 + dk + dv + gated)
+    r = lambda *s: torch.randn(*s, generator=gen_, device=dev())  # noqa: E731
+    q = (0.3 * r(total, H, dk)).to(dtype)
+    k = (2.0 * r(total, H, dk)).to(dtype)
+    v = r(total, H, dv).to(dtype)
+    a = (2.0 * r(total, H, dk)).to(dtype)
+    b = r(total, H)
+    s0 = 0.05 * r(len(lens), H, dk, dv)
+    gt = r(total, H, dv).to(dtype) if gated else None
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev())
+    y, S, ck = kda.chunk_fwd_varlen(q, k, v, a, b, cu, max(lens), s0, gate=gt, every=every,
+                                    prologue=True)
+    torch.cuda.synchronize()
+    g, beta = decay_gates(f64(a), f64(b))
+    x_all = [l2_normalize(f64(q)), l2_normalize(f64(k)), f64(v), g, beta]
+    for i, n in enumerate(lens):
+        st = int(sum(lens[:i]))
+        if n == 0:
+            assert torch.equal(S[i], s0[i]), "an empty sequence keeps its initial state"
+            continue
+        x = [t[st:st + n][None] for t in x_all]
+        o_ref, S_ref = o_recurrent(*x, f64(s0[i:i + 1]))
+        if gt is not None:
+            o_ref = o_gate_rmsnorm(o_ref, f64(gt[st:st + n])[None], None, 1e-6)
+        assert_close(f64(y[st:st + n]), o_ref[0], TOL[dtype], f"y seq {i} (len {n})", dtype)
+        assert_close(f64(S[i]), S_ref[0], TOL[dtype], f"state seq {i}")
+        for j in range(n // every):
+            _, Sj = o_recurrent(*(t[:, :(j + 1) * every] for t in x), f64(s0[i:i + 1]))
+            assert_close(f64(ck[i, j]), Sj[0], TOL[dtype], f"checkpoint {j} seq {i}")
