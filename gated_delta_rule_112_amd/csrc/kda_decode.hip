@@ -332,15 +332,17 @@ kda_decode_multi_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
 //   S_n = Diag(e^G_{n-1}) (S + Kc[:n]^T D[:n])   (the state after the first n tokens)
 // so the K dependent token steps of kda_decode_multi_kernel become a few
 // block-wide phases.  dk = dv = 128, the state in the same float4 strips as
-// the single-token kernel; same contract as kda_decode_multi_kernel.
-template <typename IO>
+// the single-token kernel; same contract as kda_decode_multi_kernel (with ga:
+// from the raw projections, q and k normalised and g, beta from their logits).
+template <typename IO, bool LOGITS>
 __global__ void __launch_bounds__(256, 3)
 kda_multi_chunk_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
                        const IO* __restrict__ v, const float* __restrict__ g,
                        const float* __restrict__ beta, float* __restrict__ state,
                        const int* __restrict__ n_commit, IO* __restrict__ o,
                        const IO* __restrict__ gate, const float* __restrict__ norm_w, float eps,
-                       float scale, int64_t B, int64_t K, int64_t H) {
+                       float scale, int64_t B, int64_t K, int64_t H,
+                       const IO* __restrict__ ga) {
   constexpr int D = 128, KM = 4, CG = D / 4, RG = 256 / CG, RPT = D / RG;
   __shared__ float kh[KM][D], qh[KM][D], kc[KM][D], ex[KM][D];
   __shared__ float vv[KM][D];            // values, then D (the deltas)
@@ -370,11 +372,34 @@ kda_multi_chunk_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
       const int64_t rw = row(u, t);
       kh[t][c] = ld_f32(k + rw * D + c);
       qh[t][c] = ld_f32(q + rw * D + c);
-      kc[t][c] = g[rw * D + c];
+      kc[t][c] = LOGITS ? -5.f * sigmoidf_(ld_f32(ga + rw * D + c)) : g[rw * D + c];
       vv[t][c] = ld_f32(v + rw * D + c);
     }
-    if (tid < L) bt[tid] = beta[row(u, tid)];
+    if (tid < L) {
+      const float bb = beta[row(u, tid)];
+      bt[tid] = LOGITS ? sigmoidf_(bb) : bb;
+    }
     __syncthreads();
+    if constexpr (LOGITS) {  // from raw projections: wave t L2-normalises q and k of token t
+      const int t = tid / 64, l = tid % 64;
+      const bool live = t < L;
+      const float q0 = live ? qh[t][l] : 0.f, q1 = live ? qh[t][l + 64] : 0.f;
+      const float k0 = live ? kh[t][l] : 0.f, k1 = live ? kh[t][l + 64] : 0.f;
+      float nq = q0 * q0 + q1 * q1, nk = k0 * k0 + k1 * k1;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        nq += __shfl_xor(nq, off);
+        nk += __shfl_xor(nk, off);
+      }
+      if (live) {
+        const float rq = rsqrtf(fmaxf(nq, 1e-24f)), rk = rsqrtf(fmaxf(nk, 1e-24f));
+        qh[t][l] = q0 * rq;
+        qh[t][l + 64] = q1 * rq;
+        kh[t][l] = k0 * rk;
+        kh[t][l + 64] = k1 * rk;
+      }
+      __syncthreads();
+    }
     // 2. cumulative log-decay per channel, the rescaled keys and queries
     if (tid < D) {
       float gam = 0.f;
@@ -521,13 +546,14 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
   using Sh = DecodeShape<DK, DV>;
   const int64_t bhn = a.B * a.H;
   const int nblk = decode_grid(bhn);
-  if (a.K >= 2 && a.K <= 4 && a.o != nullptr && DK == 128 && DV == 128 && a.ga == nullptr) {
+  if (a.K >= 2 && a.K <= 4 && a.o != nullptr && DK == 128 && DV == 128) {
     // verify calls with few draft tokens: the chunkwise form, three workgroups per CU
     const int64_t cblk = bhn < 3 * (int64_t)nblk ? bhn : 3 * (int64_t)nblk;
-    hipLaunchKernelGGL((kda_multi_chunk_kernel<IO>), dim3((unsigned)cblk), dim3(256), 0,
-                       (hipStream_t)a.stream, (const IO*)a.q, (const IO*)a.k, (const IO*)a.v,
-                       a.g, a.beta, a.state, a.n_commit, (IO*)a.o, (const IO*)a.gate,
-                       a.norm_w, a.eps, a.scale, a.B, a.K, a.H);
+    auto kern = a.ga != nullptr ? kda_multi_chunk_kernel<IO, true> : kda_multi_chunk_kernel<IO, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)cblk), dim3(256), 0, (hipStream_t)a.stream,
+                       (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta, a.state,
+                       a.n_commit, (IO*)a.o, (const IO*)a.gate, a.norm_w, a.eps, a.scale, a.B,
+                       a.K, a.H, (const IO*)a.ga);
     return hipGetLastError();
   }
   if (a.K > 0) {

@@ -140,17 +140,19 @@ def test_decode_prologue_match_oracle(kda, dk, dv, dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_decode_multi_prologue_match_oracle(kda, dtype):
-    """K = 5 raw tokens per sequence, verify then commit of the accepted counts."""
-    B, K, H, dk, dv = 4, 5, 3, 128, 128
-    q, k, v, a, b, _, gt = gen(B, K, H, dk, dv, dtype, 2250, gate=True)
+@pytest.mark.parametrize("K", [2, 4, 5])
+def test_decode_multi_prologue_match_oracle(kda, dtype, K):
+    """K raw tokens per sequence, verify then commit of the accepted counts
+    (verify with 2-4 tokens runs the chunkwise kernel, 5 the token kernel)."""
+    B, H, dk, dv = 4, 3, 128, 128
+    q, k, v, a, b, _, gt = gen(B, K, H, dk, dv, dtype, 2250 + K, gate=True)
     gen_ = torch.Generator(device=dev())
     gen_.manual_seed(2251)
     state = 0.3 * torch.randn(B, H, dk, dv, generator=gen_, device=dev())
     S0 = state.clone()
     y = kda.decode_multi(q, k, v, a, b, state, torch.zeros(B, dtype=torch.int32, device=dev()),
                          gate=gt, prologue=True)
-    acc = [0, 2, 5, 3]
+    acc = [0, min(2, K), K, min(3, K)]
     kda.decode_multi(q, k, v, a, b, state, torch.tensor(acc, dtype=torch.int32, device=dev()),
                      output=False, prologue=True)
     g, beta = decay_gates(f64(a), f64(b))
