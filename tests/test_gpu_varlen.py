@@ -107,18 +107,16 @@ def test_varlen_serving_batch(kda):
     check(kda, lens, 8, 128, 128, torch.bfloat16, 1790, gate=True)
 
 
-@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, torch.bfloat16), (64, 32, torch.float32)])
-@pytest.mark.parametrize("gated", [False, True])
-def test_varlen_prologue_matches_oracle(kda, dk, dv, dtype, gated):
+def check_prologue(kda, lens, H, dk, dv, dtype, seed, gated=False, every=0, output=True,
+                   final_state=True):
     """kda_chunk_fwd_varlen_prologue: raw q and k (norms far from 1), decay and
     write-strength logits; per sequence the oracle normalises q and k
     (l2_normalize), forms g and beta (decay_gates) and runs the token
     recurrence from the sequence's own initial state; checkpoints too."""
     from oracle.kda_oracle import decay_gates, l2_normalize
-    lens, H, every = [1, 37, 0, 100, 64, 33], 3, 32
     total = sum(lens)
     gen_ = torch.Generator(device=dev())
-    gen_.manual_seed(1800 + dk + dv + gated)
+    gen_.manual_seed(seed)
     r = lambda *s: torch.randn(*s, generator=gen_, device=dev())  # noqa: E731
     q = (0.3 * r(total, H, dk)).to(dtype)
     k = (2.0 * r(total, H, dk)).to(dtype)
@@ -129,21 +127,43 @@ def test_varlen_prologue_matches_oracle(kda, dk, dv, dtype, gated):
     gt = r(total, H, dv).to(dtype) if gated else None
     cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev())
     y, S, ck = kda.chunk_fwd_varlen(q, k, v, a, b, cu, max(lens), s0, gate=gt, every=every,
-                                    prologue=True)
+                                    output=output, final_state=final_state, prologue=True)
     torch.cuda.synchronize()
     g, beta = decay_gates(f64(a), f64(b))
     x_all = [l2_normalize(f64(q)), l2_normalize(f64(k)), f64(v), g, beta]
     for i, n in enumerate(lens):
         st = int(sum(lens[:i]))
         if n == 0:
-            assert torch.equal(S[i], s0[i]), "an empty sequence keeps its initial state"
+            if final_state:
+                assert torch.equal(S[i], s0[i]), "an empty sequence keeps its initial state"
             continue
         x = [t[st:st + n][None] for t in x_all]
         o_ref, S_ref = o_recurrent(*x, f64(s0[i:i + 1]))
         if gt is not None:
             o_ref = o_gate_rmsnorm(o_ref, f64(gt[st:st + n])[None], None, 1e-6)
-        assert_close(f64(y[st:st + n]), o_ref[0], TOL[dtype], f"y seq {i} (len {n})", dtype)
-        assert_close(f64(S[i]), S_ref[0], TOL[dtype], f"state seq {i}")
-        for j in range(n // every):
+        if output:
+            assert_close(f64(y[st:st + n]), o_ref[0], TOL[dtype], f"y seq {i} (len {n})", dtype)
+        if final_state:
+            assert_close(f64(S[i]), S_ref[0], TOL[dtype], f"state seq {i}")
+        for j in range(n // every if every else 0):
             _, Sj = o_recurrent(*(t[:, :(j + 1) * every] for t in x), f64(s0[i:i + 1]))
             assert_close(f64(ck[i, j]), Sj[0], TOL[dtype], f"checkpoint {j} seq {i}")
+
+
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, torch.bfloat16), (64, 32, torch.float32)])
+@pytest.mark.parametrize("gated", [False, True])
+def test_varlen_prologue_matches_oracle(kda, dk, dv, dtype, gated):
+    check_prologue(kda, [1, 37, 0, 100, 64, 33], 3, dk, dv, dtype, 1800 + dk + dv + gated,
+                   gated=gated, every=32)
+
+
+@pytest.mark.parametrize("split", ["1", "2"])
+@pytest.mark.parametrize("seg", ["1", "3"])
+@pytest.mark.parametrize("what", ["output", "state"])
+def test_varlen_prologue_segments(kda, monkeypatch, split, seg, what):
+    """Matrix-core path from raw projections: segments of one and three pairs,
+    one or two state workgroups per head, output-only and state-only calls."""
+    monkeypatch.setenv("KDA_CHUNK_SPLIT", split)
+    monkeypatch.setenv("KDA_SEG_PAIRS", seg)
+    check_prologue(kda, [70, 0, 130, 5], 2, 128, 128, torch.bfloat16, 1850 + int(seg),
+                   output=what == "output", final_state=what == "state")
