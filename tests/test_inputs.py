@@ -1,4 +1,6 @@
 """Seeded input generators: determinism, shapes and the stated distributions."""
+import os
+
 import torch
 
 from gated_delta_rule_112_amd.inputs import (WORKLOADS, Workload, make_decode_state,
@@ -63,3 +65,15 @@ def test_bench_byte_accounting():
     assert v == 2 * 3 * (4 * 128 * 128 + 4 * (tok_in + 2 * 128 * 2))
     assert c == 4 + (3 * (8 * 128 * 128 + 3 * tok_in) + 4)          # nothing read for 0 accepted
     assert bench.prefill_flops(1, 1, 1, 128, 128) == 6 * 16 * 128 + 4 * 16 * 128 + 6 * 128 * 128
+
+
+def test_bench_refuses_several_gpus():
+    """The benchmark measures one GPU: --gpus above 1 exits with status 2 and a
+    message, before any GPU work."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
