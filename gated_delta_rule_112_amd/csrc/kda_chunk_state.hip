@@ -676,6 +676,7 @@ bool chunk_mfma_supports(int dk, int dv, bool io_bf16) {
 // rather than state and tile workgroups taking turns on the compute units.
 int64_t group_seqs(int64_t B, int64_t H, int cus) {
   int64_t g = (3 * (int64_t)cus / 8) / H;
+  if (const char* e = getenv("KDA_GROUP_SEQS")) g = atoll(e);  // tests and tuning
   if (g < 1) g = 1;
   return g < B ? g : B;
 }

@@ -167,3 +167,12 @@ def test_varlen_prologue_segments(kda, monkeypatch, split, seg, what):
     monkeypatch.setenv("KDA_SEG_PAIRS", seg)
     check_prologue(kda, [70, 0, 130, 5], 2, 128, 128, torch.bfloat16, 1850 + int(seg),
                    output=what == "output", final_state=what == "state")
+
+
+@pytest.mark.parametrize("group", ["1", "2", "4"])
+def test_varlen_launch_groups(kda, monkeypatch, group):
+    """Sequences split into launch groups of 1, 2 or 4 (6 sequences: 6, 3 or 2
+    groups, the last one short), records and carried state handed from group
+    to group inside one pipeline; gated, with checkpoints."""
+    monkeypatch.setenv("KDA_GROUP_SEQS", group)
+    check(kda, LENS, 3, 128, 128, torch.bfloat16, 1900 + int(group), gate=True, every=32)
