@@ -392,3 +392,67 @@ def test_l2_normalize_pins():
     assert np.allclose(l2_normalize(3.7 * x), y, atol=1e-15)
     assert np.all(l2_normalize(np.zeros((2, 4))) == 0.0)
     assert np.array_equal(l2_normalize(np.array([3.0, 4.0])), np.array([0.6, 0.8]))
+
+
+# ----------------------------------------------------------------------------- gradient oracle
+def _vjp_case(seed, B=1, T=3, H=2, dk=3, dv=2):
+    rng = np.random.default_rng(seed)
+    x = {"q": rng.normal(size=(B, T, H, dk)), "k": rng.normal(size=(B, T, H, dk)) / 2,
+         "v": rng.normal(size=(B, T, H, dv)), "g": -5.0 / (1 + np.exp(-rng.normal(size=(B, T, H, dk)))),
+         "beta": 1.0 / (1 + np.exp(-rng.normal(size=(B, T, H)))),
+         "s0": 0.5 * rng.normal(size=(B, H, dk, dv))}
+    do = rng.normal(size=(B, T, H, dv))
+    dsf = rng.normal(size=(B, H, dk, dv))
+    return x, do, dsf
+
+
+def test_vjp_central_differences():
+    """Every gradient element of kda_recurrent_vjp (autograd through a torch
+    loop) against a central difference of the NumPy forward kda_recurrent
+    (independent code), for L = sum(o * do) + sum(S_T * dS_T) and scale 0.7."""
+    from oracle.kda_oracle_grad import kda_recurrent_vjp
+    x, do, dsf = _vjp_case(11)
+    scale = 0.7
+
+    def loss(xx):
+        o, S = kda_recurrent(xx["q"], xx["k"], xx["v"], xx["g"], xx["beta"], xx["s0"], scale)
+        return float(np.sum(o * do) + np.sum(S * dsf))
+
+    got = kda_recurrent_vjp(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], do, dsf, scale)
+    h = 1e-5
+    for name, key in [("q", "dq"), ("k", "dk"), ("v", "dv"), ("g", "dg"), ("beta", "dbeta"),
+                      ("s0", "ds0")]:
+        fd = np.zeros_like(x[name])
+        for idx in np.ndindex(x[name].shape):
+            xp = {n: a.copy() for n, a in x.items()}
+            xm = {n: a.copy() for n, a in x.items()}
+            xp[name][idx] += h
+            xm[name][idx] -= h
+            fd[idx] = (loss(xp) - loss(xm)) / (2 * h)
+        assert got[key].shape == x[name].shape
+        np.testing.assert_allclose(got[key], fd, rtol=1e-6, atol=1e-8, err_msg=key)
+
+
+def test_vjp_single_token_closed_form():
+    """One token: S_1 = M S_0 + beta k v^T with M = (I - beta k k^T) Diag(a),
+    o = scale S_1^T q.  From S_0 = 0: dv = scale beta (k.q) do,
+    dq = scale beta (v.do) k, dk = scale beta (v.do) q, dbeta = scale (k.q)(v.do),
+    dg = 0 (the decay multiplies a zero state), and for any S_0
+    dS_0 = M^T (scale q do^T) = Diag(a) (I - beta k k^T) scale q do^T."""
+    from oracle.kda_oracle_grad import kda_recurrent_vjp
+    rng = np.random.default_rng(5)
+    dk, dv, scale = 4, 3, 1.3
+    q, k, v = rng.normal(size=dk), rng.normal(size=dk), rng.normal(size=dv)
+    g, beta, do = -rng.uniform(0.1, 5.0, size=dk), 0.6, rng.normal(size=dv)
+    r = lambda a: a.reshape(1, 1, 1, -1)  # noqa: E731
+    got = kda_recurrent_vjp(r(q), r(k), r(v), r(g), np.full((1, 1, 1), beta), None, r(do),
+                            None, scale)
+    kq, vd = k @ q, v @ do
+    np.testing.assert_allclose(got["dv"].ravel(), scale * beta * kq * do, rtol=1e-12)
+    np.testing.assert_allclose(got["dq"].ravel(), scale * beta * vd * k, rtol=1e-12)
+    np.testing.assert_allclose(got["dk"].ravel(), scale * beta * vd * q, rtol=1e-12)
+    np.testing.assert_allclose(got["dbeta"].ravel(), [scale * kq * vd], rtol=1e-12)
+    np.testing.assert_array_equal(got["dg"], np.zeros((1, 1, 1, dk)))
+    M = (np.eye(dk) - beta * np.outer(k, k)) @ np.diag(np.exp(g))
+    np.testing.assert_allclose(got["ds0"][0, 0], M.T @ (scale * np.outer(q, do)), rtol=1e-12,
+                               atol=1e-15)
