@@ -310,6 +310,35 @@ def bench_packed(kda, torch, w, steps, prologue=False):
     return e0.elapsed_time(e1) / steps, total, max_len
 
 
+def bench_backward(kda, torch, w, steps):
+    """The backward pass (kda_recurrent_bwd) over a prefill workload's inputs,
+    with dO drawn like v and a final-state gradient; returns ms per call."""
+    from gated_delta_rule_112_amd.inputs import make_prefill_inputs
+    dev = torch.device("cuda:0")
+    x = make_prefill_inputs(w, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed + 21)
+    dout = torch.randn(x["v"].shape, generator=gen, device=dev).to(x["v"].dtype)
+    dsf = torch.randn((w.B, w.H, w.dk, w.dv), generator=gen, device=dev)
+    nws = kda.load_library().kda_recurrent_bwd_workspace_size(w.B, w.T, w.H, w.dk, w.dv)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        kda.recurrent_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], dout, x["s0"], dsf,
+                          workspace=ws, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def bench_decode(kda, torch, w, repeats=1):
     from gated_delta_rule_112_amd.inputs import make_decode_state, make_decode_step_inputs
     dev = torch.device("cuda:0")
@@ -393,6 +422,7 @@ def main():
                     choices=["small_prefill", "full_width_prefill", "million_token_prefill"])
     ap.add_argument("--decode-repeats", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-checkpoints", action="store_true")
     ap.add_argument("--no-packed", action="store_true")
@@ -503,6 +533,24 @@ def main():
             log(f"[bench] packed batch from raw projections: {rms:.3f} ms, "
                 f"{ptot / (rms * 1e-3) / 1e6:.2f} M tok/s")
 
+    backward = None
+    if not a.no_backward:
+        wb = WORKLOADS["small_prefill"]
+        bms = bench_backward(kda, torch, wb, 3)
+        ntok = wb.B * wb.T
+        # per token and head: q, k, v, dO read and dq, dk, dv written (io dtype),
+        # g read and dg written (float32), beta and dbeta; plus s0, dS_T, ds0 per head
+        es = 2 if wb.io == "bf16" else 4
+        per = 7 * wb.dk * es + 2 * wb.dk * 4 + 8
+        bbytes = ntok * wb.H * per + 3 * wb.B * wb.H * wb.dk * wb.dv * 4
+        bgbs = bbytes / (bms * 1e-3) / 1e9
+        backward = {"workload": wb.name, "B": wb.B, "H": wb.H, "T": wb.T,
+                    "ms": round(bms, 4), "tokens_per_s": round(ntok / (bms * 1e-3), 1),
+                    "algorithmic_bytes": bbytes, "achieved": round(bgbs, 1), "unit": "GB/s",
+                    "peak": HBM_PEAK_GBS, "frac": round(bgbs / HBM_PEAK_GBS, 4)}
+        log(f"[bench] backward ({wb.name}): {bms:.3f} ms, "
+            f"{ntok / (bms * 1e-3) / 1e6:.3f} M tok/s")
+
     decode = None
     if not a.no_decode:
         wd = WORKLOADS["batched_decode"]
@@ -561,6 +609,7 @@ def main():
         "prologue": prologue,
         "decode": decode,
         "verify": verify,
+        "backward": backward,
     }
     print(json.dumps(line), flush=True)
 

@@ -55,6 +55,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                          vp, f32, i64, ci, ci, f32, ci, vp, ctypes.c_size_t,
                                          vp, i64, vp]
     lib.kda_chunk_fwd_varlen.restype = ci
+    lib.kda_recurrent_bwd.argtypes = [vp] * 14 + [i64, i64, i64, ci, ci, f32, ci, vp,
+                                                 ctypes.c_size_t, vp]
+    lib.kda_recurrent_bwd.restype = ci
+    lib.kda_recurrent_bwd_workspace_size.argtypes = [i64, i64, i64, ci, ci]
+    lib.kda_recurrent_bwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_chunk_fwd_varlen_prologue.argtypes = lib.kda_chunk_fwd_varlen.argtypes
     lib.kda_chunk_fwd_varlen_prologue.restype = ci
     lib.kda_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, ci, ci, ci]
@@ -399,3 +404,40 @@ def gate_rmsnorm(x, gate, norm_w=None, *, eps: float = 1e-6, out=None, stream=No
                               _IO[io], _stream(dev, stream))
     _check(lib, "kda_gate_rmsnorm", st)
     return out
+
+
+def recurrent_bwd(q, k, v, g, beta, dout, s0=None, ds_final=None, *, scale: float = 1.0,
+                  workspace=None, stream=None):
+    """Gradients of the token recurrence (kda_recurrent_bwd): q, k, v, dout [B, T, H, 128]
+    (io dtype), g [B, T, H, 128] and beta [B, T, H] float32, s0 / ds_final [B, H, 128, 128]
+    float32 or None.  Returns (dq, dk, dv, dg, dbeta, ds0)."""
+    lib = load_library()
+    if q.device.type != "cuda":
+        raise ValueError("kda ops need CUDA (HIP) tensors")
+    dev = q.device
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    io = q.dtype
+    if io not in _IO:
+        raise TypeError(f"unsupported io dtype {io}")
+    _need(q, "q", io, (B, T, H, dk), dev)
+    _need(k, "k", io, (B, T, H, dk), dev)
+    _need(v, "v", io, (B, T, H, dv), dev)
+    _need(dout, "dout", io, (B, T, H, dv), dev)
+    _need(g, "g", torch.float32, (B, T, H, dk), dev)
+    _need(beta, "beta", torch.float32, (B, T, H), dev)
+    for t, n in ((s0, "s0"), (ds_final, "ds_final")):
+        if t is not None:
+            _need(t, n, torch.float32, (B, H, dk, dv), dev)
+    dq, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg, dbeta = torch.empty_like(g), torch.empty_like(beta)
+    ds0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    nws = lib.kda_recurrent_bwd_workspace_size(B, T, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    st = lib.kda_recurrent_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(dout), _ptr(ds_final),
+        _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(dbeta), _ptr(ds0), B, T, H, dk, dv,
+        float(scale), _IO[io], _ptr(workspace), workspace.numel(), _stream(dev, stream))
+    _check(lib, "kda_recurrent_bwd", st)
+    return dq, dk_, dv_, dg, dbeta, ds0

@@ -86,6 +86,55 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk, int
   return kda::chunk_mfma_workspace(B, T, H);
 }
 
+size_t kda_recurrent_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk, int dv) {
+  if (dk != 128 || dv != 128 || prod(B, T, H, dk) < 0) return 0;
+  const int64_t n = kda::bwd_workspace_floats(B, T, H);
+  return n > 0 && n < kMaxElems ? (size_t)n * 4 : 0;
+}
+
+kda_status kda_recurrent_bwd(const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const float* s0, const void* dout,
+                             const float* ds_final, void* dq, void* dk_out, void* dv_out,
+                             float* dg, float* dbeta, float* ds0, int64_t B, int64_t T,
+                             int64_t H, int dk, int dv, float scale, kda_dtype io,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !g || !beta || !dout || !dq || !dk_out || !dv_out || !dg || !dbeta)
+    return KDA_ERR_NULL_POINTER;
+  if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_BAD_DTYPE;
+  if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED_DIM;
+  if (dk != 128 || dv != 128) return KDA_ERR_UNSUPPORTED_DIM;
+  const int64_t nqk = prod(B, T, H, dk), nb = prod(B, T, H), ns = prod(B, H, dk, dv);
+  if (nqk < 0 || nb < 0 || ns < 0 || B * H > 0x7fffffffLL) return KDA_ERR_BAD_SHAPE;
+  if (!isfinite(scale)) return KDA_ERR_BAD_ARGUMENT;
+  const size_t need = kda_recurrent_bwd_workspace_size(B, T, H, dk, dv);
+  if (need == 0) return KDA_ERR_BAD_SHAPE;
+  if (workspace == nullptr || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+  const uintptr_t ea = (io == KDA_BF16) ? 2 : 4;
+  for (const void* p : {q, k, v, dout, (const void*)dq, (const void*)dk_out, (const void*)dv_out})
+    if (!aligned(p, ea)) return KDA_ERR_MISALIGNED;
+  for (const void* p : {(const void*)g, (const void*)beta, (const void*)dg, (const void*)dbeta})
+    if (!aligned(p, 4)) return KDA_ERR_MISALIGNED;
+  for (const void* p : {(const void*)s0, (const void*)ds_final, (const void*)ds0,
+                        (const void*)workspace})
+    if (!aligned(p, 16)) return KDA_ERR_MISALIGNED;
+
+  const int64_t es = (io == KDA_BF16) ? 2 : 4;
+  const Span in[] = {{q, nqk * es}, {k, nqk * es}, {v, nqk * es}, {g, nqk * 4}, {beta, nb * 4},
+                     {s0, ns * 4}, {dout, nqk * es}, {ds_final, ns * 4}};
+  const Span out[] = {{dq, nqk * es}, {dk_out, nqk * es}, {dv_out, nqk * es}, {dg, nqk * 4},
+                      {dbeta, nb * 4}, {ds0, ns * 4}, {workspace, (int64_t)need}};
+  for (int i = 0; i < 7; ++i) {
+    for (const Span& x : in)
+      if (overlap(out[i], x)) return KDA_ERR_ALIAS;
+    for (int j = i + 1; j < 7; ++j)
+      if (overlap(out[i], out[j])) return KDA_ERR_ALIAS;
+  }
+
+  kda::BwdArgs a{q, k, v, g, beta, s0, dout, ds_final, dq, dk_out, dv_out, dg, dbeta, ds0,
+                 B, T, H, scale, io == KDA_BF16, (float*)workspace, stream};
+  return kda::launch_recurrent_bwd(a) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 int64_t kda_chunk_fwd_launches(int64_t B, int64_t T, int64_t H, int dk, int dv, kda_dtype io) {
   if ((io != KDA_F32 && io != KDA_BF16) || !dim_ok(dk) || !dim_ok(dv)) return 0;
   if (prod(B, T, H, dk) < 0 || prod(B, H, dk, dv) < 0) return 0;

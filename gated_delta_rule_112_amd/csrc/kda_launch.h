@@ -81,4 +81,32 @@ size_t chunk_mfma_workspace(int64_t B, int64_t T, int64_t H);
 int64_t chunk_mfma_launches(int64_t B, int64_t T, int64_t H);
 hipError_t launch_gate_rmsnorm(const NormArgs& a);
 
+// Backward of the token recurrence (dk = dv = 128): gradients of a loss given
+// dO for every token and dS_T for the final state.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const float* s0;   // NULL: zero initial state
+  const void* dout;  // dO [B, T, H, dv]
+  const float* ds_final;  // NULL: no final-state term
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+  float* dbeta;
+  float* ds0;        // NULL: not written
+  int64_t B, T, H;
+  float scale;
+  bool io_bf16;
+  float* workspace;  // bwd_workspace_floats(B, T, H) floats
+  void* stream;
+};
+// Pieces of the reverse sweep: the state is checkpointed every kBwdPiece tokens.
+constexpr int kBwdPiece = 64;
+int64_t bwd_workspace_floats(int64_t B, int64_t T, int64_t H);
+hipError_t launch_recurrent_bwd(const BwdArgs& a);
+
 }  // namespace kda

@@ -331,6 +331,43 @@ kda_status kda_gate_rmsnorm(const void* x, const void* gate, const float* norm_w
                             int64_t rows, int dv, float eps, kda_dtype io, void* stream);
 
 /*
+ * kda_recurrent_bwd -- gradients of the token recurrence (the backward pass).
+ *
+ * The forward is the recurrence of kda_decode_step over T tokens ("Kimi K3
+ * Architecture Explained ...", section "Token mixing"):
+ *   S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T,  o_t = scale S_t^T q_t.
+ * The pages give no backward pass; this returns the plain gradients of a loss
+ * L given dL/do_t = dout[t] for every token and dL/dS_T = ds_final:
+ *   dq, dk, dv, dg (with respect to the log-decay g), dbeta and ds0 (the initial state).
+ * The state is recomputed from checkpoints every 64 tokens held in the workspace.
+ *
+ *   q, k, v, dout     [B, T, H, 128]  io dtype
+ *   g                 [B, T, H, 128]  float32;  beta [B, T, H] float32
+ *   s0, ds_final      [B, H, 128, 128] float32 or NULL (zero initial state; no final-state term)
+ *   dq, dk, dv        [B, T, H, 128]  io dtype, written
+ *   dg                [B, T, H, 128]  float32, written;  dbeta [B, T, H] float32, written
+ *   ds0               [B, H, 128, 128] float32 or NULL (not written)
+ *   dk = dv = 128 only (else KDA_ERR_UNSUPPORTED_DIM).
+ *   workspace         at least kda_recurrent_bwd_workspace_size(B, T, H, 128, 128) bytes, 16-byte
+ *                     aligned; contents undefined after the call.
+ *   Alignment: s0, ds_final, ds0 16 bytes; every other pointer to its element size.
+ *   No output may overlap an input or another output.
+ */
+kda_status kda_recurrent_bwd(const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const float* s0, const void* dout,
+                             const float* ds_final, void* dq, void* dk_out, void* dv_out,
+                             float* dg, float* dbeta, float* ds0, int64_t B, int64_t T,
+                             int64_t H, int dk, int dv, float scale, kda_dtype io,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_recurrent_bwd_workspace_size -- bytes of workspace kda_recurrent_bwd
+ * needs: per (b, h), float32 states for ceil(T / 64) checkpoints plus 64
+ * recomputed tokens (64 KiB each).  0 for unsupported sizes.
+ */
+size_t kda_recurrent_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk, int dv);
+
+/*
  * kda_chunk_fwd_launches -- number of kernel launches one kda_chunk_fwd call
  * makes for these sizes (matrix-core path: one per segment of tiles plus one),
  * or 0 for arguments kda_chunk_fwd would reject.  For profiling and reporting.

@@ -296,3 +296,32 @@ def test_chunk_kernel_query(lib):
     assert lib.kda_chunk_fwd_kernel(16, 16, 0) in (b"kda_chunk_valu", b"kda_chunk_mfma")
     assert lib.kda_chunk_fwd_kernel(48, 16, 0) is None
     assert lib.kda_chunk_fwd_kernel(16, 16, 5) is None
+
+
+def test_recurrent_bwd_validation(lib):
+    """kda_recurrent_bwd: required pointers, dk = dv = 128 only, workspace size,
+    alignment of the float4 state arguments, and no output over an input or
+    another output; every rejection happens before any launch."""
+    f = lib.kda_recurrent_bwd
+    B, T, H = 2, 70, 2
+    need = lib.kda_recurrent_bwd_workspace_size(B, T, H, 128, 128)
+    assert need == B * H * (2 + 64) * 128 * 128 * 4      # ceil(70 / 64) checkpoints + 64 states
+    assert lib.kda_recurrent_bwd_workspace_size(B, T, H, 64, 64) == 0
+
+    def call(q=1, dq=9, ds0=14, s0=6, dk=128, ws=15, nws=None, io=0):
+        a = {i: P(i) for i in range(1, 16)}
+        a[1], a[9], a[14], a[6], a[15] = (None if q is None else P(q)), P(dq), \
+            (None if ds0 is None else P(ds0)), (None if s0 is None else P(s0)), \
+            (None if ws is None else (P(ws) if isinstance(ws, int) else ws))
+        return f(a[1], a[2], a[3], a[4], a[5], a[6], a[7], a[8], a[9], a[10], a[11], a[12],
+                 a[13], a[14], B, T, H, dk, dk, 1.0, io, a[15], need if nws is None else nws, None)
+
+    assert call(q=None) == NULLP
+    assert call(dk=64) == DIM
+    assert call(dk=100) == DIM
+    assert call(io=7) == DTYPE
+    assert call(ws=None) == WORKSPACE
+    assert call(nws=need - 1) == WORKSPACE
+    assert call(ws=P(15, 4)) == ALIGN
+    assert call(s0=None, ds0=None, dq=1) == ALIAS     # dq over q
+    assert call(ds0=9) == ALIAS                        # ds0 over dq
