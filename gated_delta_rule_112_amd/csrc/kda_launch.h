@@ -106,6 +106,8 @@ struct BwdArgs {
 };
 // Pieces of the reverse sweep: the state is checkpointed every kBwdPiece tokens.
 constexpr int kBwdPiece = 64;
+// Workgroups per (b, h) in the backward pass (each holds 128 / kBwdSplit value columns).
+constexpr int kBwdSplit = 4;
 int64_t bwd_workspace_floats(int64_t B, int64_t T, int64_t H);
 hipError_t launch_recurrent_bwd(const BwdArgs& a);
 

@@ -363,7 +363,8 @@ kda_status kda_recurrent_bwd(const void* q, const void* k, const void* v, const 
 /*
  * kda_recurrent_bwd_workspace_size -- bytes of workspace kda_recurrent_bwd
  * needs: per (b, h), float32 states for ceil(T / 64) checkpoints plus 64
- * recomputed tokens (64 KiB each).  0 for unsupported sizes.
+ * recomputed tokens (64 KiB each), then four column-partial sums of dq, dk, dg
+ * and dbeta per token and head.  0 for unsupported sizes.
  */
 size_t kda_recurrent_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk, int dv);
 

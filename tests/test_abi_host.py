@@ -305,7 +305,8 @@ def test_recurrent_bwd_validation(lib):
     f = lib.kda_recurrent_bwd
     B, T, H = 2, 70, 2
     need = lib.kda_recurrent_bwd_workspace_size(B, T, H, 128, 128)
-    assert need == B * H * (2 + 64) * 128 * 128 * 4      # ceil(70 / 64) checkpoints + 64 states
+    # ceil(70 / 64) checkpoints + 64 states per head, then 4 column parts of dq, dk, dg, dbeta
+    assert need == (B * H * (2 + 64) * 128 * 128 + 4 * B * T * H * (3 * 128 + 1)) * 4
     assert lib.kda_recurrent_bwd_workspace_size(B, T, H, 64, 64) == 0
 
     def call(q=1, dq=9, ds0=14, s0=6, dk=128, ws=15, nws=None, io=0):
