@@ -34,8 +34,12 @@ def rel_max_err(x, ref, out_dtype=None):
 
 
 def assert_close(x, ref, tol, what, out_dtype=None):
+    """max|x - ref| <= tol * RMS(ref), net of the final rounding's half-ulp when
+    ``out_dtype`` is given.  Prints both the raw and the net error, so that the
+    margin where the elements are largest can be read off the log."""
     err = rel_max_err(x, ref, out_dtype)
-    print(f"[parity] {what}: max|d|/RMS = {err:.3e} (tol {tol:.0e})")
+    raw = rel_max_err(x, ref) if out_dtype is not None else err
+    print(f"[parity] {what}: max|d|/RMS = {err:.3e} net, {raw:.3e} raw (tol {tol:.0e})")
     assert np.all(np.isfinite(np.asarray(x, dtype=np.float64))), f"{what}: non-finite values"
     assert err <= tol, f"{what}: max|d|/RMS = {err:.3e} > {tol:.1e}"
     return err

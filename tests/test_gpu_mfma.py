@@ -193,9 +193,10 @@ def test_mfma_decay_floor(kda, split):
 def test_mfma_deterministic(kda, split):
     q, k, v, g, beta, s0, _ = gen(1, 130, 4, 1101, s0_std=0.05)
     a = kda.chunk_fwd(q, k, v, g, beta, s0)
-    b = kda.chunk_fwd(q, k, v, g, beta, s0)
-    torch.cuda.synchronize()
-    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    for _ in range(9):  # bitwise-equal over 10 runs
+        b = kda.chunk_fwd(q, k, v, g, beta, s0)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
 def test_small_prefill_workload_sampled(kda):
