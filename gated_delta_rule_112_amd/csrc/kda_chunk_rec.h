@@ -8,10 +8,10 @@
 // tile of 16 tokens (rows past the end of the sequence are zero inputs with
 // g = beta = 0, which leave the state unchanged) with start state S (dk x dv,
 // rows = key channels) and G = in-tile inclusive cumulative sum of g:
-//   Qh = scale q e^G,  Kh = k e^G,  Kc = k e^-G,  Kb = k e^(G_15 - G),  E = e^G_15
+//   Qh = q e^G,  Kh = k e^G,  Kc = k e^-G,  Kb = k e^(G_15 - G),  E = e^G_15
 //   A  = strict_lower(Diag(beta) Kh Kc^T)     Aqk = lower(Qh Kc^T)
 //   T  = (I + A)^-1 Diag(beta)                W = T Kh
-//   D  = T V - W S                            O = Qh S + Aqk D
+//   D  = T V - W S                            O = scale (Qh S + Aqk D)
 //   S <- Diag(E) S + Kb^T D
 // The state pass steps over two tiles a, b at once.  Substituting the state
 // after tile a into tile b's lines gives, with every factor bounded by the
@@ -40,7 +40,8 @@
 //   [T_b | P], [Q_ba | Aqk_b]
 //                [lane][8] f16               lane (i, g): X[i][4 g + e] (e < 4),
 //                                                         Y[i][4 g + e - 4] (e >= 4)
-//   norms        [2][16] f32                 1/|q_a|, 1/|q_b| per token, when q and k are
+//   norms        [2][16] f32, f32            1/|q_a|, 1/|q_b| per token, then the largest 1/|k|
+//                                            of the pair, when q and k are
 //                                            normalised in the kernels (else unused; the key
 //                                            norms are then folded into T, W and P, whose rows
 //                                            carry 1/|k|, so that D' = Diag(1/|k|) D is what the
@@ -74,7 +75,7 @@ constexpr int kTa = 25088;
 constexpr int kAa = 25600;
 constexpr int kTbP = 26112;
 constexpr int kQbaAb = 27136;
-constexpr int kNorm = 28160;   // with q and k normalised in the kernels: 1/|q| per token
+constexpr int kNorm = 28160;   // with q and k normalised in the kernels: 1/|q| per token, max 1/|k|
 constexpr int kBytes = 28416;  // record stride, a multiple of 256
 
 __host__ __device__ constexpr int chan(int b, int p) {

@@ -43,9 +43,16 @@
 // stored at chunk position swz(t, u), so that the 8-byte reads of the state
 // waves (one token per lane, 4 columns) fall in distinct banks.
 //
-// Precision: the state and every accumulation are float32; the state and D
-// enter the products as float16 (11-bit significand), which requires the
-// state, the values and D to stay below 65504 in magnitude.
+// Precision: the state and every accumulation are float32; the state, V and
+// D enter the products as float16 (11-bit significand).  Float16's range is
+// kept out of the way by a power-of-two scale per state wavefront: the method
+// is linear in (V, S) for fixed q, k, g, beta, so each wavefront runs on
+// sigma V and sigma S (its own value columns; columns are independent) and
+// divides its outputs and stored states by sigma, all exactly.  Before each
+// pair it takes the largest magnitude m of its scaled state and values; when
+// m leaves [2^2, 2^11) it rescales the accumulators so that m lands in
+// [2^9, 2^10) (then |D| < 2^15 with unit keys), which keeps every float16
+// operand normal and finite for any float32 state or bfloat16 values.
 #include <stdlib.h>
 
 #include <vector>
@@ -77,6 +84,51 @@ __device__ __forceinline__ f16x8 with_low(f16x8 x, f16x4 lo) {
 // Elements 4 h .. 4 h + 3 of x (h = 0 or 1).
 __device__ __forceinline__ bf16x4 half4(bf16x8 x, int h) {
   return h == 0 ? __builtin_shufflevector(x, x, 0, 1, 2, 3) : __builtin_shufflevector(x, x, 4, 5, 6, 7);
+}
+
+// Largest of x over the 64 lanes (x >= 0), in every lane: a max-scan over
+// each 16-lane DPP row, then the four row maxima, compared as integers (the
+// bit patterns of non-negative floats order like their values).
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  x = fmaxf(x, dpp<0x111, true>(x));
+  x = fmaxf(x, dpp<0x112, true>(x));
+  x = fmaxf(x, dpp<0x114, true>(x));
+  x = fmaxf(x, dpp<0x118, true>(x));
+  const unsigned b = __builtin_bit_cast(unsigned, x);
+  unsigned m = (unsigned)__builtin_amdgcn_readlane((int)b, 15);
+  const unsigned m1 = (unsigned)__builtin_amdgcn_readlane((int)b, 31);
+  const unsigned m2 = (unsigned)__builtin_amdgcn_readlane((int)b, 47);
+  const unsigned m3 = (unsigned)__builtin_amdgcn_readlane((int)b, 63);
+  m = m1 > m ? m1 : m;
+  m = m2 > m ? m2 : m;
+  m = m3 > m ? m3 : m;
+  return __builtin_bit_cast(float, m);
+}
+
+// Unbiased binary exponent of a non-negative float (x in [2^e, 2^(e+1))),
+// or kNoExp for zero.  Denormals read as -127; inf and NaN as 128.
+constexpr int kNoExp = -1000;
+__device__ __forceinline__ int exp_of(float x) {
+  const int b = (int)(__builtin_bit_cast(unsigned, x) >> 23);
+  return x == 0.f ? kNoExp : b - 127;
+}
+
+// 2^e as a float, e in [-126, 127].
+__device__ __forceinline__ float exp2i(int e) {
+  return __builtin_bit_cast(float, (unsigned)(e + 127) << 23);
+}
+
+// Power-of-two scale of a state wavefront's operands.  The wavefront holds
+// sigma S (sigma = 2^sh) and forms sigma V; em is the exponent of the largest
+// magnitude among them.  While em stays in [kLoExp, kHiExp] the scale is
+// kept; otherwise the returned shift d moves em to kTargetExp (the caller
+// multiplies its accumulators by 2^d).  sh stays within [-120, 120].
+constexpr int kLoExp = 2, kHiExp = 10, kTargetExp = 9;
+__device__ __forceinline__ int scale_shift(int em, int sh) {
+  if (em == kNoExp || (em >= kLoExp && em <= kHiExp)) return 0;
+  int n = sh + (kTargetExp - em);
+  n = n < -120 ? -120 : (n > 120 ? 120 : n);
+  return n - sh;
 }
 
 // A slot is a whole number of 1 KB blocks (one direct-to-LDS load of a wave
@@ -117,7 +169,7 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
                  const float* __restrict__ norm_w, float eps, Seqs<PACKED> seqs, int64_t H,
                  int64_t BH,
                  int64_t x0, int64_t nseg, int64_t n_state_wg, float* __restrict__ ckpt,
-                 int64_t ckpt_every, tile::Args<PACKED, LOGITS> next) {
+                 int64_t ckpt_every, float scale, tile::Args<PACKED, LOGITS> next) {
   using SC = SlotCfg<DVW, GATE>;
   constexpr int kRing = SC::kRing, kLead = SC::kLead;
   constexpr int NSW = DVW / CPW;   // state wavefronts
@@ -327,7 +379,10 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
 
   // State: block kb of column block cb, lane (c, g), r = row chan(kb, 4 g + r),
   // column vcol(cb, c).
+  // It holds sigma S with sigma = 2^sh (wave-uniform), see the precision note.
   f32x4 S[NCB][8];
+  int sh = 0;
+  float sig = 1.f, isig = 1.f;  // 2^sh, 2^-sh
   // This wave's columns of the state, to a [dk, dv] row-major float32 state at p.
   auto store_state = [&](float* p) {
 #pragma unroll
@@ -336,7 +391,8 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
       for (int kb = 0; kb < 8; ++kb) {
         float* pc = p + col0 + vcol(cb, lc);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pc[rec::chan(kb, 4 * lg + r) * rec::kDV] = S[cb][kb][r];
+        for (int r = 0; r < 4; ++r)
+          pc[rec::chan(kb, 4 * lg + r) * rec::kDV] = S[cb][kb][r] * isig;
       }
   };
 #pragma unroll
@@ -434,15 +490,84 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     // ---- D_a, D_b.  Every accumulation chain uses one instruction shape,
     // 16x16x32 (a 16x16x16 result fed straight into a 16x16x32 accumulator
     // read stale values on gfx950).
+    // V in the k-operand layout, float32 (exact): lane (c, g): V_a[4 g + e][vcol(cb, c)]
+    f32x4 vf[NCB][2];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      vf[cb][0] = mma16b(half4(vna, cb), ident, zero4());
+      vf[cb][1] = mma16b(half4(vnb, cb), ident, zero4());
+    }
+    // The scale: the largest magnitude m of sigma S and sigma V, one
+    // reduction over the wave.  When m leaves the window (rare) it is taken
+    // again with V unscaled (sigma V may have overflowed), and the state and
+    // sigma V are moved.
+    f32x4 vs[NCB][2];  // sigma V
+    {
+      float m0 = 0.f, m1 = 0.f;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        vs[cb][0] = vf[cb][0] * sig;
+        vs[cb][1] = vf[cb][1] * sig;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m0 = fmaxf(m0, fmaxf(fabsf(vs[cb][0][r]), fabsf(vs[cb][1][r])));
+#pragma unroll
+        for (int kb = 0; kb < 8; kb += 2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            m0 = fmaxf(m0, fabsf(S[cb][kb][r]));
+            m1 = fmaxf(m1, fabsf(S[cb][kb + 1][r]));
+          }
+      }
+      // raw keys: D' = Diag(1/|k|) D exceeds D by up to the pair's largest 1/|k|
+      int ek = 0;
+      if constexpr (LOGITS) {
+        ek = exp_of(((const float*)(Rs + rec::kNorm))[32]);
+        ek = ek > 0 ? ek : 0;
+      }
+      int em = exp_of(wave_max_nonneg(fmaxf(m0, m1)));
+      if (em != kNoExp) em += ek;
+      if (scale_shift(em, sh) != 0) {  // wave-uniform
+        float ms = 0.f, mv = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mv = fmaxf(mv, fmaxf(fabsf(vf[cb][0][r]), fabsf(vf[cb][1][r])));
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ms = fmaxf(ms, fabsf(S[cb][kb][r]));
+        }
+        const int es = exp_of(wave_max_nonneg(ms));
+        int ev = exp_of(wave_max_nonneg(mv));
+        ev = ev == kNoExp ? kNoExp : ev + sh;
+        em = es > ev ? es : ev;
+        if (em != kNoExp) em += ek;
+        const int d = scale_shift(em, sh);
+        if (d != 0) {
+          const float f = exp2i(d);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) S[cb][kb] *= f;
+          sh += d;
+          sig = exp2i(sh);
+          isig = exp2i(-sh);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            vs[cb][0] = vf[cb][0] * sig;
+            vs[cb][1] = vf[cb][1] * sig;
+          }
+        }
+      }
+    }
     f16x8 sop[NCB][4];
     f16x8 dab[NCB];  // [D_a ; D_b] in k-operand order (lane (c, g): D[4 g + e][c])
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) sop[cb][s] = cat8(to_h4(S[cb][2 * s]), to_h4(S[cb][2 * s + 1]));
-      // lane (c, g): V_a[4 g + e][vcol(cb, c)]
-      const f16x4 va = to_h4(mma16b(half4(vna, cb), ident, zero4()));
-      const f16x4 vb = to_h4(mma16b(half4(vnb, cb), ident, zero4()));
+      const f16x4 va = to_h4(vs[cb][0]);
+      const f16x4 vb = to_h4(vs[cb][1]);
       f32x4 d = mma32h(ta8, cat8(va, vb), zero4());  // k-values 4..7 of ta8 are zero
 #pragma unroll
       for (int s = 0; s < 4; ++s) d = mma32h(wa[s], sop[cb][s], d);
@@ -467,10 +592,12 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
     // With q and k normalised in the kernels, D above is D' = Diag(1/|k|) D
     // (the record's T, W and P rows carry 1/|k|), which is what the raw-key
     // factors Kb, Aqk and Q_ba take, and each output row takes 1/|q| of its token.
-    float rqa = 1.f, rqb = 1.f;
+    // Every output row is also multiplied by scale / sigma (the records hold
+    // the unscaled queries; the state and D are sigma times theirs).
+    float rqa = scale * isig, rqb = scale * isig;
     if constexpr (LOGITS) {
-      rqa = ((const float*)(Rs + rec::kNorm))[lc];
-      rqb = ((const float*)(Rs + rec::kNorm))[16 + lc];
+      rqa *= ((const float*)(Rs + rec::kNorm))[lc];
+      rqb *= ((const float*)(Rs + rec::kNorm))[16 + lc];
     }
     f32x4 Oa[NCB], Ob[NCB];
 #pragma unroll
@@ -481,12 +608,8 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
         x = mma32h(sop[cb][s], qa[s], x);
         y = mma32h(sop[cb][s], qb[s], y);
       }
-      Oa[cb] = mma32h(dab[cb], aa8, x);     // + D_a^T Aqk_a^T (k-values 4..7 of aa8 are zero)
-      Ob[cb] = mma32h(dab[cb], qbaab, y);   // + D_a^T Q_ba^T + D_b^T Aqk_b^T
-      if constexpr (LOGITS) {  // the raw-query rows, normalised
-        Oa[cb] *= rqa;
-        Ob[cb] *= rqb;
-      }
+      Oa[cb] = mma32h(dab[cb], aa8, x) * rqa;    // + D_a^T Aqk_a^T (k-values 4..7 of aa8 are zero)
+      Ob[cb] = mma32h(dab[cb], qbaab, y) * rqb;  // + D_a^T Q_ba^T + D_b^T Aqk_b^T
     }
     if constexpr (GATE) {
       float pa = 0.f, pb = 0.f;
@@ -596,12 +719,12 @@ hipError_t launch_state_t(const ChunkArgs& a, Seg cur, const float* s_in, float*
   const Seqs<PACKED> seqb{ab.cu, ab.T, PACKED ? ab.total : ab.B * ab.T};
   tile::Args<PACKED, LOGITS> tb{(const bf16_t*)ab.q, (const bf16_t*)ab.k, ab.g, ab.beta,
                                 (const bf16_t*)ab.ga, nxt.recs, seqb, ab.H, BHb, nxt.x0,
-                                nxt.n > 0 ? nxt.n : 1, ab.scale};
+                                nxt.n > 0 ? nxt.n : 1};
   hipLaunchKernelGGL((kda_state_kernel<DVW, CPW, GATE, WO, PACKED, LOGITS>),
                      dim3((unsigned)nblk), dim3(64 * NW),
                      0, (hipStream_t)a.stream, cur.recs, (const bf16_t*)a.v, s_in, s_next,
                      (bf16_t*)a.o, (const bf16_t*)a.gate, a.norm_w, a.eps, seqs, a.H, BH, cur.x0,
-                     cur.n > 0 ? cur.n : 1, n_state, a.ckpt, a.ckpt_every, tb);
+                     cur.n > 0 ? cur.n : 1, n_state, a.ckpt, a.ckpt_every, a.scale, tb);
   return hipGetLastError();
 }
 

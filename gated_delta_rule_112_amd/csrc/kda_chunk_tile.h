@@ -119,7 +119,7 @@ struct SlabVals {
 // (then q = k = g = 0); FULL tiles skip that mask.
 // With LOGITS, nq and nk also accumulate this lane's part of |q|^2 and |k|^2.
 template <bool FULL, bool LOGITS>
-__device__ __forceinline__ void slab_vals(const SlabIn& in, float lv, float scale, SlabVals& o,
+__device__ __forceinline__ void slab_vals(const SlabIn& in, float lv, SlabVals& o,
                                           f32x4& acc_a, f32x4& acc_q, float& nq, float& nk) {
   float gm[8];
 #pragma unroll
@@ -130,7 +130,7 @@ __device__ __forceinline__ void slab_vals(const SlabIn& in, float lv, float scal
       gm[e] = e < 4 ? in.g0[e] : in.g1[e - 4];
   }
   const float gs = FULL ? kLog2e : kLog2e * lv;
-  const float qs = FULL ? scale : scale * lv;
+  const float qs = FULL ? 1.f : lv;  // the output scale is applied by the state pass
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float gl = row_scan16(gm[e] * gs);         // G in log2 units
@@ -156,13 +156,13 @@ __device__ __forceinline__ void slab_vals(const SlabIn& in, float lv, float scal
 }
 
 template <bool LOGITS>
-__device__ __forceinline__ void slab_vals_any(bool full, const SlabIn& in, float lv, float scale,
+__device__ __forceinline__ void slab_vals_any(bool full, const SlabIn& in, float lv,
                                               SlabVals& o, f32x4& acc_a, f32x4& acc_q, float& nq,
                                               float& nk) {
   if (full)
-    slab_vals<true, LOGITS>(in, 1.f, scale, o, acc_a, acc_q, nq, nk);
+    slab_vals<true, LOGITS>(in, 1.f, o, acc_a, acc_q, nq, nk);
   else
-    slab_vals<false, LOGITS>(in, lv, scale, o, acc_a, acc_q, nq, nk);
+    slab_vals<false, LOGITS>(in, lv, o, acc_a, acc_q, nq, nk);
 }
 
 __device__ __forceinline__ f16x8 to_h8(const float (&x)[8]) {
@@ -344,7 +344,6 @@ struct Args {
   Seqs<PACKED> seqs;    // where each sequence's tokens are; seqs.T = longest length
   int64_t H, BH;
   int64_t x0, nseg;     // first pair and pair count of the segment
-  float scale;
 };
 
 // Position of a pair: head (b, h) and pair xl of the segment.
@@ -418,7 +417,7 @@ __device__ __forceinline__ void build_pair(const Args<PACKED, LOGITS>& a, const 
     }
     // tile a: its values, then everything that needs only them
     SlabVals va;
-    slab_vals_any<LOGITS>(fulla, cur.a, lva, a.scale, va, aa, qa, nqa, nka);
+    slab_vals_any<LOGITS>(fulla, cur.a, lva, va, aa, qa, nqa, nka);
     transpose_slab(va.kh, sm, lane, khTa[s]);
     const f16x8 kba = to_h8(va.kb);  // Kb_a, token-major
     *(f16x8*)(R + rec::kQa + s * 1024 + lane * 16) = to_h8(va.qh);
@@ -429,7 +428,7 @@ __device__ __forceinline__ void build_pair(const Args<PACKED, LOGITS>& a, const 
     }
     // tile b, and the cross terms
     SlabVals vb;
-    slab_vals_any<LOGITS>(fullb, cur.b, lvb, a.scale, vb, ab, qb, nqb, nkb);
+    slab_vals_any<LOGITS>(fullb, cur.b, lvb, vb, ab, qb, nqb, nkb);
     transpose_slab(vb.kh, sm, lane, khTb[s]);
     // Q_ba^T: lane (i, g) accumulates (Qh_b Kb_a^T)[i][4 g + r];
     // M = Kh_b Kb_a^T: lane (j, g) accumulates M[4 g + r][j]
@@ -469,13 +468,24 @@ __device__ __forceinline__ void build_pair(const Args<PACKED, LOGITS>& a, const 
     nqb += __shfl_xor(nqb, 32);
     nkb += __shfl_xor(nkb, 32);
     rqa = rsqrtf(fmaxf(nqa, 1e-24f));
-    rka = rsqrtf(fmaxf(nka, 1e-24f));
     rqb = rsqrtf(fmaxf(nqb, 1e-24f));
-    rkb = rsqrtf(fmaxf(nkb, 1e-24f));
+    // A zero key (also every token past the sequence's end) writes nothing:
+    // every use of its row of D' = Diag(1/|k|) D is multiplied by the key, so
+    // the row is set to zero rather than to an overflowing 1e12 D.
+    rka = nka > 0.f ? rsqrtf(fmaxf(nka, 1e-24f)) : 0.f;
+    rkb = nkb > 0.f ? rsqrtf(fmaxf(nkb, 1e-24f)) : 0.f;
+    // the largest 1/|k| of the pair: the state pass forms D' = Diag(1/|k|) D
+    // and scales its float16 operands for it
+    float rkm = fmaxf(rka, rkb);
+    rkm = fmaxf(rkm, dpp<0x111, true>(rkm));
+    rkm = fmaxf(rkm, dpp<0x112, true>(rkm));
+    rkm = fmaxf(rkm, dpp<0x114, true>(rkm));
+    rkm = fmaxf(rkm, dpp<0x118, true>(rkm));
     if (lg == 0) {
       float* nr = (float*)(R + rec::kNorm);
       nr[t] = rqa;
       nr[16 + t] = rqb;
+      if (t == 15) nr[32] = rkm;
       ds_write4(lds_addr(&sm->rk[t]), rka);
     }
   }

@@ -39,9 +39,30 @@
  *   - Supported head sizes: dk, dv in {16, 32, 64, 128}; any other value gives
  *     KDA_ERR_UNSUPPORTED_DIM.  Sizes B, T, H must be >= 1 (T >= 1); element
  *     offsets are 64-bit, so tensors above 2^31 elements are fine.
- *   - Precondition (documented, not checked): -5 <= g <= 0, as produced by
- *     g = -5 * sigmoid(.).  The chunked prefill relies on a 16-token sum of g
- *     staying above -80 so that exp(-sum) stays finite in float32/bfloat16.
+ *   - Precondition (documented; checked only in the input-check mode below):
+ *     -5 <= g <= 0, as produced by g = -5 * sigmoid(.).  The chunked prefill
+ *     relies on a 16-token sum of g staying above -80 so that exp(-sum) stays
+ *     finite in float32/bfloat16.  Keys are expected to have unit L2 norm
+ *     (the delta rule's write is a projection only then).
+ *   - Magnitudes: values, initial states and outputs may take any finite
+ *     float32 / bfloat16 magnitude.  The matrix-core prefill rounds the state,
+ *     the values and the delta to float16 for its products; it keeps them in
+ *     float16's normal range with an exact power-of-two scale per wavefront
+ *     (the method is linear in (v, s0)), so no magnitude limit follows from
+ *     that.  With the gated epilogue the row's mean square must stay finite in
+ *     float32 (|o| below about 1e18).  The entry points that normalise raw q and
+ *     k (the _prologue variants) form some matrix-core operands from the raw
+ *     rows: there raw q and k norms between 2^-4 and 2^7 per token and head
+ *     are supported (outside that range the float16 operands lose precision or
+ *     overflow); all-zero rows are exact.
+ *   - Input-check mode: with the environment variable KDA_CHECK_INPUTS=1 set
+ *     when a call is made, kda_chunk_fwd*, kda_decode_step* and
+ *     kda_decode_multi* first run a check kernel over their inputs and wait
+ *     for it; if any floating-point input is not finite, any g is outside
+ *     [-5, 0], or (prologue variants on the matrix-core path) a raw q or k norm
+ *     lies outside [2^-4, 2^7] and is not zero, the call returns
+ *     KDA_ERR_INPUT_RANGE and launches nothing else.  The check synchronises
+ *     the stream (a debugging aid, not for graph capture).
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -63,7 +84,9 @@ typedef enum {
   KDA_ERR_ALIAS = 6,             /* an output overlaps an input it may not overlap     */
   KDA_ERR_BAD_ARGUMENT = 7,      /* a scalar argument is not finite or out of range    */
   KDA_ERR_LAUNCH = 8,            /* the HIP runtime rejected a kernel launch           */
-  KDA_ERR_WORKSPACE = 9          /* workspace NULL, too small or not 256-byte aligned  */
+  KDA_ERR_WORKSPACE = 9,         /* workspace NULL, too small or not 256-byte aligned  */
+  KDA_ERR_INPUT_RANGE = 10       /* input-check mode: an input is not finite or out of
+                                    its documented range (see KDA_CHECK_INPUTS)        */
 } kda_status;
 
 typedef enum {
