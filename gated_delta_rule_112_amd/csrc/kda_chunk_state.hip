@@ -55,8 +55,6 @@
 // operand normal and finite for any float32 state or bfloat16 values.
 #include <stdlib.h>
 
-#include <vector>
-
 #include <type_traits>
 
 #include "kda_chunk_rec.h"
@@ -825,43 +823,46 @@ struct Group {
   int64_t seg = 1, nsegs = 0;
 };
 
-// The groups of a call, in order.  ws_half is the size of one record buffer
-// (the workspace holds two and a carried state): a group's segments are
-// capped so that its records fit.
-template <typename F>
-void for_each_group(const ChunkArgs& a, int cus, int64_t ws_half, F&& f) {
+// Group gi of a call (sequences gi * gB .. of gB per group; the last may be
+// smaller).  ws_half is the size of one record buffer (the workspace holds two
+// and a carried state): a group's segments are capped so that its records fit.
+Group group_at(const ChunkArgs& a, int cus, int64_t ws_half, int64_t gi) {
   const int64_t gB = group_seqs(a.B, a.H, cus), np = pairs_of(a.T);
   const int64_t sd = a.H * rec::kDK * rec::kDV;  // state elements per sequence
-  for (int64_t b0 = 0; b0 < a.B; b0 += gB) {
-    Group gr;
-    ChunkArgs& g = gr.a;
-    g = a;
-    g.B = (a.B - b0) < gB ? (a.B - b0) : gB;
-    if (a.cu != nullptr) {
-      g.cu = a.cu + b0;  // packed rows stay absolute
-    } else {
-      const int64_t rows = b0 * a.T * a.H;  // token rows of the sequences before the group
-      g.q = (const bf16_t*)a.q + rows * rec::kDK;
-      g.k = (const bf16_t*)a.k + rows * rec::kDK;
-      g.v = (const bf16_t*)a.v + rows * rec::kDV;
-      if (a.g != nullptr) g.g = a.g + rows * rec::kDK;
-      if (a.ga != nullptr) g.ga = (const bf16_t*)a.ga + rows * rec::kDK;
-      g.beta = a.beta + rows;
-      if (a.o != nullptr) g.o = (bf16_t*)a.o + rows * rec::kDV;
-      if (a.gate != nullptr) g.gate = (const bf16_t*)a.gate + rows * rec::kDV;
-    }
-    if (a.s0 != nullptr) g.s0 = a.s0 + b0 * sd;
-    if (a.s_out != nullptr) g.s_out = a.s_out + b0 * sd;
-    if (a.ckpt != nullptr) g.ckpt = a.ckpt + b0 * (a.T / a.ckpt_every) * sd;
-    const int64_t BH = g.B * g.H;
-    gr.split = split_for(g, cus);
-    gr.seg = seg_pairs(BH, np, cus, gr.split);
-    const int64_t fit = ws_half / (BH * (int64_t)rec::kBytes);
-    if (gr.seg > fit) gr.seg = fit;
-    if (gr.seg < 1) gr.seg = 1;
-    gr.nsegs = (np + gr.seg - 1) / gr.seg;
-    f(gr);
+  const int64_t b0 = gi * gB;
+  Group gr;
+  ChunkArgs& g = gr.a;
+  g = a;
+  g.B = (a.B - b0) < gB ? (a.B - b0) : gB;
+  if (a.cu != nullptr) {
+    g.cu = a.cu + b0;  // packed rows stay absolute
+  } else {
+    const int64_t rows = b0 * a.T * a.H;  // token rows of the sequences before the group
+    g.q = (const bf16_t*)a.q + rows * rec::kDK;
+    g.k = (const bf16_t*)a.k + rows * rec::kDK;
+    g.v = (const bf16_t*)a.v + rows * rec::kDV;
+    if (a.g != nullptr) g.g = a.g + rows * rec::kDK;
+    if (a.ga != nullptr) g.ga = (const bf16_t*)a.ga + rows * rec::kDK;
+    g.beta = a.beta + rows;
+    if (a.o != nullptr) g.o = (bf16_t*)a.o + rows * rec::kDV;
+    if (a.gate != nullptr) g.gate = (const bf16_t*)a.gate + rows * rec::kDV;
   }
+  if (a.s0 != nullptr) g.s0 = a.s0 + b0 * sd;
+  if (a.s_out != nullptr) g.s_out = a.s_out + b0 * sd;
+  if (a.ckpt != nullptr) g.ckpt = a.ckpt + b0 * (a.T / a.ckpt_every) * sd;
+  const int64_t BH = g.B * g.H;
+  gr.split = split_for(g, cus);
+  gr.seg = seg_pairs(BH, np, cus, gr.split);
+  const int64_t fit = ws_half / (BH * (int64_t)rec::kBytes);
+  if (gr.seg > fit) gr.seg = fit;
+  if (gr.seg < 1) gr.seg = 1;
+  gr.nsegs = (np + gr.seg - 1) / gr.seg;
+  return gr;
+}
+
+int64_t n_groups(const ChunkArgs& a, int cus) {
+  const int64_t gB = group_seqs(a.B, a.H, cus);
+  return (a.B + gB - 1) / gB;
 }
 
 int64_t record_half(int64_t B, int64_t T, int64_t H, int cus) {
@@ -877,8 +878,11 @@ int64_t chunk_mfma_launches(int64_t B, int64_t T, int64_t H) {
   a.B = B;
   a.T = T;
   a.H = H;
+  const int64_t half = record_half(B, T, H, cus), ng = n_groups(a, cus);
   int64_t n = 1;  // the first segment's records
-  for_each_group(a, cus, record_half(B, T, H, cus), [&](const Group& g) { n += g.nsegs; });
+  // every group but the last has the same shape
+  if (ng > 1) n += (ng - 1) * group_at(a, cus, half, 0).nsegs;
+  n += group_at(a, cus, half, ng - 1).nsegs;
   return n;
 }
 
@@ -890,37 +894,46 @@ hipError_t launch_chunk_mfma(const ChunkArgs& a) {
   // Every segment of every group, in order, as one pipeline: launch i runs
   // the state pass over item i and builds the records of item i + 1, also
   // when that item starts the next group.  Records alternate between the two
-  // halves of the workspace; the carried state follows them.
+  // halves of the workspace; the carried state follows them.  Items are
+  // walked with a cursor (group index, segment index), nothing is stored.
+  const int64_t ng = n_groups(a, cus);
   struct Item {
-    int group;
-    int64_t j;
+    Group g;
+    int64_t gi = -1, j = 0;  // gi < 0: no item
   };
-  std::vector<Group> groups;
-  std::vector<Item> items;
-  for_each_group(a, cus, half, [&](const Group& g) {
-    for (int64_t j = 0; j < g.nsegs; ++j) items.push_back({(int)groups.size(), j});
-    groups.push_back(g);
-  });
+  auto next_item = [&](const Item& it) {
+    Item n;
+    if (it.gi < 0) return n;
+    if (it.j + 1 < it.g.nsegs) {
+      n = it;
+      ++n.j;
+    } else if (it.gi + 1 < ng) {
+      n.g = group_at(a, cus, half, it.gi + 1);
+      n.gi = it.gi + 1;
+    }
+    return n;
+  };
   unsigned char* buf[2] = {(unsigned char*)a.workspace, (unsigned char*)a.workspace + half};
   float* carry_ws = (float*)((unsigned char*)a.workspace + 2 * half);
-  auto seg_of = [&](int64_t i) {
+  auto seg_of = [&](const Item& it, int64_t i) {
     Seg sg;
-    if (i >= 0 && i < (int64_t)items.size()) {
-      const Group& g = groups[items[i].group];
-      sg.x0 = items[i].j * g.seg;
-      sg.n = (np - sg.x0) < g.seg ? (np - sg.x0) : g.seg;
+    if (it.gi >= 0) {
+      sg.x0 = it.j * it.g.seg;
+      sg.n = (np - sg.x0) < it.g.seg ? (np - sg.x0) : it.g.seg;
       sg.recs = buf[i & 1];
     }
     return sg;
   };
-  const int64_t n_items = (int64_t)items.size();
-  for (int64_t i = -1; i < n_items; ++i) {
-    const Seg cur = seg_of(i), nxt = seg_of(i + 1);
-    const Group& gs = groups[items[i < 0 ? 0 : i].group];                   // state pass
-    const Group& gb = groups[items[i + 1 < n_items ? i + 1 : i].group];     // tile builder
+  Item cur, nxt;  // items i and i + 1
+  nxt.g = group_at(a, cus, half, 0);
+  nxt.gi = 0;
+  for (int64_t i = -1; i < 0 || cur.gi >= 0; ++i) {
+    const Seg scur = seg_of(cur, i), snxt = seg_of(nxt, i + 1);
+    const Group& gs = cur.gi >= 0 ? cur.g : nxt.g;  // state pass
+    const Group& gb = nxt.gi >= 0 ? nxt.g : cur.g;  // tile builder
     const ChunkArgs& as = gs.a;
     float* carry = as.s_out != nullptr ? as.s_out : carry_ws;
-    const int64_t j = i < 0 ? 0 : items[i].j;
+    const int64_t j = cur.gi >= 0 ? cur.j : 0;
     const float* s_in = j == 0 ? as.s0 : carry;
     float* s_next = j == gs.nsegs - 1 ? as.s_out : carry;
     // 32 state columns per state wavefront: one state and one loader
@@ -928,14 +941,16 @@ hipError_t launch_chunk_mfma(const ChunkArgs& a) {
     // running in the same launch needs them).
     hipError_t e;
     if (a.cu != nullptr && a.ga != nullptr)
-      e = launch_layout<true, true>(as, gs.split, cur, s_in, s_next, gb.a, nxt, cus);
+      e = launch_layout<true, true>(as, gs.split, scur, s_in, s_next, gb.a, snxt, cus);
     else if (a.cu != nullptr)
-      e = launch_layout<true, false>(as, gs.split, cur, s_in, s_next, gb.a, nxt, cus);
+      e = launch_layout<true, false>(as, gs.split, scur, s_in, s_next, gb.a, snxt, cus);
     else if (a.ga != nullptr)
-      e = launch_layout<false, true>(as, gs.split, cur, s_in, s_next, gb.a, nxt, cus);
+      e = launch_layout<false, true>(as, gs.split, scur, s_in, s_next, gb.a, snxt, cus);
     else
-      e = launch_layout<false, false>(as, gs.split, cur, s_in, s_next, gb.a, nxt, cus);
+      e = launch_layout<false, false>(as, gs.split, scur, s_in, s_next, gb.a, snxt, cus);
     if (e != hipSuccess) return e;
+    cur = nxt;
+    nxt = next_item(nxt);
   }
   return hipSuccess;
 }
