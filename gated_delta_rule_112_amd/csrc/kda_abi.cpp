@@ -9,6 +9,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include "kda_check.h"
 #include "kda_launch.h"
 
 namespace {
@@ -43,6 +44,16 @@ int64_t prod(int64_t a, int64_t b, int64_t c = 1, int64_t d = 1) {
   return r;
 }
 
+// Input-check mode: the check kernels over a call's inputs (kda_check.hip).
+kda_status run_checks(const kda::CheckItem* items, int n, void* stream) {
+  bool bad = false;
+  if (kda::check_inputs(items, n, stream, &bad) != hipSuccess) return KDA_ERR_LAUNCH;
+  return bad ? KDA_ERR_INPUT_RANGE : KDA_OK;
+}
+
+// The raw q and k norms the matrix-core path of the normalising entry points supports.
+constexpr float kRawNormLo = 0.0625f, kRawNormHi = 128.f;
+
 bool force_valu() {
   const char* e = getenv("KDA_FORCE_VALU");
   return e != nullptr && e[0] == '1';
@@ -66,6 +77,9 @@ const char* kda_status_string(kda_status s) {
     case KDA_ERR_WORKSPACE:
       return "KDA_ERR_WORKSPACE: the workspace is NULL, smaller than "
              "kda_chunk_fwd_workspace_size() or not 256-byte aligned";
+    case KDA_ERR_INPUT_RANGE:
+      return "KDA_ERR_INPUT_RANGE: an input is not finite, a log-decay g lies outside [-5, 0], "
+             "or a raw q or k norm lies outside its supported range (KDA_CHECK_INPUTS=1)";
   }
   return "KDA_ERR_UNKNOWN";
 }
@@ -207,6 +221,25 @@ kda_status chunk_fwd(const void* q, const void* k, const void* v, const float* g
       return KDA_ERR_ALIAS;
   }
 
+  if (kda::check_mode_on()) {
+    using namespace kda;
+    const int fk = io == KDA_BF16 ? kCheckFiniteBF16 : kCheckFiniteF32;
+    // raw q and k on the matrix-core path: their norms must suit its float16 operands
+    const bool norms = ga != nullptr && mfma;
+    const CheckItem qk = norms ? CheckItem{q, rows * H, kCheckRowNormBF16, dk, kRawNormLo, kRawNormHi}
+                               : CheckItem{q, nqk, fk, 0, 0.f, 0.f};
+    CheckItem kk = qk;
+    kk.p = k;
+    const CheckItem it[] = {
+        qk, kk, {v, nv, fk, 0, 0.f, 0.f},
+        ga != nullptr ? CheckItem{ga, nqk, fk, 0, 0.f, 0.f}
+                      : CheckItem{g, nqk, kCheckRangeF32, 0, -5.f, 0.f},
+        {beta, nb, kCheckFiniteF32, 0, 0.f, 0.f}, {s0, ns, kCheckFiniteF32, 0, 0.f, 0.f},
+        {gate, nv, fk, 0, 0.f, 0.f}, {norm_w, dv, kCheckFiniteF32, 0, 0.f, 0.f}};
+    const kda_status st = run_checks(it, 8, stream);
+    if (st != KDA_OK) return st;
+  }
+
   kda::ChunkArgs a{q, k, v, g, beta, s0, o, s_out, gate, norm_w, eps,
                    B, T, H, dk, dv, scale, io == KDA_BF16, workspace, stream};
   if (ckpt != nullptr && T >= ckpt_every) {
@@ -310,6 +343,23 @@ kda_status kda_chunk_fwd_varlen_prologue(const void* q, const void* k, const voi
 
 namespace {
 
+// Input-check mode for the decode entry points (float32 arithmetic: every
+// input finite, g in [-5, 0]).
+kda_status check_decode(const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const float* state, const void* gate,
+                        const float* norm_w, int64_t nqk, int64_t nv, int64_t nb, int64_t ns,
+                        int dv, kda_dtype io, const void* ga, void* stream) {
+  using namespace kda;
+  const int fk = io == KDA_BF16 ? kCheckFiniteBF16 : kCheckFiniteF32;
+  const CheckItem it[] = {
+      {q, nqk, fk, 0, 0.f, 0.f}, {k, nqk, fk, 0, 0.f, 0.f}, {v, nv, fk, 0, 0.f, 0.f},
+      ga != nullptr ? CheckItem{ga, nqk, fk, 0, 0.f, 0.f}
+                    : CheckItem{g, nqk, kCheckRangeF32, 0, -5.f, 0.f},
+      {beta, nb, kCheckFiniteF32, 0, 0.f, 0.f}, {state, ns, kCheckFiniteF32, 0, 0.f, 0.f},
+      {gate, nv, fk, 0, 0.f, 0.f}, {norm_w, dv, kCheckFiniteF32, 0, 0.f, 0.f}};
+  return run_checks(it, 8, stream);
+}
+
 // kda_decode_step, with the prologue (q, k normalised, gates from their logits)
 // when ga is non-NULL.
 kda_status decode_step(const void* q, const void* k, const void* v, const float* g,
@@ -341,6 +391,12 @@ kda_status decode_step(const void* q, const void* k, const void* v, const float*
     if (overlap(so, in)) return KDA_ERR_ALIAS;
   for (Span in : {sq, sk, sv, sg, sb, sgt, sw})
     if (overlap(sst, in)) return KDA_ERR_ALIAS;
+
+  if (kda::check_mode_on()) {
+    const kda_status st = check_decode(q, k, v, g, beta, state, gate, norm_w, nqk, nv, nb, ns,
+                                       dv, io, ga, stream);
+    if (st != KDA_OK) return st;
+  }
 
   kda::DecodeArgs a{q, k, v, g, beta, state, o, gate, norm_w, eps,
                     B, H, dk, dv, scale, io == KDA_BF16, stream};
@@ -406,6 +462,12 @@ kda_status decode_multi(const void* q, const void* k, const void* v, const float
     if (overlap(so, in)) return KDA_ERR_ALIAS;
   for (Span in : {sq, sk, sv, sg, sb, sgt, sw, sn})
     if (overlap(sst, in)) return KDA_ERR_ALIAS;
+
+  if (kda::check_mode_on()) {
+    const kda_status st = check_decode(q, k, v, g, beta, state, gate, norm_w, nqk, nv, nb, ns,
+                                       dv, io, ga, stream);
+    if (st != KDA_OK) return st;
+  }
 
   kda::DecodeArgs a{q, k, v, g, beta, state, o, gate, norm_w, eps,
                     B, H, dk, dv, scale, io == KDA_BF16, stream};

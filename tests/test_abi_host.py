@@ -14,7 +14,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, NULLP, SHAPE, DIM, DTYPE, ALIGN, ALIAS, ARG, LAUNCH, WORKSPACE = range(10)
+OK, NULLP, SHAPE, DIM, DTYPE, ALIGN, ALIAS, ARG, LAUNCH, WORKSPACE, INPUT_RANGE = range(11)
 
 
 def declared_functions():
@@ -46,10 +46,11 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(0, 10):
+    for s in range(0, 11):
         assert lib.kda_status_string(s)
         assert b"UNKNOWN" not in lib.kda_status_string(s)
     assert lib.kda_status_string(0) == b"KDA_OK"
+    assert lib.kda_status_string(INPUT_RANGE).startswith(b"KDA_ERR_INPUT_RANGE")
     assert b"UNKNOWN" in lib.kda_status_string(99)
     assert lib.kda_version() >= 100
 
