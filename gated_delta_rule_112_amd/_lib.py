@@ -86,6 +86,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_chunk_fwd_kernel.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
     lib.kda_version.restype = ci
+    lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32,
+                                          i64, i64, i64, ci, ci, f32, ci, vp]
+    lib.kda_chunk_fwd_noalloc.restype = ci
+    lib.kda_chunk_fwd_noalloc_scratch_bytes.argtypes = []
+    lib.kda_chunk_fwd_noalloc_scratch_bytes.restype = ctypes.c_size_t
     if path is None:
         _lib = lib
     return lib
@@ -135,6 +140,18 @@ def chunk_fwd(q, k, v, g, beta, s0=None, *, scale: float = 1.0, gate=None, norm_
     """
     o, s, _ = _chunk_fwd(q, k, v, g, beta, s0, scale, gate, norm_w, eps, output, final_state,
                          out, s_out, workspace, 0, None, stream, prologue)
+    return o, s
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, s0=None, *, scale: float = 1.0, gate=None,
+                      norm_w=None, eps: float = 1e-6, output: bool = True,
+                      final_state: bool = True, out=None, s_out=None,
+                      stream=None) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """``chunk_fwd`` through kda_chunk_fwd_noalloc: no workspace, the library's
+    fixed device scratch instead (for callers that cannot allocate; pass ``out``
+    and ``s_out`` to allocate nothing here either)."""
+    o, s, _ = _chunk_fwd(q, k, v, g, beta, s0, scale, gate, norm_w, eps, output, final_state,
+                         out, s_out, None, 0, None, stream, noalloc=True)
     return o, s
 
 
@@ -223,7 +240,7 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, max_len: int, s0=None, *,
 
 
 def _chunk_fwd(q, k, v, g, beta, s0, scale, gate, norm_w, eps, output, final_state, out, s_out,
-               workspace, every, ckpt, stream, prologue=False):
+               workspace, every, ckpt, stream, prologue=False, noalloc=False):
     lib = load_library()
     if q.device.type != "cuda":
         raise ValueError("kda ops need CUDA (HIP) tensors")
@@ -256,6 +273,13 @@ def _chunk_fwd(q, k, v, g, beta, s0, scale, gate, norm_w, eps, output, final_sta
         s_out = None
     elif s_out is not None:
         _need(s_out, "s_out", torch.float32, (B, H, dk, dv), dev)
+    if noalloc:
+        st = lib.kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0),
+                                       _ptr(out), _ptr(s_out), _ptr(gate), _ptr(norm_w),
+                                       float(eps), B, T, H, dk, dv, float(scale), _IO[io],
+                                       _stream(dev, stream))
+        _check(lib, "kda_chunk_fwd_noalloc", st)
+        return out, s_out, None
     ws_bytes = lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, _IO[io])
     if workspace is None and ws_bytes > 0:
         # torch's caching allocator hands out 512-byte aligned blocks

@@ -76,7 +76,8 @@ const char* kda_status_string(kda_status s) {
     case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
     case KDA_ERR_WORKSPACE:
       return "KDA_ERR_WORKSPACE: the workspace is NULL, smaller than "
-             "kda_chunk_fwd_workspace_size() or not 256-byte aligned";
+             "kda_chunk_fwd_workspace_size() or not 256-byte aligned (kda_chunk_fwd_noalloc: "
+             "the fixed scratch cannot hold one pair of records per head)";
     case KDA_ERR_INPUT_RANGE:
       return "KDA_ERR_INPUT_RANGE: an input is not finite, a log-decay g lies outside [-5, 0], "
              "or a raw q or k norm lies outside its supported range (KDA_CHECK_INPUTS=1)";
@@ -167,9 +168,11 @@ kda_status chunk_fwd(const void* q, const void* k, const void* v, const float* g
                      const float* norm_w, float eps, int64_t B, int64_t T, int64_t H, int dk,
                      int dv, float scale, kda_dtype io, void* workspace, size_t workspace_bytes,
                      float* ckpt, int64_t ckpt_every, const int32_t* cu, int64_t total,
-                     const void* ga, void* stream) {
+                     const void* ga, void* stream, bool small_ws = false) {
   // ga: the log-decay logits a (g = -5 sigmoid(a)) in place of g; beta then holds logits,
-  // and q, k are L2-normalised in the kernels
+  // and q, k are L2-normalised in the kernels.  small_ws: the workspace may be smaller
+  // than kda_chunk_fwd_workspace_size() (at least chunk_mfma_workspace_min()); the
+  // matrix-core path then runs shorter segments.
   if (!q || !k || !v || (!g && !ga) || !beta) return KDA_ERR_NULL_POINTER;
   if (!o && !s_out) return KDA_ERR_NULL_POINTER;
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_BAD_DTYPE;
@@ -211,7 +214,11 @@ kda_status chunk_fwd(const void* q, const void* k, const void* v, const float* g
 
   const bool mfma = !force_valu() && kda::chunk_mfma_supports(dk, dv, io == KDA_BF16);
   if (mfma) {
-    const size_t need = kda::chunk_mfma_workspace(B, T, H);
+    size_t need = kda::chunk_mfma_workspace(B, T, H);
+    if (small_ws) {
+      if (workspace_bytes < kda::chunk_mfma_workspace_min(B, H)) return KDA_ERR_WORKSPACE;
+      need = workspace_bytes < need ? workspace_bytes : need;
+    }
     if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
       return KDA_ERR_WORKSPACE;
     const Span sws{workspace, (int64_t)need};
@@ -248,6 +255,7 @@ kda_status chunk_fwd(const void* q, const void* k, const void* v, const float* g
   }
   a.cu = cu;
   a.total = rows;
+  if (small_ws) a.ws_bytes = (int64_t)workspace_bytes;
   if (ga != nullptr) {
     a.g = nullptr;
     a.ga = ga;
@@ -255,6 +263,26 @@ kda_status chunk_fwd(const void* q, const void* k, const void* v, const float* g
   const hipError_t err = mfma ? kda::launch_chunk_mfma(a) : kda::launch_chunk_valu(a);
   return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
+
+}  // namespace
+
+namespace kda {
+
+// kda_chunk_fwd on a workspace that may be smaller than the default one (the
+// library's fixed scratch of kda_chunk_fwd_noalloc).
+kda_status chunk_fwd_fixed_scratch(const void* q, const void* k, const void* v, const float* g,
+                                   const float* beta, const float* s0, void* o, float* s_out,
+                                   const void* gate, const float* norm_w, float eps, int64_t B,
+                                   int64_t T, int64_t H, int dk, int dv, float scale,
+                                   kda_dtype io, void* scratch, size_t scratch_bytes,
+                                   void* stream) {
+  return chunk_fwd(q, k, v, g, beta, s0, o, s_out, gate, norm_w, eps, B, T, H, dk, dv, scale, io,
+                   scratch, scratch_bytes, nullptr, 0, nullptr, 0, nullptr, stream, true);
+}
+
+}  // namespace kda
+
+namespace {
 
 // Packed sequences: the checks of the varlen entry points, then chunk_fwd.
 kda_status varlen_fwd(const void* q, const void* k, const void* v, const float* g,

@@ -813,6 +813,12 @@ size_t chunk_mfma_workspace(int64_t B, int64_t T, int64_t H) {
   return (size_t)(2 * BH * seg * rec::kBytes) + (size_t)(BH * rec::kDK * rec::kDV * 4);
 }
 
+size_t chunk_mfma_workspace_min(int64_t B, int64_t H) {
+  const int64_t BH = group_seqs(B, H, device_cus()) * H;
+  // one pair of every head of a launch group in each record buffer, and the carried state
+  return (size_t)(2 * BH * rec::kBytes) + (size_t)(BH * rec::kDK * rec::kDV * 4);
+}
+
 namespace {
 
 // One group of sequences as the state pass and the tile builder see it: the
@@ -870,6 +876,16 @@ int64_t record_half(int64_t B, int64_t T, int64_t H, int cus) {
   return ((int64_t)chunk_mfma_workspace(B, T, H) - BH * rec::kDK * rec::kDV * 4) / 2;
 }
 
+// One record buffer of a call's workspace: the default size, or less when the
+// call brings a smaller workspace (ws_bytes; the segments are then shorter).
+int64_t record_half_of(const ChunkArgs& a, int cus) {
+  const int64_t half = record_half(a.B, a.T, a.H, cus);
+  if (a.ws_bytes <= 0) return half;
+  const int64_t BH = group_seqs(a.B, a.H, cus) * a.H;
+  const int64_t fit = ((a.ws_bytes - BH * rec::kDK * rec::kDV * 4) / 2) & ~int64_t(255);
+  return fit < half ? fit : half;
+}
+
 }  // namespace
 
 int64_t chunk_mfma_launches(int64_t B, int64_t T, int64_t H) {
@@ -889,7 +905,7 @@ int64_t chunk_mfma_launches(int64_t B, int64_t T, int64_t H) {
 hipError_t launch_chunk_mfma(const ChunkArgs& a) {
   if (!chunk_mfma_supports(a.dk, a.dv, a.io_bf16)) return hipErrorNotSupported;
   const int cus = device_cus();
-  const int64_t half = record_half(a.B, a.T, a.H, cus);
+  const int64_t half = record_half_of(a, cus);
   const int64_t np = pairs_of(a.T);
   // Every segment of every group, in order, as one pipeline: launch i runs
   // the state pass over item i and builds the records of item i + 1, also

@@ -36,6 +36,10 @@ struct ChunkArgs {
   // Gates from logits: ga [rows, H, dk] in the io dtype holds a, and g = -5 sigmoid(a);
   // beta then holds the logit b of the write strength, beta = sigmoid(b).  NULL: g, beta given.
   const void* ga = nullptr;
+  // Bytes of the workspace when it is smaller than chunk_mfma_workspace() (at
+  // least chunk_mfma_workspace_min()): the matrix-core path then runs shorter
+  // segments.  0: the default size.
+  int64_t ws_bytes = 0;
 };
 
 struct DecodeArgs {
@@ -78,6 +82,8 @@ hipError_t launch_chunk_valu(const ChunkArgs& a);
 hipError_t launch_chunk_mfma(const ChunkArgs& a);
 bool chunk_mfma_supports(int dk, int dv, bool io_bf16);
 size_t chunk_mfma_workspace(int64_t B, int64_t T, int64_t H);
+// The smallest workspace the matrix-core path runs with (one pair per head per segment).
+size_t chunk_mfma_workspace_min(int64_t B, int64_t H);
 int64_t chunk_mfma_launches(int64_t B, int64_t T, int64_t H);
 hipError_t launch_gate_rmsnorm(const NormArgs& a);
 

@@ -152,6 +152,30 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk, int
                                     kda_dtype io);
 
 /*
+ * kda_chunk_fwd_noalloc -- kda_chunk_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Every argument as in kda_chunk_fwd, without the
+ * workspace: the call uses a fixed scratch array that the library declares in
+ * device memory (kda_chunk_fwd_noalloc_scratch_bytes() = 64 MiB per GPU, held
+ * until the process ends) and calls no allocator.  On the matrix-core path the
+ * segments of per-pair records are shortened to fit it (more launches, so
+ * slower than kda_chunk_fwd with its default workspace); results agree with
+ * kda_chunk_fwd to rounding.  KDA_ERR_WORKSPACE when the scratch cannot hold
+ * one pair of records per head of a launch group and the carried state (at
+ * dk = dv = 128: H above about 540).  All calls on one GPU share its scratch:
+ * calls that overlap in time on one GPU race, and the caller must serialise
+ * them.
+ */
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const float* s0,
+                                 void* o, float* s_out, const void* gate, const float* norm_w,
+                                 float eps, int64_t B, int64_t T, int64_t H, int dk, int dv,
+                                 float scale, kda_dtype io, void* stream);
+
+/* Bytes of the fixed scratch kda_chunk_fwd_noalloc uses on each GPU. */
+size_t kda_chunk_fwd_noalloc_scratch_bytes(void);
+
+/*
  * kda_chunk_fwd_prologue -- kda_chunk_fwd from the raw projections: q and k
  * are L2-normalised per head, and the decay and the write strength are formed
  * from their logits, all inside the kernels.
