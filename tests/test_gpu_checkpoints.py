@@ -11,7 +11,6 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.kda_oracle import kda_chunked as o_chunked
 from oracle.kda_oracle import kda_recurrent as o_recurrent
 from tests.gpu_helpers import assert_close, dev, f64
 
@@ -109,7 +108,7 @@ def test_checkpoints_short_sequence(kda):
 def test_checkpoints_full_width_sampled(kda):
     """B=1, H=96, T=32768 with the gated epilogue (the benchmark's workload and
     launch) and a checkpoint every 2048 tokens: all 16 checkpoints of 3 sampled
-    heads against the chunked float64 form of the oracle."""
+    heads against the oracle's token-by-token recurrence."""
     from gated_delta_rule_112_amd.inputs import WORKLOADS, make_prefill_inputs
     w = WORKLOADS["full_width_prefill"]
     x = make_prefill_inputs(w, device=dev())
@@ -118,6 +117,6 @@ def test_checkpoints_full_width_sampled(kda):
     torch.cuda.synchronize()
     for h in [0, 47, 95]:
         sl = [x[key][:, :, h:h + 1] for key in ["q", "k", "v", "g", "beta"]]
-        ref = oracle_checkpoints(*sl, np.zeros((1, 1, 128, 128)), 2048, run=o_chunked)
+        ref = oracle_checkpoints(*sl, np.zeros((1, 1, 128, 128)), 2048)
         assert_close(f64(ck[:, :, h:h + 1]), ref, TOL[torch.bfloat16], f"checkpoints head {h}")
         assert_close(f64(ck[0, -1, h]), f64(S[0, h]), 1e-6, f"last checkpoint == state, {h}")
