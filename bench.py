@@ -148,6 +148,51 @@ def _oracle_worker(args):
     return done, time.perf_counter() - t0
 
 
+def _decode_oracle_worker(args):
+    """The float64 oracle's decode step over a sample of (b, h) states of the
+    batched decode workload, for every one of its steps."""
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    n_bh, steps, seed = args
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    from oracle.kda_oracle import gate_rmsnorm, kda_decode_step
+    dk = dv = 128
+    S = 0.02 * rng.standard_normal((n_bh, dk, dv))
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        q = rng.standard_normal((n_bh, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        k = rng.standard_normal((n_bh, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        v = rng.standard_normal((n_bh, dv))
+        g = -5.0 / (1.0 + np.exp(-rng.standard_normal((n_bh, dk))))
+        beta = 1.0 / (1.0 + np.exp(-rng.standard_normal(n_bh)))
+        o, S = kda_decode_step(q, k, v, g, beta, S)
+        gate_rmsnorm(o, rng.standard_normal((n_bh, dv)), None, 1e-6)
+    return n_bh * steps, time.perf_counter() - t0
+
+
+def cpu_decode_baseline(H, workers, bh_per_worker, steps):
+    """Oracle decode steps on the host cores: (b, h)-steps/s, as sequence
+    tokens/s (each token carries H heads) and as the state bytes it streams."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    ctx = mp.get_context("spawn")
+    jobs = [(bh_per_worker, steps, 60_000 + i) for i in range(workers)]
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
+        res = list(ex.map(_decode_oracle_worker, jobs))
+    bh_steps = sum(r[0] for r in res)
+    busy = max(r[1] for r in res)
+    return {
+        "value": bh_steps / busy / H,
+        "unit": "tokens/s",
+        "state_gb_per_s": round(bh_steps / busy * 8 * 128 * 128 / 1e9, 2),
+        "cores": workers,
+        "kind": "oracle",
+        "sample": (f"{workers} processes x {bh_per_worker} (b, h) states x {steps} steps of the "
+                   f"batched_decode distributions (float64 decode step + epilogue); "
+                   f"rate = (b, h)-steps/s / H={H}; slowest worker {busy:.1f} s"),
+    }
+
+
 def cpu_baseline(workload, H, workers, heads_per_worker, T):
     """Oracle token-heads/s on the host cores, converted to tokens/s of the
     workload (each token carries H heads)."""
@@ -204,6 +249,67 @@ def bench_prefill(kda, torch, w, steps, warmup):
     ms = e0.elapsed_time(e1) / steps
     del x, out, s_out, ws
     return ms, io
+
+
+def bench_prefill_median(kda, torch, w, reps, evict_bytes=0, output=True):
+    """Median over ``reps`` single prefill calls of workload ``w``, each timed by
+    HIP events on the launch stream.  With ``evict_bytes``, a buffer that size
+    is overwritten between calls (outside the timed region) so that no input
+    is left in the 256 MB memory-side cache; with ``output`` False only the
+    final state is computed (o = NULL).  Returns (median ms, all ms)."""
+    from gated_delta_rule_112_amd.inputs import make_prefill_inputs
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {w.name} inputs on the device")
+    x = make_prefill_inputs(w, device=dev)
+    io = x["q"].dtype
+    out = torch.empty((w.B, w.T, w.H, w.dv), dtype=io, device=dev) if output else None
+    s_out = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    nws = kda.chunk_workspace_size(w.B, w.T, w.H, w.dk, w.dv, io)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    evict = torch.empty(evict_bytes // 4, dtype=torch.float32, device=dev) if evict_bytes else None
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], gate=x["gate"],
+                      out=out, s_out=s_out, output=output, workspace=ws, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    times = []
+    for i in range(reps):
+        if evict is not None:
+            evict.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del x, out, s_out, ws, evict
+    torch.cuda.empty_cache()
+    st = sorted(times)
+    return st[len(st) // 2], times
+
+
+def prefill_leg(kda, torch, w, reps, evict_bytes=0, output=True):
+    """One prefill workload as a bench sub-object: tokens/s and its HBM
+    roofline fraction (algorithmic bytes of the call / median time)."""
+    ms, _ = bench_prefill_median(kda, torch, w, reps, evict_bytes, output)
+    es = 2 if w.io == "bf16" else 4
+    nbytes, per_tok = prefill_bytes(w.B, w.T, w.H, w.dk, w.dv, es, with_o=output,
+                                    with_gate=w.gate, with_s0=w.s0_std is not None)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    flops = prefill_flops(w.B, w.T, w.H, w.dk, w.dv)
+    leg = {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "output": output,
+           "reps": reps, "evict_bytes_between_reps": evict_bytes,
+           "ms_median": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "algorithmic_bytes": nbytes, "bytes_per_token_head": per_tok,
+                        "matrix_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}}
+    log(f"[bench] {w.name} (o {'written' if output else 'NULL'}): {ms:.3f} ms, "
+        f"{w.B * w.T / (ms * 1e-3) / 1e6:.2f} M tok/s, {gbs:.0f} GB/s")
+    return leg
 
 
 def bench_checkpoints(kda, torch, w, every, steps):
@@ -428,6 +534,8 @@ def main():
     ap.add_argument("--no-packed", action="store_true")
     ap.add_argument("--no-prologue", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-small", action="store_true", help="skip the small-prefill leg")
+    ap.add_argument("--no-million", action="store_true", help="skip the million-token leg")
     ap.add_argument("--cpu-heads-per-worker", type=int, default=4)
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--copy-probe", action="store_true",
@@ -445,13 +553,17 @@ def main():
 
     # The oracle leg runs first, in spawned CPU-only processes, before this
     # process touches the GPU.
-    cpu = None
+    cpu = cpu_dec = None
     if not a.no_cpu_baseline:
         workers = max(1, min(16, len(os.sched_getaffinity(0))))
         log(f"[bench] cpu oracle leg: {workers} workers")
         cpu = cpu_baseline(a.workload, w.H, workers, a.cpu_heads_per_worker,
                            min(a.cpu_tokens, w.T))
         log(f"[bench] cpu oracle: {cpu['value']:.1f} tokens/s")
+        cpu_dec = None
+        if not a.no_decode:
+            cpu_dec = cpu_decode_baseline(96, workers, 384, 64)
+            log(f"[bench] cpu oracle decode: {cpu_dec['value']:.1f} tokens/s")
 
     import torch
     import gated_delta_rule_112_amd as kda
@@ -499,6 +611,16 @@ def main():
                        "checkpoint_bytes": ck_bytes,
                        "overhead_vs_prefill": round(cms / ms - 1.0, 4)}
         log(f"[bench] prefill with a checkpoint every {every} tokens: {cms:.3f} ms/step")
+
+    small = None
+    if not a.no_small:  # 0.41 GB per call: a 512 MB write between calls evicts the inputs
+        small = prefill_leg(kda, torch, WORKLOADS["small_prefill"], 20, evict_bytes=512 << 20)
+
+    million = None
+    if not a.no_million:
+        wm = WORKLOADS["million_token_prefill"]
+        million = {"with_o": prefill_leg(kda, torch, wm, 5),
+                   "state_only": prefill_leg(kda, torch, wm, 5, output=False)}
 
     prologue = None
     if not a.no_prologue:
@@ -568,6 +690,7 @@ def main():
                          "traffic": measured_traffic("kda_decode", wd.name),
                          "algorithmic_bytes_per_step": dbytes,
                          "bytes_per_bh": dper},
+            "cpu_baseline": cpu_dec,
         }
         log(f"[bench] decode {dms:.4f} ms/step, {dgbs:.0f} GB/s")
 
@@ -604,6 +727,8 @@ def main():
                    "initial_state": w.s0_std is not None},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "small_prefill": small,
+        "million_token_prefill": million,
         "checkpoints": checkpoints,
         "packed": packed,
         "prologue": prologue,
