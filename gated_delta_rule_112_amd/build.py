@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libkda.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["kda_abi.cpp", "kda_decode.hip", "kda_chunk_valu.hip", "kda_chunk_state.hip",
-           "kda_epilogue.hip", "kda_backward.hip", "kda_check.hip",
+           "kda_epilogue.hip", "kda_backward.hip", "kda_bwd_chunk.hip", "kda_check.hip",
            "kda_noalloc.hip"]
 
 HIPCC_FLAGS = [

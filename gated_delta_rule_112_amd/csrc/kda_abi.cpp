@@ -54,6 +54,11 @@ kda_status run_checks(const kda::CheckItem* items, int n, void* stream) {
 // The raw q and k norms the matrix-core path of the normalising entry points supports.
 constexpr float kRawNormLo = 0.0625f, kRawNormHi = 128.f;
 
+bool force_token_bwd() {
+  const char* e = getenv("KDA_BWD_TOKEN");
+  return e != nullptr && e[0] == '1';
+}
+
 bool force_valu() {
   const char* e = getenv("KDA_FORCE_VALU");
   return e != nullptr && e[0] == '1';
@@ -104,7 +109,10 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk, int
 size_t kda_recurrent_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk, int dv) {
   if (dk != 128 || dv != 128 || prod(B, T, H, dk) < 0) return 0;
   const int64_t n = kda::bwd_workspace_floats(B, T, H);
-  return n > 0 && n < kMaxElems ? (size_t)n * 4 : 0;
+  if (n <= 0 || n >= kMaxElems) return 0;
+  // the larger of the two paths' needs (the path depends on the io dtype and alignment)
+  const int64_t c = kda::bwd_chunk_workspace_bytes(B, T, H);
+  return (size_t)(4 * n > c ? 4 * n : c);
 }
 
 kda_status kda_recurrent_bwd(const void* q, const void* k, const void* v, const float* g,
@@ -147,7 +155,14 @@ kda_status kda_recurrent_bwd(const void* q, const void* k, const void* v, const 
 
   kda::BwdArgs a{q, k, v, g, beta, s0, dout, ds_final, dq, dk_out, dv_out, dg, dbeta, ds0,
                  B, T, H, scale, io == KDA_BF16, (float*)workspace, stream};
-  return kda::launch_recurrent_bwd(a) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+  // bfloat16 with 16-byte aligned token tensors: the chunkwise matrix-core pass;
+  // otherwise (and with KDA_BWD_TOKEN=1) the token-serial vector kernel
+  bool chunk = io == KDA_BF16 && !force_token_bwd();
+  for (const void* p : {q, k, v, dout, (const void*)g, (const void*)dq, (const void*)dk_out,
+                        (const void*)dv_out})
+    chunk = chunk && aligned(p, 16);
+  const hipError_t err = chunk ? kda::launch_bwd_chunk(a) : kda::launch_recurrent_bwd(a);
+  return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 int64_t kda_chunk_fwd_launches(int64_t B, int64_t T, int64_t H, int dk, int dv, kda_dtype io) {

@@ -1,0 +1,784 @@
+// Backward of the KDA layer core on the matrix cores (bfloat16 io,
+// dk = dv = 128), chunkwise in 16-token tiles.
+//
+// The forward over a tile of C = 16 tokens with start state S (dk x dv, rows
+// are key channels) and G the in-tile cumulative sum of g ("Kimi K3:
+// Engineering a 2.8 Trillion Parameter Frontier", section "Dimension 1":
+// 16-token tiles whose cumulative log-decay stays in (-80, 0)):
+//   Kh = k e^G, Kc = k e^-G, Qh = q e^G, Kb = k e^(G_15 - G), E = e^G_15
+//   P = Kh Kc^T, A = strict_lower(Diag(beta) P), M = (I + A)^-1, T = M Diag(beta)
+//   Aqk = lower(Qh Kc^T)
+//   X = V - Kh S,  Delta = T X,  O = scale (Qh S + Aqk Delta),  S' = Diag(E) S + Kb^T Delta
+// The pages give no backward pass; these are the plain gradients of a loss
+// given dO for every token and dS_T for the final state.  With dO' = scale dO
+// and dS' the adjoint of the tile's end state, the adjoint of the tile is
+//   dDelta = Aqk^T dO' + Kb dS'          dX = T^T dDelta          dV = dX
+//   dS     = Diag(E) dS' + Qh^T dO' - Kh^T dX                     (the previous tile's dS')
+//   Y1 = dO' S^T,  Y2 = dX S^T,  Y3 = Delta dS'^T,  dE = rowsum(S * dS')
+//   dT = dDelta X^T,  dAqk = lower(dO' Delta^T)
+// and, per tile from those (float32):
+//   dM = dT Diag(beta),  dbeta_j = sum_i dT_ij M_ij + sum_k dA_jk P_jk,
+//   dA = strict_lower(-M^T dM M^T),  dP = Diag(beta) dA
+//   dq  = e^G (Y1 + dAqk Kc)
+//   dk  = e^G (-Y2 + dP Kc) + e^-G (dAqk^T Qh + dP^T Kh) + e^(G_15 - G) Y3
+//   dG  = k (dk_h - dk_c - dk_b) + q dq  (the three parts of dk), dG_15 += sum_rows k dk_b + dE E
+//   dg  = reverse cumulative sum of dG over the tile.
+// Every product with a factor e^-G (up to e^80) is formed in float32 with the
+// masked (causal) entries only, so each term carries e^(G_i - G_j) <= 1.
+//
+// The pass runs as five steps on the caller's stream:
+//   1. the matrix-core forward, state only, with the state kept every 64
+//      tokens (a block of four tiles);
+//   2. kda_bwd_rec_kernel: per tile and in parallel, the operands of the two
+//      chains (the record below), as float16 matrix-core operand images;
+//   3. kda_bwd_chain_kernel: per head, the tiles last to first, dS' resident
+//      in matrix-core accumulators; it keeps dS' at the end of every block
+//      and returns dS_0;
+//   4. kda_bwd_block_kernel: per head and block, in parallel: for each tile
+//      of the block (last to first) the forward state recomputed from the
+//      block's start state, the tile's adjoint step, the products Y1, Y2, Y3,
+//      dE, dT, dAqk over all value columns (float32, summed in a fixed order,
+//      so the pass is deterministic) and dV;
+//   5. kda_bwd_fin_kernel: per tile, the float32 part above.
+// The state and its adjoint enter the products as float16 with a power-of-two
+// scale per wavefront (scale_shift), as in the forward's state pass; the
+// method is linear in the forward values and in the adjoint values, and each
+// wavefront divides what it contributes by both scales.
+#include "kda_chunk_rec.h"
+#include "kda_chunk_tile.h"
+#include "kda_launch.h"
+
+namespace kda {
+namespace bwd {
+
+constexpr int kC = 16, kDK = 128, kDV = 128;
+constexpr int64_t kDD = (int64_t)kDK * kDV;
+constexpr int kBlkTiles = 4;                 // tiles per block
+constexpr int kBlkTok = kBlkTiles * kC;      // 64 tokens
+
+// Record of one tile (float16 operand images of one 64-lane wavefront,
+// lane l = 16 g + c; chan(b, p) is the key channel of row p of state block b):
+constexpr int kKh = 0;        // [slab < 4][lane][8]  lane (t, g): Kh[t][32 s + 8 g + e]
+constexpr int kKb = 4096;     // [slab < 4][lane][8]  lane (t, g): Kb[t][32 s + 8 g + e]
+constexpr int kQK = 8192;     // [block < 8][lane][8] lane (c, g): Qh[4 g + e][chan(b, c)] (e < 4),
+                              //                      -Kh[4 g + e - 4][chan(b, c)] (e >= 4)
+constexpr int kKbC = 16384;   // [block < 8][lane][4] lane (c, g): Kb[4 g + e][chan(b, c)]
+constexpr int kT = 20480;     // [lane][4]            lane (i, g): T[i][4 g + e]
+constexpr int kTt = 20992;    // [lane][4]            T[4 g + e][i]
+constexpr int kAqkT = 21504;  // [lane][4]            Aqk[4 g + e][i]
+constexpr int kE = 22016;     // [128] f32            E per key channel
+constexpr int kTlo = 22528;   // [lane][4]            T - kT (the float16 rounding of T)
+constexpr int kRecBytes = 23552;  // a whole number of 1 KB blocks
+
+// Products of one tile (float32), from the block kernel to the finishing kernel:
+constexpr int kY1 = 0, kY2 = 2048, kY3 = 4096;  // [16][128] each
+constexpr int kDE = 6144;                       // [128]
+constexpr int kDT = 6272, kDAqk = 6528;         // [16][16] each
+constexpr int kYFloats = 6784;
+
+__device__ __forceinline__ f16x8 lo8(f16x4 x) {
+  return f16x8{x[0], x[1], x[2], x[3], (f16)0.f, (f16)0.f, (f16)0.f, (f16)0.f};
+}
+__device__ __forceinline__ f16x8 ld16h(const unsigned char* p) { return *(const f16x8*)p; }
+__device__ __forceinline__ f16x4 ld8h(const unsigned char* p) { return *(const f16x4*)p; }
+
+// X transposed: lane (i, g) holds X[i][4 g + e] on entry and X[4 g + e][i] on return.
+__device__ __forceinline__ f16x4 transpose16(f16x4 x, tile::Scratch* sm, int lane) {
+  f16* buf = (f16*)&sm->tr[0][0];
+  const int i = lane % 16, g = lane / 16;
+  wave_lds_sync();
+  *(f16x4*)(buf + i * 16 + 4 * g) = x;
+  wave_lds_sync();
+  f16x4 y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = buf[(4 * g + e) * 16 + i];
+  wave_lds_sync();
+  return y;
+}
+
+// ------------------------------------------------------------------ 2. records
+struct RecArgs {
+  const bf16_t* q;
+  const bf16_t* k;
+  const float* g;
+  const float* beta;
+  unsigned char* recs;  // [B H][nt][kRecBytes]
+  int64_t B, T, H, nt;
+};
+
+// The record of tile x of head bh, built by one wavefront.  Lane (t, g) holds
+// token t and, per 32-channel slab s, channels 32 s + 8 g + 0..7.
+__device__ __forceinline__ void build_tile(const RecArgs& a, int64_t bh, int64_t x,
+                                           tile::Scratch* sm, int lane) {
+  const int t = lane % 16, lg = lane / 16;
+  const int64_t b = bh / a.H, h = bh % a.H;
+  const int64_t tok0 = x * kC, tok = tok0 + t;
+  const bool full = tok0 + kC <= a.T;
+  const float lv = tok < a.T ? 1.f : 0.f;  // tokens past the end: identity tokens
+  const int64_t row = (b * a.T + (tok < a.T ? tok : a.T - 1)) * a.H + h;
+  const float bt = a.beta[row] * lv;
+  unsigned char* R = a.recs + (bh * a.nt + x) * (int64_t)kRecBytes;
+  f32x4 acc_a = zero4(), acc_q = zero4();
+  float nq = 0.f, nk = 0.f;
+  tile::SlabIn in;
+  bf16x8 q1, k1;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    bf16x8 qn, kn;
+    tile::load_slab<false>(in, qn, kn, a.q, a.k, a.g, nullptr, row, s, lane);
+    if (s % 2 == 0) {
+      q1 = qn;
+      k1 = kn;
+    } else {
+      in.q = q1;
+      in.k = k1;
+    }
+    tile::SlabVals v;
+    tile::slab_vals_any<false>(full, in, lv, v, acc_a, acc_q, nq, nk);
+    *(f16x8*)(R + kKh + s * 1024 + lane * 16) = tile::to_h8(v.kh);
+    *(f16x8*)(R + kKb + s * 1024 + lane * 16) = tile::to_h8(v.kb);
+    f16x4 kbT[2], qT[2], khT[2];
+    tile::transpose_slab(v.kb, sm, lane, kbT);
+    tile::transpose_slab(v.qh, sm, lane, qT);
+    tile::transpose_slab(v.kh, sm, lane, khT);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      *(f16x4*)(R + kKbC + (2 * s + hb) * 512 + lane * 8) = kbT[hb];
+      *(f16x8*)(R + kQK + (2 * s + hb) * 1024 + lane * 16) = cat8(qT[hb], -khT[hb]);
+    }
+    if (t == 15) {
+      f32x4* ep = (f32x4*)(R + kE + (32 * s + 8 * lg) * 4);
+      ep[0] = f32x4{v.en[0], v.en[1], v.en[2], v.en[3]};
+      ep[1] = f32x4{v.en[4], v.en[5], v.en[6], v.en[7]};
+    }
+  }
+  f16x4 tb, aq, tw;
+  f32x4 tf;
+  tile::finish<false>(acc_a, acc_q, bt, 1.f, sm, lane, tb, aq, tw, &tf);
+  *(f16x4*)(R + kT + lane * 8) = tb;
+  *(f16x4*)(R + kTlo + lane * 8) = to_h4(tf - f32x4{(float)tb[0], (float)tb[1], (float)tb[2],
+                                                    (float)tb[3]});
+  *(f16x4*)(R + kTt + lane * 8) = transpose16(tb, sm, lane);
+  *(f16x4*)(R + kAqkT + lane * 8) = transpose16(aq, sm, lane);
+}
+
+__global__ void __launch_bounds__(256) kda_bwd_rec_kernel(RecArgs a) {
+  __shared__ tile::Scratch scratch[4];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int lane = threadIdx.x % 64;
+  const int64_t total = a.B * a.H * a.nt;
+  for (int64_t w = (int64_t)blockIdx.x * 4 + wave; w < total; w += (int64_t)gridDim.x * 4)
+    build_tile(a, w % (a.B * a.H), w / (a.B * a.H), &scratch[wave], lane);
+}
+
+// --------------------------------------------- scale of a wavefront's operands
+// The wavefront holds sigma Z (sigma = 2^sh) in f32 accumulators Z[8] and forms
+// sigma W from w (16 values per lane); returns the rescale already applied.
+struct Scale {
+  int sh = 0;
+  float sig = 1.f, isig = 1.f;
+};
+
+// Chooses the scale for accumulators z and incoming values w (unscaled),
+// rescales z when it moves, and returns sigma w.
+__device__ __forceinline__ f32x4 rescale(Scale& sc, f32x4 (&z)[8], f32x4 w) {
+  f32x4 ws = w * sc.sig;
+  float m0 = 0.f, m1 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) m0 = fmaxf(m0, fabsf(ws[r]));
+#pragma unroll
+  for (int kb = 0; kb < 8; kb += 2)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      m0 = fmaxf(m0, fabsf(z[kb][r]));
+      m1 = fmaxf(m1, fabsf(z[kb + 1][r]));
+    }
+  const int em = exp_of(wave_max_nonneg(fmaxf(m0, m1)));
+  if (scale_shift(em, sc.sh) != 0) {  // rare: measured again with w unscaled
+    float mz = 0.f, mw = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mw = fmaxf(mw, fabsf(w[r]));
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mz = fmaxf(mz, fabsf(z[kb][r]));
+    const int ez = exp_of(wave_max_nonneg(mz));
+    int ew = exp_of(wave_max_nonneg(mw));
+    ew = ew == kNoExp ? kNoExp : ew + sc.sh;
+    const int d = scale_shift(ez > ew ? ez : ew, sc.sh);
+    if (d != 0) {
+      const float f = exp2i(d);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) z[kb] *= f;
+      sc.sh += d;
+      sc.sig = exp2i(sc.sh);
+      sc.isig = exp2i(-sc.sh);
+    }
+    ws = w * sc.sig;
+  }
+  return ws;
+}
+
+// The k-operand image of a wavefront's 16 value columns of a [dk, dv] state
+// in accumulators (lane (c, g) of block kb: rows chan(kb, 4 g + r), column c).
+__device__ __forceinline__ void state_op(const f32x4 (&z)[8], f16x8 (&op)[4]) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) op[s] = cat8(to_h4(z[2 * s]), to_h4(z[2 * s + 1]));
+}
+
+__device__ __forceinline__ void load_state(f32x4 (&z)[8], const float* p, int col, int lane) {
+  const int lc = lane % 16, lg = lane / 16;
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      z[kb][r] = p != nullptr ? p[rec::chan(kb, 4 * lg + r) * kDV + col + lc] : 0.f;
+}
+
+__device__ __forceinline__ void store_state(float* p, const f32x4 (&z)[8], float f, int col,
+                                            int lane) {
+  const int lc = lane % 16, lg = lane / 16;
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[rec::chan(kb, 4 * lg + r) * kDV + col + lc] = z[kb][r] * f;
+}
+
+// Selection matrix for moving 16 token rows into the k-operand layout:
+// B[k = 4 g + e][c] = (k == c).
+__device__ __forceinline__ bf16x4 ident_op(int lane) {
+  bf16x4 id;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) id[e] = (bf16_t)((4 * (lane / 16) + e == lane % 16) ? 1.f : 0.f);
+  return id;
+}
+
+// -------------------------------------------------------------- 3. the chain
+struct ChainArgs {
+  const unsigned char* recs;
+  const bf16_t* dout;
+  const float* dsf;  // [B H][dk][dv] or NULL
+  float* ds_blk;     // [B H][nblk][dk][dv]: dS' at the end of every block
+  float* ds0;        // [B H][dk][dv] or NULL
+  int64_t B, T, H, nt, nblk;
+  float scale;
+};
+
+constexpr int kRowBytes = kDV * 2;
+constexpr int kChainSlot = kRecBytes + kC * kRowBytes;  // record, then 16 dO rows
+static_assert(kChainSlot % 1024 == 0 && kRecBytes % 1024 == 0, "whole 1 KB load blocks");
+constexpr int kChainBlocks = kChainSlot / 1024;
+
+// One workgroup per (b, h), eight wavefronts of 16 value columns each, the
+// tiles last to first.  The record and the dO rows of the next tile are moved
+// into the other half of a two-slot LDS buffer with direct-to-LDS loads while
+// a tile is processed.
+__global__ void __launch_bounds__(512, 1) kda_bwd_chain_kernel(ChainArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2][kChainSlot];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int lane = threadIdx.x % 64, lc = lane % 16, lg = lane / 16;
+  const int64_t bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+  const int col = 16 * wave;
+
+  auto issue = [&](int64_t x, int slot) {
+    const unsigned char* R = a.recs + (bh * a.nt + x) * (int64_t)kRecBytes;
+    for (int blk = wave; blk < kChainBlocks; blk += 8) {
+      const unsigned char* src;
+      if (blk < kRecBytes / 1024) {
+        src = R + blk * 1024 + lane * 16;
+      } else {  // 4 dO rows per block, 16 chunks of 16 bytes per row
+        int64_t tok = x * kC + (blk - kRecBytes / 1024) * 4 + lane / 16;
+        tok = tok < a.T ? tok : a.T - 1;
+        src = (const unsigned char*)(a.dout + ((b * a.T + tok) * a.H + h) * kDV + (lane % 16) * 8);
+      }
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(lds[slot] +
+                                                                                 blk * 1024),
+                                       16, 0, 0);
+    }
+  };
+
+  // The adjoint quantities are held in units of scale / sigma, so that dO
+  // (bfloat16) enters the float16 operands exactly: sigma dO instead of a
+  // rounded sigma scale dO.  so = scale, or 1 with dO dropped when scale = 0.
+  const float so = a.scale != 0.f ? a.scale : 1.f, dmul = a.scale != 0.f ? 1.f : 0.f;
+  f32x4 dS[8];
+  load_state(dS, a.dsf != nullptr ? a.dsf + bh * kDD : nullptr, col, lane);
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) dS[kb] *= 1.f / so;
+  Scale sc;
+  const bf16x4 ident = ident_op(lane);
+
+  issue(a.nt - 1, (int)((a.nt - 1) & 1));
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int64_t x = a.nt - 1; x >= 0; --x) {
+    const int slot = (int)(x & 1);
+    if (x > 0) issue(x - 1, slot ^ 1);
+    const unsigned char* R = lds[slot];
+    // dS' at the end of the block this tile ends
+    const int64_t blk = x / kBlkTiles;
+    int64_t last = blk * kBlkTiles + kBlkTiles - 1;
+    last = last < a.nt - 1 ? last : a.nt - 1;
+    if (x == last) store_state(a.ds_blk + (bh * a.nblk + blk) * kDD, dS, so * sc.isig, col, lane);
+
+    // dO in the k-operand layout: lane (c, g): dO[4 g + r][col + c]
+    const bf16x4 dor = *(const bf16x4*)(R + kRecBytes + lc * kRowBytes + (col + 4 * lg) * 2);
+    const f32x4 dof = mma16b(dor, ident, zero4()) * dmul;
+    const f16x4 do16 = to_h4(rescale(sc, dS, dof));
+    f16x8 sop[4];
+    state_op(dS, sop);
+    f32x4 dd = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dd = mma32h(ld16h(R + kKb + s * 1024 + lane * 16), sop[s], dd);
+    dd = mma32h(lo8(ld8h(R + kAqkT + lane * 8)), cat8(do16, do16), dd);
+    const f16x4 dd16 = to_h4(dd);
+    const f32x4 dx = mma32h(lo8(ld8h(R + kTt + lane * 8)), cat8(dd16, dd16), zero4());
+    const f16x8 bop = cat8(do16, to_h4(dx));
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      const f32x4 e4 =
+          *(const f32x4*)(R + kE + 4 * (32 * (kb / 2) + 8 * lg + 4 * (kb % 2)));
+      dS[kb] = mma32h(ld16h(R + kQK + kb * 1024 + lane * 16), bop, dS[kb] * e4);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  if (a.ds0 != nullptr) store_state(a.ds0 + bh * kDD, dS, so * sc.isig, col, lane);
+}
+
+// ---------------------------------------------------------- 4. block products
+struct BlockArgs {
+  const unsigned char* recs;
+  const bf16_t* v;
+  const bf16_t* dout;
+  const float* s0;      // [B H][dk][dv] or NULL
+  const float* s_ck;    // [B][T / 64][H][dk][dv]: the state after every 64 tokens
+  const float* ds_blk;  // [B H][nblk][dk][dv]
+  bf16_t* dv;
+  float* ybuf;          // [B H][nt][kYFloats]
+  int64_t B, T, H, nt, nblk, nck;
+  float scale;
+};
+
+// Staging of one tile's operands for the products over value columns, every
+// value unscaled float32, chunk w = the 16 value columns of wavefront w.
+struct BlockSmem {
+  float st[8][kDK * 16];       // chunk w of S_t, then of dS', row-major [c][j]
+  float sx[8][5][kC * 16];     // chunk w of dO, dX, Delta, dDelta, X, row-major [t][j]
+  float dep[8][kDK];           // chunk w's part of dE
+};
+
+__device__ __forceinline__ f32x4 to_f4(f16x4 x) {
+  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+
+// A token row of v or dO (bfloat16) as the A operand of the selection-matrix
+// product: lane (t, g) columns col + 4 g .. + 3 of token t, zero past the end.
+__device__ __forceinline__ bf16x4 token_row4(const bf16_t* p, int64_t tok, int64_t T, int64_t b,
+                                             int64_t h, int64_t H, int col, int lane) {
+  bf16x4 r{};
+  if (tok < T) r = *(const bf16x4*)(p + ((b * T + tok) * H + h) * kDV + col + 4 * (lane / 16));
+  return r;
+}
+
+// This wavefront's accumulators (lane (c, g) of block kb: rows chan(kb, 4 g + r),
+// column c) times f to row-major [channel][c] float32.
+__device__ __forceinline__ void stage_state(float* st, const f32x4 (&z)[8], float f, int lane) {
+  const int lc = lane % 16, lg = lane / 16;
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st[rec::chan(kb, 4 * lg + r) * 16 + lc] = z[kb][r] * f;
+}
+
+// A [16 tokens][16 columns] accumulator (lane (c, g): rows 4 g + r) times f to
+// row-major float32.
+__device__ __forceinline__ void stage_small(float* sx, f32x4 z, float f, int lane) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) sx[(4 * (lane / 16) + r) * 16 + lane % 16] = z[r] * f;
+}
+
+// Out[4 g + r][16 m + c] of A B^T summed over all 128 value columns (the
+// eight chunks in order), A chunk w at A0 + w * as, B chunk w at B0 + w * bs.
+__device__ __forceinline__ f32x4 prod128(const float* A0, int as, const float* B0, int bs,
+                                         int lane) {
+  f32x4 o = zero4();
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const f32x4 av = *(const f32x4*)(A0 + w * as + (lane % 16) * 16 + 4 * (lane / 16));
+    const f32x4 bv = *(const f32x4*)(B0 + w * bs + (lane % 16) * 16 + 4 * (lane / 16));
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) o = mma4f(av[mm], bv[mm], o);
+  }
+  return o;
+}
+
+__global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
+  __shared__ __attribute__((aligned(16))) BlockSmem sm;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64, lc = lane % 16, lg = lane / 16;
+  const int64_t bh = blockIdx.x / a.nblk, blk = blockIdx.x % a.nblk;
+  const int64_t b = bh / a.H, h = bh % a.H;
+  const int col = 16 * wave;
+  const int64_t x0 = blk * kBlkTiles;
+  const int ntl = (int)(a.nt - x0 < kBlkTiles ? a.nt - x0 : kBlkTiles);
+
+  const bf16x4 ident = ident_op(lane);
+  // adjoint quantities in units of scale / sigma (see the chain kernel)
+  const float so = a.scale != 0.f ? a.scale : 1.f, dmul = a.scale != 0.f ? 1.f : 0.f;
+  f32x4 dS[8];
+  load_state(dS, a.ds_blk + (bh * a.nblk + blk) * kDD, col, lane);
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) dS[kb] *= 1.f / so;
+  Scale sd;
+  const float* s_start = blk == 0 ? (a.s0 != nullptr ? a.s0 + bh * kDD : nullptr)
+                                  : a.s_ck + ((b * a.nck + blk - 1) * a.H + h) * kDD;
+
+  for (int tl = ntl - 1; tl >= 0; --tl) {
+    const int64_t x = x0 + tl;
+    // ---- forward: S_tl from the block's start state.  T, X and Delta enter
+    // their products as float16 pairs (value and rounding error).
+    f32x4 S[8];
+    load_state(S, s_start, col, lane);
+    Scale sf;
+    f32x4 X = zero4(), Dl = zero4();
+    for (int u = 0; u <= tl; ++u) {
+      const unsigned char* Ru = a.recs + (bh * a.nt + x0 + u) * (int64_t)kRecBytes;
+      const bf16x4 vr = token_row4(a.v, (x0 + u) * kC + lc, a.T, b, h, a.H, col, lane);
+      const f32x4 vs = rescale(sf, S, mma16b(vr, ident, zero4()));
+      f16x8 sopS[4];
+      state_op(S, sopS);
+      f32x4 y = zero4();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) y = mma32h(ld16h(Ru + kKh + s * 1024 + lane * 16), sopS[s], y);
+      X = vs - y;
+      const f16x4 xh = to_h4(X), xl = to_h4(X - to_f4(xh));
+      const f16x8 th = lo8(ld8h(Ru + kT + lane * 8)), tlo = lo8(ld8h(Ru + kTlo + lane * 8));
+      Dl = mma32h(th, cat8(xh, xh), zero4());
+      Dl = mma32h(th, cat8(xl, xl), Dl);
+      Dl = mma32h(tlo, cat8(xh, xh), Dl);
+      if (u < tl) {
+        const f16x4 dh = to_h4(Dl), dlo = to_h4(Dl - to_f4(dh));
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+          const f32x4 e4 =
+              *(const f32x4*)(Ru + kE + 4 * (32 * (kb / 2) + 8 * lg + 4 * (kb % 2)));
+          const f16x8 kbc = lo8(ld8h(Ru + kKbC + kb * 512 + lane * 8));
+          S[kb] = mma32h(kbc, cat8(dh, dh), S[kb] * e4);
+          S[kb] = mma32h(kbc, cat8(dlo, dlo), S[kb]);
+        }
+      }
+    }
+    // ---- the adjoint step of tile tl
+    const unsigned char* R = a.recs + (bh * a.nt + x) * (int64_t)kRecBytes;
+    const bf16x4 dr = token_row4(a.dout, x * kC + lc, a.T, b, h, a.H, col, lane);
+    const f32x4 dos = rescale(sd, dS, mma16b(dr, ident, zero4()) * dmul);
+    const f16x4 do16 = to_h4(dos);  // exact: sigma dO with dO in bfloat16
+    f16x8 sopD[4];
+    state_op(dS, sopD);
+    f32x4 dd = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dd = mma32h(ld16h(R + kKb + s * 1024 + lane * 16), sopD[s], dd);
+    dd = mma32h(lo8(ld8h(R + kAqkT + lane * 8)), cat8(do16, do16), dd);
+    const f16x4 dd16 = to_h4(dd);
+    const f32x4 dx = mma32h(lo8(ld8h(R + kTt + lane * 8)), cat8(dd16, dd16), zero4());
+    const float ff = sf.isig, fd = so * sd.isig;  // back to unscaled units
+    float* Y = a.ybuf + (bh * a.nt + x) * (int64_t)kYFloats;
+
+    // dE = rowsum(S_t * dS') in float32: each lane's column, summed over the
+    // 16 lanes of its row group (lane 15 of the group then holds the sum)
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = row_scan16(S[kb][r] * dS[kb][r]);
+        if (lc == 15) sm.dep[wave][rec::chan(kb, 4 * lg + r)] = p * ff * fd;
+      }
+
+    // ---- the products over the 128 value columns, float32: every chunk
+    // staged unscaled, then wavefront w forms output columns 16 w .. 16 w + 15
+    // (channels) summing the chunks in order
+    stage_state(sm.st[wave], S, ff, lane);
+    stage_small(sm.sx[wave][0], dos, fd, lane);
+    stage_small(sm.sx[wave][1], dx, fd, lane);
+    stage_small(sm.sx[wave][2], Dl, ff, lane);
+    stage_small(sm.sx[wave][3], dd, fd, lane);
+    stage_small(sm.sx[wave][4], X, ff, lane);
+    __syncthreads();
+    {
+      constexpr int kXs = 5 * kC * 16, kSs = kDK * 16;
+      const f32x4 y1 = prod128(sm.sx[0][0], kXs, sm.st[0] + 16 * wave * 16, kSs, lane);
+      const f32x4 y2 = prod128(sm.sx[0][1], kXs, sm.st[0] + 16 * wave * 16, kSs, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int o = (4 * lg + r) * kDK + 16 * wave + lc;
+        Y[kY1 + o] = y1[r];  // dO S^T
+        Y[kY2 + o] = y2[r];  // dX S^T
+      }
+      if (wave < 2) {  // dDelta X^T and dO Delta^T
+        const f32x4 d = wave == 0 ? prod128(sm.sx[0][3], kXs, sm.sx[0][4], kXs, lane)
+                                  : prod128(sm.sx[0][0], kXs, sm.sx[0][2], kXs, lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Y[(wave == 0 ? kDT : kDAqk) + (4 * lg + r) * 16 + lc] = d[r];
+      } else if (wave == 2) {
+        for (int c = lane; c < kDK; c += 64) {
+          float e = 0.f;
+#pragma unroll
+          for (int w = 0; w < 8; ++w) e += sm.dep[w][c];
+          Y[kDE + c] = e;
+        }
+      }
+    }
+    __syncthreads();
+    stage_state(sm.st[wave], dS, fd, lane);
+    __syncthreads();
+    {
+      constexpr int kXs = 5 * kC * 16, kSs = kDK * 16;
+      const f32x4 y3 = prod128(sm.sx[0][2], kXs, sm.st[0] + 16 * wave * 16, kSs, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Y[kY3 + (4 * lg + r) * kDK + 16 * wave + lc] = y3[r];  // Delta dS'^T
+    }
+    // dV = dX: lane (t, g) stores columns col + 4 g .. + 3 of token t
+    {
+      const int64_t tok = x * kC + lc;
+      if (tok < a.T) {
+        const f32x4 d = *(const f32x4*)&sm.sx[wave][1][lc * 16 + 4 * lg];
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (bf16_t)d[e];
+        *(bf16x4*)(a.dv + ((b * a.T + tok) * a.H + h) * kDV + col + 4 * lg) = o;
+      }
+    }
+    // dS' of the tile before (the adjoint of this tile's start state)
+    {
+      const f16x8 bop = cat8(do16, to_h4(dx));
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        const f32x4 e4 = *(const f32x4*)(R + kE + 4 * (32 * (kb / 2) + 8 * lg + 4 * (kb % 2)));
+        dS[kb] = mma32h(ld16h(R + kQK + kb * 1024 + lane * 16), bop, dS[kb] * e4);
+      }
+    }
+    __syncthreads();  // the staging is free for the next tile
+  }
+}
+
+// ------------------------------------------------------------ 5. finishing
+struct FinArgs {
+  const bf16_t* q;
+  const bf16_t* k;
+  const float* g;
+  const float* beta;
+  const float* ybuf;
+  bf16_t* dq;
+  bf16_t* dk;
+  float* dg;
+  float* dbeta;
+  int64_t B, T, H, nt;
+};
+
+struct FinSmem {
+  float k[kC][kDK], q[kC][kDK], eg[kC][kDK], ieg[kC][kDK], dG[kC][kDK];
+  float P[kC][kC + 1], M[kC][kC + 1], dM[kC][kC + 1], Z[kC][kC + 1], dP[kC][kC + 1],
+      dAq[kC][kC + 1];
+  float beta[kC], dbT[kC], dbA[kC];
+  float kdkb[2][kDK];
+};
+
+// One workgroup per tile (256 threads), float32 throughout.
+__global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
+  __shared__ FinSmem sm;
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.x / a.nt, x = blockIdx.x % a.nt;
+  const int64_t b = bh / a.H, h = bh % a.H;
+  const float* Y = a.ybuf + (bh * a.nt + x) * (int64_t)kYFloats;
+  auto row_of = [&](int t) {
+    int64_t tok = x * kC + t;
+    tok = tok < a.T ? tok : a.T - 1;
+    return (b * a.T + tok) * a.H + h;
+  };
+  auto valid = [&](int t) { return x * kC + t < a.T; };
+
+  // inputs, cumulative log-decay per channel (tokens past the end: zero inputs)
+  if (tid < kDK) {
+    const int c = tid;
+    float G = 0.f;
+    for (int t = 0; t < kC; ++t) {
+      const bool ok = valid(t);
+      const int64_t r = row_of(t);
+      G += ok ? a.g[r * kDK + c] : 0.f;
+      sm.eg[t][c] = __expf(G);
+      sm.ieg[t][c] = __expf(-G);
+      sm.k[t][c] = ok ? (float)a.k[r * kDK + c] : 0.f;
+      sm.q[t][c] = ok ? (float)a.q[r * kDK + c] : 0.f;
+    }
+  } else if (tid < kDK + kC) {
+    const int t = tid - kDK;
+    sm.beta[t] = valid(t) ? a.beta[row_of(t)] : 0.f;
+  }
+  __syncthreads();
+  const int i = tid / kC, j = tid % kC;  // a (row, column) of a 16 x 16 matrix
+  {
+    float p = 0.f;  // P = Kh Kc^T; only j < i is used
+    if (j < i)
+      for (int c = 0; c < kDK; ++c) p = fmaf(sm.k[i][c] * sm.eg[i][c], sm.k[j][c] * sm.ieg[j][c], p);
+    sm.P[i][j] = p;
+  }
+  __syncthreads();
+  if (tid < kC) {  // M = (I + A)^-1, A = strict_lower(Diag(beta) P): column tid, rows in order
+    const int cj = tid;
+    for (int r = 0; r < kC; ++r) {
+      float m = r == cj ? 1.f : 0.f;
+      for (int kk = 0; kk < r; ++kk) m -= sm.beta[r] * sm.P[r][kk] * sm.M[kk][cj];
+      sm.M[r][cj] = m;
+    }
+  }
+  __syncthreads();
+  const float dT = Y[kDT + i * kC + j];
+  sm.dM[i][j] = dT * sm.beta[j];
+  sm.dAq[i][j] = j <= i ? Y[kDAqk + i * kC + j] : 0.f;
+  __syncthreads();
+  {
+    float z = 0.f;  // Z = dM M^T
+    for (int c = 0; c < kC; ++c) z = fmaf(sm.dM[i][c], sm.M[j][c], z);
+    sm.Z[i][j] = z;
+  }
+  if (tid < kC) {  // dbeta from T = M Diag(beta): column sums of dT * M
+    float s = 0.f;
+    for (int r = 0; r < kC; ++r) s = fmaf(Y[kDT + r * kC + tid], sm.M[r][tid], s);
+    sm.dbT[tid] = s;
+  }
+  __syncthreads();
+  {
+    float d = 0.f;  // dA = strict_lower(-M^T Z)
+    if (j < i)
+      for (int c = 0; c < kC; ++c) d -= sm.M[c][i] * sm.Z[c][j];
+    sm.dP[i][j] = sm.beta[i] * d;  // dP = Diag(beta) dA
+    sm.dM[i][j] = d * sm.P[i][j];   // dM is spent: row sums of dA * P, for dbeta
+  }
+  __syncthreads();
+  if (tid < kC) {
+    float s = 0.f;
+    for (int c = 0; c < kC; ++c) s += sm.dM[tid][c];
+    sm.dbA[tid] = s;
+  }
+
+  // per (token, channel): thread (c, half) takes tokens 8 half .. 8 half + 7
+  const int c = tid % kDK, half = tid / kDK;
+  float kdkb = 0.f;
+  for (int t = 8 * half; t < 8 * half + 8; ++t) {
+    float i1 = 0.f, i2 = 0.f, i3 = 0.f;
+    for (int jj = 0; jj < kC; ++jj) {
+      const float kcj = sm.k[jj][c] * sm.ieg[jj][c];
+      const float khj = sm.k[jj][c] * sm.eg[jj][c];
+      const float qhj = sm.q[jj][c] * sm.eg[jj][c];
+      i1 = fmaf(sm.dP[t][jj], kcj, i1);    // (dP Kc)[t]:   jj < t
+      i2 = fmaf(sm.dAq[t][jj], kcj, i2);   // (dAqk Kc)[t]: jj <= t
+      i3 = fmaf(sm.dAq[jj][t], qhj, i3);   // (dAqk^T Qh)[t]: jj >= t
+      i3 = fmaf(sm.dP[jj][t], khj, i3);    // (dP^T Kh)[t]:  jj > t
+    }
+    const int o = t * kDK + c;
+    const float egt = sm.eg[t][c], iegt = sm.ieg[t][c];
+    const float dq = egt * (Y[kY1 + o] + i2);
+    const float dkh = egt * (i1 - Y[kY2 + o]);
+    const float dkc = iegt * i3;
+    const float dkb = sm.eg[kC - 1][c] * iegt * Y[kY3 + o];
+    const float kt = sm.k[t][c];
+    kdkb = fmaf(kt, dkb, kdkb);
+    sm.dG[t][c] = kt * (dkh - dkc - dkb) + sm.q[t][c] * dq;
+    if (valid(t)) {
+      const int64_t r = row_of(t);
+      a.dq[r * kDK + c] = (bf16_t)dq;
+      a.dk[r * kDK + c] = (bf16_t)(dkh + dkc + dkb);
+    }
+  }
+  sm.kdkb[half][c] = kdkb;
+  __syncthreads();
+  if (tid < kDK) {  // dG_15 += sum_rows k dk_b + dE E, then dg = reverse cumulative sum
+    float acc = sm.kdkb[0][c] + sm.kdkb[1][c] + Y[kDE + c] * sm.eg[kC - 1][c];
+    for (int t = kC - 1; t >= 0; --t) {
+      acc += sm.dG[t][c];
+      if (valid(t)) a.dg[row_of(t) * kDK + c] = acc;
+    }
+  } else if (tid < kDK + kC) {
+    const int t = tid - kDK;
+    if (valid(t)) a.dbeta[row_of(t)] = sm.dbT[t] + sm.dbA[t];
+  }
+}
+
+}  // namespace bwd
+
+// Workspace of the chunkwise backward, in 256-byte aligned parts.
+struct BwdChunkWs {
+  int64_t fwd, s_tmp, s_ck, ds_blk, recs, ybuf, total;
+};
+
+static int64_t al256(int64_t n) { return (n + 255) / 256 * 256; }
+
+static BwdChunkWs bwd_chunk_layout(int64_t B, int64_t T, int64_t H) {
+  using namespace bwd;
+  const int64_t BH = B * H, nt = (T + kC - 1) / kC, nblk = (nt + kBlkTiles - 1) / kBlkTiles;
+  BwdChunkWs w;
+  w.fwd = 0;
+  w.s_tmp = al256((int64_t)chunk_mfma_workspace(B, T, H));
+  w.s_ck = w.s_tmp + al256(BH * kDD * 4);
+  w.ds_blk = w.s_ck + al256(B * (T / kBlkTok) * H * kDD * 4);
+  w.recs = w.ds_blk + al256(BH * nblk * kDD * 4);
+  w.ybuf = w.recs + al256(BH * nt * (int64_t)kRecBytes);
+  w.total = w.ybuf + al256(BH * nt * (int64_t)kYFloats * 4);
+  return w;
+}
+
+int64_t bwd_chunk_workspace_bytes(int64_t B, int64_t T, int64_t H) {
+  return bwd_chunk_layout(B, T, H).total;
+}
+
+hipError_t launch_bwd_chunk(const BwdArgs& a) {
+  using namespace bwd;
+  const int64_t BH = a.B * a.H, nt = (a.T + kC - 1) / kC;
+  const int64_t nblk = (nt + kBlkTiles - 1) / kBlkTiles, nck = a.T / kBlkTok;
+  if (BH * nt > 0x7fffffffLL || BH * nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+  const BwdChunkWs w = bwd_chunk_layout(a.B, a.T, a.H);
+  unsigned char* ws = (unsigned char*)a.workspace;
+  hipStream_t st = (hipStream_t)a.stream;
+
+  // 1. forward states every 64 tokens
+  ChunkArgs ca{a.q, a.k, a.v, a.g, a.beta, a.s0, nullptr, (float*)(ws + w.s_tmp), nullptr,
+               nullptr, 0.f, a.B, a.T, a.H, kDK, kDV, 1.f, true, ws + w.fwd, a.stream};
+  ca.total = a.B * a.T;
+  if (nck > 0) {
+    ca.ckpt = (float*)(ws + w.s_ck);
+    ca.ckpt_every = kBlkTok;
+  }
+  hipError_t e = launch_chunk_mfma(ca);
+  if (e != hipSuccess) return e;
+
+  // 2. records
+  RecArgs ra{(const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, ws + w.recs, a.B, a.T, a.H, nt};
+  int64_t nrec = (BH * nt + 3) / 4;
+  nrec = nrec < 16384 ? nrec : 16384;
+  hipLaunchKernelGGL(kda_bwd_rec_kernel, dim3((unsigned)nrec), dim3(256), 0, st, ra);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  // 3. the adjoint chain
+  ChainArgs cha{ws + w.recs, (const bf16_t*)a.dout, a.ds_final, (float*)(ws + w.ds_blk), a.ds0,
+                a.B, a.T, a.H, nt, nblk, a.scale};
+  hipLaunchKernelGGL(kda_bwd_chain_kernel, dim3((unsigned)BH), dim3(512), 0, st, cha);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  // 4. block products
+  BlockArgs ba{ws + w.recs, (const bf16_t*)a.v, (const bf16_t*)a.dout, a.s0,
+               (const float*)(ws + w.s_ck), (const float*)(ws + w.ds_blk), (bf16_t*)a.dv,
+               (float*)(ws + w.ybuf), a.B, a.T, a.H, nt, nblk, nck, a.scale};
+  hipLaunchKernelGGL(kda_bwd_block_kernel, dim3((unsigned)(BH * nblk)), dim3(512), 0, st, ba);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  // 5. finishing
+  FinArgs fa{(const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, (const float*)(ws + w.ybuf),
+             (bf16_t*)a.dq, (bf16_t*)a.dk, a.dg, a.dbeta, a.B, a.T, a.H, nt};
+  hipLaunchKernelGGL(kda_bwd_fin_kernel, dim3((unsigned)(BH * nt)), dim3(256), 0, st, fa);
+  return hipGetLastError();
+}
+
+}  // namespace kda

@@ -145,4 +145,50 @@ __device__ __forceinline__ float row_bcast(float x) {
   return dpp<0x150 + M, false>(x);
 }
 
+// Largest of x over the 64 lanes (x >= 0), in every lane: a max-scan over
+// each 16-lane DPP row, then the four row maxima, compared as integers (the
+// bit patterns of non-negative floats order like their values).
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  x = fmaxf(x, dpp<0x111, true>(x));
+  x = fmaxf(x, dpp<0x112, true>(x));
+  x = fmaxf(x, dpp<0x114, true>(x));
+  x = fmaxf(x, dpp<0x118, true>(x));
+  const unsigned b = __builtin_bit_cast(unsigned, x);
+  unsigned m = (unsigned)__builtin_amdgcn_readlane((int)b, 15);
+  const unsigned m1 = (unsigned)__builtin_amdgcn_readlane((int)b, 31);
+  const unsigned m2 = (unsigned)__builtin_amdgcn_readlane((int)b, 47);
+  const unsigned m3 = (unsigned)__builtin_amdgcn_readlane((int)b, 63);
+  m = m1 > m ? m1 : m;
+  m = m2 > m ? m2 : m;
+  m = m3 > m ? m3 : m;
+  return __builtin_bit_cast(float, m);
+}
+
+// Unbiased binary exponent of a non-negative float (x in [2^e, 2^(e+1))),
+// or kNoExp for zero.  Denormals read as -127; inf and NaN as 128.
+constexpr int kNoExp = -1000;
+__device__ __forceinline__ int exp_of(float x) {
+  const int b = (int)(__builtin_bit_cast(unsigned, x) >> 23);
+  return x == 0.f ? kNoExp : b - 127;
+}
+
+// 2^e as a float, e in [-126, 127].
+__device__ __forceinline__ float exp2i(int e) {
+  return __builtin_bit_cast(float, (unsigned)(e + 127) << 23);
+}
+
+// Power-of-two scale of a state wavefront's float16 operands.  The wavefront
+// holds sigma S (sigma = 2^sh) and forms sigma V (or the adjoint quantities
+// of the backward pass); em is the exponent of the largest
+// magnitude among them.  While em stays in [kLoExp, kHiExp] the scale is
+// kept; otherwise the returned shift d moves em to kTargetExp (the caller
+// multiplies its accumulators by 2^d).  sh stays within [-120, 120].
+constexpr int kLoExp = 2, kHiExp = 10, kTargetExp = 9;
+__device__ __forceinline__ int scale_shift(int em, int sh) {
+  if (em == kNoExp || (em >= kLoExp && em <= kHiExp)) return 0;
+  int n = sh + (kTargetExp - em);
+  n = n < -120 ? -120 : (n > 120 ? 120 : n);
+  return n - sh;
+}
+
 }  // namespace kda

@@ -116,5 +116,8 @@ constexpr int kBwdPiece = 64;
 constexpr int kBwdSplit = 4;
 int64_t bwd_workspace_floats(int64_t B, int64_t T, int64_t H);
 hipError_t launch_recurrent_bwd(const BwdArgs& a);
+// Chunkwise backward on the matrix cores (bfloat16 io, 16-byte aligned tensors).
+int64_t bwd_chunk_workspace_bytes(int64_t B, int64_t T, int64_t H);
+hipError_t launch_bwd_chunk(const BwdArgs& a);
 
 }  // namespace kda
