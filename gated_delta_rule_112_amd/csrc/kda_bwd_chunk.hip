@@ -39,7 +39,8 @@
 //      block's start state, the tile's adjoint step, the products Y1, Y2, Y3,
 //      dE, dT, dAqk over all value columns (float32, summed in a fixed order,
 //      so the pass is deterministic) and dV;
-//   5. kda_bwd_fin_kernel: per tile, the float32 part above.
+//   5. kda_bwd_fin_kernel: per tile, the float32 part above (P and M come
+//      from the record builder).
 // The state and its adjoint enter the products as float16 with a power-of-two
 // scale per wavefront (scale_shift), as in the forward's state pass; the
 // method is linear in the forward values and in the adjoint values, and each
@@ -103,6 +104,7 @@ struct RecArgs {
   const float* g;
   const float* beta;
   unsigned char* recs;  // [B H][nt][kRecBytes]
+  float* pm;            // [B H][nt][2][16][16]: P = Kh Kc^T and M = (I + A)^-1, float32
   int64_t B, T, H, nt;
 };
 
@@ -153,8 +155,13 @@ __device__ __forceinline__ void build_tile(const RecArgs& a, int64_t bh, int64_t
     }
   }
   f16x4 tb, aq, tw;
-  f32x4 tf;
-  tile::finish<false>(acc_a, acc_q, bt, 1.f, sm, lane, tb, aq, tw, &tf);
+  f32x4 tf, mf;
+  tile::finish<false>(acc_a, acc_q, bt, 1.f, sm, lane, tb, aq, tw, &tf, &mf);
+  {  // lane (i, g) holds row i, columns 4 g .. 4 g + 3 of P and of M
+    float* pm = a.pm + (bh * a.nt + x) * 512 + t * 16 + 4 * lg;
+    *(f32x4*)pm = acc_a;
+    *(f32x4*)(pm + 256) = mf;
+  }
   *(f16x4*)(R + kT + lane * 8) = tb;
   *(f16x4*)(R + kTlo + lane * 8) = to_h4(tf - f32x4{(float)tb[0], (float)tb[1], (float)tb[2],
                                                     (float)tb[3]});
@@ -228,11 +235,15 @@ __device__ __forceinline__ void state_op(const f32x4 (&z)[8], f16x8 (&op)[4]) {
 
 __device__ __forceinline__ void load_state(f32x4 (&z)[8], const float* p, int col, int lane) {
   const int lc = lane % 16, lg = lane / 16;
+  if (p == nullptr) {
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) z[kb] = zero4();
+    return;
+  }
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      z[kb][r] = p != nullptr ? p[rec::chan(kb, 4 * lg + r) * kDV + col + lc] : 0.f;
+    for (int r = 0; r < 4; ++r) z[kb][r] = p[rec::chan(kb, 4 * lg + r) * kDV + col + lc];
 }
 
 __device__ __forceinline__ void store_state(float* p, const f32x4 (&z)[8], float f, int col,
@@ -363,10 +374,15 @@ struct BlockArgs {
 
 // Staging of one tile's operands for the products over value columns, every
 // value unscaled float32, chunk w = the 16 value columns of wavefront w.
+// The record parts the forward steps use, per tile of the block (shared by
+// the eight wavefronts): Kh, Kb^T, T, T - float16(T), E.
+constexpr int kFwKh = 0, kFwKbC = 4096, kFwT = 8192, kFwTlo = 8704, kFwE = 9216;
+constexpr int kFwBytes = 9728;
 struct BlockSmem {
   float st[8][kDK * 16];       // chunk w of S_t, then of dS', row-major [c][j]
   float sx[8][5][kC * 16];     // chunk w of dO, dX, Delta, dDelta, X, row-major [t][j]
   float dep[8][kDK];           // chunk w's part of dE
+  unsigned char fw[kBlkTiles][kFwBytes];
 };
 
 __device__ __forceinline__ f32x4 to_f4(f16x4 x) {
@@ -424,6 +440,18 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
   const int col = 16 * wave;
   const int64_t x0 = blk * kBlkTiles;
   const int ntl = (int)(a.nt - x0 < kBlkTiles ? a.nt - x0 : kBlkTiles);
+  // the forward-step parts of the block's records, once for all wavefronts
+  for (int i = tid; i < ntl * (kFwBytes / 16); i += 512) {
+    const int u = i / (kFwBytes / 16), o = 16 * (i % (kFwBytes / 16));
+    const unsigned char* Ru = a.recs + (bh * a.nt + x0 + u) * (int64_t)kRecBytes;
+    const int src = o < kFwKbC ? kKh + o
+                  : o < kFwT   ? kKbC + (o - kFwKbC)
+                  : o < kFwTlo ? kT + (o - kFwT)
+                  : o < kFwE   ? kTlo + (o - kFwTlo)
+                               : kE + (o - kFwE);
+    *(f32x4*)&sm.fw[u][o] = *(const f32x4*)(Ru + src);
+  }
+  __syncthreads();
 
   const bf16x4 ident = ident_op(lane);
   // adjoint quantities in units of scale / sigma (see the chain kernel)
@@ -445,17 +473,17 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
     Scale sf;
     f32x4 X = zero4(), Dl = zero4();
     for (int u = 0; u <= tl; ++u) {
-      const unsigned char* Ru = a.recs + (bh * a.nt + x0 + u) * (int64_t)kRecBytes;
+      const unsigned char* Ru = sm.fw[u];
       const bf16x4 vr = token_row4(a.v, (x0 + u) * kC + lc, a.T, b, h, a.H, col, lane);
       const f32x4 vs = rescale(sf, S, mma16b(vr, ident, zero4()));
       f16x8 sopS[4];
       state_op(S, sopS);
       f32x4 y = zero4();
 #pragma unroll
-      for (int s = 0; s < 4; ++s) y = mma32h(ld16h(Ru + kKh + s * 1024 + lane * 16), sopS[s], y);
+      for (int s = 0; s < 4; ++s) y = mma32h(ld16h(Ru + kFwKh + s * 1024 + lane * 16), sopS[s], y);
       X = vs - y;
       const f16x4 xh = to_h4(X), xl = to_h4(X - to_f4(xh));
-      const f16x8 th = lo8(ld8h(Ru + kT + lane * 8)), tlo = lo8(ld8h(Ru + kTlo + lane * 8));
+      const f16x8 th = lo8(ld8h(Ru + kFwT + lane * 8)), tlo = lo8(ld8h(Ru + kFwTlo + lane * 8));
       Dl = mma32h(th, cat8(xh, xh), zero4());
       Dl = mma32h(th, cat8(xl, xl), Dl);
       Dl = mma32h(tlo, cat8(xh, xh), Dl);
@@ -464,8 +492,8 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
           const f32x4 e4 =
-              *(const f32x4*)(Ru + kE + 4 * (32 * (kb / 2) + 8 * lg + 4 * (kb % 2)));
-          const f16x8 kbc = lo8(ld8h(Ru + kKbC + kb * 512 + lane * 8));
+              *(const f32x4*)(Ru + kFwE + 4 * (32 * (kb / 2) + 8 * lg + 4 * (kb % 2)));
+          const f16x8 kbc = lo8(ld8h(Ru + kFwKbC + kb * 512 + lane * 8));
           S[kb] = mma32h(kbc, cat8(dh, dh), S[kb] * e4);
           S[kb] = mma32h(kbc, cat8(dlo, dlo), S[kb]);
         }
@@ -571,6 +599,7 @@ struct FinArgs {
   const float* g;
   const float* beta;
   const float* ybuf;
+  const float* pm;
   bf16_t* dq;
   bf16_t* dk;
   float* dg;
@@ -586,13 +615,20 @@ struct FinSmem {
   float kdkb[2][kDK];
 };
 
-// One workgroup per tile (256 threads), float32 throughout.
+// One workgroup per tile (256 threads), float32 throughout.  Every global
+// load is issued before the arithmetic that needs it, with rows clamped into
+// the sequence and tokens past its end zeroed by a factor (no load behind a
+// branch), so a workgroup waits for memory a few times, not once per token.
 __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
   __shared__ FinSmem sm;
   const int tid = threadIdx.x;
   const int64_t bh = blockIdx.x / a.nt, x = blockIdx.x % a.nt;
   const int64_t b = bh / a.H, h = bh % a.H;
-  const float* Y = a.ybuf + (bh * a.nt + x) * (int64_t)kYFloats;
+  const float* __restrict__ Y = a.ybuf + (bh * a.nt + x) * (int64_t)kYFloats;
+  const float* __restrict__ PM = a.pm + (bh * a.nt + x) * 512;
+  const bf16_t* __restrict__ qp = a.q;
+  const bf16_t* __restrict__ kp = a.k;
+  const float* __restrict__ gp = a.g;
   auto row_of = [&](int t) {
     int64_t tok = x * kC + t;
     tok = tok < a.T ? tok : a.T - 1;
@@ -600,54 +636,56 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
   };
   auto valid = [&](int t) { return x * kC + t < a.T; };
 
-  // inputs, cumulative log-decay per channel (tokens past the end: zero inputs)
-  if (tid < kDK) {
+  // the tile's inputs: element e = tid + 256 m is (token e / 128, channel e % 128)
+  {
+    float kv[8], qv[8], gv[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int e = tid + 256 * m, t = e / kDK, c = e % kDK;
+      const int64_t r = row_of(t);
+      kv[m] = (float)kp[r * kDK + c];
+      qv[m] = (float)qp[r * kDK + c];
+      gv[m] = gp[r * kDK + c];
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int e = tid + 256 * m, t = e / kDK, c = e % kDK;
+      const float lv = valid(t) ? 1.f : 0.f;
+      sm.k[t][c] = kv[m] * lv;
+      sm.q[t][c] = qv[m] * lv;
+      sm.dG[t][c] = gv[m] * lv;  // g for now
+    }
+    const int i = tid / kC, j = tid % kC;
+    sm.P[i][j] = PM[tid];
+    sm.M[i][j] = PM[256 + tid];
+    const float dT = Y[kDT + tid], dAq = Y[kDAqk + tid];
+    if (tid < kC) sm.beta[tid] = valid(tid) ? a.beta[row_of(tid)] : 0.f;
+    __syncthreads();
+    sm.dM[i][j] = dT * sm.beta[j];
+    sm.dAq[i][j] = j <= i ? dAq : 0.f;
+    sm.Z[i][j] = dT * sm.M[i][j];  // for dbeta from T = M Diag(beta): column sums
+  }
+  if (tid < kDK) {  // cumulative log-decay per channel
     const int c = tid;
     float G = 0.f;
     for (int t = 0; t < kC; ++t) {
-      const bool ok = valid(t);
-      const int64_t r = row_of(t);
-      G += ok ? a.g[r * kDK + c] : 0.f;
+      G += sm.dG[t][c];
       sm.eg[t][c] = __expf(G);
       sm.ieg[t][c] = __expf(-G);
-      sm.k[t][c] = ok ? (float)a.k[r * kDK + c] : 0.f;
-      sm.q[t][c] = ok ? (float)a.q[r * kDK + c] : 0.f;
     }
-  } else if (tid < kDK + kC) {
-    const int t = tid - kDK;
-    sm.beta[t] = valid(t) ? a.beta[row_of(t)] : 0.f;
   }
   __syncthreads();
   const int i = tid / kC, j = tid % kC;  // a (row, column) of a 16 x 16 matrix
-  {
-    float p = 0.f;  // P = Kh Kc^T; only j < i is used
-    if (j < i)
-      for (int c = 0; c < kDK; ++c) p = fmaf(sm.k[i][c] * sm.eg[i][c], sm.k[j][c] * sm.ieg[j][c], p);
-    sm.P[i][j] = p;
+  if (tid < kC) {
+    float s = 0.f;
+    for (int r = 0; r < kC; ++r) s += sm.Z[r][tid];
+    sm.dbT[tid] = s;
   }
-  __syncthreads();
-  if (tid < kC) {  // M = (I + A)^-1, A = strict_lower(Diag(beta) P): column tid, rows in order
-    const int cj = tid;
-    for (int r = 0; r < kC; ++r) {
-      float m = r == cj ? 1.f : 0.f;
-      for (int kk = 0; kk < r; ++kk) m -= sm.beta[r] * sm.P[r][kk] * sm.M[kk][cj];
-      sm.M[r][cj] = m;
-    }
-  }
-  __syncthreads();
-  const float dT = Y[kDT + i * kC + j];
-  sm.dM[i][j] = dT * sm.beta[j];
-  sm.dAq[i][j] = j <= i ? Y[kDAqk + i * kC + j] : 0.f;
   __syncthreads();
   {
     float z = 0.f;  // Z = dM M^T
     for (int c = 0; c < kC; ++c) z = fmaf(sm.dM[i][c], sm.M[j][c], z);
     sm.Z[i][j] = z;
-  }
-  if (tid < kC) {  // dbeta from T = M Diag(beta): column sums of dT * M
-    float s = 0.f;
-    for (int r = 0; r < kC; ++r) s = fmaf(Y[kDT + r * kC + tid], sm.M[r][tid], s);
-    sm.dbT[tid] = s;
   }
   __syncthreads();
   {
@@ -655,7 +693,7 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
     if (j < i)
       for (int c = 0; c < kC; ++c) d -= sm.M[c][i] * sm.Z[c][j];
     sm.dP[i][j] = sm.beta[i] * d;  // dP = Diag(beta) dA
-    sm.dM[i][j] = d * sm.P[i][j];   // dM is spent: row sums of dA * P, for dbeta
+    sm.dM[i][j] = d * sm.P[i][j];  // dM is spent: row sums of dA * P, for dbeta
   }
   __syncthreads();
   if (tid < kC) {
@@ -666,40 +704,52 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
 
   // per (token, channel): thread (c, half) takes tokens 8 half .. 8 half + 7
   const int c = tid % kDK, half = tid / kDK;
+  float y1[8], y2[8], y3[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int o = (8 * half + u) * kDK + c;
+    y1[u] = Y[kY1 + o];
+    y2[u] = Y[kY2 + o];
+    y3[u] = Y[kY3 + o];
+  }
   float kdkb = 0.f;
-  for (int t = 8 * half; t < 8 * half + 8; ++t) {
+  bf16_t* __restrict__ dqp = a.dq;
+  bf16_t* __restrict__ dkp = a.dk;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int t = 8 * half + u;
     float i1 = 0.f, i2 = 0.f, i3 = 0.f;
+#pragma unroll
     for (int jj = 0; jj < kC; ++jj) {
-      const float kcj = sm.k[jj][c] * sm.ieg[jj][c];
-      const float khj = sm.k[jj][c] * sm.eg[jj][c];
-      const float qhj = sm.q[jj][c] * sm.eg[jj][c];
-      i1 = fmaf(sm.dP[t][jj], kcj, i1);    // (dP Kc)[t]:   jj < t
-      i2 = fmaf(sm.dAq[t][jj], kcj, i2);   // (dAqk Kc)[t]: jj <= t
-      i3 = fmaf(sm.dAq[jj][t], qhj, i3);   // (dAqk^T Qh)[t]: jj >= t
-      i3 = fmaf(sm.dP[jj][t], khj, i3);    // (dP^T Kh)[t]:  jj > t
+      const float kj = sm.k[jj][c], kcj = kj * sm.ieg[jj][c], egj = sm.eg[jj][c];
+      i1 = fmaf(sm.dP[t][jj], kcj, i1);                  // (dP Kc)[t]:     jj < t
+      i2 = fmaf(sm.dAq[t][jj], kcj, i2);                 // (dAqk Kc)[t]:   jj <= t
+      i3 = fmaf(sm.dAq[jj][t] * sm.q[jj][c] + sm.dP[jj][t] * kj, egj, i3);
+                                                         // (dAqk^T Qh + dP^T Kh)[t]
     }
-    const int o = t * kDK + c;
     const float egt = sm.eg[t][c], iegt = sm.ieg[t][c];
-    const float dq = egt * (Y[kY1 + o] + i2);
-    const float dkh = egt * (i1 - Y[kY2 + o]);
+    const float dq = egt * (y1[u] + i2);
+    const float dkh = egt * (i1 - y2[u]);
     const float dkc = iegt * i3;
-    const float dkb = sm.eg[kC - 1][c] * iegt * Y[kY3 + o];
+    const float dkb = sm.eg[kC - 1][c] * iegt * y3[u];
     const float kt = sm.k[t][c];
     kdkb = fmaf(kt, dkb, kdkb);
     sm.dG[t][c] = kt * (dkh - dkc - dkb) + sm.q[t][c] * dq;
     if (valid(t)) {
       const int64_t r = row_of(t);
-      a.dq[r * kDK + c] = (bf16_t)dq;
-      a.dk[r * kDK + c] = (bf16_t)(dkh + dkc + dkb);
+      dqp[r * kDK + c] = (bf16_t)dq;
+      dkp[r * kDK + c] = (bf16_t)(dkh + dkc + dkb);
     }
   }
   sm.kdkb[half][c] = kdkb;
   __syncthreads();
   if (tid < kDK) {  // dG_15 += sum_rows k dk_b + dE E, then dg = reverse cumulative sum
     float acc = sm.kdkb[0][c] + sm.kdkb[1][c] + Y[kDE + c] * sm.eg[kC - 1][c];
+    float* __restrict__ dgp = a.dg;
+#pragma unroll
     for (int t = kC - 1; t >= 0; --t) {
       acc += sm.dG[t][c];
-      if (valid(t)) a.dg[row_of(t) * kDK + c] = acc;
+      if (valid(t)) dgp[row_of(t) * kDK + c] = acc;
     }
   } else if (tid < kDK + kC) {
     const int t = tid - kDK;
@@ -711,7 +761,7 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
 
 // Workspace of the chunkwise backward, in 256-byte aligned parts.
 struct BwdChunkWs {
-  int64_t fwd, s_tmp, s_ck, ds_blk, recs, ybuf, total;
+  int64_t fwd, s_tmp, s_ck, ds_blk, recs, pm, ybuf, total;
 };
 
 static int64_t al256(int64_t n) { return (n + 255) / 256 * 256; }
@@ -725,7 +775,8 @@ static BwdChunkWs bwd_chunk_layout(int64_t B, int64_t T, int64_t H) {
   w.s_ck = w.s_tmp + al256(BH * kDD * 4);
   w.ds_blk = w.s_ck + al256(B * (T / kBlkTok) * H * kDD * 4);
   w.recs = w.ds_blk + al256(BH * nblk * kDD * 4);
-  w.ybuf = w.recs + al256(BH * nt * (int64_t)kRecBytes);
+  w.pm = w.recs + al256(BH * nt * (int64_t)kRecBytes);
+  w.ybuf = w.pm + al256(BH * nt * 512 * 4);
   w.total = w.ybuf + al256(BH * nt * (int64_t)kYFloats * 4);
   return w;
 }
@@ -755,7 +806,8 @@ hipError_t launch_bwd_chunk(const BwdArgs& a) {
   if (e != hipSuccess) return e;
 
   // 2. records
-  RecArgs ra{(const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, ws + w.recs, a.B, a.T, a.H, nt};
+  RecArgs ra{(const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, ws + w.recs,
+             (float*)(ws + w.pm), a.B, a.T, a.H, nt};
   int64_t nrec = (BH * nt + 3) / 4;
   nrec = nrec < 16384 ? nrec : 16384;
   hipLaunchKernelGGL(kda_bwd_rec_kernel, dim3((unsigned)nrec), dim3(256), 0, st, ra);
@@ -776,7 +828,8 @@ hipError_t launch_bwd_chunk(const BwdArgs& a) {
 
   // 5. finishing
   FinArgs fa{(const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, (const float*)(ws + w.ybuf),
-             (bf16_t*)a.dq, (bf16_t*)a.dk, a.dg, a.dbeta, a.B, a.T, a.H, nt};
+             (const float*)(ws + w.pm), (bf16_t*)a.dq, (bf16_t*)a.dk, a.dg, a.dbeta,
+             a.B, a.T, a.H, nt};
   hipLaunchKernelGGL(kda_bwd_fin_kernel, dim3((unsigned)(BH * nt)), dim3(256), 0, st, fa);
   return hipGetLastError();
 }

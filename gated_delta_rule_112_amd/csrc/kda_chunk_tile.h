@@ -273,7 +273,8 @@ __device__ __forceinline__ void forward_sub(float (&y)[4], const f32x4 (&an)[4])
 // From the intra-tile products summed over all slabs: the causal masks, the
 // solve and T.  bt = beta of this lane's token (0 past the sequence end).
 // Returns this lane's T image (lane (i, g): T[i][4 g + e]) and Aqk image (and,
-// through tf when given and the keys are not normalised here, T in float32).
+// when the keys are not normalised here, T in float32 through tf and
+// (I + A)^-1 through mf, when given).
 // NORM: the keys are normalised here, rkt = 1/|k| of this lane's token and
 // sm->rk holds it for every token of the tile.  A takes the norms of its row
 // and column (the products were formed from the raw keys); tb receives
@@ -283,7 +284,7 @@ __device__ __forceinline__ void forward_sub(float (&y)[4], const f32x4 (&an)[4])
 template <bool NORM>
 __device__ __forceinline__ void finish(f32x4 acc_a, f32x4 acc_q, float bt, float rkt,
                                        Scratch* sm, int lane, f16x4& tb, f16x4& aq, f16x4& tw,
-                                       f32x4* tf = nullptr) {
+                                       f32x4* tf = nullptr, f32x4* mf = nullptr) {
   const int t = lane % 16, lg = lane / 16;
   f32x4 rkj = {1.f, 1.f, 1.f, 1.f};  // 1/|k| of columns 4 g + r
   if constexpr (NORM) rkj = ds_read16(lds_addr(&sm->rk[4 * lg]));
@@ -322,6 +323,7 @@ __device__ __forceinline__ void finish(f32x4 acc_a, f32x4 acc_q, float bt, float
     tb = f16x4{(f16)(y[0] * bj[0]), (f16)(y[1] * bj[1]), (f16)(y[2] * bj[2]), (f16)(y[3] * bj[3])};
     tw = tb;
     if (tf != nullptr) *tf = f32x4{y[0] * bj[0], y[1] * bj[1], y[2] * bj[2], y[3] * bj[3]};
+    if (mf != nullptr) *mf = f32x4{y[0], y[1], y[2], y[3]};
   }
 }
 
