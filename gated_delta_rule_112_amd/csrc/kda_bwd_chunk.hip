@@ -26,7 +26,11 @@
 // Every product with a factor e^-G (up to e^80) is formed in float32 with the
 // masked (causal) entries only, so each term carries e^(G_i - G_j) <= 1.
 //
-// The pass runs as five steps on the caller's stream:
+// The pass runs as five steps.  Step 1 runs on a second stream of the
+// library's (one per device) at the same time as steps 2 and 3 on the
+// caller's stream: the chain is a walk over the tiles of one head per compute
+// unit, bound by what one compute unit can stream, and leaves most of the
+// chip to the forward.  Step 4 waits for both.
 //   1. the matrix-core forward, state only, with the state kept every 64
 //      tokens (a block of four tiles);
 //   2. kda_bwd_rec_kernel: per tile and in parallel, the operands of the two
@@ -47,6 +51,8 @@
 // wavefront divides what it contributes by both scales.
 #include "kda_chunk_rec.h"
 #include "kda_chunk_tile.h"
+#include <mutex>
+
 #include "kda_launch.h"
 
 namespace kda {
@@ -72,7 +78,9 @@ constexpr int kTlo = 22528;   // [lane][4]            T - kT (the float16 roundi
 constexpr int kRecBytes = 23552;  // a whole number of 1 KB blocks
 
 // Products of one tile (float32), from the block kernel to the finishing kernel:
-constexpr int kY1 = 0, kY2 = 2048, kY3 = 4096;  // [16][128] each
+// Y1, Y2, Y3 are [16 tokens][128 channels] each, in accumulator order: token t,
+// channel 16 w + c at 256 w + 4 (c + 16 (t / 4)) + t % 4.
+constexpr int kY1 = 0, kY2 = 2048, kY3 = 4096;
 constexpr int kDE = 6144;                       // [128]
 constexpr int kDT = 6272, kDAqk = 6528;         // [16][16] each
 constexpr int kYFloats = 6784;
@@ -276,39 +284,87 @@ struct ChainArgs {
 };
 
 constexpr int kRowBytes = kDV * 2;
-constexpr int kChainSlot = kRecBytes + kC * kRowBytes;  // record, then 16 dO rows
-static_assert(kChainSlot % 1024 == 0 && kRecBytes % 1024 == 0, "whole 1 KB load blocks");
-constexpr int kChainBlocks = kChainSlot / 1024;
+// The chain's part of a tile in an LDS slot, in 1 KB blocks: record blocks
+// 4 .. 15 (Kb, then [Qh^T | -Kh^T]), record blocks 20 and 21 (T, T^T, Aqk^T,
+// E), then the tile's 16 dO rows.
+constexpr int kSlotKb = 0, kSlotQK = 4096, kSlotTt = 12288 + (kTt - 20480),
+              kSlotAqkT = 12288 + (kAqkT - 20480), kSlotE = 12288 + (kE - 20480), kSlotDO = 14336;
+constexpr int kChainBlocks = 18, kChainSlot = kChainBlocks * 1024;
+constexpr int kChainRing = 8;     // slots: seven tiles in flight ahead of the one in use
+constexpr int kChainLoaders = 6;  // loader wavefronts
+constexpr int kChainPer = kChainBlocks / kChainLoaders;  // loads per loader wavefront per tile
+static_assert(kKb == 4096 && kQK == 8192 && kKbC == 16384 && kT == 20480 && kTlo == 22528,
+              "the chain's record blocks");
+static_assert(kChainPer * kChainLoaders == kChainBlocks, "whole loads per loader wavefront");
+static_assert((kChainRing - 1) * kChainPer <= 63, "loads in flight per wavefront exceed vmcnt");
 
-// One workgroup per (b, h), eight wavefronts of 16 value columns each, the
-// tiles last to first.  The record and the dO rows of the next tile are moved
-// into the other half of a two-slot LDS buffer with direct-to-LDS loads while
-// a tile is processed.
-__global__ void __launch_bounds__(512, 1) kda_bwd_chain_kernel(ChainArgs a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2][kChainSlot];
+// s_waitcnt with vmcnt = N, the other counters left alone (gfx9 encoding).
+constexpr unsigned vmcnt_only(int n) {
+  return (unsigned)((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One workgroup per (b, h): eight wavefronts of 16 value columns each walk the
+// tiles last to first, while six loader wavefronts keep the next seven tiles'
+// record parts and dO rows streaming into a ring of LDS slots with
+// direct-to-LDS loads.  One barrier per tile: after it, the tile just used
+// frees its slot and the next tile is in LDS.
+__global__ void __launch_bounds__(64 * (8 + kChainLoaders), 1) kda_bwd_chain_kernel(ChainArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kChainRing][kChainSlot];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const int lane = threadIdx.x % 64, lc = lane % 16, lg = lane / 16;
   const int64_t bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
-  const int col = 16 * wave;
 
-  auto issue = [&](int64_t x, int slot) {
-    const unsigned char* R = a.recs + (bh * a.nt + x) * (int64_t)kRecBytes;
-    for (int blk = wave; blk < kChainBlocks; blk += 8) {
-      const unsigned char* src;
-      if (blk < kRecBytes / 1024) {
-        src = R + blk * 1024 + lane * 16;
-      } else {  // 4 dO rows per block, 16 chunks of 16 bytes per row
-        int64_t tok = x * kC + (blk - kRecBytes / 1024) * 4 + lane / 16;
-        tok = tok < a.T ? tok : a.T - 1;
-        src = (const unsigned char*)(a.dout + ((b * a.T + tok) * a.H + h) * kDV + (lane % 16) * 8);
+  if (wave >= 8) {  // ------------------------------------------ loader waves
+    const int lw = wave - 8;
+    auto issue = [&](int64_t x) {
+      const unsigned char* R = a.recs + (bh * a.nt + x) * (int64_t)kRecBytes;
+      unsigned char* slot = lds[x % kChainRing];
+#pragma unroll
+      for (int i = 0; i < kChainPer; ++i) {
+        const int blk = lw + kChainLoaders * i;
+        const unsigned char* src;
+        if (blk < 12) {
+          src = R + 4096 + blk * 1024 + lane * 16;
+        } else if (blk < 14) {
+          src = R + 20480 + (blk - 12) * 1024 + lane * 16;
+        } else {  // 4 dO rows per block, 16 chunks of 16 bytes per row
+          int64_t tok = x * kC + (blk - 14) * 4 + lane / 16;
+          tok = tok < a.T ? tok : a.T - 1;
+          src = (const unsigned char*)(a.dout + ((b * a.T + tok) * a.H + h) * kDV + lc * 8);
+        }
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)(slot +
+                                                                                   blk * 1024),
+                                         16, 0, 0);
       }
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(lds[slot] +
-                                                                                 blk * 1024),
-                                       16, 0, 0);
+    };
+    // tiles nt - 1 .. nt - 7 in flight, then wait for the first
+    for (int64_t i = 0; i < kChainRing - 1 && i < a.nt; ++i) issue(a.nt - 1 - i);
+    if (a.nt >= kChainRing - 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_only((kChainRing - 2) * kChainPer));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    // A bare barrier: these waves touch LDS only through their direct-to-LDS
+    // loads, whose completion the vmcnt waits above establish; a fence here
+    // would also wait for the tiles still in flight.
+    __builtin_amdgcn_s_barrier();
+    for (int64_t x = a.nt - 1; x >= 0; --x) {
+      // the slot of tile x + 1 is free: it takes tile x - 7
+      if (x - (kChainRing - 1) >= 0) issue(x - (kChainRing - 1));
+      // tile x - 1 in LDS: the loads issued after it are those of tiles
+      // x - 2 .. max(x - 7, 0)
+      if (x - 1 >= kChainRing - 2)
+        __builtin_amdgcn_s_waitcnt(vmcnt_only((kChainRing - 2) * kChainPer));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+      __builtin_amdgcn_s_barrier();
     }
-  };
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    return;
+  }
 
+  // --------------------------------------------------------- compute waves
+  const int col = 16 * wave;
   // The adjoint quantities are held in units of scale / sigma, so that dO
   // (bfloat16) enters the float16 operands exactly: sigma dO instead of a
   // rounded sigma scale dO.  so = scale, or 1 with dO dropped when scale = 0.
@@ -319,14 +375,9 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_chain_kernel(ChainArgs a) {
   for (int kb = 0; kb < 8; ++kb) dS[kb] *= 1.f / so;
   Scale sc;
   const bf16x4 ident = ident_op(lane);
-
-  issue(a.nt - 1, (int)((a.nt - 1) & 1));
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  lds_barrier();  // tile nt - 1 is in LDS
   for (int64_t x = a.nt - 1; x >= 0; --x) {
-    const int slot = (int)(x & 1);
-    if (x > 0) issue(x - 1, slot ^ 1);
-    const unsigned char* R = lds[slot];
+    const unsigned char* R = lds[x % kChainRing];
     // dS' at the end of the block this tile ends
     const int64_t blk = x / kBlkTiles;
     int64_t last = blk * kBlkTiles + kBlkTiles - 1;
@@ -334,26 +385,25 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_chain_kernel(ChainArgs a) {
     if (x == last) store_state(a.ds_blk + (bh * a.nblk + blk) * kDD, dS, so * sc.isig, col, lane);
 
     // dO in the k-operand layout: lane (c, g): dO[4 g + r][col + c]
-    const bf16x4 dor = *(const bf16x4*)(R + kRecBytes + lc * kRowBytes + (col + 4 * lg) * 2);
+    const bf16x4 dor = *(const bf16x4*)(R + kSlotDO + lc * kRowBytes + (col + 4 * lg) * 2);
     const f32x4 dof = mma16b(dor, ident, zero4()) * dmul;
     const f16x4 do16 = to_h4(rescale(sc, dS, dof));
     f16x8 sop[4];
     state_op(dS, sop);
     f32x4 dd = zero4();
 #pragma unroll
-    for (int s = 0; s < 4; ++s) dd = mma32h(ld16h(R + kKb + s * 1024 + lane * 16), sop[s], dd);
-    dd = mma32h(lo8(ld8h(R + kAqkT + lane * 8)), cat8(do16, do16), dd);
+    for (int s = 0; s < 4; ++s) dd = mma32h(ld16h(R + kSlotKb + s * 1024 + lane * 16), sop[s], dd);
+    dd = mma32h(lo8(ld8h(R + kSlotAqkT + lane * 8)), cat8(do16, do16), dd);
     const f16x4 dd16 = to_h4(dd);
-    const f32x4 dx = mma32h(lo8(ld8h(R + kTt + lane * 8)), cat8(dd16, dd16), zero4());
+    const f32x4 dx = mma32h(lo8(ld8h(R + kSlotTt + lane * 8)), cat8(dd16, dd16), zero4());
     const f16x8 bop = cat8(do16, to_h4(dx));
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
       const f32x4 e4 =
-          *(const f32x4*)(R + kE + 4 * (32 * (kb / 2) + 8 * lg + 4 * (kb % 2)));
-      dS[kb] = mma32h(ld16h(R + kQK + kb * 1024 + lane * 16), bop, dS[kb] * e4);
+          *(const f32x4*)(R + kSlotE + 4 * (32 * (kb / 2) + 8 * lg + 4 * (kb % 2)));
+      dS[kb] = mma32h(ld16h(R + kSlotQK + kb * 1024 + lane * 16), bop, dS[kb] * e4);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    lds_barrier();
   }
   if (a.ds0 != nullptr) store_state(a.ds0 + bh * kDD, dS, so * sc.isig, col, lane);
 }
@@ -440,42 +490,67 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
   const int col = 16 * wave;
   const int64_t x0 = blk * kBlkTiles;
   const int ntl = (int)(a.nt - x0 < kBlkTiles ? a.nt - x0 : kBlkTiles);
-  // the forward-step parts of the block's records, once for all wavefronts
-  for (int i = tid; i < ntl * (kFwBytes / 16); i += 512) {
-    const int u = i / (kFwBytes / 16), o = 16 * (i % (kFwBytes / 16));
-    const unsigned char* Ru = a.recs + (bh * a.nt + x0 + u) * (int64_t)kRecBytes;
-    const int src = o < kFwKbC ? kKh + o
-                  : o < kFwT   ? kKbC + (o - kFwKbC)
-                  : o < kFwTlo ? kT + (o - kFwT)
-                  : o < kFwE   ? kTlo + (o - kFwTlo)
-                               : kE + (o - kFwE);
-    *(f32x4*)&sm.fw[u][o] = *(const f32x4*)(Ru + src);
+  // the forward-step parts of the block's records, moved to LDS once for all
+  // wavefronts; then dS' at the block's end, the v rows and the block's start
+  // state, which stay in flight over the barrier
+  constexpr int kFwChunks = kFwBytes / 16, kFwPer = (kBlkTiles * kFwChunks + 511) / 512;
+  {
+    f32x4 fwv[kFwPer];  // all loads in flight at once, then the LDS stores
+#pragma unroll
+    for (int j = 0; j < kFwPer; ++j) {
+      const int i = tid + 512 * j;
+      if (i < ntl * kFwChunks) {
+        const int u = i / kFwChunks, o = 16 * (i % kFwChunks);
+        const unsigned char* Ru = a.recs + (bh * a.nt + x0 + u) * (int64_t)kRecBytes;
+        const int src = o < kFwKbC ? kKh + o
+                      : o < kFwT   ? kKbC + (o - kFwKbC)
+                      : o < kFwTlo ? kT + (o - kFwT)
+                      : o < kFwE   ? kTlo + (o - kFwTlo)
+                                   : kE + (o - kFwE);
+        fwv[j] = *(const f32x4*)(Ru + src);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kFwPer; ++j) {
+      const int i = tid + 512 * j;
+      if (i < ntl * kFwChunks) *(f32x4*)&sm.fw[i / kFwChunks][16 * (i % kFwChunks)] = fwv[j];
+    }
   }
-  __syncthreads();
+  // keeps the loads below from being scheduled into the staging above, where
+  // they would hold registers the staging needs
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 dS[8];
+  load_state(dS, a.ds_blk + (bh * a.nblk + blk) * kDD, col, lane);
+  const float* s_start = blk == 0 ? (a.s0 != nullptr ? a.s0 + bh * kDD : nullptr)
+                                  : a.s_ck + ((b * a.nck + blk - 1) * a.H + h) * kDD;
+  // every v row this wavefront reads, loaded once (a load issued after the
+  // stores of a tile waits for those stores)
+  bf16x4 vrow[kBlkTiles];
+#pragma unroll
+  for (int u = 0; u < kBlkTiles; ++u)
+    vrow[u] = token_row4(a.v, (x0 + u) * kC + lc, a.T, b, h, a.H, col, lane);
+  f32x4 S[8];  // S_tl; reloaded for the next tile once it is staged
+  load_state(S, s_start, col, lane);
+  lds_barrier();
 
   const bf16x4 ident = ident_op(lane);
   // adjoint quantities in units of scale / sigma (see the chain kernel)
   const float so = a.scale != 0.f ? a.scale : 1.f, dmul = a.scale != 0.f ? 1.f : 0.f;
-  f32x4 dS[8];
-  load_state(dS, a.ds_blk + (bh * a.nblk + blk) * kDD, col, lane);
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb) dS[kb] *= 1.f / so;
   Scale sd;
-  const float* s_start = blk == 0 ? (a.s0 != nullptr ? a.s0 + bh * kDD : nullptr)
-                                  : a.s_ck + ((b * a.nck + blk - 1) * a.H + h) * kDD;
 
   for (int tl = ntl - 1; tl >= 0; --tl) {
     const int64_t x = x0 + tl;
+    // the tile's dO rows, needed after the forward steps
+    const bf16x4 drow = token_row4(a.dout, x * kC + lc, a.T, b, h, a.H, col, lane);
     // ---- forward: S_tl from the block's start state.  T, X and Delta enter
     // their products as float16 pairs (value and rounding error).
-    f32x4 S[8];
-    load_state(S, s_start, col, lane);
     Scale sf;
     f32x4 X = zero4(), Dl = zero4();
     for (int u = 0; u <= tl; ++u) {
       const unsigned char* Ru = sm.fw[u];
-      const bf16x4 vr = token_row4(a.v, (x0 + u) * kC + lc, a.T, b, h, a.H, col, lane);
-      const f32x4 vs = rescale(sf, S, mma16b(vr, ident, zero4()));
+      const f32x4 vs = rescale(sf, S, mma16b(vrow[u], ident, zero4()));
       f16x8 sopS[4];
       state_op(S, sopS);
       f32x4 y = zero4();
@@ -483,26 +558,24 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
       for (int s = 0; s < 4; ++s) y = mma32h(ld16h(Ru + kFwKh + s * 1024 + lane * 16), sopS[s], y);
       X = vs - y;
       const f16x4 xh = to_h4(X), xl = to_h4(X - to_f4(xh));
-      const f16x8 th = lo8(ld8h(Ru + kFwT + lane * 8)), tlo = lo8(ld8h(Ru + kFwTlo + lane * 8));
-      Dl = mma32h(th, cat8(xh, xh), zero4());
-      Dl = mma32h(th, cat8(xl, xl), Dl);
-      Dl = mma32h(tlo, cat8(xh, xh), Dl);
+      // T (xh + xl) in one product (both halves of k hold T), then T_lo xh
+      const f16x4 t4 = ld8h(Ru + kFwT + lane * 8);
+      Dl = mma32h(cat8(t4, t4), cat8(xh, xl), zero4());
+      Dl = mma32h(lo8(ld8h(Ru + kFwTlo + lane * 8)), cat8(xh, xh), Dl);
       if (u < tl) {
         const f16x4 dh = to_h4(Dl), dlo = to_h4(Dl - to_f4(dh));
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
           const f32x4 e4 =
               *(const f32x4*)(Ru + kFwE + 4 * (32 * (kb / 2) + 8 * lg + 4 * (kb % 2)));
-          const f16x8 kbc = lo8(ld8h(Ru + kFwKbC + kb * 512 + lane * 8));
-          S[kb] = mma32h(kbc, cat8(dh, dh), S[kb] * e4);
-          S[kb] = mma32h(kbc, cat8(dlo, dlo), S[kb]);
+          const f16x4 k4 = ld8h(Ru + kFwKbC + kb * 512 + lane * 8);
+          S[kb] = mma32h(cat8(k4, k4), cat8(dh, dlo), S[kb] * e4);  // Kb^T (dh + dlo)
         }
       }
     }
     // ---- the adjoint step of tile tl
     const unsigned char* R = a.recs + (bh * a.nt + x) * (int64_t)kRecBytes;
-    const bf16x4 dr = token_row4(a.dout, x * kC + lc, a.T, b, h, a.H, col, lane);
-    const f32x4 dos = rescale(sd, dS, mma16b(dr, ident, zero4()) * dmul);
+    const f32x4 dos = rescale(sd, dS, mma16b(drow, ident, zero4()) * dmul);
     const f16x4 do16 = to_h4(dos);  // exact: sigma dO with dO in bfloat16
     f16x8 sopD[4];
     state_op(dS, sopD);
@@ -534,61 +607,64 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
     stage_small(sm.sx[wave][2], Dl, ff, lane);
     stage_small(sm.sx[wave][3], dd, fd, lane);
     stage_small(sm.sx[wave][4], X, ff, lane);
-    __syncthreads();
-    {
-      constexpr int kXs = 5 * kC * 16, kSs = kDK * 16;
-      const f32x4 y1 = prod128(sm.sx[0][0], kXs, sm.st[0] + 16 * wave * 16, kSs, lane);
-      const f32x4 y2 = prod128(sm.sx[0][1], kXs, sm.st[0] + 16 * wave * 16, kSs, lane);
+    lds_barrier();
+    constexpr int kXs = 5 * kC * 16, kSs = kDK * 16;
+    const f32x4 y1 = prod128(sm.sx[0][0], kXs, sm.st[0] + 16 * wave * 16, kSs, lane);  // dO S^T
+    const f32x4 y2 = prod128(sm.sx[0][1], kXs, sm.st[0] + 16 * wave * 16, kSs, lane);  // dX S^T
+    f32x4 ysm = zero4();  // wave 0: dDelta X^T, wave 1: dO Delta^T, wave 2: dE
+    if (wave == 0) {
+      ysm = prod128(sm.sx[0][3], kXs, sm.sx[0][4], kXs, lane);
+    } else if (wave == 1) {
+      ysm = prod128(sm.sx[0][0], kXs, sm.sx[0][2], kXs, lane);
+    } else if (wave == 2) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int o = (4 * lg + r) * kDK + 16 * wave + lc;
-        Y[kY1 + o] = y1[r];  // dO S^T
-        Y[kY2 + o] = y2[r];  // dX S^T
-      }
-      if (wave < 2) {  // dDelta X^T and dO Delta^T
-        const f32x4 d = wave == 0 ? prod128(sm.sx[0][3], kXs, sm.sx[0][4], kXs, lane)
-                                  : prod128(sm.sx[0][0], kXs, sm.sx[0][2], kXs, lane);
+      for (int m = 0; m < 2; ++m) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Y[(wave == 0 ? kDT : kDAqk) + (4 * lg + r) * 16 + lc] = d[r];
-      } else if (wave == 2) {
-        for (int c = lane; c < kDK; c += 64) {
-          float e = 0.f;
-#pragma unroll
-          for (int w = 0; w < 8; ++w) e += sm.dep[w][c];
-          Y[kDE + c] = e;
-        }
+        for (int w = 0; w < 8; ++w) ysm[m] += sm.dep[w][lane + 64 * m];
       }
     }
-    __syncthreads();
+    // [Qh^T | -Kh^T] for the update of dS' at the end, loaded now so that the
+    // last product hides the wait
+    f16x8 qk[8];
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) qk[kb] = ld16h(R + kQK + kb * 1024 + lane * 16);
+    lds_barrier();
     stage_state(sm.st[wave], dS, fd, lane);
-    __syncthreads();
+    lds_barrier();
+    const f32x4 y3 = prod128(sm.sx[0][2], kXs, sm.st[0] + 16 * wave * 16, kSs, lane);  // Delta dS'^T
+    // dV = dX: lane (t, g) holds columns col + 4 g .. + 3 of token t
+    bf16x4 dvo;
     {
-      constexpr int kXs = 5 * kC * 16, kSs = kDK * 16;
-      const f32x4 y3 = prod128(sm.sx[0][2], kXs, sm.st[0] + 16 * wave * 16, kSs, lane);
+      const f32x4 d = *(const f32x4*)&sm.sx[wave][1][lc * 16 + 4 * lg];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Y[kY3 + (4 * lg + r) * kDK + 16 * wave + lc] = y3[r];  // Delta dS'^T
-    }
-    // dV = dX: lane (t, g) stores columns col + 4 g .. + 3 of token t
-    {
-      const int64_t tok = x * kC + lc;
-      if (tok < a.T) {
-        const f32x4 d = *(const f32x4*)&sm.sx[wave][1][lc * 16 + 4 * lg];
-        bf16x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (bf16_t)d[e];
-        *(bf16x4*)(a.dv + ((b * a.T + tok) * a.H + h) * kDV + col + 4 * lg) = o;
-      }
+      for (int e = 0; e < 4; ++e) dvo[e] = (bf16_t)d[e];
     }
     // dS' of the tile before (the adjoint of this tile's start state)
     {
       const f16x8 bop = cat8(do16, to_h4(dx));
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
-        const f32x4 e4 = *(const f32x4*)(R + kE + 4 * (32 * (kb / 2) + 8 * lg + 4 * (kb % 2)));
-        dS[kb] = mma32h(ld16h(R + kQK + kb * 1024 + lane * 16), bop, dS[kb] * e4);
+        const f32x4 e4 =
+            *(const f32x4*)(sm.fw[tl] + kFwE + 4 * (32 * (kb / 2) + 8 * lg + 4 * (kb % 2)));
+        dS[kb] = mma32h(qk[kb], bop, dS[kb] * e4);
       }
     }
-    __syncthreads();  // the staging is free for the next tile
+    // the next tile's start state, loaded before this tile's stores so that
+    // its wait does not take them in
+    if (tl > 0) load_state(S, s_start, col, lane);
+    *(f32x4*)(Y + kY1 + 256 * wave + 4 * lane) = y1;
+    *(f32x4*)(Y + kY2 + 256 * wave + 4 * lane) = y2;
+    *(f32x4*)(Y + kY3 + 256 * wave + 4 * lane) = y3;
+    if (wave < 2) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Y[(wave == 0 ? kDT : kDAqk) + (4 * lg + r) * 16 + lc] = ysm[r];
+    } else if (wave == 2) {
+      Y[kDE + lane] = ysm[0];
+      Y[kDE + lane + 64] = ysm[1];
+    }
+    if (x * kC + lc < a.T)
+      *(bf16x4*)(a.dv + ((b * a.T + x * kC + lc) * a.H + h) * kDV + col + 4 * lg) = dvo;
+    lds_barrier();  // the staging is free for the next tile
   }
 }
 
@@ -636,6 +712,17 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
   };
   auto valid = [&](int t) { return x * kC + t < a.T; };
 
+  // Y1, Y2, Y3 of thread (c, half): tokens 8 half + 4 m .. + 3 of channel c,
+  // loaded first and waited for last
+  const int c = tid % kDK, half = tid / kDK;
+  f32x4 y1[2], y2[2], y3[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int o = 256 * (c / 16) + 4 * (c % 16 + 16 * (2 * half + m));
+    y1[m] = *(const f32x4*)(Y + kY1 + o);
+    y2[m] = *(const f32x4*)(Y + kY2 + o);
+    y3[m] = *(const f32x4*)(Y + kY3 + o);
+  }
   // the tile's inputs: element e = tid + 256 m is (token e / 128, channel e % 128)
   {
     float kv[8], qv[8], gv[8];
@@ -660,7 +747,7 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
     sm.M[i][j] = PM[256 + tid];
     const float dT = Y[kDT + tid], dAq = Y[kDAqk + tid];
     if (tid < kC) sm.beta[tid] = valid(tid) ? a.beta[row_of(tid)] : 0.f;
-    __syncthreads();
+    lds_barrier();
     sm.dM[i][j] = dT * sm.beta[j];
     sm.dAq[i][j] = j <= i ? dAq : 0.f;
     sm.Z[i][j] = dT * sm.M[i][j];  // for dbeta from T = M Diag(beta): column sums
@@ -674,20 +761,20 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
       sm.ieg[t][c] = __expf(-G);
     }
   }
-  __syncthreads();
+  lds_barrier();
   const int i = tid / kC, j = tid % kC;  // a (row, column) of a 16 x 16 matrix
   if (tid < kC) {
     float s = 0.f;
     for (int r = 0; r < kC; ++r) s += sm.Z[r][tid];
     sm.dbT[tid] = s;
   }
-  __syncthreads();
+  lds_barrier();
   {
     float z = 0.f;  // Z = dM M^T
     for (int c = 0; c < kC; ++c) z = fmaf(sm.dM[i][c], sm.M[j][c], z);
     sm.Z[i][j] = z;
   }
-  __syncthreads();
+  lds_barrier();
   {
     float d = 0.f;  // dA = strict_lower(-M^T Z)
     if (j < i)
@@ -695,7 +782,7 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
     sm.dP[i][j] = sm.beta[i] * d;  // dP = Diag(beta) dA
     sm.dM[i][j] = d * sm.P[i][j];  // dM is spent: row sums of dA * P, for dbeta
   }
-  __syncthreads();
+  lds_barrier();
   if (tid < kC) {
     float s = 0.f;
     for (int c = 0; c < kC; ++c) s += sm.dM[tid][c];
@@ -703,15 +790,6 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
   }
 
   // per (token, channel): thread (c, half) takes tokens 8 half .. 8 half + 7
-  const int c = tid % kDK, half = tid / kDK;
-  float y1[8], y2[8], y3[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int o = (8 * half + u) * kDK + c;
-    y1[u] = Y[kY1 + o];
-    y2[u] = Y[kY2 + o];
-    y3[u] = Y[kY3 + o];
-  }
   float kdkb = 0.f;
   bf16_t* __restrict__ dqp = a.dq;
   bf16_t* __restrict__ dkp = a.dk;
@@ -728,10 +806,10 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
                                                          // (dAqk^T Qh + dP^T Kh)[t]
     }
     const float egt = sm.eg[t][c], iegt = sm.ieg[t][c];
-    const float dq = egt * (y1[u] + i2);
-    const float dkh = egt * (i1 - y2[u]);
+    const float dq = egt * (y1[u / 4][u % 4] + i2);
+    const float dkh = egt * (i1 - y2[u / 4][u % 4]);
     const float dkc = iegt * i3;
-    const float dkb = sm.eg[kC - 1][c] * iegt * y3[u];
+    const float dkb = sm.eg[kC - 1][c] * iegt * y3[u / 4][u % 4];
     const float kt = sm.k[t][c];
     kdkb = fmaf(kt, dkb, kdkb);
     sm.dG[t][c] = kt * (dkh - dkc - dkb) + sm.q[t][c] * dq;
@@ -742,7 +820,7 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
     }
   }
   sm.kdkb[half][c] = kdkb;
-  __syncthreads();
+  lds_barrier();
   if (tid < kDK) {  // dG_15 += sum_rows k dk_b + dE E, then dg = reverse cumulative sum
     float acc = sm.kdkb[0][c] + sm.kdkb[1][c] + Y[kDE + c] * sm.eg[kC - 1][c];
     float* __restrict__ dgp = a.dg;
@@ -785,6 +863,43 @@ int64_t bwd_chunk_workspace_bytes(int64_t B, int64_t T, int64_t H) {
   return bwd_chunk_layout(B, T, H).total;
 }
 
+// The second stream of a device (default priority, non-blocking) and the two
+// events that fork step 1 onto it and join it back.  Created on first use;
+// the device's mutex makes each call's fork and join one unit, so calls from
+// several host threads stay ordered against their own streams.
+namespace {
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex side_mutex[kMaxDevices];
+SideStream side_streams[kMaxDevices];
+
+hipError_t side_stream_locked(int dev, SideStream** out) {
+  SideStream& ss = side_streams[dev];
+  hipError_t e;
+  if (ss.s == nullptr) {
+    if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) {
+      ss.s = nullptr;
+      return e;
+    }
+  }
+  if (ss.fork == nullptr &&
+      (e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) {
+    ss.fork = nullptr;
+    return e;
+  }
+  if (ss.join == nullptr &&
+      (e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) {
+    ss.join = nullptr;
+    return e;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
+}  // namespace
+
 hipError_t launch_bwd_chunk(const BwdArgs& a) {
   using namespace bwd;
   const int64_t BH = a.B * a.H, nt = (a.T + kC - 1) / kC;
@@ -794,16 +909,27 @@ hipError_t launch_bwd_chunk(const BwdArgs& a) {
   unsigned char* ws = (unsigned char*)a.workspace;
   hipStream_t st = (hipStream_t)a.stream;
 
-  // 1. forward states every 64 tokens
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(side_mutex[dev]);
+  SideStream* side = nullptr;
+  if ((e = side_stream_locked(dev, &side)) != hipSuccess) return e;
+
+  // 1. forward states every 64 tokens, on the side stream once the caller's
+  //    stream has reached this call
+  if ((e = hipEventRecord(side->fork, st)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return e;
   ChunkArgs ca{a.q, a.k, a.v, a.g, a.beta, a.s0, nullptr, (float*)(ws + w.s_tmp), nullptr,
-               nullptr, 0.f, a.B, a.T, a.H, kDK, kDV, 1.f, true, ws + w.fwd, a.stream};
+               nullptr, 0.f, a.B, a.T, a.H, kDK, kDV, 1.f, true, ws + w.fwd, side->s};
   ca.total = a.B * a.T;
   if (nck > 0) {
     ca.ckpt = (float*)(ws + w.s_ck);
     ca.ckpt_every = kBlkTok;
   }
-  hipError_t e = launch_chunk_mfma(ca);
-  if (e != hipSuccess) return e;
+  if ((e = launch_chunk_mfma(ca)) != hipSuccess) return e;
+  if ((e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;
 
   // 2. records
   RecArgs ra{(const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, ws + w.recs,
@@ -816,10 +942,12 @@ hipError_t launch_bwd_chunk(const BwdArgs& a) {
   // 3. the adjoint chain
   ChainArgs cha{ws + w.recs, (const bf16_t*)a.dout, a.ds_final, (float*)(ws + w.ds_blk), a.ds0,
                 a.B, a.T, a.H, nt, nblk, a.scale};
-  hipLaunchKernelGGL(kda_bwd_chain_kernel, dim3((unsigned)BH), dim3(512), 0, st, cha);
+  hipLaunchKernelGGL(kda_bwd_chain_kernel, dim3((unsigned)BH), dim3(64 * (8 + kChainLoaders)), 0,
+                     st, cha);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  // 4. block products
+  // 4. block products, once the forward states are there
+  if ((e = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return e;
   BlockArgs ba{ws + w.recs, (const bf16_t*)a.v, (const bf16_t*)a.dout, a.s0,
                (const float*)(ws + w.s_ck), (const float*)(ws + w.ds_blk), (bf16_t*)a.dv,
                (float*)(ws + w.ybuf), a.B, a.T, a.H, nt, nblk, nck, a.scale};

@@ -145,6 +145,17 @@ __device__ __forceinline__ float row_bcast(float x) {
   return dpp<0x150 + M, false>(x);
 }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads also waits
+// for every global load and store the wavefront has in flight (vmcnt(0));
+// this one leaves them in flight, so loads issued ahead stay ahead.  Data
+// that direct-to-LDS loads bring in is covered by the issuing wavefront's own
+// vmcnt wait before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Largest of x over the 64 lanes (x >= 0), in every lane: a max-scan over
 // each 16-lane DPP row, then the four row maxima, compared as integers (the
 // bit patterns of non-negative floats order like their values).
