@@ -241,7 +241,20 @@ __device__ __forceinline__ void state_op(const f32x4 (&z)[8], f16x8 (&op)[4]) {
   for (int s = 0; s < 4; ++s) op[s] = cat8(to_h4(z[2 * s]), to_h4(z[2 * s + 1]));
 }
 
-__device__ __forceinline__ void load_state(f32x4 (&z)[8], const float* p, int col, int lane) {
+// The value columns of wavefront w: column index c (lane (c, g) of an
+// accumulator) is column 32 (w / 2) + 8 (c / 4) + 4 (w % 2) + c % 4, the
+// forward's state pass numbering, so that its checkpoints in accumulator
+// order load here as they are; a lane (t, g) of a row operand holds the four
+// adjacent columns of indices 4 g .. 4 g + 3, from row_col(w, g) on.
+__device__ __forceinline__ int acc_col(int wave, int c) {
+  return 32 * (wave / 2) + 8 * (c / 4) + 4 * (wave % 2) + c % 4;
+}
+__device__ __forceinline__ int row_col(int wave, int g) {
+  return 32 * (wave / 2) + 8 * g + 4 * (wave % 2);
+}
+
+// A wavefront's columns of a [dk][dv] row-major state (caller buffers).
+__device__ __forceinline__ void load_state(f32x4 (&z)[8], const float* p, int wave, int lane) {
   const int lc = lane % 16, lg = lane / 16;
   if (p == nullptr) {
 #pragma unroll
@@ -251,16 +264,31 @@ __device__ __forceinline__ void load_state(f32x4 (&z)[8], const float* p, int co
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) z[kb][r] = p[rec::chan(kb, 4 * lg + r) * kDV + col + lc];
+    for (int r = 0; r < 4; ++r) z[kb][r] = p[rec::chan(kb, 4 * lg + r) * kDV + acc_col(wave, lc)];
 }
 
-__device__ __forceinline__ void store_state(float* p, const f32x4 (&z)[8], float f, int col,
+__device__ __forceinline__ void store_state(float* p, const f32x4 (&z)[8], float f, int wave,
                                             int lane) {
   const int lc = lane % 16, lg = lane / 16;
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[rec::chan(kb, 4 * lg + r) * kDV + col + lc] = z[kb][r] * f;
+    for (int r = 0; r < 4; ++r) p[rec::chan(kb, 4 * lg + r) * kDV + acc_col(wave, lc)] = z[kb][r] * f;
+}
+
+// A state held by the eight wavefronts in accumulator order, for buffers that
+// only these kernels read: wavefront w's block kb at [w][kb][lane][4], so
+// every lane moves 16 contiguous bytes (a [dk][dv] row-major layout takes
+// four times as many narrower accesses).
+__device__ __forceinline__ void store_frag(float* p, const f32x4 (&z)[8], float f, int wave,
+                                           int lane) {
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) *(f32x4*)(p + 2048 * wave + 4 * (64 * kb + lane)) = z[kb] * f;
+}
+
+__device__ __forceinline__ void load_frag(f32x4 (&z)[8], const float* p, int wave, int lane) {
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) z[kb] = *(const f32x4*)(p + 2048 * wave + 4 * (64 * kb + lane));
 }
 
 // Selection matrix for moving 16 token rows into the k-operand layout:
@@ -277,7 +305,7 @@ struct ChainArgs {
   const unsigned char* recs;
   const bf16_t* dout;
   const float* dsf;  // [B H][dk][dv] or NULL
-  float* ds_blk;     // [B H][nblk][dk][dv]: dS' at the end of every block
+  float* ds_blk;     // [B H][nblk] states in accumulator order: dS' at the end of every block
   float* ds0;        // [B H][dk][dv] or NULL
   int64_t B, T, H, nt, nblk;
   float scale;
@@ -364,13 +392,12 @@ __global__ void __launch_bounds__(64 * (8 + kChainLoaders), 1) kda_bwd_chain_ker
   }
 
   // --------------------------------------------------------- compute waves
-  const int col = 16 * wave;
   // The adjoint quantities are held in units of scale / sigma, so that dO
   // (bfloat16) enters the float16 operands exactly: sigma dO instead of a
   // rounded sigma scale dO.  so = scale, or 1 with dO dropped when scale = 0.
   const float so = a.scale != 0.f ? a.scale : 1.f, dmul = a.scale != 0.f ? 1.f : 0.f;
   f32x4 dS[8];
-  load_state(dS, a.dsf != nullptr ? a.dsf + bh * kDD : nullptr, col, lane);
+  load_state(dS, a.dsf != nullptr ? a.dsf + bh * kDD : nullptr, wave, lane);
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb) dS[kb] *= 1.f / so;
   Scale sc;
@@ -382,10 +409,10 @@ __global__ void __launch_bounds__(64 * (8 + kChainLoaders), 1) kda_bwd_chain_ker
     const int64_t blk = x / kBlkTiles;
     int64_t last = blk * kBlkTiles + kBlkTiles - 1;
     last = last < a.nt - 1 ? last : a.nt - 1;
-    if (x == last) store_state(a.ds_blk + (bh * a.nblk + blk) * kDD, dS, so * sc.isig, col, lane);
+    if (x == last) store_frag(a.ds_blk + (bh * a.nblk + blk) * kDD, dS, so * sc.isig, wave, lane);
 
-    // dO in the k-operand layout: lane (c, g): dO[4 g + r][col + c]
-    const bf16x4 dor = *(const bf16x4*)(R + kSlotDO + lc * kRowBytes + (col + 4 * lg) * 2);
+    // dO in the k-operand layout: lane (c, g): dO[4 g + r][column index c]
+    const bf16x4 dor = *(const bf16x4*)(R + kSlotDO + lc * kRowBytes + row_col(wave, lg) * 2);
     const f32x4 dof = mma16b(dor, ident, zero4()) * dmul;
     const f16x4 do16 = to_h4(rescale(sc, dS, dof));
     f16x8 sop[4];
@@ -405,7 +432,7 @@ __global__ void __launch_bounds__(64 * (8 + kChainLoaders), 1) kda_bwd_chain_ker
     }
     lds_barrier();
   }
-  if (a.ds0 != nullptr) store_state(a.ds0 + bh * kDD, dS, so * sc.isig, col, lane);
+  if (a.ds0 != nullptr) store_state(a.ds0 + bh * kDD, dS, so * sc.isig, wave, lane);
 }
 
 // ---------------------------------------------------------- 4. block products
@@ -414,8 +441,8 @@ struct BlockArgs {
   const bf16_t* v;
   const bf16_t* dout;
   const float* s0;      // [B H][dk][dv] or NULL
-  const float* s_ck;    // [B][T / 64][H][dk][dv]: the state after every 64 tokens
-  const float* ds_blk;  // [B H][nblk][dk][dv]
+  const float* s_ck;    // [B][T / 64][H] states in accumulator order: the state after every 64 tokens
+  const float* ds_blk;  // [B H][nblk] states in accumulator order
   bf16_t* dv;
   float* ybuf;          // [B H][nt][kYFloats]
   int64_t B, T, H, nt, nblk, nck;
@@ -440,11 +467,11 @@ __device__ __forceinline__ f32x4 to_f4(f16x4 x) {
 }
 
 // A token row of v or dO (bfloat16) as the A operand of the selection-matrix
-// product: lane (t, g) columns col + 4 g .. + 3 of token t, zero past the end.
+// product: lane (t, g) the four columns from c0 on of token t, zero past the end.
 __device__ __forceinline__ bf16x4 token_row4(const bf16_t* p, int64_t tok, int64_t T, int64_t b,
-                                             int64_t h, int64_t H, int col, int lane) {
+                                             int64_t h, int64_t H, int c0) {
   bf16x4 r{};
-  if (tok < T) r = *(const bf16x4*)(p + ((b * T + tok) * H + h) * kDV + col + 4 * (lane / 16));
+  if (tok < T) r = *(const bf16x4*)(p + ((b * T + tok) * H + h) * kDV + c0);
   return r;
 }
 
@@ -487,7 +514,7 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
   const int lane = tid % 64, lc = lane % 16, lg = lane / 16;
   const int64_t bh = blockIdx.x / a.nblk, blk = blockIdx.x % a.nblk;
   const int64_t b = bh / a.H, h = bh % a.H;
-  const int col = 16 * wave;
+  const int rc0 = row_col(wave, lg);  // this lane's first column in row layout
   const int64_t x0 = blk * kBlkTiles;
   const int ntl = (int)(a.nt - x0 < kBlkTiles ? a.nt - x0 : kBlkTiles);
   // the forward-step parts of the block's records, moved to LDS once for all
@@ -520,17 +547,25 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
   // they would hold registers the staging needs
   __builtin_amdgcn_sched_barrier(0);
   f32x4 dS[8];
-  load_state(dS, a.ds_blk + (bh * a.nblk + blk) * kDD, col, lane);
+  load_frag(dS, a.ds_blk + (bh * a.nblk + blk) * kDD, wave, lane);
+  // the block's start state: the caller's s0 ([dk][dv]) for the first block,
+  // else the forward's checkpoint (accumulator order)
   const float* s_start = blk == 0 ? (a.s0 != nullptr ? a.s0 + bh * kDD : nullptr)
                                   : a.s_ck + ((b * a.nck + blk - 1) * a.H + h) * kDD;
+  auto load_start = [&](f32x4 (&z)[8]) {
+    if (blk == 0)
+      load_state(z, s_start, wave, lane);
+    else
+      load_frag(z, s_start, wave, lane);
+  };
   // every v row this wavefront reads, loaded once (a load issued after the
   // stores of a tile waits for those stores)
   bf16x4 vrow[kBlkTiles];
 #pragma unroll
   for (int u = 0; u < kBlkTiles; ++u)
-    vrow[u] = token_row4(a.v, (x0 + u) * kC + lc, a.T, b, h, a.H, col, lane);
+    vrow[u] = token_row4(a.v, (x0 + u) * kC + lc, a.T, b, h, a.H, rc0);
   f32x4 S[8];  // S_tl; reloaded for the next tile once it is staged
-  load_state(S, s_start, col, lane);
+  load_start(S);
   lds_barrier();
 
   const bf16x4 ident = ident_op(lane);
@@ -543,7 +578,7 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
   for (int tl = ntl - 1; tl >= 0; --tl) {
     const int64_t x = x0 + tl;
     // the tile's dO rows, needed after the forward steps
-    const bf16x4 drow = token_row4(a.dout, x * kC + lc, a.T, b, h, a.H, col, lane);
+    const bf16x4 drow = token_row4(a.dout, x * kC + lc, a.T, b, h, a.H, rc0);
     // ---- forward: S_tl from the block's start state.  T, X and Delta enter
     // their products as float16 pairs (value and rounding error).
     Scale sf;
@@ -632,7 +667,7 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
     stage_state(sm.st[wave], dS, fd, lane);
     lds_barrier();
     const f32x4 y3 = prod128(sm.sx[0][2], kXs, sm.st[0] + 16 * wave * 16, kSs, lane);  // Delta dS'^T
-    // dV = dX: lane (t, g) holds columns col + 4 g .. + 3 of token t
+    // dV = dX: lane (t, g) holds the four columns from rc0 on of token t
     bf16x4 dvo;
     {
       const f32x4 d = *(const f32x4*)&sm.sx[wave][1][lc * 16 + 4 * lg];
@@ -651,7 +686,7 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
     }
     // the next tile's start state, loaded before this tile's stores so that
     // its wait does not take them in
-    if (tl > 0) load_state(S, s_start, col, lane);
+    if (tl > 0) load_start(S);
     *(f32x4*)(Y + kY1 + 256 * wave + 4 * lane) = y1;
     *(f32x4*)(Y + kY2 + 256 * wave + 4 * lane) = y2;
     *(f32x4*)(Y + kY3 + 256 * wave + 4 * lane) = y3;
@@ -663,7 +698,7 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
       Y[kDE + lane + 64] = ysm[1];
     }
     if (x * kC + lc < a.T)
-      *(bf16x4*)(a.dv + ((b * a.T + x * kC + lc) * a.H + h) * kDV + col + 4 * lg) = dvo;
+      *(bf16x4*)(a.dv + ((b * a.T + x * kC + lc) * a.H + h) * kDV + rc0) = dvo;
     lds_barrier();  // the staging is free for the next tile
   }
 }
@@ -684,7 +719,7 @@ struct FinArgs {
 };
 
 struct FinSmem {
-  float k[kC][kDK], q[kC][kDK], eg[kC][kDK], ieg[kC][kDK], dG[kC][kDK];
+  float k[kC][kDK], q[kC][kDK], dG[kC][kDK];
   float P[kC][kC + 1], M[kC][kC + 1], dM[kC][kC + 1], Z[kC][kC + 1], dP[kC][kC + 1],
       dAq[kC][kC + 1];
   float beta[kC], dbT[kC], dbA[kC];
@@ -752,13 +787,16 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
     sm.dAq[i][j] = j <= i ? dAq : 0.f;
     sm.Z[i][j] = dT * sm.M[i][j];  // for dbeta from T = M Diag(beta): column sums
   }
-  if (tid < kDK) {  // cumulative log-decay per channel
-    const int c = tid;
+  // e^G and e^-G of channel c at every token of the tile (G the cumulative
+  // log-decay), in registers: both threads of a channel form their own copy
+  float egr[kC], iegr[kC];
+  {
     float G = 0.f;
+#pragma unroll
     for (int t = 0; t < kC; ++t) {
       G += sm.dG[t][c];
-      sm.eg[t][c] = __expf(G);
-      sm.ieg[t][c] = __expf(-G);
+      egr[t] = __expf(G);
+      iegr[t] = __expf(-G);
     }
   }
   lds_barrier();
@@ -799,17 +837,17 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
     float i1 = 0.f, i2 = 0.f, i3 = 0.f;
 #pragma unroll
     for (int jj = 0; jj < kC; ++jj) {
-      const float kj = sm.k[jj][c], kcj = kj * sm.ieg[jj][c], egj = sm.eg[jj][c];
+      const float kj = sm.k[jj][c], kcj = kj * iegr[jj], egj = egr[jj];
       i1 = fmaf(sm.dP[t][jj], kcj, i1);                  // (dP Kc)[t]:     jj < t
       i2 = fmaf(sm.dAq[t][jj], kcj, i2);                 // (dAqk Kc)[t]:   jj <= t
       i3 = fmaf(sm.dAq[jj][t] * sm.q[jj][c] + sm.dP[jj][t] * kj, egj, i3);
                                                          // (dAqk^T Qh + dP^T Kh)[t]
     }
-    const float egt = sm.eg[t][c], iegt = sm.ieg[t][c];
+    const float egt = egr[t], iegt = iegr[t];
     const float dq = egt * (y1[u / 4][u % 4] + i2);
     const float dkh = egt * (i1 - y2[u / 4][u % 4]);
     const float dkc = iegt * i3;
-    const float dkb = sm.eg[kC - 1][c] * iegt * y3[u / 4][u % 4];
+    const float dkb = egr[kC - 1] * iegt * y3[u / 4][u % 4];
     const float kt = sm.k[t][c];
     kdkb = fmaf(kt, dkb, kdkb);
     sm.dG[t][c] = kt * (dkh - dkc - dkb) + sm.q[t][c] * dq;
@@ -822,7 +860,7 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
   sm.kdkb[half][c] = kdkb;
   lds_barrier();
   if (tid < kDK) {  // dG_15 += sum_rows k dk_b + dE E, then dg = reverse cumulative sum
-    float acc = sm.kdkb[0][c] + sm.kdkb[1][c] + Y[kDE + c] * sm.eg[kC - 1][c];
+    float acc = sm.kdkb[0][c] + sm.kdkb[1][c] + Y[kDE + c] * egr[kC - 1];
     float* __restrict__ dgp = a.dg;
 #pragma unroll
     for (int t = kC - 1; t >= 0; --t) {
@@ -927,6 +965,7 @@ hipError_t launch_bwd_chunk(const BwdArgs& a) {
   if (nck > 0) {
     ca.ckpt = (float*)(ws + w.s_ck);
     ca.ckpt_every = kBlkTok;
+    ca.ckpt_frag = true;
   }
   if ((e = launch_chunk_mfma(ca)) != hipSuccess) return e;
   if ((e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;

@@ -122,7 +122,8 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
                  const float* __restrict__ norm_w, float eps, Seqs<PACKED> seqs, int64_t H,
                  int64_t BH,
                  int64_t x0, int64_t nseg, int64_t n_state_wg, float* __restrict__ ckpt,
-                 int64_t ckpt_every, float scale, tile::Args<PACKED, LOGITS> next) {
+                 int64_t ckpt_every, bool ckpt_frag, float scale,
+                 tile::Args<PACKED, LOGITS> next) {
   using SC = SlotCfg<DVW, GATE>;
   constexpr int kRing = SC::kRing, kLead = SC::kLead;
   constexpr int NSW = DVW / CPW;   // state wavefronts
@@ -347,6 +348,15 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
         for (int r = 0; r < 4; ++r)
           pc[rec::chan(kb, 4 * lg + r) * rec::kDV] = S[cb][kb][r] * isig;
       }
+  };
+  // The same in accumulator order (16-column group 2 (col0 + wl) / 32 + cb).
+  auto store_state_frag = [&](float* p) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      float* pw = p + 2048 * (2 * ((col0 + wl) / 32) + cb) + 4 * lane;
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) *(f32x4*)(pw + 256 * kb) = S[cb][kb] * isig;
+    }
   };
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
@@ -618,7 +628,11 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
       const int64_t done = (x0 + xl + 1) * rec::kP;  // tokens consumed (uniform)
       if (done % ckpt_every == 0 && done <= T) {
         const int64_t nck = seqs.T / ckpt_every, ic = done / ckpt_every - 1;
-        store_state(ckpt + ((b * nck + ic) * H + h) * (int64_t)(rec::kDK * rec::kDV));
+        float* pk = ckpt + ((b * nck + ic) * H + h) * (int64_t)(rec::kDK * rec::kDV);
+        if (ckpt_frag)
+          store_state_frag(pk);
+        else
+          store_state(pk);
       }
     }
     if constexpr (GATE) {
@@ -677,7 +691,7 @@ hipError_t launch_state_t(const ChunkArgs& a, Seg cur, const float* s_in, float*
                      dim3((unsigned)nblk), dim3(64 * NW),
                      0, (hipStream_t)a.stream, cur.recs, (const bf16_t*)a.v, s_in, s_next,
                      (bf16_t*)a.o, (const bf16_t*)a.gate, a.norm_w, a.eps, seqs, a.H, BH, cur.x0,
-                     cur.n > 0 ? cur.n : 1, n_state, a.ckpt, a.ckpt_every, a.scale, tb);
+                     cur.n > 0 ? cur.n : 1, n_state, a.ckpt, a.ckpt_every, a.ckpt_frag, a.scale, tb);
   return hipGetLastError();
 }
 

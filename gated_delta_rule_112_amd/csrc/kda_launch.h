@@ -29,6 +29,11 @@ struct ChunkArgs {
   // state after every ckpt_every tokens (a multiple of 32).
   float* ckpt = nullptr;
   int64_t ckpt_every = 0;
+  // Checkpoints in accumulator order instead of [dk, dv] (for the backward,
+  // which reads them back as whole 16-byte runs per lane): 16-column group
+  // w = columns 32 (w / 2) + 8 q + 4 (w % 2) + [0, 4), q < 4, at [w][kb][lane][4]
+  // with lane (c, g) holding rows chan(kb, 4 g + r) of column index c.
+  bool ckpt_frag = false;
   // Packed sequences: B sequences at rows cu[b] .. cu[b + 1] - 1 of total rows
   // (device array of B + 1 entries), T the longest; NULL for B x T.
   const int* cu = nullptr;
