@@ -75,7 +75,10 @@ constexpr int kTt = 20992;    // [lane][4]            T[4 g + e][i]
 constexpr int kAqkT = 21504;  // [lane][4]            Aqk[4 g + e][i]
 constexpr int kE = 22016;     // [128] f32            E per key channel
 constexpr int kTlo = 22528;   // [lane][4]            T - kT (the float16 rounding of T)
-constexpr int kRecBytes = 23552;  // a whole number of 1 KB blocks
+// the float16 roundings (x - float16(x)) of two of the adjoint step's operands
+constexpr int kTtlo = 23040;  // [lane][4]            of kTt
+constexpr int kAqkTlo = 23552;  // [lane][4]          of kAqkT
+constexpr int kRecBytes = 24576;  // a whole number of 1 KB blocks
 
 // Products of one tile (float32), from the block kernel to the finishing kernel:
 // Y1, Y2, Y3 are [16 tokens][128 channels] each, in accumulator order: token t,
@@ -170,11 +173,16 @@ __device__ __forceinline__ void build_tile(const RecArgs& a, int64_t bh, int64_t
     *(f32x4*)pm = acc_a;
     *(f32x4*)(pm + 256) = mf;
   }
+  const f16x4 tlo = to_h4(tf - f32x4{(float)tb[0], (float)tb[1], (float)tb[2], (float)tb[3]});
+  f32x4 aqlo;  // Aqk - float16(Aqk), Aqk = lower(Qh Kc^T) as finish() masks it
+#pragma unroll
+  for (int r = 0; r < 4; ++r) aqlo[r] = (4 * lg + r <= t ? acc_q[r] : 0.f) - (float)aq[r];
   *(f16x4*)(R + kT + lane * 8) = tb;
-  *(f16x4*)(R + kTlo + lane * 8) = to_h4(tf - f32x4{(float)tb[0], (float)tb[1], (float)tb[2],
-                                                    (float)tb[3]});
+  *(f16x4*)(R + kTlo + lane * 8) = tlo;
   *(f16x4*)(R + kTt + lane * 8) = transpose16(tb, sm, lane);
+  *(f16x4*)(R + kTtlo + lane * 8) = transpose16(tlo, sm, lane);
   *(f16x4*)(R + kAqkT + lane * 8) = transpose16(aq, sm, lane);
+  *(f16x4*)(R + kAqkTlo + lane * 8) = transpose16(to_h4(aqlo), sm, lane);
 }
 
 __global__ void __launch_bounds__(256) kda_bwd_rec_kernel(RecArgs a) {
@@ -612,14 +620,37 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
     const unsigned char* R = a.recs + (bh * a.nt + x) * (int64_t)kRecBytes;
     const f32x4 dos = rescale(sd, dS, mma16b(drow, ident, zero4()) * dmul);
     const f16x4 do16 = to_h4(dos);  // exact: sigma dO with dO in bfloat16
-    f16x8 sopD[4];
+    // dDelta and dX with dS', Aqk, dDelta and T as float16 pairs (value and
+    // rounding error; Kb alone stays one float16 rounding): the largest
+    // gradients come from the final-state term in the last tiles, and four
+    // float16 roundings there would cost a few times their rounding relative
+    // to gradients 100 times their RMS.
+    f16x8 sopD[4], sopDl[4];
     state_op(dS, sopD);
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      f16x4 l0, l1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        l0[e] = (f16)(dS[2 * s2][e] - (float)sopD[s2][e]);
+        l1[e] = (f16)(dS[2 * s2 + 1][e] - (float)sopD[s2][4 + e]);
+      }
+      sopDl[s2] = cat8(l0, l1);
+    }
     f32x4 dd = zero4();
 #pragma unroll
-    for (int s = 0; s < 4; ++s) dd = mma32h(ld16h(R + kKb + s * 1024 + lane * 16), sopD[s], dd);
-    dd = mma32h(lo8(ld8h(R + kAqkT + lane * 8)), cat8(do16, do16), dd);
-    const f16x4 dd16 = to_h4(dd);
-    const f32x4 dx = mma32h(lo8(ld8h(R + kTt + lane * 8)), cat8(dd16, dd16), zero4());
+    for (int s = 0; s < 4; ++s) {
+      const f16x8 kbh = ld16h(R + kKb + s * 1024 + lane * 16);
+      dd = mma32h(kbh, sopD[s], dd);
+      dd = mma32h(kbh, sopDl[s], dd);
+    }
+    // Aqk^T dO' (dO' exact in float16): value and rounding in one product
+    dd = mma32h(cat8(ld8h(R + kAqkT + lane * 8), ld8h(R + kAqkTlo + lane * 8)),
+                cat8(do16, do16), dd);
+    const f16x4 dd16 = to_h4(dd), ddl = to_h4(dd - to_f4(dd16));
+    const f16x4 tt4 = ld8h(R + kTt + lane * 8);
+    f32x4 dx = mma32h(cat8(tt4, tt4), cat8(dd16, ddl), zero4());  // T^T (dd16 + ddl)
+    dx = mma32h(lo8(ld8h(R + kTtlo + lane * 8)), cat8(dd16, dd16), dx);
     const float ff = sf.isig, fd = so * sd.isig;  // back to unscaled units
     float* Y = a.ybuf + (bh * a.nt + x) * (int64_t)kYFloats;
 

@@ -102,3 +102,33 @@ def test_backward_deterministic(kda):
         torch.cuda.synchronize()
         for a, b in zip(ref, got):
             assert torch.equal(a, b)
+
+
+@pytest.mark.timeout(600)
+def test_backward_small_prefill_workload_sampled(kda):
+    """The backward at the benchmark's size and launch configuration (B=2, H=32,
+    T=4096, bfloat16, with s0 and a final-state gradient, dO drawn like v):
+    two sampled heads against the gradient oracle run on those heads' inputs
+    alone (heads are independent), every gradient at the bfloat16 bar."""
+    from gated_delta_rule_112_amd.inputs import WORKLOADS, make_prefill_inputs
+    w = WORKLOADS["small_prefill"]
+    x = make_prefill_inputs(w, device=dev())
+    g_ = torch.Generator(device=dev())
+    g_.manual_seed(w.seed + 21)
+    do = torch.randn(x["v"].shape, generator=g_, device=dev()).to(x["v"].dtype)
+    dsf = torch.randn((w.B, w.H, w.dk, w.dv), generator=g_, device=dev())
+    scale = w.dk ** -0.5
+    print(f"backward full size B={w.B} T={w.T} H={w.H}", flush=True)
+    got = kda.recurrent_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["s0"], dsf,
+                            scale=scale)
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (1, 31)]:
+        sl = lambda t: f64(t[b:b + 1, :, h:h + 1])  # noqa: E731
+        ref = kda_recurrent_vjp(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]),
+                                f64(x["s0"][b:b + 1, h:h + 1]), sl(do),
+                                f64(dsf[b:b + 1, h:h + 1]), scale)
+        for name, t in zip(["dq", "dk", "dv", "dg", "dbeta", "ds0"], got):
+            part = t[b:b + 1, h:h + 1] if name == "ds0" else t[b:b + 1, :, h:h + 1]
+            io_out = name in ("dq", "dk", "dv")
+            assert_close(f64(part), ref[name], TOL[torch.bfloat16],
+                         f"{name} (b={b}, h={h}) full size", torch.bfloat16 if io_out else None)
