@@ -30,7 +30,8 @@
 // library's (one per device) at the same time as steps 2 and 3 on the
 // caller's stream: the chain is a walk over the tiles of one head per compute
 // unit, bound by what one compute unit can stream, and leaves most of the
-// chip to the forward.  Step 4 waits for both.
+// chip to the forward.  Step 4 waits for both.  Under stream capture all five
+// run on the caller's stream.
 //   1. the matrix-core forward, state only, with the state kept every 64
 //      tokens (a block of four tiles);
 //   2. kda_bwd_rec_kernel: per tile and in parallel, the operands of the two
@@ -982,16 +983,26 @@ hipError_t launch_bwd_chunk(const BwdArgs& a) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(side_mutex[dev]);
+  // Under stream capture every step stays on the caller's stream.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if ((e = hipStreamIsCapturing(st, &cap)) != hipSuccess) return e;
+  const bool fork = cap == hipStreamCaptureStatusNone;
+  std::unique_lock<std::mutex> lock(side_mutex[dev], std::defer_lock);
   SideStream* side = nullptr;
-  if ((e = side_stream_locked(dev, &side)) != hipSuccess) return e;
+  if (fork) {
+    lock.lock();
+    if ((e = side_stream_locked(dev, &side)) != hipSuccess) return e;
+  }
 
   // 1. forward states every 64 tokens, on the side stream once the caller's
   //    stream has reached this call
-  if ((e = hipEventRecord(side->fork, st)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return e;
+  if (fork) {
+    if ((e = hipEventRecord(side->fork, st)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return e;
+  }
   ChunkArgs ca{a.q, a.k, a.v, a.g, a.beta, a.s0, nullptr, (float*)(ws + w.s_tmp), nullptr,
-               nullptr, 0.f, a.B, a.T, a.H, kDK, kDV, 1.f, true, ws + w.fwd, side->s};
+               nullptr, 0.f, a.B, a.T, a.H, kDK, kDV, 1.f, true, ws + w.fwd,
+               fork ? side->s : st};
   ca.total = a.B * a.T;
   if (nck > 0) {
     ca.ckpt = (float*)(ws + w.s_ck);
@@ -999,7 +1010,7 @@ hipError_t launch_bwd_chunk(const BwdArgs& a) {
     ca.ckpt_frag = true;
   }
   if ((e = launch_chunk_mfma(ca)) != hipSuccess) return e;
-  if ((e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;
+  if (fork && (e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;
 
   // 2. records
   RecArgs ra{(const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, ws + w.recs,
@@ -1017,7 +1028,7 @@ hipError_t launch_bwd_chunk(const BwdArgs& a) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   // 4. block products, once the forward states are there
-  if ((e = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return e;
+  if (fork && (e = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return e;
   BlockArgs ba{ws + w.recs, (const bf16_t*)a.v, (const bf16_t*)a.dout, a.s0,
                (const float*)(ws + w.s_ck), (const float*)(ws + w.ds_blk), (bf16_t*)a.dv,
                (float*)(ws + w.ybuf), a.B, a.T, a.H, nt, nblk, nck, a.scale};

@@ -388,6 +388,20 @@ kda_status kda_gate_rmsnorm(const void* x, const void* gate, const float* norm_w
  *   dq, dk, dv, dg (with respect to the log-decay g), dbeta and ds0 (the initial state).
  * The state is recomputed from checkpoints every 64 tokens held in the workspace.
  *
+ * Two kernels, chosen per call:
+ *   bfloat16 io with q, k, v, dout, g, dq, dk, dv all 16-byte aligned: the chunkwise
+ *     pass on the matrix cores (16-token tiles; float16 operands with float32
+ *     accumulation, the last tile's final-state terms as float16 value-and-rounding
+ *     pairs).  Each gradient is within 2e-2 x its RMS of the float64 gradients (dq, dk,
+ *     dv net of half a bfloat16 ulp), the forward's bfloat16-input bar.  Deterministic.
+ *     It runs its first step (a forward pass) on a second stream the library creates
+ *     once per device (default priority) and joins back into `stream` with events
+ *     before the call's later kernels, so the call is ordered on `stream` like any
+ *     other; calls on one device from several host threads are serialised by a mutex
+ *     while they enqueue.  Under stream capture every step runs on `stream`.
+ *   otherwise (float32 io, or a bfloat16 tensor not 16-byte aligned, or the environment
+ *     variable KDA_BWD_TOKEN=1): a token-serial float32 vector kernel, within 1e-4 x RMS.
+ *
  *   q, k, v, dout     [B, T, H, 128]  io dtype
  *   g                 [B, T, H, 128]  float32;  beta [B, T, H] float32
  *   s0, ds_final      [B, H, 128, 128] float32 or NULL (zero initial state; no final-state term)
@@ -409,9 +423,13 @@ kda_status kda_recurrent_bwd(const void* q, const void* k, const void* v, const 
 
 /*
  * kda_recurrent_bwd_workspace_size -- bytes of workspace kda_recurrent_bwd
- * needs: per (b, h), float32 states for ceil(T / 64) checkpoints plus 64
- * recomputed tokens (64 KiB each), then four column-partial sums of dq, dk, dg
- * and dbeta per token and head.  0 for unsupported sizes.
+ * needs: the larger of its two kernels' needs.  Token-serial: per (b, h), float32
+ * states for ceil(T / 64) checkpoints plus 64 recomputed tokens (64 KiB each), then
+ * four column-partial sums of dq, dk, dg and dbeta per token and head.  Chunkwise:
+ * the forward's workspace, the state every 64 tokens and the adjoint at the end of
+ * every 64 tokens (64 KiB each per head), and per 16-token tile a 24 KiB record,
+ * 2 KiB of float32 16x16 factors and 26.5 KiB of products (about 5.3 KiB per token
+ * and head in all; 2.0 GiB at B=2, H=32, T=4096).  0 for unsupported sizes.
  */
 size_t kda_recurrent_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk, int dv);
 

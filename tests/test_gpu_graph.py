@@ -137,3 +137,41 @@ def test_decode_graph_replays(kda):
         assert torch.equal(o1, a_e), f"replay {i}: decode output differs"
         assert torch.equal(ov, b_e), f"replay {i}: verify output differs"
         assert torch.equal(st["state"], S_e), f"replay {i}: state differs"
+
+
+def test_backward_graph_replays(kda):
+    """The chunkwise backward captured whole: under capture its forward step
+    runs on the caller's stream instead of the library's second stream; every
+    replay equals the eager call (which forks that step) bit for bit."""
+    B, T, H, D = 1, 200, 2, 128
+    bf = torch.bfloat16
+    x = {"q": torch.empty(B, T, H, D, dtype=bf, device=dev()),
+         "k": torch.empty(B, T, H, D, dtype=bf, device=dev()),
+         "v": torch.empty(B, T, H, D, dtype=bf, device=dev()),
+         "dout": torch.empty(B, T, H, D, dtype=bf, device=dev()),
+         "g": torch.empty(B, T, H, D, device=dev()),
+         "beta": torch.empty(B, T, H, device=dev()),
+         "state": torch.empty(B, H, D, D, device=dev()),
+         "dsf": torch.empty(B, H, D, D, device=dev())}
+    nws = kda.load_library().kda_recurrent_bwd_workspace_size(B, T, H, D, D)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev())
+    ws_e = torch.empty(nws, dtype=torch.uint8, device=dev())
+    fill(x, 3200)
+    held = {}
+
+    def run(w):
+        return kda.recurrent_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["dout"],
+                                 x["state"], x["dsf"], scale=0.7, workspace=w)
+
+    def captured():
+        held["out"] = run(ws)
+
+    graph = capture(captured)
+    for i in range(REPLAYS):
+        fill(x, 3210 + i)
+        eager = run(ws_e)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(["dq", "dk", "dv", "dg", "dbeta", "ds0"], held["out"], eager):
+            assert torch.equal(a, b), f"replay {i}: {name} differs"
