@@ -26,12 +26,10 @@
 // Every product with a factor e^-G (up to e^80) is formed in float32 with the
 // masked (causal) entries only, so each term carries e^(G_i - G_j) <= 1.
 //
-// The pass runs as five steps.  Step 1 runs on a second stream of the
-// library's (one per device) at the same time as steps 2 and 3 on the
-// caller's stream: the chain is a walk over the tiles of one head per compute
-// unit, bound by what one compute unit can stream, and leaves most of the
-// chip to the forward.  Step 4 waits for both.  Under stream capture all five
-// run on the caller's stream.
+// The pass runs as five steps on the caller's stream.  (Running step 1 on a
+// second stream beside steps 2 and 3 saved about 0.1 ms of 1.8 at B=2, H=32,
+// T=4096, but the extra hardware queue slowed later kernels of the process:
+// the decode step by 4 %.)
 //   1. the matrix-core forward, state only, with the state kept every 64
 //      tokens (a block of four tiles);
 //   2. kda_bwd_rec_kernel: per tile and in parallel, the operands of the two
@@ -52,8 +50,6 @@
 // wavefront divides what it contributes by both scales.
 #include "kda_chunk_rec.h"
 #include "kda_chunk_tile.h"
-#include <mutex>
-
 #include "kda_launch.h"
 
 namespace kda {
@@ -933,43 +929,6 @@ int64_t bwd_chunk_workspace_bytes(int64_t B, int64_t T, int64_t H) {
   return bwd_chunk_layout(B, T, H).total;
 }
 
-// The second stream of a device (default priority, non-blocking) and the two
-// events that fork step 1 onto it and join it back.  Created on first use;
-// the device's mutex makes each call's fork and join one unit, so calls from
-// several host threads stay ordered against their own streams.
-namespace {
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-constexpr int kMaxDevices = 64;
-std::mutex side_mutex[kMaxDevices];
-SideStream side_streams[kMaxDevices];
-
-hipError_t side_stream_locked(int dev, SideStream** out) {
-  SideStream& ss = side_streams[dev];
-  hipError_t e;
-  if (ss.s == nullptr) {
-    if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) {
-      ss.s = nullptr;
-      return e;
-    }
-  }
-  if (ss.fork == nullptr &&
-      (e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) {
-    ss.fork = nullptr;
-    return e;
-  }
-  if (ss.join == nullptr &&
-      (e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) {
-    ss.join = nullptr;
-    return e;
-  }
-  *out = &ss;
-  return hipSuccess;
-}
-}  // namespace
-
 hipError_t launch_bwd_chunk(const BwdArgs& a) {
   using namespace bwd;
   const int64_t BH = a.B * a.H, nt = (a.T + kC - 1) / kC;
@@ -979,38 +938,17 @@ hipError_t launch_bwd_chunk(const BwdArgs& a) {
   unsigned char* ws = (unsigned char*)a.workspace;
   hipStream_t st = (hipStream_t)a.stream;
 
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  // Under stream capture every step stays on the caller's stream.
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if ((e = hipStreamIsCapturing(st, &cap)) != hipSuccess) return e;
-  const bool fork = cap == hipStreamCaptureStatusNone;
-  std::unique_lock<std::mutex> lock(side_mutex[dev], std::defer_lock);
-  SideStream* side = nullptr;
-  if (fork) {
-    lock.lock();
-    if ((e = side_stream_locked(dev, &side)) != hipSuccess) return e;
-  }
-
-  // 1. forward states every 64 tokens, on the side stream once the caller's
-  //    stream has reached this call
-  if (fork) {
-    if ((e = hipEventRecord(side->fork, st)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return e;
-  }
+  // 1. forward states every 64 tokens
   ChunkArgs ca{a.q, a.k, a.v, a.g, a.beta, a.s0, nullptr, (float*)(ws + w.s_tmp), nullptr,
-               nullptr, 0.f, a.B, a.T, a.H, kDK, kDV, 1.f, true, ws + w.fwd,
-               fork ? side->s : st};
+               nullptr, 0.f, a.B, a.T, a.H, kDK, kDV, 1.f, true, ws + w.fwd, a.stream};
   ca.total = a.B * a.T;
   if (nck > 0) {
     ca.ckpt = (float*)(ws + w.s_ck);
     ca.ckpt_every = kBlkTok;
     ca.ckpt_frag = true;
   }
-  if ((e = launch_chunk_mfma(ca)) != hipSuccess) return e;
-  if (fork && (e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;
+  hipError_t e = launch_chunk_mfma(ca);
+  if (e != hipSuccess) return e;
 
   // 2. records
   RecArgs ra{(const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, ws + w.recs,
@@ -1027,8 +965,7 @@ hipError_t launch_bwd_chunk(const BwdArgs& a) {
                      st, cha);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  // 4. block products, once the forward states are there
-  if (fork && (e = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return e;
+  // 4. block products
   BlockArgs ba{ws + w.recs, (const bf16_t*)a.v, (const bf16_t*)a.dout, a.s0,
                (const float*)(ws + w.s_ck), (const float*)(ws + w.ds_blk), (bf16_t*)a.dv,
                (float*)(ws + w.ybuf), a.B, a.T, a.H, nt, nblk, nck, a.scale};

@@ -394,11 +394,6 @@ kda_status kda_gate_rmsnorm(const void* x, const void* gate, const float* norm_w
  *     accumulation, the last tile's final-state terms as float16 value-and-rounding
  *     pairs).  Each gradient is within 2e-2 x its RMS of the float64 gradients (dq, dk,
  *     dv net of half a bfloat16 ulp), the forward's bfloat16-input bar.  Deterministic.
- *     It runs its first step (a forward pass) on a second stream the library creates
- *     once per device (default priority) and joins back into `stream` with events
- *     before the call's later kernels, so the call is ordered on `stream` like any
- *     other; calls on one device from several host threads are serialised by a mutex
- *     while they enqueue.  Under stream capture every step runs on `stream`.
  *   otherwise (float32 io, or a bfloat16 tensor not 16-byte aligned, or the environment
  *     variable KDA_BWD_TOKEN=1): a token-serial float32 vector kernel, within 1e-4 x RMS.
  *

@@ -140,9 +140,8 @@ def test_decode_graph_replays(kda):
 
 
 def test_backward_graph_replays(kda):
-    """The chunkwise backward captured whole: under capture its forward step
-    runs on the caller's stream instead of the library's second stream; every
-    replay equals the eager call (which forks that step) bit for bit."""
+    """The chunkwise backward captured whole (five launches); every replay
+    equals the eager call bit for bit."""
     B, T, H, D = 1, 200, 2, 128
     bf = torch.bfloat16
     x = {"q": torch.empty(B, T, H, D, dtype=bf, device=dev()),
