@@ -46,6 +46,10 @@ KERNEL_SOURCES = {
                        "gated_delta_rule_112_amd/csrc/kda_chunk_rec.h"],
     "kda_chunk_valu": ["gated_delta_rule_112_amd/csrc/kda_chunk_valu.hip"],
     "kda_decode": ["gated_delta_rule_112_amd/csrc/kda_decode.hip"],
+    "kda_bwd_chunk": ["gated_delta_rule_112_amd/csrc/kda_bwd_chunk.hip",
+                      "gated_delta_rule_112_amd/csrc/kda_chunk_tile.h",
+                      "gated_delta_rule_112_amd/csrc/kda_chunk_state.hip",
+                      "gated_delta_rule_112_amd/csrc/kda_chunk_rec.h"],
 }
 
 
@@ -508,6 +512,31 @@ def bench_verify(kda, torch, w, repeats=20):
     return res, x["n_commit"].cpu().tolist(), x["q"].dtype
 
 
+def stream_ceiling(torch, nbytes, reps=20):
+    """The streaming ceiling the decode step is held to: an in-place
+    read-modify-write of a float32 buffer of the decode state's size (torch's
+    vectorised elementwise kernel, x *= c) and a copy between two such buffers;
+    GB/s counting every byte read and every byte written."""
+    dev = torch.device("cuda:0")
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for name, fn in [("rmw", lambda: x.mul_(1.0000001)), ("copy", lambda: y.copy_(x))]:
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[f"{name}_gbs"] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+    del x, y
+    return res
+
+
 def copy_probe(torch, nbytes=1 << 30):
     """A plain device copy of known size, run once so that a counter pass over
     this process can scale FETCH_SIZE / WRITE_SIZE against it."""
@@ -669,7 +698,9 @@ def main():
         backward = {"workload": wb.name, "B": wb.B, "H": wb.H, "T": wb.T,
                     "ms": round(bms, 4), "tokens_per_s": round(ntok / (bms * 1e-3), 1),
                     "algorithmic_bytes": bbytes, "achieved": round(bgbs, 1), "unit": "GB/s",
-                    "peak": HBM_PEAK_GBS, "frac": round(bgbs / HBM_PEAK_GBS, 4)}
+                    "peak": HBM_PEAK_GBS, "frac": round(bgbs / HBM_PEAK_GBS, 4),
+                    "kernel": "kda_bwd_chunk",
+                    "traffic": measured_traffic("kda_bwd_chunk", wb.name)}
         log(f"[bench] backward ({wb.name}): {bms:.3f} ms, "
             f"{ntok / (bms * 1e-3) / 1e6:.3f} M tok/s")
 
@@ -693,6 +724,11 @@ def main():
             "cpu_baseline": cpu_dec,
         }
         log(f"[bench] decode {dms:.4f} ms/step, {dgbs:.0f} GB/s")
+        ceil = stream_ceiling(torch, wd.B * wd.H * wd.dk * wd.dv * 4)
+        ceil["decode_frac_of_rmw"] = round(dgbs / ceil["rmw_gbs"], 4)
+        decode["streaming_ceiling"] = ceil
+        log(f"[bench] streaming ceiling over the state's size: in-place read-modify-write "
+            f"{ceil['rmw_gbs']:.0f} GB/s, copy {ceil['copy_gbs']:.0f} GB/s")
 
     verify = None
     if not a.no_verify:
