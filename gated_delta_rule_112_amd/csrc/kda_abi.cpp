@@ -108,6 +108,9 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk, int
 
 size_t kda_recurrent_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk, int dv) {
   if (dk != 128 || dv != 128 || prod(B, T, H, dk) < 0) return 0;
+  // At most 2^40 token-heads (far beyond any device), so that every size term
+  // below (under 2^17 bytes per token-head) stays within int64.
+  if (prod(B, T, H, 1) > (int64_t(1) << 40)) return 0;
   const int64_t n = kda::bwd_workspace_floats(B, T, H);
   if (n <= 0 || n >= kMaxElems) return 0;
   // the larger of the two paths' needs (the path depends on the io dtype and alignment)

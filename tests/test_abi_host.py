@@ -309,6 +309,12 @@ def test_recurrent_bwd_validation(lib):
     # ceil(70 / 64) checkpoints + 64 states per head, then 4 column parts of dq, dk, dg, dbeta
     assert need == (B * H * (2 + 64) * 128 * 128 + 4 * B * T * H * (3 * 128 + 1)) * 4
     assert lib.kda_recurrent_bwd_workspace_size(B, T, H, 64, 64) == 0
+    # beyond 2^40 token-heads the size would leave int64: reported as unsupported
+    assert lib.kda_recurrent_bwd_workspace_size(1 << 20, 1 << 20, 2, 128, 128) == 0
+    # the chunkwise pass needs more than the token-serial one at long T (records and
+    # products per tile): the reported size covers the larger
+    nl = lib.kda_recurrent_bwd_workspace_size(2, 4096, 32, 128, 128)
+    assert nl >= 2 * 32 * (4096 // 16) * (24576 + 2048 + 6784 * 4)
 
     def call(q=1, dq=9, ds0=14, s0=6, dk=128, ws=15, nws=None, io=0):
         a = {i: P(i) for i in range(1, 16)}
