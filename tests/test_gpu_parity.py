@@ -227,6 +227,39 @@ def test_decode_equals_prefill(kda):
     assert_close(f64(state), f64(S), 2e-2, "decode vs prefill state")
 
 
+def test_decode_time_independent_of_step(kda):
+    """A decode step costs the same at every position of the sequence: the
+    state has a fixed size ("Kimi K3 Architecture Explained ...", section
+    "Token mixing"), so the steps of the second half of a run take as long as
+    those of the first (HIP events around each step; medians within 30 %)."""
+    B, H, D, steps = 64, 16, 128, 64
+    g_ = torch.Generator(device=dev())
+    g_.manual_seed(97)
+    r = lambda *s: torch.randn(*s, generator=g_, device=dev())  # noqa: E731
+    state = 0.05 * r(B, H, D, D)
+    xs = []
+    for _ in range(steps):
+        q = r(B, H, D)
+        k = r(B, H, D)
+        xs.append(((q / q.norm(dim=-1, keepdim=True)).to(torch.bfloat16),
+                   (k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16),
+                   r(B, H, D).to(torch.bfloat16), -5.0 * torch.sigmoid(r(B, H, D)),
+                   torch.sigmoid(r(B, H))))
+    out = torch.empty(B, H, D, dtype=torch.bfloat16, device=dev())
+    kda.decode_step(*xs[0], state, out=out)  # warm-up
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for t in range(steps):
+        kda.decode_step(*xs[t], state, out=out)
+        ev[t + 1].record()
+    torch.cuda.synchronize()
+    ms = np.array([ev[t].elapsed_time(ev[t + 1]) for t in range(steps)])
+    first, second = np.median(ms[: steps // 2]), np.median(ms[steps // 2:])
+    print(f"[timing] decode step median: steps 0-31 {first:.4f} ms, 32-63 {second:.4f} ms")
+    assert abs(second - first) <= 0.3 * first
+
+
 def test_deterministic(kda, path):
     q, k, v, g, beta, s0, gate = gen_prefill(1, 64, 4, 128, 128, torch.bfloat16, 91, gate=True)
     # the same input gives bitwise-equal results over 10 runs (no races, no
