@@ -748,8 +748,9 @@ struct FinArgs {
 
 struct FinSmem {
   float k[kC][kDK], q[kC][kDK], dG[kC][kDK];
-  float P[kC][kC + 1], M[kC][kC + 1], dM[kC][kC + 1], Z[kC][kC + 1], dP[kC][kC + 1],
-      dAq[kC][kC + 1];
+  float P[kC][kC + 1], M[kC][kC + 1], dM[kC][kC + 1], Z[kC][kC + 1];
+  // dP and dAqk and their transposes, rows of 16 read whole (broadcast) by a wavefront
+  __attribute__((aligned(16))) float dP[kC][kC], dAq[kC][kC], dPT[kC][kC], dAqT[kC][kC];
   float beta[kC], dbT[kC], dbA[kC];
   float kdkb[2][kDK];
 };
@@ -812,7 +813,7 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
     if (tid < kC) sm.beta[tid] = valid(tid) ? a.beta[row_of(tid)] : 0.f;
     lds_barrier();
     sm.dM[i][j] = dT * sm.beta[j];
-    sm.dAq[i][j] = j <= i ? dAq : 0.f;
+    sm.dAq[i][j] = sm.dAqT[j][i] = j <= i ? dAq : 0.f;
     sm.Z[i][j] = dT * sm.M[i][j];  // for dbeta from T = M Diag(beta): column sums
   }
   // e^G and e^-G of channel c at every token of the tile (G the cumulative
@@ -845,7 +846,7 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
     float d = 0.f;  // dA = strict_lower(-M^T Z)
     if (j < i)
       for (int c = 0; c < kC; ++c) d -= sm.M[c][i] * sm.Z[c][j];
-    sm.dP[i][j] = sm.beta[i] * d;  // dP = Diag(beta) dA
+    sm.dP[i][j] = sm.dPT[j][i] = sm.beta[i] * d;  // dP = Diag(beta) dA
     sm.dM[i][j] = d * sm.P[i][j];  // dM is spent: row sums of dA * P, for dbeta
   }
   lds_barrier();
@@ -855,7 +856,17 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
     sm.dbA[tid] = s;
   }
 
-  // per (token, channel): thread (c, half) takes tokens 8 half .. 8 half + 7
+  // per (token, channel): thread (c, half) takes tokens 8 half .. 8 half + 7;
+  // channel c's Kc, Kh and Qh at every token of the tile in registers, the rows
+  // of dP, dAqk and their transposes read whole (the token is wavefront-uniform)
+  float kcr[kC], khr[kC], qhr[kC];
+#pragma unroll
+  for (int jj = 0; jj < kC; ++jj) {
+    const float kj = sm.k[jj][c];
+    kcr[jj] = kj * iegr[jj];
+    khr[jj] = kj * egr[jj];
+    qhr[jj] = sm.q[jj][c] * egr[jj];
+  }
   float kdkb = 0.f;
   bf16_t* __restrict__ dqp = a.dq;
   bf16_t* __restrict__ dkp = a.dk;
@@ -864,12 +875,16 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
     const int t = 8 * half + u;
     float i1 = 0.f, i2 = 0.f, i3 = 0.f;
 #pragma unroll
-    for (int jj = 0; jj < kC; ++jj) {
-      const float kj = sm.k[jj][c], kcj = kj * iegr[jj], egj = egr[jj];
-      i1 = fmaf(sm.dP[t][jj], kcj, i1);                  // (dP Kc)[t]:     jj < t
-      i2 = fmaf(sm.dAq[t][jj], kcj, i2);                 // (dAqk Kc)[t]:   jj <= t
-      i3 = fmaf(sm.dAq[jj][t] * sm.q[jj][c] + sm.dP[jj][t] * kj, egj, i3);
-                                                         // (dAqk^T Qh + dP^T Kh)[t]
+    for (int j4 = 0; j4 < kC / 4; ++j4) {
+      const f32x4 p4 = *(const f32x4*)&sm.dP[t][4 * j4], a4 = *(const f32x4*)&sm.dAq[t][4 * j4];
+      const f32x4 pt4 = *(const f32x4*)&sm.dPT[t][4 * j4], at4 = *(const f32x4*)&sm.dAqT[t][4 * j4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jj = 4 * j4 + e;
+        i1 = fmaf(p4[e], kcr[jj], i1);   // (dP Kc)[t]:     jj < t
+        i2 = fmaf(a4[e], kcr[jj], i2);   // (dAqk Kc)[t]:   jj <= t
+        i3 = fmaf(at4[e], qhr[jj], fmaf(pt4[e], khr[jj], i3));  // (dAqk^T Qh + dP^T Kh)[t]
+      }
     }
     const float egt = egr[t], iegt = iegr[t];
     const float dq = egt * (y1[u / 4][u % 4] + i2);
