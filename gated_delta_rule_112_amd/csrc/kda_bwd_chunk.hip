@@ -460,10 +460,12 @@ struct BlockArgs {
 // the eight wavefronts): Kh, Kb^T, T, T - float16(T), E.
 constexpr int kFwKh = 0, kFwKbC = 4096, kFwT = 8192, kFwTlo = 8704, kFwE = 9216;
 constexpr int kFwBytes = 9728;
+// The staged operands are bfloat16 pairs: h = bfloat16(x) and l = bfloat16(x - h)
+// (x = h + l to about 2^-17 relative); a product takes hh + hl + lh.
 struct BlockSmem {
-  float st[8][kDK * 16];       // chunk w of S_t, then of dS', row-major [c][j]
-  float sx[8][5][kC * 16];     // chunk w of dO, dX, Delta, dDelta, X, row-major [t][j]
-  float dep[8][kDK];           // chunk w's part of dE
+  bf16_t sth[8][kDK * 16], stl[8][kDK * 16];  // chunk w of S_t, then of dS', row-major [c][j]
+  bf16_t sxh[8][5][kC * 16], sxl[8][5][kC * 16];  // chunk w of dO', dX, Delta, dDelta, X: [t][j]
+  float dep[8][kDK];                          // chunk w's part of dE
   unsigned char fw[kBlkTiles][kFwBytes];
 };
 
@@ -482,32 +484,54 @@ __device__ __forceinline__ bf16x4 token_row4(const bf16_t* p, int64_t tok, int64
 
 // This wavefront's accumulators (lane (c, g) of block kb: rows chan(kb, 4 g + r),
 // column c) times f to row-major [channel][c] float32.
-__device__ __forceinline__ void stage_state(float* st, const f32x4 (&z)[8], float f, int lane) {
+__device__ __forceinline__ void split_bf16(float x, bf16_t* h, bf16_t* l) {
+  const bf16_t hv = (bf16_t)x;
+  *h = hv;
+  *l = (bf16_t)(x - (float)hv);
+}
+
+__device__ __forceinline__ f32x4 mma32b(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void stage_state(bf16_t* sh, bf16_t* sl, const f32x4 (&z)[8], float f,
+                                            int lane) {
   const int lc = lane % 16, lg = lane / 16;
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st[rec::chan(kb, 4 * lg + r) * 16 + lc] = z[kb][r] * f;
+    for (int r = 0; r < 4; ++r) {
+      const int i = rec::chan(kb, 4 * lg + r) * 16 + lc;
+      split_bf16(z[kb][r] * f, sh + i, sl + i);
+    }
 }
 
 // A [16 tokens][16 columns] accumulator (lane (c, g): rows 4 g + r) times f to
-// row-major float32.
-__device__ __forceinline__ void stage_small(float* sx, f32x4 z, float f, int lane) {
+// row-major bfloat16 pairs.
+__device__ __forceinline__ void stage_small(bf16_t* sh, bf16_t* sl, f32x4 z, float f, int lane) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) sx[(4 * (lane / 16) + r) * 16 + lane % 16] = z[r] * f;
+  for (int r = 0; r < 4; ++r) {
+    const int i = (4 * (lane / 16) + r) * 16 + lane % 16;
+    split_bf16(z[r] * f, sh + i, sl + i);
+  }
 }
 
-// Out[4 g + r][16 m + c] of A B^T summed over all 128 value columns (the
-// eight chunks in order), A chunk w at A0 + w * as, B chunk w at B0 + w * bs.
-__device__ __forceinline__ f32x4 prod128(const float* A0, int as, const float* B0, int bs,
-                                         int lane) {
+// Out[4 g + r][c] of A B^T summed over all 128 value columns, in four 32-deep
+// steps over chunks 2s, 2s + 1 (fixed order), each as hh + hl + lh: lane
+// (x, g) takes row x, columns 8 (g % 2) .. + 7 of chunk 2 s + g / 2; A chunk w
+// at A0 + w * as, B chunk w at B0 + w * bs (h and l arrays alike).
+__device__ __forceinline__ f32x4 prod128(const bf16_t* Ah, const bf16_t* Al, int as,
+                                         const bf16_t* Bh, const bf16_t* Bl, int bs, int lane) {
+  const int off = (lane % 16) * 16 + 8 * ((lane / 16) % 2), wg = (lane / 16) / 2;
   f32x4 o = zero4();
-#pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    const f32x4 av = *(const f32x4*)(A0 + w * as + (lane % 16) * 16 + 4 * (lane / 16));
-    const f32x4 bv = *(const f32x4*)(B0 + w * bs + (lane % 16) * 16 + 4 * (lane / 16));
-#pragma unroll
-    for (int mm = 0; mm < 4; ++mm) o = mma4f(av[mm], bv[mm], o);
+#pragma unroll 2
+  for (int s = 0; s < 4; ++s) {
+    const int w = 2 * s + wg;
+    const bf16x8 ah = *(const bf16x8*)(Ah + w * as + off), al = *(const bf16x8*)(Al + w * as + off);
+    const bf16x8 bh = *(const bf16x8*)(Bh + w * bs + off), bl = *(const bf16x8*)(Bl + w * bs + off);
+    o = mma32b(ah, bh, o);
+    o = mma32b(ah, bl, o);
+    o = mma32b(al, bh, o);
   }
   return o;
 }
@@ -664,21 +688,24 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
     // ---- the products over the 128 value columns, float32: every chunk
     // staged unscaled, then wavefront w forms output columns 16 w .. 16 w + 15
     // (channels) summing the chunks in order
-    stage_state(sm.st[wave], S, ff, lane);
-    stage_small(sm.sx[wave][0], dos, fd, lane);
-    stage_small(sm.sx[wave][1], dx, fd, lane);
-    stage_small(sm.sx[wave][2], Dl, ff, lane);
-    stage_small(sm.sx[wave][3], dd, fd, lane);
-    stage_small(sm.sx[wave][4], X, ff, lane);
+    stage_state(sm.sth[wave], sm.stl[wave], S, ff, lane);
+    stage_small(sm.sxh[wave][0], sm.sxl[wave][0], dos, fd, lane);
+    stage_small(sm.sxh[wave][1], sm.sxl[wave][1], dx, fd, lane);
+    stage_small(sm.sxh[wave][2], sm.sxl[wave][2], Dl, ff, lane);
+    stage_small(sm.sxh[wave][3], sm.sxl[wave][3], dd, fd, lane);
+    stage_small(sm.sxh[wave][4], sm.sxl[wave][4], X, ff, lane);
     lds_barrier();
     constexpr int kXs = 5 * kC * 16, kSs = kDK * 16;
-    const f32x4 y1 = prod128(sm.sx[0][0], kXs, sm.st[0] + 16 * wave * 16, kSs, lane);  // dO S^T
-    const f32x4 y2 = prod128(sm.sx[0][1], kXs, sm.st[0] + 16 * wave * 16, kSs, lane);  // dX S^T
+    const int srow = 16 * wave * 16;  // this wavefront's 16 output channels
+    const f32x4 y1 = prod128(sm.sxh[0][0], sm.sxl[0][0], kXs, sm.sth[0] + srow, sm.stl[0] + srow,
+                             kSs, lane);  // dO S^T
+    const f32x4 y2 = prod128(sm.sxh[0][1], sm.sxl[0][1], kXs, sm.sth[0] + srow, sm.stl[0] + srow,
+                             kSs, lane);  // dX S^T
     f32x4 ysm = zero4();  // wave 0: dDelta X^T, wave 1: dO Delta^T, wave 2: dE
     if (wave == 0) {
-      ysm = prod128(sm.sx[0][3], kXs, sm.sx[0][4], kXs, lane);
+      ysm = prod128(sm.sxh[0][3], sm.sxl[0][3], kXs, sm.sxh[0][4], sm.sxl[0][4], kXs, lane);
     } else if (wave == 1) {
-      ysm = prod128(sm.sx[0][0], kXs, sm.sx[0][2], kXs, lane);
+      ysm = prod128(sm.sxh[0][0], sm.sxl[0][0], kXs, sm.sxh[0][2], sm.sxl[0][2], kXs, lane);
     } else if (wave == 2) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
@@ -692,16 +719,13 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) qk[kb] = ld16h(R + kQK + kb * 1024 + lane * 16);
     lds_barrier();
-    stage_state(sm.st[wave], dS, fd, lane);
+    stage_state(sm.sth[wave], sm.stl[wave], dS, fd, lane);
     lds_barrier();
-    const f32x4 y3 = prod128(sm.sx[0][2], kXs, sm.st[0] + 16 * wave * 16, kSs, lane);  // Delta dS'^T
+    const f32x4 y3 = prod128(sm.sxh[0][2], sm.sxl[0][2], kXs, sm.sth[0] + srow, sm.stl[0] + srow,
+                             kSs, lane);  // Delta dS'^T
     // dV = dX: lane (t, g) holds the four columns from rc0 on of token t
-    bf16x4 dvo;
-    {
-      const f32x4 d = *(const f32x4*)&sm.sx[wave][1][lc * 16 + 4 * lg];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dvo[e] = (bf16_t)d[e];
-    }
+    // (the staged h of dX is its bfloat16 rounding)
+    const bf16x4 dvo = *(const bf16x4*)&sm.sxh[wave][1][lc * 16 + 4 * lg];
     // dS' of the tile before (the adjoint of this tile's start state)
     {
       const f16x8 bop = cat8(do16, to_h4(dx));
