@@ -422,7 +422,9 @@ def bench_packed(kda, torch, w, steps, prologue=False):
 
 def bench_backward(kda, torch, w, steps):
     """The backward pass (kda_recurrent_bwd) over a prefill workload's inputs,
-    with dO drawn like v and a final-state gradient; returns ms per call."""
+    with dO drawn like v and a final-state gradient; returns ms per call, and ms
+    per call of kda_recurrent_bwd_ckpt given the forward's states every 64 tokens
+    (kept by one kda_chunk_fwd_checkpoints call beforehand, outside the timing)."""
     from gated_delta_rule_112_amd.inputs import make_prefill_inputs
     dev = torch.device("cuda:0")
     x = make_prefill_inputs(w, device=dev)
@@ -434,19 +436,26 @@ def bench_backward(kda, torch, w, steps):
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        kda.recurrent_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], dout, x["s0"], dsf,
-                          workspace=ws, stream=stream)
+    scale = w.dk ** -0.5
+    _, _, ck = kda.chunk_fwd_checkpoints(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"],
+                                         every=64, scale=scale, output=False, stream=stream)
 
-    step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
+    def timed(ckpt):
+        def step():
+            kda.recurrent_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], dout, x["s0"], dsf,
+                              scale=scale, workspace=ws, stream=stream, ckpt=ckpt)
+
         step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    return timed(None), timed(ck)
 
 
 def bench_decode(kda, torch, w, repeats=1):
@@ -687,7 +696,7 @@ def main():
     backward = None
     if not a.no_backward:
         wb = WORKLOADS["small_prefill"]
-        bms = bench_backward(kda, torch, wb, 3)
+        bms, bcms = bench_backward(kda, torch, wb, 3)
         ntok = wb.B * wb.T
         # per token and head: q, k, v, dO read and dq, dk, dv written (io dtype),
         # g read and dg written (float32), beta and dbeta; plus s0, dS_T, ds0 per head
@@ -700,9 +709,11 @@ def main():
                     "algorithmic_bytes": bbytes, "achieved": round(bgbs, 1), "unit": "GB/s",
                     "peak": HBM_PEAK_GBS, "frac": round(bgbs / HBM_PEAK_GBS, 4),
                     "kernel": "kda_bwd_chunk",
-                    "traffic": measured_traffic("kda_bwd_chunk", wb.name)}
+                    "traffic": measured_traffic("kda_bwd_chunk", wb.name),
+                    "with_forward_checkpoints_ms": round(bcms, 4)}
         log(f"[bench] backward ({wb.name}): {bms:.3f} ms, "
-            f"{ntok / (bms * 1e-3) / 1e6:.3f} M tok/s")
+            f"{ntok / (bms * 1e-3) / 1e6:.3f} M tok/s; given the forward's checkpoints "
+            f"{bcms:.3f} ms")
 
     decode = None
     if not a.no_decode:

@@ -58,6 +58,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_recurrent_bwd.argtypes = [vp] * 14 + [i64, i64, i64, ci, ci, f32, ci, vp,
                                                  ctypes.c_size_t, vp]
     lib.kda_recurrent_bwd.restype = ci
+    lib.kda_recurrent_bwd_ckpt.argtypes = [vp] * 15 + [i64, i64, i64, ci, ci, f32, ci, vp,
+                                                      ctypes.c_size_t, vp]
+    lib.kda_recurrent_bwd_ckpt.restype = ci
     lib.kda_recurrent_bwd_workspace_size.argtypes = [i64, i64, i64, ci, ci]
     lib.kda_recurrent_bwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_chunk_fwd_varlen_prologue.argtypes = lib.kda_chunk_fwd_varlen.argtypes
@@ -431,10 +434,12 @@ def gate_rmsnorm(x, gate, norm_w=None, *, eps: float = 1e-6, out=None, stream=No
 
 
 def recurrent_bwd(q, k, v, g, beta, dout, s0=None, ds_final=None, *, scale: float = 1.0,
-                  workspace=None, stream=None):
+                  workspace=None, stream=None, ckpt=None):
     """Gradients of the token recurrence (kda_recurrent_bwd): q, k, v, dout [B, T, H, 128]
     (io dtype), g [B, T, H, 128] and beta [B, T, H] float32, s0 / ds_final [B, H, 128, 128]
-    float32 or None.  Returns (dq, dk, dv, dg, dbeta, ds0)."""
+    float32 or None.  ``ckpt``: the forward's states every 64 tokens [B, T // 64, H, 128, 128]
+    float32 (kda_chunk_fwd_checkpoints with every = 64), which the chunkwise pass then uses
+    instead of recomputing them (kda_recurrent_bwd_ckpt).  Returns (dq, dk, dv, dg, dbeta, ds0)."""
     lib = load_library()
     if q.device.type != "cuda":
         raise ValueError("kda ops need CUDA (HIP) tensors")
@@ -459,9 +464,18 @@ def recurrent_bwd(q, k, v, g, beta, dout, s0=None, ds_final=None, *, scale: floa
     nws = lib.kda_recurrent_bwd_workspace_size(B, T, H, dk, dv)
     if workspace is None:
         workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
-    st = lib.kda_recurrent_bwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(dout), _ptr(ds_final),
-        _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(dbeta), _ptr(ds0), B, T, H, dk, dv,
-        float(scale), _IO[io], _ptr(workspace), workspace.numel(), _stream(dev, stream))
-    _check(lib, "kda_recurrent_bwd", st)
+    if ckpt is None:
+        st = lib.kda_recurrent_bwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(dout), _ptr(ds_final),
+            _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(dbeta), _ptr(ds0), B, T, H, dk, dv,
+            float(scale), _IO[io], _ptr(workspace), workspace.numel(), _stream(dev, stream))
+        _check(lib, "kda_recurrent_bwd", st)
+    else:
+        _need(ckpt, "ckpt", torch.float32, (B, T // 64, H, dk, dv), dev)
+        st = lib.kda_recurrent_bwd_ckpt(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(dout), _ptr(ds_final),
+            _ptr(ckpt), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(dbeta), _ptr(ds0),
+            B, T, H, dk, dv, float(scale), _IO[io], _ptr(workspace), workspace.numel(),
+            _stream(dev, stream))
+        _check(lib, "kda_recurrent_bwd_ckpt", st)
     return dq, dk_, dv_, dg, dbeta, ds0

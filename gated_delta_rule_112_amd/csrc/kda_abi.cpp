@@ -118,15 +118,22 @@ size_t kda_recurrent_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int dk,
   return (size_t)(4 * n > c ? 4 * n : c);
 }
 
-kda_status kda_recurrent_bwd(const void* q, const void* k, const void* v, const float* g,
-                             const float* beta, const float* s0, const void* dout,
-                             const float* ds_final, void* dq, void* dk_out, void* dv_out,
-                             float* dg, float* dbeta, float* ds0, int64_t B, int64_t T,
-                             int64_t H, int dk, int dv, float scale, kda_dtype io,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// kda_recurrent_bwd and kda_recurrent_bwd_ckpt: ckpt is NULL for the former.
+kda_status recurrent_bwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* s0, const void* dout,
+                         const float* ds_final, void* dq, void* dk_out, void* dv_out, float* dg,
+                         float* dbeta, float* ds0, int64_t B, int64_t T, int64_t H, int dk, int dv,
+                         float scale, kda_dtype io, void* workspace, size_t workspace_bytes,
+                         const float* ckpt, bool with_ckpt, void* stream) {
   if (!q || !k || !v || !g || !beta || !dout || !dq || !dk_out || !dv_out || !dg || !dbeta)
     return KDA_ERR_NULL_POINTER;
+  if (with_ckpt && ckpt == nullptr) return KDA_ERR_NULL_POINTER;
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_BAD_DTYPE;
+  if (with_ckpt && io != KDA_BF16) return KDA_ERR_BAD_DTYPE;  // the chunkwise pass only
   if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED_DIM;
   if (dk != 128 || dv != 128) return KDA_ERR_UNSUPPORTED_DIM;
   const int64_t nqk = prod(B, T, H, dk), nb = prod(B, T, H), ns = prod(B, H, dk, dv);
@@ -141,12 +148,22 @@ kda_status kda_recurrent_bwd(const void* q, const void* k, const void* v, const 
   for (const void* p : {(const void*)g, (const void*)beta, (const void*)dg, (const void*)dbeta})
     if (!aligned(p, 4)) return KDA_ERR_MISALIGNED;
   for (const void* p : {(const void*)s0, (const void*)ds_final, (const void*)ds0,
-                        (const void*)workspace})
+                        (const void*)workspace, (const void*)ckpt})
     if (!aligned(p, 16)) return KDA_ERR_MISALIGNED;
+  // bfloat16 with 16-byte aligned token tensors: the chunkwise matrix-core pass;
+  // otherwise (and with KDA_BWD_TOKEN=1) the token-serial vector kernel
+  bool tok_aligned = true;
+  for (const void* p : {q, k, v, dout, (const void*)g, (const void*)dq, (const void*)dk_out,
+                        (const void*)dv_out})
+    tok_aligned = tok_aligned && aligned(p, 16);
+  if (with_ckpt && !tok_aligned) return KDA_ERR_MISALIGNED;
+  const bool chunk = with_ckpt || (io == KDA_BF16 && !force_token_bwd() && tok_aligned);
 
   const int64_t es = (io == KDA_BF16) ? 2 : 4;
+  const int64_t nck = with_ckpt ? B * (T / 64) * H * dk * dv : 0;
   const Span in[] = {{q, nqk * es}, {k, nqk * es}, {v, nqk * es}, {g, nqk * 4}, {beta, nb * 4},
-                     {s0, ns * 4}, {dout, nqk * es}, {ds_final, ns * 4}};
+                     {s0, ns * 4}, {dout, nqk * es}, {ds_final, ns * 4},
+                     {nck > 0 ? ckpt : nullptr, nck * 4}};
   const Span out[] = {{dq, nqk * es}, {dk_out, nqk * es}, {dv_out, nqk * es}, {dg, nqk * 4},
                       {dbeta, nb * 4}, {ds0, ns * 4}, {workspace, (int64_t)need}};
   for (int i = 0; i < 7; ++i) {
@@ -158,14 +175,35 @@ kda_status kda_recurrent_bwd(const void* q, const void* k, const void* v, const 
 
   kda::BwdArgs a{q, k, v, g, beta, s0, dout, ds_final, dq, dk_out, dv_out, dg, dbeta, ds0,
                  B, T, H, scale, io == KDA_BF16, (float*)workspace, stream};
-  // bfloat16 with 16-byte aligned token tensors: the chunkwise matrix-core pass;
-  // otherwise (and with KDA_BWD_TOKEN=1) the token-serial vector kernel
-  bool chunk = io == KDA_BF16 && !force_token_bwd();
-  for (const void* p : {q, k, v, dout, (const void*)g, (const void*)dq, (const void*)dk_out,
-                        (const void*)dv_out})
-    chunk = chunk && aligned(p, 16);
+  a.ckpt = with_ckpt ? ckpt : nullptr;
   const hipError_t err = chunk ? kda::launch_bwd_chunk(a) : kda::launch_recurrent_bwd(a);
   return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_recurrent_bwd(const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const float* s0, const void* dout,
+                             const float* ds_final, void* dq, void* dk_out, void* dv_out,
+                             float* dg, float* dbeta, float* ds0, int64_t B, int64_t T,
+                             int64_t H, int dk, int dv, float scale, kda_dtype io,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return recurrent_bwd(q, k, v, g, beta, s0, dout, ds_final, dq, dk_out, dv_out, dg, dbeta, ds0,
+                       B, T, H, dk, dv, scale, io, workspace, workspace_bytes, nullptr, false,
+                       stream);
+}
+
+kda_status kda_recurrent_bwd_ckpt(const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, const float* s0, const void* dout,
+                                  const float* ds_final, const float* ckpt, void* dq,
+                                  void* dk_out, void* dv_out, float* dg, float* dbeta,
+                                  float* ds0, int64_t B, int64_t T, int64_t H, int dk, int dv,
+                                  float scale, kda_dtype io, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return recurrent_bwd(q, k, v, g, beta, s0, dout, ds_final, dq, dk_out, dv_out, dg, dbeta, ds0,
+                       B, T, H, dk, dv, scale, io, workspace, workspace_bytes, ckpt, true, stream);
 }
 
 int64_t kda_chunk_fwd_launches(int64_t B, int64_t T, int64_t H, int dk, int dv, kda_dtype io) {

@@ -446,7 +446,8 @@ struct BlockArgs {
   const bf16_t* v;
   const bf16_t* dout;
   const float* s0;      // [B H][dk][dv] or NULL
-  const float* s_ck;    // [B][T / 64][H] states in accumulator order: the state after every 64 tokens
+  const float* s_ck;    // [B][T / 64][H] states: the state after every 64 tokens
+  bool ck_rowmajor;     // s_ck [dk][dv] row-major (the caller's); else in accumulator order
   const float* ds_blk;  // [B H][nblk] states in accumulator order
   bf16_t* dv;
   float* ybuf;          // [B H][nt][kYFloats]
@@ -582,7 +583,7 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
   const float* s_start = blk == 0 ? (a.s0 != nullptr ? a.s0 + bh * kDD : nullptr)
                                   : a.s_ck + ((b * a.nck + blk - 1) * a.H + h) * kDD;
   auto load_start = [&](f32x4 (&z)[8]) {
-    if (blk == 0)
+    if (blk == 0 || a.ck_rowmajor)
       load_state(z, s_start, wave, lane);
     else
       load_frag(z, s_start, wave, lane);
@@ -977,17 +978,19 @@ hipError_t launch_bwd_chunk(const BwdArgs& a) {
   unsigned char* ws = (unsigned char*)a.workspace;
   hipStream_t st = (hipStream_t)a.stream;
 
-  // 1. forward states every 64 tokens
-  ChunkArgs ca{a.q, a.k, a.v, a.g, a.beta, a.s0, nullptr, (float*)(ws + w.s_tmp), nullptr,
-               nullptr, 0.f, a.B, a.T, a.H, kDK, kDV, 1.f, true, ws + w.fwd, a.stream};
-  ca.total = a.B * a.T;
-  if (nck > 0) {
-    ca.ckpt = (float*)(ws + w.s_ck);
-    ca.ckpt_every = kBlkTok;
-    ca.ckpt_frag = true;
+  // 1. forward states every 64 tokens (unless the caller brings them)
+  hipError_t e;
+  if (a.ckpt == nullptr) {
+    ChunkArgs ca{a.q, a.k, a.v, a.g, a.beta, a.s0, nullptr, (float*)(ws + w.s_tmp), nullptr,
+                 nullptr, 0.f, a.B, a.T, a.H, kDK, kDV, 1.f, true, ws + w.fwd, a.stream};
+    ca.total = a.B * a.T;
+    if (nck > 0) {
+      ca.ckpt = (float*)(ws + w.s_ck);
+      ca.ckpt_every = kBlkTok;
+      ca.ckpt_frag = true;
+    }
+    if ((e = launch_chunk_mfma(ca)) != hipSuccess) return e;
   }
-  hipError_t e = launch_chunk_mfma(ca);
-  if (e != hipSuccess) return e;
 
   // 2. records
   RecArgs ra{(const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, ws + w.recs,
@@ -1006,7 +1009,8 @@ hipError_t launch_bwd_chunk(const BwdArgs& a) {
 
   // 4. block products
   BlockArgs ba{ws + w.recs, (const bf16_t*)a.v, (const bf16_t*)a.dout, a.s0,
-               (const float*)(ws + w.s_ck), (const float*)(ws + w.ds_blk), (bf16_t*)a.dv,
+               a.ckpt != nullptr ? a.ckpt : (const float*)(ws + w.s_ck), a.ckpt != nullptr,
+               (const float*)(ws + w.ds_blk), (bf16_t*)a.dv,
                (float*)(ws + w.ybuf), a.B, a.T, a.H, nt, nblk, nck, a.scale};
   hipLaunchKernelGGL(kda_bwd_block_kernel, dim3((unsigned)(BH * nblk)), dim3(512), 0, st, ba);
   if ((e = hipGetLastError()) != hipSuccess) return e;

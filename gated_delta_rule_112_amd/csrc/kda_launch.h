@@ -114,6 +114,9 @@ struct BwdArgs {
   bool io_bf16;
   float* workspace;  // bwd_workspace_floats(B, T, H) floats
   void* stream;
+  // The caller's forward states after every 64 tokens, [B, T / 64, H, dk, dv]
+  // ([dk, dv] row-major), or NULL: recomputed (chunkwise path only).
+  const float* ckpt = nullptr;
 };
 // Pieces of the reverse sweep: the state is checkpointed every kBwdPiece tokens.
 constexpr int kBwdPiece = 64;

@@ -417,6 +417,30 @@ kda_status kda_recurrent_bwd(const void* q, const void* k, const void* v, const 
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_recurrent_bwd_ckpt -- kda_recurrent_bwd given the forward's states, for a
+ * training step that runs the forward anyway: the chunkwise pass then skips its
+ * own forward pass (one fifth to one sixth of its time at B=2, H=32, T=4096).
+ *
+ * Every argument of kda_recurrent_bwd, with the same meaning, plus
+ *   ckpt   [B, T / 64, H, 128, 128] float32: entry [b, i, h] the state of (b, h) after
+ *          its first 64 (i + 1) tokens, as kda_chunk_fwd_checkpoints with
+ *          ckpt_every = 64 writes it over the same q, k, v, g, beta and s0 (not
+ *          checked: other states give the gradients of another forward).  16-byte
+ *          aligned; must not overlap an output.  Read only when T > 64.
+ * bfloat16 io with q, k, v, dout, g, dq, dk, dv 16-byte aligned only (the chunkwise
+ * pass): else KDA_ERR_BAD_DTYPE or KDA_ERR_MISALIGNED.  The workspace is the one
+ * kda_recurrent_bwd_workspace_size gives.  With the forward's own checkpoints the
+ * gradients equal kda_recurrent_bwd's.
+ */
+kda_status kda_recurrent_bwd_ckpt(const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, const float* s0, const void* dout,
+                                  const float* ds_final, const float* ckpt, void* dq,
+                                  void* dk_out, void* dv_out, float* dg, float* dbeta,
+                                  float* ds0, int64_t B, int64_t T, int64_t H, int dk, int dv,
+                                  float scale, kda_dtype io, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * kda_recurrent_bwd_workspace_size -- bytes of workspace kda_recurrent_bwd
  * needs: the larger of its two kernels' needs.  Token-serial: per (b, h), float32
  * states for ceil(T / 64) checkpoints plus 64 recomputed tokens (64 KiB each), then

@@ -132,3 +132,26 @@ def test_backward_small_prefill_workload_sampled(kda):
             io_out = name in ("dq", "dk", "dv")
             assert_close(f64(part), ref[name], TOL[torch.bfloat16],
                          f"{name} (b={b}, h={h}) full size", torch.bfloat16 if io_out else None)
+
+
+@pytest.mark.parametrize("B,T,H,with_s0,with_dsf", [(2, 300, 3, True, True), (1, 200, 2, False, False),
+                                                    (1, 64, 2, True, True)])
+def test_backward_with_forward_checkpoints(kda, B, T, H, with_s0, with_dsf):
+    """kda_recurrent_bwd_ckpt with the states kda_chunk_fwd_checkpoints keeps every
+    64 tokens: the same gradients as kda_recurrent_bwd, bit for bit (the same
+    forward arithmetic produced both sets of states), and within the bar of the
+    gradient oracle."""
+    q, k, v, g, beta, do, s0, dsf = gen(B, T, H, torch.bfloat16, 4500 + T, with_s0, with_dsf)
+    _, _, ck = kda.chunk_fwd_checkpoints(q, k, v, g, beta, s0, every=64, output=False)
+    got = kda.recurrent_bwd(q, k, v, g, beta, do, s0, dsf, scale=0.7, ckpt=ck)
+    ref_gpu = kda.recurrent_bwd(q, k, v, g, beta, do, s0, dsf, scale=0.7)
+    torch.cuda.synchronize()
+    for name, a_, b_ in zip(["dq", "dk", "dv", "dg", "dbeta", "ds0"], got, ref_gpu):
+        assert torch.equal(a_, b_), f"{name} differs from kda_recurrent_bwd"
+    ref = kda_recurrent_vjp(f64(q), f64(k), f64(v), f64(g), f64(beta),
+                            None if s0 is None else f64(s0), f64(do),
+                            None if dsf is None else f64(dsf), 0.7)
+    for name, x in zip(["dq", "dk", "dv", "dg", "dbeta", "ds0"], got):
+        io_out = name in ("dq", "dk", "dv")
+        assert_close(f64(x), ref[name], TOL[torch.bfloat16], f"{name} with checkpoints T={T}",
+                     torch.bfloat16 if io_out else None)
