@@ -199,8 +199,69 @@ struct Scale {
   float sig = 1.f, isig = 1.f;
 };
 
-// Chooses the scale for accumulators z and incoming values w (unscaled),
-// rescales z when it moves, and returns sigma w.
+// Whether scale_shift() keeps the scale, given each lane's largest magnitude
+// m (>= 0): the wavefront's largest lies in [2^kLoExp, 2^(kHiExp + 1)), or
+// every value is zero.  Three lane votes instead of a reduction across lanes.
+__device__ __forceinline__ bool scale_kept(float m) {
+  static_assert(kLoExp >= 0 && kHiExp + 1 < 31, "bounds as integers");
+  constexpr float kLo = (float)(1 << kLoExp), kHi = (float)(1 << (kHiExp + 1));
+  if (__builtin_amdgcn_ballot_w64(m >= kHi) != 0) return false;
+  return __builtin_amdgcn_ballot_w64(m >= kLo) != 0 || __builtin_amdgcn_ballot_w64(m > 0.f) == 0;
+}
+
+// Chooses the scale for accumulators z and incoming values w (unscaled) of a
+// wavefront that holds N 16-column blocks (one scale for all), rescales z
+// when the scale moves, and sets ws[n] = sigma w[n].
+template <int N>
+__device__ __forceinline__ void rescale_n(Scale& sc, f32x4 (&z)[N][8], const f32x4 (&w)[N],
+                                          f32x4 (&ws)[N]) {
+  float m0 = 0.f, m1 = 0.f;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    ws[n] = w[n] * sc.sig;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m0 = fmaxf(m0, fabsf(ws[n][r]));
+#pragma unroll
+    for (int kb = 0; kb < 8; kb += 2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        m0 = fmaxf(m0, fabsf(z[n][kb][r]));
+        m1 = fmaxf(m1, fabsf(z[n][kb + 1][r]));
+      }
+  }
+  if (scale_kept(fmaxf(m0, m1))) return;
+  const int em = exp_of(wave_max_nonneg(fmaxf(m0, m1)));
+  if (scale_shift(em, sc.sh) != 0) {  // rare: measured again with w unscaled
+    float mz = 0.f, mw = 0.f;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mw = fmaxf(mw, fabsf(w[n][r]));
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mz = fmaxf(mz, fabsf(z[n][kb][r]));
+    }
+    const int ez = exp_of(wave_max_nonneg(mz));
+    int ew = exp_of(wave_max_nonneg(mw));
+    ew = ew == kNoExp ? kNoExp : ew + sc.sh;
+    const int d = scale_shift(ez > ew ? ez : ew, sc.sh);
+    if (d != 0) {
+      const float f = exp2i(d);
+#pragma unroll
+      for (int n = 0; n < N; ++n)
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) z[n][kb] *= f;
+      sc.sh += d;
+      sc.sig = exp2i(sc.sh);
+      sc.isig = exp2i(-sc.sh);
+    }
+#pragma unroll
+    for (int n = 0; n < N; ++n) ws[n] = w[n] * sc.sig;
+  }
+}
+
+// rescale_n() for one block, without the lane-vote shortcut: returns sigma w.
 __device__ __forceinline__ f32x4 rescale(Scale& sc, f32x4 (&z)[8], f32x4 w) {
   f32x4 ws = w * sc.sig;
   float m0 = 0.f, m1 = 0.f;
@@ -214,7 +275,7 @@ __device__ __forceinline__ f32x4 rescale(Scale& sc, f32x4 (&z)[8], f32x4 w) {
       m1 = fmaxf(m1, fabsf(z[kb + 1][r]));
     }
   const int em = exp_of(wave_max_nonneg(fmaxf(m0, m1)));
-  if (scale_shift(em, sc.sh) != 0) {  // rare: measured again with w unscaled
+  if (scale_shift(em, sc.sh) != 0) {
     float mz = 0.f, mw = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) mw = fmaxf(mw, fabsf(w[r]));
@@ -316,39 +377,90 @@ struct ChainArgs {
   float scale;
 };
 
-constexpr int kRowBytes = kDV * 2;
+// The value columns of the adjoint recurrence are independent of each other
+// (every product acts on them column by column), so each head's walk is split
+// over kChainSplit workgroups of 128 / kChainSplit columns.
+constexpr int kChainSplit = 4;
+constexpr int kChainCols = kDV / kChainSplit;
+constexpr int kRowBytes = kChainCols * 2;  // a dO row of one workgroup's columns
 // The chain's part of a tile in an LDS slot, in 1 KB blocks: record blocks
 // 4 .. 15 (Kb, then [Qh^T | -Kh^T]), record blocks 20 and 21 (T, T^T, Aqk^T,
-// E), then the tile's 16 dO rows.
+// E), then the workgroup's columns of the tile's 16 dO rows.
 constexpr int kSlotKb = 0, kSlotQK = 4096, kSlotTt = 12288 + (kTt - 20480),
               kSlotAqkT = 12288 + (kAqkT - 20480), kSlotE = 12288 + (kE - 20480), kSlotDO = 14336;
-constexpr int kChainBlocks = 18, kChainSlot = kChainBlocks * 1024;
+constexpr int kChainDOBlocks = 16 * kRowBytes / 1024;
+constexpr int kChainBlocks = 14 + kChainDOBlocks, kChainSlot = kChainBlocks * 1024;
 constexpr int kChainRing = 8;     // slots: seven tiles in flight ahead of the one in use
-constexpr int kChainLoaders = 6;  // loader wavefronts
+constexpr int kChainNcb = 1;      // 16-column blocks per compute wavefront
+constexpr int kChainWaves = kChainCols / 16 / kChainNcb;  // compute wavefronts
+constexpr int kChainLoaders = 3;  // loader wavefronts
 constexpr int kChainPer = kChainBlocks / kChainLoaders;  // loads per loader wavefront per tile
+static_assert(kChainDOBlocks * 1024 == 16 * kRowBytes && kChainWaves * kChainNcb * 16 == kChainCols,
+              "whole dO blocks and column blocks");
 static_assert(kKb == 4096 && kQK == 8192 && kKbC == 16384 && kT == 20480 && kTlo == 22528,
               "the chain's record blocks");
 static_assert(kChainPer * kChainLoaders == kChainBlocks, "whole loads per loader wavefront");
 static_assert((kChainRing - 1) * kChainPer <= 63, "loads in flight per wavefront exceed vmcnt");
+
+// z * E for rows 4 g + r of state block KB (r < 4), from the two values per
+// lane described at the chain's E read: four multiplies whose first source
+// is lane 2 KB + r / 2 of the DPP row (row_newbcast), so the broadcast costs
+// no instruction of its own.  The s_nops cover the wait states of a DPP
+// source after a vector-ALU write of it and of a matrix-core operand after
+// the multiplies that write it (the compiler does not see into the block).
+template <int KB>
+__device__ __forceinline__ f32x4 decay_rows(f32x2 e2, f32x4 z) {
+  f32x4 y;
+  asm("s_nop 1\n\t"
+      "v_mul_f32_dpp %0, %4, %6 row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %5, %7 row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %2, %4, %9 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %3, %5, %10 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1"
+      : "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3])
+      : "v"(e2[0]), "v"(e2[1]), "v"(z[0]), "v"(z[1]), "i"(2 * KB), "v"(z[2]), "v"(z[3]),
+        "i"(2 * KB + 1));
+  return y;
+}
 
 // s_waitcnt with vmcnt = N, the other counters left alone (gfx9 encoding).
 constexpr unsigned vmcnt_only(int n) {
   return (unsigned)((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// One workgroup per (b, h): eight wavefronts of 16 value columns each walk the
-// tiles last to first, while six loader wavefronts keep the next seven tiles'
-// record parts and dO rows streaming into a ring of LDS slots with
+// kChainSplit workgroups per (b, h), each on its own kChainCols value
+// columns: its compute wavefronts (kChainNcb 16-column blocks each) walk the
+// tiles last to first, while its loader wavefronts keep the next seven tiles'
+// record parts and dO columns streaming into a ring of LDS slots with
 // direct-to-LDS loads.  One barrier per tile: after it, the tile just used
-// frees its slot and the next tile is in LDS.
-__global__ void __launch_bounds__(64 * (8 + kChainLoaders), 1) kda_bwd_chain_kernel(ChainArgs a) {
+// frees its slot and the next tile is in LDS.  The workgroups of one head
+// get block indices equal modulo 8, which places them on one XCD (blocks are
+// dealt to the XCDs in turn), so that the head's records are read from HBM
+// once and from that XCD's L2 by the others.
+__global__ void __launch_bounds__(64 * (kChainWaves + kChainLoaders), 1)
+kda_bwd_chain_kernel(ChainArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kChainRing][kChainSlot];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const int lane = threadIdx.x % 64, lc = lane % 16, lg = lane / 16;
-  const int64_t bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+  // block -> (head, part): groups of 8 heads take 8 kChainSplit consecutive
+  // blocks, head j of a group at blocks j + 8 part (a last, smaller group
+  // when B H is not a multiple of 8 takes its blocks in head order)
+  const int64_t BH = a.B * a.H, grp = blockIdx.x / (8 * kChainSplit);
+  const int64_t in_grp = blockIdx.x % (8 * kChainSplit);
+  int64_t bh;
+  int part;
+  if ((grp + 1) * 8 <= BH) {
+    bh = grp * 8 + in_grp % 8;
+    part = (int)(in_grp / 8);
+  } else {
+    bh = grp * 8 + in_grp / kChainSplit;
+    part = (int)(in_grp % kChainSplit);
+  }
+  const int64_t b = bh / a.H, h = bh % a.H;
+  const int cg0 = part * (kChainCols / 16) + wave * kChainNcb;  // first 16-column group
 
-  if (wave >= 8) {  // ------------------------------------------ loader waves
-    const int lw = wave - 8;
+  if (wave >= kChainWaves) {  // -------------------------------- loader waves
+    const int lw = wave - kChainWaves;
     auto issue = [&](int64_t x) {
       const unsigned char* R = a.recs + (bh * a.nt + x) * (int64_t)kRecBytes;
       unsigned char* slot = lds[x % kChainRing];
@@ -360,10 +472,12 @@ __global__ void __launch_bounds__(64 * (8 + kChainLoaders), 1) kda_bwd_chain_ker
           src = R + 4096 + blk * 1024 + lane * 16;
         } else if (blk < 14) {
           src = R + 20480 + (blk - 12) * 1024 + lane * 16;
-        } else {  // 4 dO rows per block, 16 chunks of 16 bytes per row
-          int64_t tok = x * kC + (blk - 14) * 4 + lane / 16;
+        } else {  // 16-byte chunks of dO rows, kRowBytes / 16 per row
+          constexpr int kLanesPerRow = kRowBytes / 16, kRowsPerBlock = 64 / kLanesPerRow;
+          int64_t tok = x * kC + (blk - 14) * kRowsPerBlock + lane / kLanesPerRow;
           tok = tok < a.T ? tok : a.T - 1;
-          src = (const unsigned char*)(a.dout + ((b * a.T + tok) * a.H + h) * kDV + lc * 8);
+          src = (const unsigned char*)(a.dout + ((b * a.T + tok) * a.H + h) * kDV +
+                                       part * kChainCols + (lane % kLanesPerRow) * 8);
         }
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                          (__attribute__((address_space(3))) void*)(slot +
@@ -400,44 +514,97 @@ __global__ void __launch_bounds__(64 * (8 + kChainLoaders), 1) kda_bwd_chain_ker
   // The adjoint quantities are held in units of scale / sigma, so that dO
   // (bfloat16) enters the float16 operands exactly: sigma dO instead of a
   // rounded sigma scale dO.  so = scale, or 1 with dO dropped when scale = 0.
+  // Column block n of this wavefront is 16-column group cg0 + n.
   const float so = a.scale != 0.f ? a.scale : 1.f, dmul = a.scale != 0.f ? 1.f : 0.f;
-  f32x4 dS[8];
-  load_state(dS, a.dsf != nullptr ? a.dsf + bh * kDD : nullptr, wave, lane);
+  f32x4 dS[kChainNcb][8];
 #pragma unroll
-  for (int kb = 0; kb < 8; ++kb) dS[kb] *= 1.f / so;
+  for (int n = 0; n < kChainNcb; ++n) {
+    load_state(dS[n], a.dsf != nullptr ? a.dsf + bh * kDD : nullptr, cg0 + n, lane);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) dS[n][kb] *= 1.f / so;
+  }
   Scale sc;
   const bf16x4 ident = ident_op(lane);
+  // dS' at the end of block blk (the state entering its last tile)
+  auto store_ds = [&](int64_t blk) {
+#pragma unroll
+    for (int n = 0; n < kChainNcb; ++n)
+      store_frag(a.ds_blk + (bh * a.nblk + blk) * kDD, dS[n], so * sc.isig, cg0 + n, lane);
+  };
+  store_ds(a.nblk - 1);
   lds_barrier();  // tile nt - 1 is in LDS
   for (int64_t x = a.nt - 1; x >= 0; --x) {
     const unsigned char* R = lds[x % kChainRing];
-    // dS' at the end of the block this tile ends
-    const int64_t blk = x / kBlkTiles;
-    int64_t last = blk * kBlkTiles + kBlkTiles - 1;
-    last = last < a.nt - 1 ? last : a.nt - 1;
-    if (x == last) store_frag(a.ds_blk + (bh * a.nblk + blk) * kDD, dS, so * sc.isig, wave, lane);
+    // All of the tile's operand reads first (15, as many as the LDS counter
+    // tracks), those of the first products first: their latency is then
+    // exposed once, and the state update's operands arrive during the
+    // dependent chain.
+    bf16x4 dor[kChainNcb];  // dO rows: lane (c, g): dO[c][4 g + e] of block n's columns
+#pragma unroll
+    for (int n = 0; n < kChainNcb; ++n)
+      dor[n] = *(const bf16x4*)(R + kSlotDO + lc * kRowBytes +
+                                (row_col(cg0 + n, lg) - part * kChainCols) * 2);
+    f16x8 kbo[4], qk[8];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kbo[s] = ld16h(R + kSlotKb + s * 1024 + lane * 16);
+    const f16x8 aq = lo8(ld8h(R + kSlotAqkT + lane * 8)), tt = lo8(ld8h(R + kSlotTt + lane * 8));
+    // E of the channels of row group g, two per lane: lane (c, g) holds
+    // E[32 (c / 4) + 8 g + 2 (c % 4) + {0, 1}], so that the value for row
+    // 4 g + r of block kb sits in lane 2 kb + r / 2 of the same DPP row
+    const f32x2 e2 = *(const f32x2*)(R + kSlotE + 4 * (32 * (lc / 4) + 8 * lg + 2 * (lc % 4)));
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) qk[kb] = ld16h(R + kSlotQK + kb * 1024 + lane * 16);
+    // keep the reads here: neither the compiler's code motion nor its
+    // scheduler may move them down to their uses
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 
     // dO in the k-operand layout: lane (c, g): dO[4 g + r][column index c]
-    const bf16x4 dor = *(const bf16x4*)(R + kSlotDO + lc * kRowBytes + row_col(wave, lg) * 2);
-    const f32x4 dof = mma16b(dor, ident, zero4()) * dmul;
-    const f16x4 do16 = to_h4(rescale(sc, dS, dof));
-    f16x8 sop[4];
-    state_op(dS, sop);
-    f32x4 dd = zero4();
+    f32x4 dof[kChainNcb], dos[kChainNcb];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) dd = mma32h(ld16h(R + kSlotKb + s * 1024 + lane * 16), sop[s], dd);
-    dd = mma32h(lo8(ld8h(R + kSlotAqkT + lane * 8)), cat8(do16, do16), dd);
-    const f16x4 dd16 = to_h4(dd);
-    const f32x4 dx = mma32h(lo8(ld8h(R + kSlotTt + lane * 8)), cat8(dd16, dd16), zero4());
-    const f16x8 bop = cat8(do16, to_h4(dx));
+    for (int n = 0; n < kChainNcb; ++n) dof[n] = mma16b(dor[n], ident, zero4()) * dmul;
+    rescale_n<kChainNcb>(sc, dS, dof, dos);
+    f16x4 do16[kChainNcb];
+    f16x8 sop[kChainNcb][4];
+    f32x4 dd[kChainNcb];
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-      const f32x4 e4 =
-          *(const f32x4*)(R + kSlotE + 4 * (32 * (kb / 2) + 8 * lg + 4 * (kb % 2)));
-      dS[kb] = mma32h(ld16h(R + kSlotQK + kb * 1024 + lane * 16), bop, dS[kb] * e4);
+    for (int n = 0; n < kChainNcb; ++n) {
+      do16[n] = to_h4(dos[n]);
+      state_op(dS[n], sop[n]);
+      dd[n] = zero4();
     }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int n = 0; n < kChainNcb; ++n) dd[n] = mma32h(kbo[s], sop[n][s], dd[n]);
+    f16x8 bop[kChainNcb];
+#pragma unroll
+    for (int n = 0; n < kChainNcb; ++n) {
+      dd[n] = mma32h(aq, cat8(do16[n], do16[n]), dd[n]);
+      const f16x4 dd16 = to_h4(dd[n]);
+      const f32x4 dx = mma32h(tt, cat8(dd16, dd16), zero4());
+      bop[n] = cat8(do16[n], to_h4(dx));
+    }
+#pragma unroll
+    for (int n = 0; n < kChainNcb; ++n) {
+      dS[n][0] = mma32h(qk[0], bop[n], decay_rows<0>(e2, dS[n][0]));
+      dS[n][1] = mma32h(qk[1], bop[n], decay_rows<1>(e2, dS[n][1]));
+      dS[n][2] = mma32h(qk[2], bop[n], decay_rows<2>(e2, dS[n][2]));
+      dS[n][3] = mma32h(qk[3], bop[n], decay_rows<3>(e2, dS[n][3]));
+      dS[n][4] = mma32h(qk[4], bop[n], decay_rows<4>(e2, dS[n][4]));
+      dS[n][5] = mma32h(qk[5], bop[n], decay_rows<5>(e2, dS[n][5]));
+      dS[n][6] = mma32h(qk[6], bop[n], decay_rows<6>(e2, dS[n][6]));
+      dS[n][7] = mma32h(qk[7], bop[n], decay_rows<7>(e2, dS[n][7]));
+    }
+    // dS' entering tile x - 1, the last tile of block x / kBlkTiles - 1
+    if (x > 0 && x % kBlkTiles == 0) store_ds(x / kBlkTiles - 1);
     lds_barrier();
   }
-  if (a.ds0 != nullptr) store_state(a.ds0 + bh * kDD, dS, so * sc.isig, wave, lane);
+  if (a.ds0 != nullptr) {
+#pragma unroll
+    for (int n = 0; n < kChainNcb; ++n)
+      store_state(a.ds0 + bh * kDD, dS[n], so * sc.isig, cg0 + n, lane);
+  }
 }
 
 // ---------------------------------------------------------- 4. block products
@@ -1003,7 +1170,8 @@ hipError_t launch_bwd_chunk(const BwdArgs& a) {
   // 3. the adjoint chain
   ChainArgs cha{ws + w.recs, (const bf16_t*)a.dout, a.ds_final, (float*)(ws + w.ds_blk), a.ds0,
                 a.B, a.T, a.H, nt, nblk, a.scale};
-  hipLaunchKernelGGL(kda_bwd_chain_kernel, dim3((unsigned)BH), dim3(64 * (8 + kChainLoaders)), 0,
+  hipLaunchKernelGGL(kda_bwd_chain_kernel, dim3((unsigned)(BH * kChainSplit)),
+                     dim3(64 * (kChainWaves + kChainLoaders)), 0,
                      st, cha);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
