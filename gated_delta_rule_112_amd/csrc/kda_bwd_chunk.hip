@@ -261,43 +261,13 @@ __device__ __forceinline__ void rescale_n(Scale& sc, f32x4 (&z)[N][8], const f32
   }
 }
 
-// rescale_n() for one block, without the lane-vote shortcut: returns sigma w.
+// rescale_n() for one block: returns sigma w.
 __device__ __forceinline__ f32x4 rescale(Scale& sc, f32x4 (&z)[8], f32x4 w) {
-  f32x4 ws = w * sc.sig;
-  float m0 = 0.f, m1 = 0.f;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) m0 = fmaxf(m0, fabsf(ws[r]));
-#pragma unroll
-  for (int kb = 0; kb < 8; kb += 2)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      m0 = fmaxf(m0, fabsf(z[kb][r]));
-      m1 = fmaxf(m1, fabsf(z[kb + 1][r]));
-    }
-  const int em = exp_of(wave_max_nonneg(fmaxf(m0, m1)));
-  if (scale_shift(em, sc.sh) != 0) {
-    float mz = 0.f, mw = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mw = fmaxf(mw, fabsf(w[r]));
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mz = fmaxf(mz, fabsf(z[kb][r]));
-    const int ez = exp_of(wave_max_nonneg(mz));
-    int ew = exp_of(wave_max_nonneg(mw));
-    ew = ew == kNoExp ? kNoExp : ew + sc.sh;
-    const int d = scale_shift(ez > ew ? ez : ew, sc.sh);
-    if (d != 0) {
-      const float f = exp2i(d);
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb) z[kb] *= f;
-      sc.sh += d;
-      sc.sig = exp2i(sc.sh);
-      sc.isig = exp2i(-sc.sh);
-    }
-    ws = w * sc.sig;
-  }
-  return ws;
+  f32x4(&zn)[1][8] = *reinterpret_cast<f32x4(*)[1][8]>(&z);
+  const f32x4 wn[1] = {w};
+  f32x4 ws[1];
+  rescale_n<1>(sc, zn, wn, ws);
+  return ws[0];
 }
 
 // The k-operand image of a wavefront's 16 value columns of a [dk, dv] state
@@ -421,6 +391,15 @@ __device__ __forceinline__ f32x4 decay_rows(f32x2 e2, f32x4 z) {
       : "v"(e2[0]), "v"(e2[1]), "v"(z[0]), "v"(z[1]), "i"(2 * KB), "v"(z[2]), "v"(z[3]),
         "i"(2 * KB + 1));
   return y;
+}
+
+// f(integral_constant<int, KB>) for KB = 0 .. 7.
+template <int KB = 0, class F>
+__device__ __forceinline__ void unroll8(F&& f) {
+  if constexpr (KB < 8) {
+    f(std::integral_constant<int, KB>{});
+    unroll8<KB + 1>(f);
+  }
 }
 
 // s_waitcnt with vmcnt = N, the other counters left alone (gfx9 encoding).
@@ -822,13 +801,12 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
       Dl = mma32h(lo8(ld8h(Ru + kFwTlo + lane * 8)), cat8(xh, xh), Dl);
       if (u < tl) {
         const f16x4 dh = to_h4(Dl), dlo = to_h4(Dl - to_f4(dh));
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-          const f32x4 e4 =
-              *(const f32x4*)(Ru + kFwE + 4 * (32 * (kb / 2) + 8 * lg + 4 * (kb % 2)));
+        const f32x2 e2 = *(const f32x2*)(Ru + kFwE + 4 * (32 * (lc / 4) + 8 * lg + 2 * (lc % 4)));
+        unroll8([&](auto kbc) {
+          constexpr int kb = decltype(kbc)::value;
           const f16x4 k4 = ld8h(Ru + kFwKbC + kb * 512 + lane * 8);
-          S[kb] = mma32h(cat8(k4, k4), cat8(dh, dlo), S[kb] * e4);  // Kb^T (dh + dlo)
-        }
+          S[kb] = mma32h(cat8(k4, k4), cat8(dh, dlo), decay_rows<kb>(e2, S[kb]));  // Kb^T (dh + dlo)
+        });
       }
     }
     // ---- the adjoint step of tile tl
@@ -926,12 +904,12 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
     // dS' of the tile before (the adjoint of this tile's start state)
     {
       const f16x8 bop = cat8(do16, to_h4(dx));
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        const f32x4 e4 =
-            *(const f32x4*)(sm.fw[tl] + kFwE + 4 * (32 * (kb / 2) + 8 * lg + 4 * (kb % 2)));
-        dS[kb] = mma32h(qk[kb], bop, dS[kb] * e4);
-      }
+      const f32x2 e2 =
+          *(const f32x2*)(sm.fw[tl] + kFwE + 4 * (32 * (lc / 4) + 8 * lg + 2 * (lc % 4)));
+      unroll8([&](auto kbc) {
+        constexpr int kb = decltype(kbc)::value;
+        dS[kb] = mma32h(qk[kb], bop, decay_rows<kb>(e2, dS[kb]));
+      });
     }
     // the next tile's start state, loaded before this tile's stores so that
     // its wait does not take them in
