@@ -655,27 +655,34 @@ __device__ __forceinline__ bf16x4 token_row4(const bf16_t* p, int64_t tok, int64
   return r;
 }
 
-// This wavefront's accumulators (lane (c, g) of block kb: rows chan(kb, 4 g + r),
-// column c) times f to row-major [channel][c] float32.
-__device__ __forceinline__ void split_bf16(float x, bf16_t* h, bf16_t* l) {
-  const bf16_t hv = (bf16_t)x;
-  *h = hv;
-  *l = (bf16_t)(x - (float)hv);
-}
-
 __device__ __forceinline__ f32x4 mma32b(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void stage_state(bf16_t* sh, bf16_t* sl, const f32x4 (&z)[8], float f,
-                                            int lane) {
+// Pairs x = h + l with h = bfloat16(x), l = bfloat16(x - h) (x = h + l to
+// about 2^-17 relative), two values per conversion.
+__device__ __forceinline__ void split2(f32x2 x, bf16x2& h, bf16x2& l) {
+  h = __builtin_convertvector(x, bf16x2);
+  l = __builtin_convertvector(x - __builtin_convertvector(h, f32x2), bf16x2);
+}
+
+// This wavefront's accumulators (lane (c, g) of block kb: rows chan(kb, 4 g + r),
+// column c) to row-major [channel][c] bfloat16 pairs, as held (the caller
+// moves the wavefront's scale onto the other operand of each product; a
+// power-of-two factor commutes with the bfloat16 rounding).
+__device__ __forceinline__ void stage_state(bf16_t* sh, bf16_t* sl, const f32x4 (&z)[8], int lane) {
   const int lc = lane % 16, lg = lane / 16;
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = rec::chan(kb, 4 * lg + r) * 16 + lc;
-      split_bf16(z[kb][r] * f, sh + i, sl + i);
+    for (int r = 0; r < 4; r += 2) {
+      bf16x2 h, l;
+      split2(f32x2{z[kb][r], z[kb][r + 1]}, h, l);
+      const int i = rec::chan(kb, 4 * lg + r) * 16 + lc;  // rows r, r + 1: channels i, i + 1
+      sh[i] = h[0];
+      sh[i + 16] = h[1];
+      sl[i] = l[0];
+      sl[i + 16] = l[1];
     }
 }
 
@@ -683,9 +690,14 @@ __device__ __forceinline__ void stage_state(bf16_t* sh, bf16_t* sl, const f32x4 
 // row-major bfloat16 pairs.
 __device__ __forceinline__ void stage_small(bf16_t* sh, bf16_t* sl, f32x4 z, float f, int lane) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < 4; r += 2) {
+    bf16x2 h, l;
+    split2(f32x2{z[r] * f, z[r + 1] * f}, h, l);
     const int i = (4 * (lane / 16) + r) * 16 + lane % 16;
-    split_bf16(z[r] * f, sh + i, sl + i);
+    sh[i] = h[0];
+    sh[i + 16] = h[1];
+    sl[i] = l[0];
+    sl[i + 16] = l[1];
   }
 }
 
@@ -785,7 +797,10 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
     // their products as float16 pairs (value and rounding error).
     Scale sf;
     f32x4 X = zero4(), Dl = zero4();
-    for (int u = 0; u <= tl; ++u) {
+    // unrolled, so that vrow[u] is a register and not a select over the array
+#pragma unroll
+    for (int u = 0; u < kBlkTiles; ++u) {
+      if (u > tl) break;
       const unsigned char* Ru = sm.fw[u];
       const f32x4 vs = rescale(sf, S, mma16b(vrow[u], ident, zero4()));
       f16x8 sopS[4];
@@ -863,10 +878,12 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
     // ---- the products over the 128 value columns, float32: every chunk
     // staged unscaled, then wavefront w forms output columns 16 w .. 16 w + 15
     // (channels) summing the chunks in order
-    stage_state(sm.sth[wave], sm.stl[wave], S, ff, lane);
-    stage_small(sm.sxh[wave][0], sm.sxl[wave][0], dos, fd, lane);
-    stage_small(sm.sxh[wave][1], sm.sxl[wave][1], dx, fd, lane);
-    stage_small(sm.sxh[wave][2], sm.sxl[wave][2], Dl, ff, lane);
+    // S as held (sigma_f S): its factor ff moves to dO' and dX; Delta as held
+    // for dO' Delta^T, with dO' carrying ff (ff is a power of two)
+    stage_state(sm.sth[wave], sm.stl[wave], S, lane);
+    stage_small(sm.sxh[wave][0], sm.sxl[wave][0], dos, fd * ff, lane);
+    stage_small(sm.sxh[wave][1], sm.sxl[wave][1], dx, fd * ff, lane);
+    stage_small(sm.sxh[wave][2], sm.sxl[wave][2], Dl, 1.f, lane);
     stage_small(sm.sxh[wave][3], sm.sxl[wave][3], dd, fd, lane);
     stage_small(sm.sxh[wave][4], sm.sxl[wave][4], X, ff, lane);
     lds_barrier();
@@ -894,13 +911,19 @@ __global__ void __launch_bounds__(512, 1) kda_bwd_block_kernel(BlockArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) qk[kb] = ld16h(R + kQK + kb * 1024 + lane * 16);
     lds_barrier();
-    stage_state(sm.sth[wave], sm.stl[wave], dS, fd, lane);
+    // dS' as held: its factor fd moves to Delta
+    stage_state(sm.sth[wave], sm.stl[wave], dS, lane);
+    stage_small(sm.sxh[wave][2], sm.sxl[wave][2], Dl, ff * fd, lane);
     lds_barrier();
     const f32x4 y3 = prod128(sm.sxh[0][2], sm.sxl[0][2], kXs, sm.sth[0] + srow, sm.stl[0] + srow,
                              kSs, lane);  // Delta dS'^T
-    // dV = dX: lane (t, g) holds the four columns from rc0 on of token t
-    // (the staged h of dX is its bfloat16 rounding)
-    const bf16x4 dvo = *(const bf16x4*)&sm.sxh[wave][1][lc * 16 + 4 * lg];
+    // dV = dX in bfloat16: lane (t, g) holds the four columns from rc0 on of
+    // token t, moved there by the selection-matrix product (exact: the
+    // operand is already bfloat16)
+    const f32x4 dvt = mma16b(
+        bf16x4{(bf16_t)(dx[0] * fd), (bf16_t)(dx[1] * fd), (bf16_t)(dx[2] * fd), (bf16_t)(dx[3] * fd)},
+        ident, zero4());
+    const bf16x4 dvo = {(bf16_t)dvt[0], (bf16_t)dvt[1], (bf16_t)dvt[2], (bf16_t)dvt[3]};
     // dS' of the tile before (the adjoint of this tile's start state)
     {
       const f16x8 bop = cat8(do16, to_h4(dx));
