@@ -1092,36 +1092,45 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
   float kdkb = 0.f;
   bf16_t* __restrict__ dqp = a.dq;
   bf16_t* __restrict__ dkp = a.dk;
+  // the token index as a constant in each of the two copies, so that egr[t]
+  // and iegr[t] are registers (half is the same across a wavefront)
+  auto tokens = [&](auto hc) {
+    constexpr int kHalf = decltype(hc)::value;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int t = 8 * half + u;
-    float i1 = 0.f, i2 = 0.f, i3 = 0.f;
+    for (int u = 0; u < 8; ++u) {
+      const int t = 8 * kHalf + u;
+      float i1 = 0.f, i2 = 0.f, i3 = 0.f;
 #pragma unroll
-    for (int j4 = 0; j4 < kC / 4; ++j4) {
-      const f32x4 p4 = *(const f32x4*)&sm.dP[t][4 * j4], a4 = *(const f32x4*)&sm.dAq[t][4 * j4];
-      const f32x4 pt4 = *(const f32x4*)&sm.dPT[t][4 * j4], at4 = *(const f32x4*)&sm.dAqT[t][4 * j4];
+      for (int j4 = 0; j4 < kC / 4; ++j4) {
+        const f32x4 p4 = *(const f32x4*)&sm.dP[t][4 * j4], a4 = *(const f32x4*)&sm.dAq[t][4 * j4];
+        const f32x4 pt4 = *(const f32x4*)&sm.dPT[t][4 * j4], at4 = *(const f32x4*)&sm.dAqT[t][4 * j4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int jj = 4 * j4 + e;
-        i1 = fmaf(p4[e], kcr[jj], i1);   // (dP Kc)[t]:     jj < t
-        i2 = fmaf(a4[e], kcr[jj], i2);   // (dAqk Kc)[t]:   jj <= t
-        i3 = fmaf(at4[e], qhr[jj], fmaf(pt4[e], khr[jj], i3));  // (dAqk^T Qh + dP^T Kh)[t]
+        for (int e = 0; e < 4; ++e) {
+          const int jj = 4 * j4 + e;
+          i1 = fmaf(p4[e], kcr[jj], i1);   // (dP Kc)[t]:     jj < t
+          i2 = fmaf(a4[e], kcr[jj], i2);   // (dAqk Kc)[t]:   jj <= t
+          i3 = fmaf(at4[e], qhr[jj], fmaf(pt4[e], khr[jj], i3));  // (dAqk^T Qh + dP^T Kh)[t]
+        }
+      }
+      const float egt = egr[t], iegt = iegr[t];
+      const float dq = egt * (y1[u / 4][u % 4] + i2);
+      const float dkh = egt * (i1 - y2[u / 4][u % 4]);
+      const float dkc = iegt * i3;
+      const float dkb = egr[kC - 1] * iegt * y3[u / 4][u % 4];
+      const float kt = sm.k[t][c];
+      kdkb = fmaf(kt, dkb, kdkb);
+      sm.dG[t][c] = kt * (dkh - dkc - dkb) + sm.q[t][c] * dq;
+      if (valid(t)) {
+        const int64_t r = row_of(t);
+        dqp[r * kDK + c] = (bf16_t)dq;
+        dkp[r * kDK + c] = (bf16_t)(dkh + dkc + dkb);
       }
     }
-    const float egt = egr[t], iegt = iegr[t];
-    const float dq = egt * (y1[u / 4][u % 4] + i2);
-    const float dkh = egt * (i1 - y2[u / 4][u % 4]);
-    const float dkc = iegt * i3;
-    const float dkb = egr[kC - 1] * iegt * y3[u / 4][u % 4];
-    const float kt = sm.k[t][c];
-    kdkb = fmaf(kt, dkb, kdkb);
-    sm.dG[t][c] = kt * (dkh - dkc - dkb) + sm.q[t][c] * dq;
-    if (valid(t)) {
-      const int64_t r = row_of(t);
-      dqp[r * kDK + c] = (bf16_t)dq;
-      dkp[r * kDK + c] = (bf16_t)(dkh + dkc + dkb);
-    }
-  }
+  };
+  if (__builtin_amdgcn_readfirstlane(half) == 0)
+    tokens(std::integral_constant<int, 0>{});
+  else
+    tokens(std::integral_constant<int, 1>{});
   sm.kdkb[half][c] = kdkb;
   lds_barrier();
   if (tid < kDK) {  // dG_15 += sum_rows k dk_b + dE E, then dg = reverse cumulative sum
