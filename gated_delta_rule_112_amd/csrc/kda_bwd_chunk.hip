@@ -34,9 +34,9 @@
 //      tokens (a block of four tiles);
 //   2. kda_bwd_rec_kernel: per tile and in parallel, the operands of the two
 //      chains (the record below), as float16 matrix-core operand images;
-//   3. kda_bwd_chain_kernel: per head, the tiles last to first, dS' resident
-//      in matrix-core accumulators; it keeps dS' at the end of every block
-//      and returns dS_0;
+//   3. kda_bwd_chain_kernel: per head (its value columns split over four
+//      workgroups), the tiles last to first, dS' resident in matrix-core
+//      accumulators; it keeps dS' at the end of every block and returns dS_0;
 //   4. kda_bwd_block_kernel: per head and block, in parallel: for each tile
 //      of the block (last to first) the forward state recomputed from the
 //      block's start state, the tile's adjoint step, the products Y1, Y2, Y3,
