@@ -487,9 +487,17 @@ kda_state_kernel(const unsigned char* __restrict__ recs, const bf16_t* __restric
         ek = exp_of(((const float*)(Rs + rec::kNorm))[32]);
         ek = ek > 0 ? ek : 0;
       }
-      int em = exp_of(wave_max_nonneg(fmaxf(m0, m1)));
+      // The scale stays when the largest magnitude times 2^ek lies in
+      // [2^kLoExp, 2^(kHiExp + 1)) or every value is zero: three lane votes;
+      // the reduction across lanes only when it moves.
+      const float mm = fmaxf(m0, m1), fk = exp2i(-ek);
+      const bool kept =
+          __builtin_amdgcn_ballot_w64(mm >= (float)(1 << (kHiExp + 1)) * fk) == 0 &&
+          (__builtin_amdgcn_ballot_w64(mm >= (float)(1 << kLoExp) * fk) != 0 ||
+           __builtin_amdgcn_ballot_w64(mm > 0.f) == 0);
+      int em = kept ? kNoExp : exp_of(wave_max_nonneg(mm));
       if (em != kNoExp) em += ek;
-      if (scale_shift(em, sh) != 0) {  // wave-uniform
+      if (!kept && scale_shift(em, sh) != 0) {  // wave-uniform
         float ms = 0.f, mv = 0.f;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
