@@ -71,10 +71,12 @@ def test_backward_matches_oracle(kda, dtype, B, T, H, with_s0, with_dsf):
 
 
 @pytest.mark.parametrize("B,T,H,with_s0,with_dsf", [(1, 300, 2, True, True), (2, 257, 3, False, False),
-                                                    (1, 16, 4, True, True), (1, 191, 1, False, True)])
+                                                    (1, 16, 4, True, True), (1, 191, 1, False, True),
+                                                    (2, 150, 6, True, True)])
 def test_backward_chunked_blocks(kda, B, T, H, with_s0, with_dsf):
     """The chunkwise pass (bfloat16) over several 64-token blocks, ragged last
-    tiles, one-tile sequences."""
+    tiles, one-tile sequences; 12 (b, h) chains: the adjoint chain's workgroups
+    of one group of 8 heads interleaved on the XCDs, then a last group of 4."""
     check(kda, torch.bfloat16, B, T, H, with_s0, with_dsf, 4100 + T + B)
 
 
