@@ -415,7 +415,8 @@ constexpr unsigned vmcnt_only(int n) {
 // frees its slot and the next tile is in LDS.  The workgroups of one head
 // get block indices equal modulo 8, which places them on one XCD (blocks are
 // dealt to the XCDs in turn), so that the head's records are read from HBM
-// once and from that XCD's L2 by the others.
+// once and from that XCD's L2 by the others (a matter of speed only: the
+// results do not depend on where the blocks run).
 __global__ void __launch_bounds__(64 * (kChainWaves + kChainLoaders), 1)
 kda_bwd_chain_kernel(ChainArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kChainRing][kChainSlot];
@@ -514,10 +515,10 @@ kda_bwd_chain_kernel(ChainArgs a) {
   lds_barrier();  // tile nt - 1 is in LDS
   for (int64_t x = a.nt - 1; x >= 0; --x) {
     const unsigned char* R = lds[x % kChainRing];
-    // All of the tile's operand reads first (15, as many as the LDS counter
-    // tracks), those of the first products first: their latency is then
-    // exposed once, and the state update's operands arrive during the
-    // dependent chain.
+    // All of the tile's operand reads first (16 with one column block: the
+    // first is waited for at the LDS counter's largest value, 15), those of
+    // the first products first: their latency is then exposed once, and the
+    // state update's operands arrive during the dependent chain.
     bf16x4 dor[kChainNcb];  // dO rows: lane (c, g): dO[c][4 g + e] of block n's columns
 #pragma unroll
     for (int n = 0; n < kChainNcb; ++n)
