@@ -12,24 +12,25 @@
 // The kernel is bound by HBM: every state element is read once and written
 // once (8 bytes per element per step).  A workgroup holds a float4 column
 // strip of RPT rows per thread in registers between the read and the in-place
-// write, so the write never re-reads memory.  The grid is persistent (one
-// workgroup per compute unit) and walks the (b, h) states with a stride of the
-// grid size; the next state and its per-token vectors are loaded into a
-// second register set while the current one is reduced and written, which
-// keeps reads in flight across the write phase.  Measured on MI355X this runs
-// closer to the read+write streaming ceiling than one workgroup per state.
+// write, so the write never re-reads memory.  One workgroup of 1024 threads
+// per (b, h) (four float4 per thread, two workgroups per compute unit):
+// measured on MI355X at B = 256, H = 96 this streams 2-4 % faster than a
+// persistent grid of one 256-thread workgroup per compute unit with the next
+// state loading into a second register set (0.577-0.581 against
+// 0.589-0.605 ms per step on one box), and than 256 or 512 threads per state.
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace kda {
 
-template <int DK, int DV>
+// W: the most threads per workgroup.
+template <int DK, int DV, int W = 256>
 struct DecodeShape {
   static constexpr int CG = DV / 4;                                   // float4 column groups
-  static constexpr int RG = (DK < 256 / CG) ? DK : 256 / CG;          // row groups
+  static constexpr int RG = (DK < W / CG) ? DK : W / CG;              // row groups
   static constexpr int RPT = DK / RG;                                 // rows per thread
   static constexpr int NT = CG * RG;                                  // threads per block
-  static_assert(NT <= 256 && NT % 64 == 0, "decode block must be whole wavefronts");
+  static_assert(NT <= W && NT <= 1024 && NT % 64 == 0, "decode block must be whole wavefronts");
   static_assert(RPT * RG == DK, "rows must split evenly");
   static_assert(NT >= DK && NT >= DV, "one thread per key channel and per value column");
 };
@@ -41,9 +42,9 @@ struct DecodeTok {
 };
 
 // One (b, h): its state strip and the per-token vectors of its next token.
-template <int DK, int DV>
+template <int DK, int DV, int W = 256>
 struct DecodeTile {
-  f32x4 s[DecodeShape<DK, DV>::RPT];
+  f32x4 s[DecodeShape<DK, DV, W>::RPT];
   DecodeTok x;
 };
 
@@ -75,15 +76,15 @@ __device__ __forceinline__ DecodeTok decode_load_tok(const IO* __restrict__ q,
 }
 
 // The state strip of (b, h) = bh and the inputs of token row `row`.
-template <int DK, int DV, typename IO>
-__device__ __forceinline__ void decode_load(DecodeTile<DK, DV>& t, const IO* __restrict__ q,
+template <int DK, int DV, typename IO, int W = 256>
+__device__ __forceinline__ void decode_load(DecodeTile<DK, DV, W>& t, const IO* __restrict__ q,
                                             const IO* __restrict__ k, const IO* __restrict__ v,
                                             const float* __restrict__ g,
                                             const float* __restrict__ beta,
                                             const float* __restrict__ state,
                                             const IO* __restrict__ gate, int64_t bh,
                                             int64_t row, const IO* __restrict__ ga) {
-  using Sh = DecodeShape<DK, DV>;
+  using Sh = DecodeShape<DK, DV, W>;
   const int tid = threadIdx.x;
   const int cg = tid % Sh::CG, rg = tid / Sh::CG;
   const float* Sp = state + bh * (int64_t)(DK * DV);
@@ -93,9 +94,9 @@ __device__ __forceinline__ void decode_load(DecodeTile<DK, DV>& t, const IO* __r
   t.x = decode_load_tok<DK, DV, IO>(q, k, v, g, beta, gate, row, ga);
 }
 
-template <int DK, int DV>
+template <int DK, int DV, int W = 256>
 struct DecodeSmem {
-  using Sh = DecodeShape<DK, DV>;
+  using Sh = DecodeShape<DK, DV, W>;
   float a[DK];         // a_i = exp(g_i)
   float kk[DK];        // k_i
   float ak[DK];        // a_i * k_i
@@ -110,13 +111,13 @@ struct DecodeSmem {
 // One token against the state strip s.  The updated state is stored to Sp
 // (the state of (b, h); NULL: not stored) and, with KEEP, kept in s for the
 // next token; the output row goes to orow (NULL: none).
-template <int DK, int DV, typename IO, bool KEEP>
-__device__ __forceinline__ void decode_one(DecodeSmem<DK, DV>& sm,
-                                           f32x4 (&s)[DecodeShape<DK, DV>::RPT],
+template <int DK, int DV, typename IO, bool KEEP, int W = 256>
+__device__ __forceinline__ void decode_one(DecodeSmem<DK, DV, W>& sm,
+                                           f32x4 (&s)[DecodeShape<DK, DV, W>::RPT],
                                            const DecodeTok& tin, float* __restrict__ Sp,
                                            IO* __restrict__ orow, bool gated, float wn,
                                            float eps, float scale, bool norm) {
-  using Sh = DecodeShape<DK, DV>;
+  using Sh = DecodeShape<DK, DV, W>;
   constexpr int CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT, NT = Sh::NT;
   const int tid = threadIdx.x;
   const int cg = tid % CG, rg = tid / CG;
@@ -227,37 +228,25 @@ __device__ __forceinline__ void decode_one(DecodeSmem<DK, DV>& sm,
   __syncthreads();
 }
 
-template <int DK, int DV, typename IO>
-__global__ void __launch_bounds__((DecodeShape<DK, DV>::NT), 1)
-kda_decode_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
-                  const float* __restrict__ g, const float* __restrict__ beta,
-                  float* __restrict__ state, IO* __restrict__ o,
-                  const IO* __restrict__ gate, const float* __restrict__ norm_w,
-                  float eps, float scale, int64_t BH, const IO* __restrict__ ga) {
-  __shared__ DecodeSmem<DK, DV> sm;
+// The single-token step: one workgroup of up to W threads per (b, h).
+constexpr int kDecodeThreads = 1024;
+template <int DK, int DV, typename IO, int W>
+__global__ void __launch_bounds__((DecodeShape<DK, DV, W>::NT))
+kda_decode_state_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
+                        const IO* __restrict__ v, const float* __restrict__ g,
+                        const float* __restrict__ beta, float* __restrict__ state,
+                        IO* __restrict__ o, const IO* __restrict__ gate,
+                        const float* __restrict__ norm_w, float eps, float scale,
+                        const IO* __restrict__ ga) {
+  __shared__ DecodeSmem<DK, DV, W> sm;
   const int tid = threadIdx.x;
   const bool gated = gate != nullptr;
   const float wn = (gated && norm_w != nullptr && tid < DV) ? norm_w[tid] : 1.f;
-  const int64_t stride = gridDim.x;
-
-  // Two register sets: while one state is reduced and written, the next is loading.
-  DecodeTile<DK, DV> t0, t1;
-  int64_t bh = blockIdx.x;
-  auto run = [&](DecodeTile<DK, DV>& t, int64_t u) {
-    decode_one<DK, DV, IO, false>(sm, t.s, t.x, state + u * (int64_t)(DK * DV), o + u * DV,
-                                  gated, wn, eps, scale, ga != nullptr);
-  };
-  if (bh < BH) decode_load<DK, DV, IO>(t0, q, k, v, g, beta, state, gate, bh, bh, ga);
-  while (bh < BH) {
-    const int64_t b1 = bh + stride;
-    if (b1 < BH) decode_load<DK, DV, IO>(t1, q, k, v, g, beta, state, gate, b1, b1, ga);
-    run(t0, bh);
-    if (b1 >= BH) break;
-    const int64_t b2 = b1 + stride;
-    if (b2 < BH) decode_load<DK, DV, IO>(t0, q, k, v, g, beta, state, gate, b2, b2, ga);
-    run(t1, b1);
-    bh = b2;
-  }
+  const int64_t bh = blockIdx.x;
+  DecodeTile<DK, DV, W> t;
+  decode_load<DK, DV, IO, W>(t, q, k, v, g, beta, state, gate, bh, bh, ga);
+  decode_one<DK, DV, IO, false, W>(sm, t.s, t.x, state + bh * (int64_t)(DK * DV), o + bh * DV,
+                                   gated, wn, eps, scale, ga != nullptr);
 }
 
 // K consecutive tokens of every (b, h) against its resident state: the state
@@ -271,18 +260,18 @@ kda_decode_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* 
 // few block-wide reductions) is latency-bound on one workgroup, so three
 // workgroups share a compute unit (one register set each, grid of three per
 // compute unit): measured on MI355X at B = 256, H = 96, K = 4 this verifies in
-// 0.63 ms against 1.55 ms with the single-token kernel's layout (one
-// double-buffered workgroup per compute unit); four or more per compute unit
+// 0.63 ms against 1.55 ms with one double-buffered workgroup per compute
+// unit; four or more per compute unit
 // were slower.  The next token's inputs load while a token is reduced.
-template <int DK, int DV, typename IO>
-__global__ void __launch_bounds__((DecodeShape<DK, DV>::NT), 1)
+template <int DK, int DV, typename IO, int W>
+__global__ void __launch_bounds__((DecodeShape<DK, DV, W>::NT), 1)
 kda_decode_multi_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
                         const IO* __restrict__ v, const float* __restrict__ g,
                         const float* __restrict__ beta, float* __restrict__ state,
                         const int* __restrict__ n_commit, IO* __restrict__ o,
                         const IO* __restrict__ gate, const float* __restrict__ norm_w, float eps,
                         float scale, int64_t B, int64_t K, int64_t H, const IO* __restrict__ ga) {
-  __shared__ DecodeSmem<DK, DV> sm;
+  __shared__ DecodeSmem<DK, DV, W> sm;
   const int tid = threadIdx.x;
   const bool gated = gate != nullptr;
   const float wn = (gated && norm_w != nullptr && tid < DV) ? norm_w[tid] : 1.f;
@@ -297,26 +286,27 @@ kda_decode_multi_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
   };
   auto runs = [&](int64_t u) { return o != nullptr ? K : commit(u); };
   // the state and first token of u, unless u has nothing to run
-  auto load = [&](DecodeTile<DK, DV>& t, int64_t u) {
-    if (runs(u) > 0) decode_load<DK, DV, IO>(t, q, k, v, g, beta, state, gate, u, row(u, 0), ga);
+  auto load = [&](DecodeTile<DK, DV, W>& t, int64_t u) {
+    if (runs(u) > 0)
+      decode_load<DK, DV, IO, W>(t, q, k, v, g, beta, state, gate, u, row(u, 0), ga);
   };
 
-  auto run = [&](DecodeTile<DK, DV>& cur, int64_t u) {
+  auto run = [&](DecodeTile<DK, DV, W>& cur, int64_t u) {
     const int64_t n = commit(u), last = runs(u);
     float* Sp = state + u * (int64_t)(DK * DV);
     DecodeTok x = cur.x;
     for (int64_t t = 0; t < last; ++t) {
       DecodeTok xn = x;
       if (t + 1 < last) xn = decode_load_tok<DK, DV, IO>(q, k, v, g, beta, gate, row(u, t + 1), ga);
-      decode_one<DK, DV, IO, true>(sm, cur.s, x, t + 1 == n ? Sp : nullptr,
-                                   o != nullptr ? o + row(u, t) * DV : nullptr, gated, wn, eps,
-                                   scale, ga != nullptr);
+      decode_one<DK, DV, IO, true, W>(sm, cur.s, x, t + 1 == n ? Sp : nullptr,
+                                      o != nullptr ? o + row(u, t) * DV : nullptr, gated, wn,
+                                      eps, scale, ga != nullptr);
       x = xn;
     }
   };
 
   for (int64_t u = blockIdx.x; u < BH; u += stride) {
-    DecodeTile<DK, DV> t;
+    DecodeTile<DK, DV, W> t;
     load(t, u);
     run(t, u);
   }
@@ -533,17 +523,18 @@ kda_multi_chunk_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
   }
 }
 
+// The compute units of the device, at most `units`: the multi-token kernels'
+// persistent grids are a multiple of it.
 int decode_grid(int64_t units) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (cus < 1) cus = 256;
-  return (int)(units < cus ? units : cus);  // one persistent workgroup per compute unit
+  return (int)(units < cus ? units : cus);
 }
 
 template <int DK, int DV, typename IO>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
-  using Sh = DecodeShape<DK, DV>;
   const int64_t bhn = a.B * a.H;
   const int nblk = decode_grid(bhn);
   if (a.K >= 2 && a.K <= 4 && a.o != nullptr && DK == 128 && DV == 128) {
@@ -557,17 +548,26 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
     return hipGetLastError();
   }
   if (a.K > 0) {
-    const int64_t mblk = bhn < 3 * (int64_t)nblk ? bhn : 3 * (int64_t)nblk;  // three per CU
-    hipLaunchKernelGGL((kda_decode_multi_kernel<DK, DV, IO>), dim3((unsigned)mblk), dim3(Sh::NT),
-                       0, (hipStream_t)a.stream, (const IO*)a.q, (const IO*)a.k, (const IO*)a.v,
-                       a.g, a.beta, a.state, a.n_commit, (IO*)a.o, (const IO*)a.gate, a.norm_w,
-                       a.eps, a.scale, a.B, a.K, a.H, (const IO*)a.ga);
+    // three persistent 256-thread workgroups per CU: the chain of token steps
+    // is latency-bound, and the single-token step's shape (one 1024-thread
+    // workgroup per state) measured 0.81 against 0.52 ms for the commit call
+    // at B = 256, H = 96, K = 4
+    const int64_t mblk = bhn < 3 * (int64_t)nblk ? bhn : 3 * (int64_t)nblk;
+    constexpr int MW = 256;
+    using Sm = DecodeShape<DK, DV, MW>;
+    hipLaunchKernelGGL((kda_decode_multi_kernel<DK, DV, IO, MW>), dim3((unsigned)mblk),
+                       dim3(Sm::NT), 0, (hipStream_t)a.stream, (const IO*)a.q, (const IO*)a.k,
+                       (const IO*)a.v, a.g, a.beta, a.state, a.n_commit, (IO*)a.o,
+                       (const IO*)a.gate, a.norm_w, a.eps, a.scale, a.B, a.K, a.H,
+                       (const IO*)a.ga);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((kda_decode_kernel<DK, DV, IO>), dim3((unsigned)nblk), dim3(Sh::NT), 0,
-                     (hipStream_t)a.stream, (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g,
-                     a.beta, a.state, (IO*)a.o, (const IO*)a.gate, a.norm_w, a.eps, a.scale, bhn,
-                     (const IO*)a.ga);
+  if (bhn < 1 || bhn > 0x7fffffffLL) return hipErrorInvalidValue;
+  using Sw = DecodeShape<DK, DV, kDecodeThreads>;
+  hipLaunchKernelGGL((kda_decode_state_kernel<DK, DV, IO, kDecodeThreads>), dim3((unsigned)bhn),
+                     dim3(Sw::NT), 0, (hipStream_t)a.stream, (const IO*)a.q, (const IO*)a.k,
+                     (const IO*)a.v, a.g, a.beta, a.state, (IO*)a.o, (const IO*)a.gate, a.norm_w,
+                     a.eps, a.scale, (const IO*)a.ga);
   return hipGetLastError();
 }
 

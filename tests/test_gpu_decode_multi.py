@@ -104,8 +104,12 @@ def test_decode_multi_negative_count_and_default(kda):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_decode_multi_k1_equals_decode_step(kda, dtype):
-    """K = 1 with every token committed computes what kda_decode_step does, with
-    the same arithmetic: bit-identical outputs and states."""
+    """K = 1 with every token committed computes what kda_decode_step does.  The
+    two kernels split a state over different workgroup shapes (256 threads per
+    state in the multi-token kernel, 1024 in the single-token one), so each
+    column's dk-term sums are added in another order: the results agree to the
+    float32 rounding of those sums (states within 1e-5 x RMS, outputs within
+    one ulp of the io dtype where it is bfloat16), not bit for bit."""
     B, H, dk, dv = 4, 5, 128, 128
     q, k, v, g, beta, state, gate = gen(B, 1, H, dk, dv, dtype, 620, gate=True)
     st1, st2 = state.clone(), state.clone()
@@ -113,8 +117,15 @@ def test_decode_multi_k1_equals_decode_step(kda, dtype):
     o2 = kda.decode_step(*(x[:, 0].contiguous() for x in (q, k, v, g, beta)), st2,
                          gate=gate[:, 0].contiguous())
     torch.cuda.synchronize()
-    assert torch.equal(o1[:, 0], o2)
-    assert torch.equal(st1, st2)
+    assert_close(f64(st2), f64(st1), STATE_TOL, "state, single-token vs K = 1")
+    a, b = o1[:, 0].double(), o2.double()
+    if dtype == torch.bfloat16:
+        # one bfloat16 ulp of the larger magnitude (8 significant bits)
+        ulp = torch.maximum(a.abs(), b.abs()) * 2.0 ** -7
+        assert bool(((a - b).abs() <= ulp).all()), "outputs differ by more than one ulp"
+        assert (a != b).double().mean().item() < 0.05, "more than 5% of outputs differ"
+    else:
+        assert_close(f64(o2), f64(o1[:, 0]), 1e-5, "o, single-token vs K = 1")
 
 
 def test_decode_multi_verify_then_commit(kda):
