@@ -60,7 +60,10 @@ __device__ __forceinline__ DecodeTok decode_load_tok(const IO* __restrict__ q,
                                                      const IO* __restrict__ ga) {
   const int tid = threadIdx.x;
   const int ci = tid % DK, cj = tid % DV;
-  DecodeTok x;
+  DecodeTok x{};
+  // only the threads of a key channel or a value column use these (the first
+  // max(dk, dv)); the others load nothing (wave-uniform when dk, dv >= 64)
+  if (tid >= (DK > DV ? DK : DV)) return x;
   x.q = ld_f32(q + row * DK + ci);
   x.k = ld_f32(k + row * DK + ci);
   x.v = ld_f32(v + row * DV + cj);
