@@ -154,7 +154,7 @@ kda_status recurrent_bwd(const void* q, const void* k, const void* v, const floa
   // otherwise (and with KDA_BWD_TOKEN=1) the token-serial vector kernel
   bool tok_aligned = true;
   for (const void* p : {q, k, v, dout, (const void*)g, (const void*)dq, (const void*)dk_out,
-                        (const void*)dv_out})
+                        (const void*)dv_out, (const void*)dg})
     tok_aligned = tok_aligned && aligned(p, 16);
   if (with_ckpt && !tok_aligned) return KDA_ERR_MISALIGNED;
   const bool chunk = with_ckpt || (io == KDA_BF16 && !force_token_bwd() && tok_aligned);

@@ -976,6 +976,7 @@ struct FinSmem {
   __attribute__((aligned(16))) float dP[kC][kC], dAq[kC][kC], dPT[kC][kC], dAqT[kC][kC];
   float beta[kC], dbT[kC], dbA[kC];
   float kdkb[2][kDK];
+  __attribute__((aligned(16))) bf16_t dqo[kC][kDK], dko[kC][kDK];  // dq, dk on their way out
 };
 
 // One workgroup per tile (256 threads), float32 throughout.  Every global
@@ -1010,25 +1011,21 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
     y2[m] = *(const f32x4*)(Y + kY2 + o);
     y3[m] = *(const f32x4*)(Y + kY3 + o);
   }
-  // the tile's inputs: element e = tid + 256 m is (token e / 128, channel e % 128)
+  // the tile's inputs, 16-byte accesses: thread tid takes token tid / 16,
+  // channels c8 .. c8 + 7 (the same split stores dq, dk and dg at the end)
+  const int t8 = tid / 16, c8 = 8 * (tid % 16);
   {
-    float kv[8], qv[8], gv[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int e = tid + 256 * m, t = e / kDK, c = e % kDK;
-      const int64_t r = row_of(t);
-      kv[m] = (float)kp[r * kDK + c];
-      qv[m] = (float)qp[r * kDK + c];
-      gv[m] = gp[r * kDK + c];
-    }
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int e = tid + 256 * m, t = e / kDK, c = e % kDK;
-      const float lv = valid(t) ? 1.f : 0.f;
-      sm.k[t][c] = kv[m] * lv;
-      sm.q[t][c] = qv[m] * lv;
-      sm.dG[t][c] = gv[m] * lv;  // g for now
-    }
+    const int64_t r = row_of(t8);
+    const bf16x8 kv = *(const bf16x8*)(kp + r * kDK + c8);
+    const bf16x8 qv = *(const bf16x8*)(qp + r * kDK + c8);
+    const f32x4 g0 = *(const f32x4*)(gp + r * kDK + c8), g1 = *(const f32x4*)(gp + r * kDK + c8 + 4);
+    const float lv = valid(t8) ? 1.f : 0.f;
+    *(f32x4*)&sm.k[t8][c8] = f32x4{(float)kv[0], (float)kv[1], (float)kv[2], (float)kv[3]} * lv;
+    *(f32x4*)&sm.k[t8][c8 + 4] = f32x4{(float)kv[4], (float)kv[5], (float)kv[6], (float)kv[7]} * lv;
+    *(f32x4*)&sm.q[t8][c8] = f32x4{(float)qv[0], (float)qv[1], (float)qv[2], (float)qv[3]} * lv;
+    *(f32x4*)&sm.q[t8][c8 + 4] = f32x4{(float)qv[4], (float)qv[5], (float)qv[6], (float)qv[7]} * lv;
+    *(f32x4*)&sm.dG[t8][c8] = g0 * lv;  // g for now
+    *(f32x4*)&sm.dG[t8][c8 + 4] = g1 * lv;
     const int i = tid / kC, j = tid % kC;
     sm.P[i][j] = PM[tid];
     sm.M[i][j] = PM[256 + tid];
@@ -1091,8 +1088,6 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
     qhr[jj] = sm.q[jj][c] * egr[jj];
   }
   float kdkb = 0.f;
-  bf16_t* __restrict__ dqp = a.dq;
-  bf16_t* __restrict__ dkp = a.dk;
   // the token index as a constant in each of the two copies, so that egr[t]
   // and iegr[t] are registers (half is the same across a wavefront)
   auto tokens = [&](auto hc) {
@@ -1121,11 +1116,8 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
       const float kt = sm.k[t][c];
       kdkb = fmaf(kt, dkb, kdkb);
       sm.dG[t][c] = kt * (dkh - dkc - dkb) + sm.q[t][c] * dq;
-      if (valid(t)) {
-        const int64_t r = row_of(t);
-        dqp[r * kDK + c] = (bf16_t)dq;
-        dkp[r * kDK + c] = (bf16_t)(dkh + dkc + dkb);
-      }
+      sm.dqo[t][c] = (bf16_t)dq;
+      sm.dko[t][c] = (bf16_t)(dkh + dkc + dkb);
     }
   };
   if (__builtin_amdgcn_readfirstlane(half) == 0)
@@ -1136,15 +1128,25 @@ __global__ void __launch_bounds__(256) kda_bwd_fin_kernel(FinArgs a) {
   lds_barrier();
   if (tid < kDK) {  // dG_15 += sum_rows k dk_b + dE E, then dg = reverse cumulative sum
     float acc = sm.kdkb[0][c] + sm.kdkb[1][c] + Y[kDE + c] * egr[kC - 1];
-    float* __restrict__ dgp = a.dg;
 #pragma unroll
     for (int t = kC - 1; t >= 0; --t) {
       acc += sm.dG[t][c];
-      if (valid(t)) dgp[row_of(t) * kDK + c] = acc;
+      sm.dG[t][c] = acc;
     }
   } else if (tid < kDK + kC) {
     const int t = tid - kDK;
     if (valid(t)) a.dbeta[row_of(t)] = sm.dbT[t] + sm.dbA[t];
+  }
+  const bool live8 = valid(t8);
+  const int64_t r8 = row_of(t8);
+  if (live8) {
+    *(bf16x8*)(a.dq + r8 * kDK + c8) = *(const bf16x8*)&sm.dqo[t8][c8];
+    *(bf16x8*)(a.dk + r8 * kDK + c8) = *(const bf16x8*)&sm.dko[t8][c8];
+  }
+  lds_barrier();
+  if (live8) {
+    *(f32x4*)(a.dg + r8 * kDK + c8) = *(const f32x4*)&sm.dG[t8][c8];
+    *(f32x4*)(a.dg + r8 * kDK + c8 + 4) = *(const f32x4*)&sm.dG[t8][c8 + 4];
   }
 }
 

@@ -389,12 +389,12 @@ kda_status kda_gate_rmsnorm(const void* x, const void* gate, const float* norm_w
  * The state is recomputed from checkpoints every 64 tokens held in the workspace.
  *
  * Two kernels, chosen per call:
- *   bfloat16 io with q, k, v, dout, g, dq, dk, dv all 16-byte aligned: the chunkwise
+ *   bfloat16 io with q, k, v, dout, g, dq, dk, dv, dg all 16-byte aligned: the chunkwise
  *     pass on the matrix cores (16-token tiles; float16 operands with float32
  *     accumulation, the last tile's final-state terms as float16 value-and-rounding
  *     pairs).  Each gradient is within 2e-2 x its RMS of the float64 gradients (dq, dk,
  *     dv net of half a bfloat16 ulp), the forward's bfloat16-input bar.  Deterministic.
- *   otherwise (float32 io, or a bfloat16 tensor not 16-byte aligned, or the environment
+ *   otherwise (float32 io, or one of those tensors not 16-byte aligned, or the environment
  *     variable KDA_BWD_TOKEN=1): a token-serial float32 vector kernel, within 1e-4 x RMS.
  *
  *   q, k, v, dout     [B, T, H, 128]  io dtype
@@ -427,7 +427,7 @@ kda_status kda_recurrent_bwd(const void* q, const void* k, const void* v, const 
  *          ckpt_every = 64 writes it over the same q, k, v, g, beta and s0 (not
  *          checked: other states give the gradients of another forward).  16-byte
  *          aligned; must not overlap an output.  Read only when T > 64.
- * bfloat16 io with q, k, v, dout, g, dq, dk, dv 16-byte aligned only (the chunkwise
+ * bfloat16 io with q, k, v, dout, g, dq, dk, dv, dg 16-byte aligned only (the chunkwise
  * pass): else KDA_ERR_BAD_DTYPE or KDA_ERR_MISALIGNED.  The workspace is the one
  * kda_recurrent_bwd_workspace_size gives.  With the forward's own checkpoints the
  * gradients equal kda_recurrent_bwd's.

@@ -343,13 +343,14 @@ def test_recurrent_bwd_ckpt_validation(lib):
     B, T, H = 1, 256, 2
     need = lib.kda_recurrent_bwd_workspace_size(B, T, H, 128, 128)
 
-    def call(ck=16, io=1, q=P(1), dq=9):
+    def call(ck=16, io=1, q=P(1), dq=9, dg=P(12)):
         a = {i: P(i) for i in range(1, 17)}
         return f(q, a[2], a[3], a[4], a[5], a[6], a[7], a[8], None if ck is None else P(ck),
-                 P(dq), a[10], a[11], a[12], a[13], a[14], B, T, H, 128, 128, 1.0, io, a[15],
+                 P(dq), a[10], a[11], dg, a[13], a[14], B, T, H, 128, 128, 1.0, io, a[15],
                  need, None)
 
     assert call(ck=None) == NULLP
     assert call(io=0) == DTYPE                         # float32: no chunkwise pass
     assert call(q=P(1, 8)) == ALIGN                    # 8 bytes off: not the chunkwise layout
+    assert call(dg=P(12, 4)) == ALIGN                  # dg float32-aligned, not 16-byte
     assert call(ck=9) == ALIAS                         # checkpoints under dq
