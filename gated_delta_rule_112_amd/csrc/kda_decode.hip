@@ -17,7 +17,9 @@
 // measured on MI355X at B = 256, H = 96 this streams 2-4 % faster than a
 // persistent grid of one 256-thread workgroup per compute unit with the next
 // state loading into a second register set (0.577-0.581 against
-// 0.589-0.605 ms per step on one box), and than 256 or 512 threads per state.
+// 0.589-0.605 ms per step on one box), and than 256 or 512 threads per state;
+// loading the token's vectors in the first 128 threads only (the others never
+// use them) then took it to 0.566-0.571 ms.
 #include "kda_device.h"
 #include "kda_launch.h"
 
