@@ -86,6 +86,38 @@ def test_backward_token_kernel_bf16(kda, monkeypatch):
     check(kda, torch.bfloat16, 2, 70, 2, True, True, 4200)
 
 
+def test_backward_misaligned_dg_takes_token_kernel(kda):
+    """dg only float32-aligned (one element into a buffer): the chunkwise pass,
+    which stores dg 16 bytes at a time, is not taken; the call runs the
+    token-serial kernel and every gradient still matches the oracle."""
+    from gated_delta_rule_112_amd import _lib as L
+    B, T, H, D = 1, 70, 2, 128
+    q, k, v, g, beta, do, s0, dsf = gen(B, T, H, torch.bfloat16, 4250, True, True)
+    lib = kda.load_library()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dgbuf = torch.empty(g.numel() + 4, dtype=torch.float32, device=dev())
+    dg = dgbuf[1:1 + g.numel()].view(g.shape)
+    assert dg.data_ptr() % 16 == 4
+    dbeta = torch.empty_like(beta)
+    ds0 = torch.empty((B, H, D, D), dtype=torch.float32, device=dev())
+    nws = lib.kda_recurrent_bwd_workspace_size(B, T, H, D, D)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev())
+    print(f"backward case misaligned dg B={B} T={T} H={H}", flush=True)
+    st = lib.kda_recurrent_bwd(L._ptr(q), L._ptr(k), L._ptr(v), L._ptr(g), L._ptr(beta),
+                               L._ptr(s0), L._ptr(do), L._ptr(dsf), L._ptr(dq), L._ptr(dk),
+                               L._ptr(dv), L._ptr(dg), L._ptr(dbeta), L._ptr(ds0), B, T, H, D, D,
+                               0.7, L._IO[torch.bfloat16], L._ptr(ws), ws.numel(),
+                               L._stream(dev(), None))
+    L._check(lib, "kda_recurrent_bwd", st)
+    torch.cuda.synchronize()
+    ref = kda_recurrent_vjp(f64(q), f64(k), f64(v), f64(g), f64(beta), f64(s0), f64(do),
+                            f64(dsf), 0.7)
+    for name, x in zip(["dq", "dk", "dv", "dg", "dbeta", "ds0"], (dq, dk, dv, dg, dbeta, ds0)):
+        io_out = name in ("dq", "dk", "dv")
+        assert_close(f64(x), ref[name], TOL[torch.bfloat16], f"{name} misaligned dg",
+                     torch.bfloat16 if io_out else None)
+
+
 def test_backward_scale_zero(kda):
     """scale = 0: the outputs carry no gradient; only the final-state term flows.
     With the workloads' decay (g = -5 sigmoid(N(0,1))) that term reaches the

@@ -65,7 +65,7 @@ def oracle_prefill(q, k, v, g, beta, s0, gate, scale=1.0, eps=1e-6, norm_w=None)
 
 
 # ----------------------------------------------------------------------------- decode
-@pytest.mark.parametrize("dk,dv", [(16, 16), (64, 32), (32, 128), (128, 128)])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (64, 32), (128, 16), (32, 128), (128, 128)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("with_gate", [False, True])
 def test_decode_matches_oracle(kda, dk, dv, dtype, with_gate):
